@@ -1,0 +1,192 @@
+"""Seeded synthetic convolution workloads.
+
+This module only draws random tensors and describes layer shapes. It holds none of the
+quantization or convolution arithmetic: both the GPU library's tests/benchmark and the CPU
+oracle take their inputs from here, and nothing else is shared between them.
+
+Shapes follow the layer types the MicroQonv pages experiment with (onedev.kr paper digest,
+sections "How it is used" and "Premises and limits": ResNet-18 style 3x3 bodies, YOLO-nano style
+stacks with a large share of 1x1 convolutions, NVFP4 / NVFP6 element formats). The public
+datasets the pages train on are not available, so every tensor is synthetic:
+
+* activations X: ReLU or SiLU of N(0,1), or a heavy-tailed Student-t(3) scaled by 0.5
+* weights W: Kaiming-normal, std = sqrt(2 / (Cin*Kh*Kw))
+* output gradients G_Y: N(0, 1e-3)
+
+Generation is numpy ``Generator(PCG64(seed))`` in float64, drawn in the order X, W, G_Y, then
+cast to float32. Tensors come out in the framework layouts NCHW (X, G_Y) and OIHW (W).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Tuple
+
+import numpy as np
+
+FP4 = 4  # NVFP4: E2M1 elements, E4M3 scale per 4x4 square, fp32 tensor scale
+FP6 = 6  # NVFP6: E2M3 elements, same scaling
+
+
+@dataclasses.dataclass(frozen=True)
+class ConvLayer:
+    """One convolution layer's shape and the recipe for its synthetic tensors."""
+
+    name: str
+    N: int
+    Cin: int
+    H: int
+    W: int
+    Cout: int
+    Kh: int
+    Kw: int
+    stride: int = 1
+    pad: int = 0
+    fmt: int = FP4
+    x_dist: str = "normal"      # normal | relu | silu | t3
+    w_dist: str = "kaiming"     # normal | kaiming
+    g_dist: str = "normal1e-3"  # normal | normal1e-3
+    seed: int = 0
+    sr_seed: int = 1
+
+    @property
+    def Ho(self) -> int:
+        return (self.H + 2 * self.pad - self.Kh) // self.stride + 1
+
+    @property
+    def Wo(self) -> int:
+        return (self.W + 2 * self.pad - self.Kw) // self.stride + 1
+
+    def gemm_flops(self) -> int:
+        """2*Cout*Cin*Kh*Kw*N*Ho*Wo: the algorithmic flop count of one of the three GEMMs."""
+        return 2 * self.Cout * self.Cin * self.Kh * self.Kw * self.N * self.Ho * self.Wo
+
+    def conv_tuple(self) -> Tuple[int, ...]:
+        """(N, Cin, H, W, Cout, Kh, Kw, stride_h, stride_w, pad_h, pad_w)."""
+        return (self.N, self.Cin, self.H, self.W, self.Cout, self.Kh, self.Kw,
+                self.stride, self.stride, self.pad, self.pad)
+
+
+def _draw(rng: np.random.Generator, shape, dist: str, fan_in: int) -> np.ndarray:
+    if dist == "normal":
+        a = rng.standard_normal(shape)
+    elif dist == "relu":
+        a = np.maximum(rng.standard_normal(shape), 0.0)
+    elif dist == "silu":
+        z = rng.standard_normal(shape)
+        a = z / (1.0 + np.exp(-z))
+    elif dist == "t3":
+        a = 0.5 * rng.standard_t(3.0, size=shape)
+    elif dist == "kaiming":
+        a = rng.standard_normal(shape) * np.sqrt(2.0 / fan_in)
+    elif dist == "normal1e-3":
+        a = rng.standard_normal(shape) * 1e-3
+    else:
+        raise ValueError(f"unknown distribution {dist!r}")
+    return a.astype(np.float32)
+
+
+def make_tensors(layer: ConvLayer):
+    """Return (X [N,Cin,H,W], W [Cout,Cin,Kh,Kw], G_Y [N,Cout,Ho,Wo]) as float32 numpy arrays."""
+    rng = np.random.Generator(np.random.PCG64(layer.seed))
+    fan_in = layer.Cin * layer.Kh * layer.Kw
+    x = _draw(rng, (layer.N, layer.Cin, layer.H, layer.W), layer.x_dist, fan_in)
+    w = _draw(rng, (layer.Cout, layer.Cin, layer.Kh, layer.Kw), layer.w_dist, fan_in)
+    g = _draw(rng, (layer.N, layer.Cout, layer.Ho, layer.Wo), layer.g_dist, fan_in)
+    return x, w, g
+
+
+def random_array(shape, seed: int, dist: str = "normal", fan_in: int = 1) -> np.ndarray:
+    """A single seeded float32 array (used by unit tests for shapes outside the layer list)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return _draw(rng, shape, dist, fan_in)
+
+
+# --- the five workloads -------------------------------------------------------------------
+
+def config1() -> List[ConvLayer]:
+    """Single 3x3 conv, stride 1, no padding, N=2, 16->16 channels at 8x8, NVFP4."""
+    return [ConvLayer("c1", N=2, Cin=16, H=8, W=8, Cout=16, Kh=3, Kw=3, stride=1, pad=0,
+                      fmt=FP4, x_dist="normal", w_dist="normal", g_dist="normal",
+                      seed=0, sr_seed=1)]
+
+
+def config2() -> List[ConvLayer]:
+    """ResNet-style 3x3 conv, stride 1, pad 1, N=32, 64->64 channels at 56x56, NVFP4."""
+    return [ConvLayer("c2", N=32, Cin=64, H=56, W=56, Cout=64, Kh=3, Kw=3, stride=1, pad=1,
+                      fmt=FP4, x_dist="relu", seed=2, sr_seed=1)]
+
+
+def config3() -> List[ConvLayer]:
+    """Strided 3x3 conv, stride 2, pad 1, N=64, 128->256 channels, 28x28 -> 14x14, NVFP4."""
+    return [ConvLayer("c3", N=64, Cin=128, H=28, W=28, Cout=256, Kh=3, Kw=3, stride=2, pad=1,
+                      fmt=FP4, x_dist="t3", seed=3, sr_seed=1)]
+
+
+def config4() -> List[ConvLayer]:
+    """YOLO-nano-like stack of 8 convs at N=16 (3 of 8 are 1x1), 160x160 -> 20x20, NVFP6."""
+    spec = [  # (Cin, Cout, H, K, stride)
+        (16, 16, 160, 3, 1),
+        (16, 32, 160, 3, 2),
+        (32, 32, 80, 1, 1),
+        (32, 64, 80, 3, 2),
+        (64, 64, 40, 1, 1),
+        (64, 128, 40, 3, 2),
+        (128, 256, 20, 1, 1),
+        (256, 256, 20, 3, 1),
+    ]
+    out = []
+    for i, (ci, co, h, k, s) in enumerate(spec):
+        out.append(ConvLayer(f"c4.l{i + 1}", N=16, Cin=ci, H=h, W=h, Cout=co, Kh=k, Kw=k,
+                             stride=s, pad=k // 2, fmt=FP6, x_dist="silu",
+                             seed=40 + i, sr_seed=1))
+    return out
+
+
+def config5() -> List[ConvLayer]:
+    """ResNet-18 conv body at N=128 (224x224 input; stem conv and FC stay fp32), NVFP4."""
+    spec = []  # (Cin, Cout, H_in, K, stride)
+    spec += [(64, 64, 56, 3, 1)] * 4
+    for cin, cout, h in ((64, 128, 56), (128, 256, 28), (256, 512, 14)):
+        spec.append((cin, cout, h, 3, 2))        # first conv of the stage
+        spec.append((cin, cout, h, 1, 2))        # 1x1 stride-2 downsample
+        spec += [(cout, cout, h // 2, 3, 1)] * 3
+    out = []
+    for i, (ci, co, h, k, s) in enumerate(spec):
+        out.append(ConvLayer(f"c5.l{i + 1}", N=128, Cin=ci, H=h, W=h, Cout=co, Kh=k, Kw=k,
+                             stride=s, pad=k // 2, fmt=FP4, x_dist="relu",
+                             seed=50 + i, sr_seed=1 + i))
+    return out
+
+
+CONFIGS = {
+    "c1": config1,
+    "c2": config2,
+    "c3": config3,
+    "c4": config4,
+    "c5": config5,
+}
+
+
+def parity_layers() -> List[ConvLayer]:
+    """Mid-sized layers that span several kernel tiles with ragged tails everywhere.
+
+    Sized so that the CPU oracle finishes each in well under a second.
+    """
+    return [
+        ConvLayer("p.3x3s1p1", N=6, Cin=20, H=11, W=13, Cout=24, Kh=3, Kw=3, stride=1, pad=1,
+                  x_dist="relu", seed=101, sr_seed=7),
+        ConvLayer("p.3x3s2p1", N=5, Cin=13, H=9, W=10, Cout=17, Kh=3, Kw=3, stride=2, pad=1,
+                  x_dist="t3", seed=102, sr_seed=8),
+        ConvLayer("p.1x1s1", N=8, Cin=36, H=7, W=6, Cout=40, Kh=1, Kw=1, stride=1, pad=0,
+                  x_dist="silu", seed=103, sr_seed=9),
+        ConvLayer("p.1x1s2", N=3, Cin=12, H=10, W=9, Cout=20, Kh=1, Kw=1, stride=2, pad=0,
+                  x_dist="relu", seed=104, sr_seed=10),
+        ConvLayer("p.3x3s1p0.fp6", N=7, Cin=9, H=12, W=12, Cout=70, Kh=3, Kw=3, stride=1,
+                  pad=0, fmt=FP6, x_dist="silu", seed=105, sr_seed=11),
+        ConvLayer("p.3x3s2p1.fp6", N=4, Cin=40, H=15, W=16, Cout=36, Kh=3, Kw=3, stride=2,
+                  pad=1, fmt=FP6, x_dist="normal", seed=106, sr_seed=12),
+        ConvLayer("p.wide", N=36, Cin=72, H=9, W=9, Cout=136, Kh=3, Kw=3, stride=1, pad=1,
+                  x_dist="relu", seed=107, sr_seed=13),
+        ConvLayer("p.5x5s1p2", N=4, Cin=8, H=10, W=10, Cout=12, Kh=5, Kw=5, stride=1, pad=2,
+                  x_dist="normal", seed=108, sr_seed=14),
+    ]
