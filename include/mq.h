@@ -1,0 +1,186 @@
+/*
+ * mq.h -- C ABI of the microscaling-quantized convolution library for MI355X (gfx950).
+ *
+ * The library implements the hot path of MicroQonv (onedev.kr paper digest "합성곱 텐서 레이아웃
+ * 재배열로 마이크로스케일링 양자화의 이중 연산과 메모리 이동을 줄이는 MicroQonv"): every convolution
+ * tensor is quantized exactly once, before any im2col expansion, into a channel-batch-first layout
+ * with 4x4 square-block scaling, and all three convolution GEMMs run directly on the quantized
+ * data with the im2col matrix formed on chip only.
+ *
+ * Conventions shared by every call:
+ *   - Every pointer argument named *_dev, and every pointer inside mq_qtensor, is device memory
+ *     on the current HIP device. The caller allocates and owns all memory; the library
+ *     allocates nothing and keeps no state between calls.
+ *   - Every call is asynchronous on `stream` (0 = the null stream). The return value reports
+ *     only synchronous host-side argument validation and launch errors; no call synchronizes.
+ *   - Data problems are not reported through the status: a tensor containing NaN or Inf
+ *     quantizes to T = NaN, scales 0x7F (E4M3 NaN) and codes 0, and any convolution that
+ *     consumes it produces NaN.
+ *   - Calls that overlap on one stream are ordered; calls on different streams that share a
+ *     buffer race.
+ */
+#ifndef MQ_H
+#define MQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MQ_OK = 0,
+    MQ_ERR_ARG = 1,         /* null pointer, non-positive size, unknown enum value */
+    MQ_ERR_SHAPE = 2,       /* tensor shapes do not match the convolution / each other */
+    MQ_ERR_UNSUPPORTED = 3, /* valid request outside the implemented set (see each call) */
+    MQ_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
+    MQ_ERR_LAUNCH = 5       /* a kernel launch failed (hipGetLastError) */
+} mq_status;
+
+/* Element formats (onedev.kr digest, sections "How it differs" and "How it is used"):
+ * NVFP4 = E2M1 elements, NVFP6 = E2M3 elements; both with one E4M3 scale per 4x4 square and one
+ * fp32 tensor scale. */
+typedef enum { MQ_NVFP4 = 4, MQ_NVFP6 = 6 } mq_format;
+
+/* Role of a quantized tensor; fixes the meaning of its four dimensions (o0, o1, r, s):
+ *   MQ_ROLE_ACT    activation X          (Hin,  Win,  Cin,  N)   channel-batch-first
+ *   MQ_ROLE_WEIGHT weight W              (Kh,   Kw,   Cout, Cin) one Cout x Cin matrix per tap
+ *   MQ_ROLE_GRAD   output gradient G_Y   (Hout, Wout, Cout, N)   channel-batch-first */
+typedef enum { MQ_ROLE_ACT = 0, MQ_ROLE_WEIGHT = 1, MQ_ROLE_GRAD = 2 } mq_role;
+
+/* Element rounding: round-to-nearest-even (weights, activations) or stochastic (gradients),
+ * per the onedev.kr digest, section "How it differs". */
+typedef enum { MQ_RNE = 0, MQ_SR = 1 } mq_round;
+
+/*
+ * A quantized tensor: logical shape [o0][o1][r][s] (s fastest), cut into 4x4 squares over
+ * (r, s) with r and s zero-padded up to multiples of 4. With R4 = ceil(r/4), S4 = ceil(s/4):
+ *   square t = ((i0*o1 + i1)*R4 + ir/4)*S4 + is/4, element e = (ir%4)*4 + is%4;
+ *   codes:  NVFP4 8 bytes per square, element e = nibble (e%2) of byte 8t + e/2 (low first);
+ *           NVFP6 12 bytes per square, element e = bits [6e, 6e+6) of the little-endian
+ *           96-bit word at byte 12t;
+ *           code bits: NVFP4 s|ee|m (bias 1), NVFP6 s|ee|mmm (bias 1); padded slots are 0;
+ *   scales: 1 byte per square, E4M3 s|eeee|mmm (bias 7, subnormals, 0x7E = 448, 0x7F = NaN);
+ *   tscale: one fp32, the tensor scale T.
+ * Value of an element: decode(code) * decode(scale) * T.
+ * fmt and role hold mq_format / mq_role values.
+ */
+typedef struct {
+    int32_t o0, o1, r, s;
+    int32_t fmt;
+    int32_t role;
+    uint8_t *codes;
+    uint8_t *scales;
+    float *tscale;
+} mq_qtensor;
+
+/* One 2-D convolution (groups 1, dilation 1, zero padding). Output size
+ * Hout = (H + 2*pad_h - Kh)/stride_h + 1, Wout likewise. */
+typedef struct {
+    int32_t N, Cin, H, W, Cout, Kh, Kw, stride_h, stride_w, pad_h, pad_w;
+} mq_conv;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *mq_status_str(mq_status st);
+
+/* Bytes needed for the code stream / scale bytes of a quantized tensor with the given logical
+ * shape and format: squares * (8 | 12) and squares * 1. Returns 0 for invalid arguments. */
+size_t mq_codes_bytes(int32_t o0, int32_t o1, int32_t r, int32_t s, int32_t fmt);
+size_t mq_scales_bytes(int32_t o0, int32_t o1, int32_t r, int32_t s);
+
+/*
+ * mq_relayout_cbf: NCHW fp32 <-> channel-batch-first fp32.
+ * Channel-batch-first X_{Cin,N} (onedev.kr digest, section "How it works"): for each pixel
+ * (h, w) all channels and all batch elements are contiguous; here [H][W][C][N], N fastest.
+ *   inverse = 0: dst[h][w][c][n] = src[n][c][h][w]
+ *   inverse = 1: dst[n][c][h][w] = src[h][w][c][n]
+ * src_dev, dst_dev: N*C*H*W floats each, must not overlap.
+ * Errors: MQ_ERR_ARG for null pointers or non-positive sizes.
+ */
+mq_status mq_relayout_cbf(const float *src_dev, float *dst_dev, int32_t N, int32_t C, int32_t H,
+                          int32_t W, int32_t inverse, hipStream_t stream);
+
+/*
+ * mq_relayout_weight: OIHW fp32 <-> tap-major [Kh][Kw][Cout][Cin] fp32, the layout of the 2-D
+ * weight matrix W_{fCout,Cin} (Cout x Kh*Kw*Cin; onedev.kr digest, section "How it differs")
+ * with one Cout x Cin block per tap.
+ *   inverse = 0: dst[kh][kw][co][ci] = src[co][ci][kh][kw];  inverse = 1: the reverse.
+ * Errors: MQ_ERR_ARG for null pointers or non-positive sizes.
+ */
+mq_status mq_relayout_weight(const float *src_dev, float *dst_dev, int32_t Cout, int32_t Cin,
+                             int32_t Kh, int32_t Kw, int32_t inverse, hipStream_t stream);
+
+/*
+ * mq_quantize: quantize one fp32 tensor, exactly once, with the NVFP4 / NVFP6 recipe of the
+ * onedev.kr digest, section "How it differs":
+ *   amax = max |x| over the tensor;
+ *   T    = amax / (448 * Emax)                              (Emax = 6 for E2M1, 7.5 for E2M3)
+ *   per 4x4 square: B = CastE4M3(max|x_i| / (T * Emax))    (nearest-even, saturating at 448)
+ *   per element:    code = Round(x_i / (B * T))            (RNE, or SR for rnd = MQ_SR)
+ * All scale arithmetic is IEEE fp32 in the written order. Stochastic rounding rounds |q| up
+ * from its lower grid neighbour lo to hi iff u16 < ((|q|-lo)/(hi-lo)) * 65536, with u16 the
+ * (e%2)-th 16-bit half of word (e%8)/2 of Philox4x32-10(counter = (2t + e/8, 0, 0, 0),
+ * key = seed) for element e of square t. Codes keep the sign bit of x. Squares with B = 0 hold
+ * codes 0; a tensor with T = 0 holds scales 0 and codes 0.
+ *
+ * src_dev: the tensor as dense fp32 [o0][o1][r][s] (for activations and gradients this is the
+ *          channel-batch-first layout).
+ * dst:     host struct describing the destination; dst->codes, dst->scales, dst->tscale are
+ *          device buffers of mq_codes_bytes / mq_scales_bytes / 4 bytes.
+ * amax_ws_dev: one device uint32 of scratch (overwritten).
+ * Errors: MQ_ERR_ARG (null pointer, bad enum, non-positive dims).
+ */
+mq_status mq_quantize(const float *src_dev, const mq_qtensor *dst, int32_t rnd, uint64_t seed,
+                      uint32_t *amax_ws_dev, hipStream_t stream);
+
+/*
+ * mq_conv_fwd: forward GEMM Y = W . X' (onedev.kr digest, section "How it differs") with the
+ * im2col matrix X' formed on chip from the channel-batch-first quantized X (section "How it
+ * works"):
+ *   Y[ho][wo][co][n] = T_W * T_X * sum_{kh,kw,ci} Wq[kh][kw][co][ci]
+ *                                               * Xq[ho*sh - ph + kh][wo*sw - pw + kw][ci][n]
+ * (zero outside the input), accumulated in fp32 from exact bf16 products.
+ * x: MQ_ROLE_ACT tensor of shape (H, W, Cin, N); w: MQ_ROLE_WEIGHT tensor (Kh, Kw, Cout, Cin);
+ * same format. y_dev: fp32 channel-batch-first [Hout][Wout][Cout][N], fully overwritten.
+ * Errors: MQ_ERR_ARG, MQ_ERR_SHAPE (dims or formats disagree with p), MQ_ERR_UNSUPPORTED.
+ */
+mq_status mq_conv_fwd(const mq_conv *p, const mq_qtensor *x, const mq_qtensor *w, float *y_dev,
+                      hipStream_t stream);
+
+/* Bytes of device workspace mq_conv_wgrad needs for this convolution (0 on invalid input). */
+size_t mq_wgrad_workspace_bytes(const mq_conv *p);
+
+/*
+ * mq_conv_wgrad: weight-gradient GEMM G_W = G_Y . X'^T (onedev.kr digest, section "How it
+ * differs"), reading the quantized G_Y and X along their batch-contiguous direction:
+ *   G_W[kh][kw][co][ci] = T_G * T_X * sum_{ho,wo,n} Gq[ho][wo][co][n]
+ *                                               * Xq[ho*sh - ph + kh][wo*sw - pw + kw][ci][n]
+ * gy: MQ_ROLE_GRAD (Hout, Wout, Cout, N); x: MQ_ROLE_ACT (H, W, Cin, N); same format.
+ * gw_dev: fp32 [Kh][Kw][Cout][Cin], fully overwritten.
+ * ws_dev / ws_bytes: device scratch of at least mq_wgrad_workspace_bytes(p) bytes (split-K
+ * partial sums; summed in a fixed order, so results are deterministic).
+ * Errors: MQ_ERR_ARG, MQ_ERR_SHAPE, MQ_ERR_WORKSPACE, MQ_ERR_UNSUPPORTED.
+ */
+mq_status mq_conv_wgrad(const mq_conv *p, const mq_qtensor *gy, const mq_qtensor *x,
+                        float *gw_dev, void *ws_dev, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * mq_conv_dgrad: input-gradient GEMM G_X' = W^T . G_Y (onedev.kr digest, section "How it
+ * differs") with the col2im sum fused, so the Kh*Kw-inflated G_X' never exists in memory:
+ *   G_X[h][w][ci][n] = T_W * T_G * sum_{kh,kw,co} Wq[kh][kw][co][ci] * Gq[ho][wo][co][n]
+ *       over (ho, wo) with ho*sh - ph + kh = h and wo*sw - pw + kw = w.
+ * w: MQ_ROLE_WEIGHT (Kh, Kw, Cout, Cin); gy: MQ_ROLE_GRAD (Hout, Wout, Cout, N); same format.
+ * gx_dev: fp32 channel-batch-first [H][W][Cin][N], fully overwritten.
+ * Errors: MQ_ERR_ARG, MQ_ERR_SHAPE, MQ_ERR_UNSUPPORTED.
+ */
+mq_status mq_conv_dgrad(const mq_conv *p, const mq_qtensor *w, const mq_qtensor *gy,
+                        float *gx_dev, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MQ_H */

@@ -1,0 +1,42 @@
+"""Build the HIP library ``libmq.so`` in-tree with hipcc for gfx950."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libmq.so")
+SOURCES = ["mq_api.cpp", "mq_relayout.hip", "mq_quantize.hip", "mq_conv.hip"]
+
+# -ffp-contract=off: the quantizer's fp32 scale arithmetic must round every operation as written.
+# fp32 division stays IEEE-correct (hipcc's default) and fp32 denormals are kept (no
+# -fgpu-flush-denormals-to-zero). Packed-fp32 instruction selection is disabled.
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
+        if c and (os.path.sep not in c or os.path.exists(c)):
+            return c
+    return "hipcc"
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into libmq.so (always recompiles). Returns the library path."""
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

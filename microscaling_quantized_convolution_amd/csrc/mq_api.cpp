@@ -1,0 +1,162 @@
+// mq_api.cpp -- C ABI of the library: host-side validation and kernel dispatch.
+//
+// Every call validates its arguments on the host, then enqueues kernels on the caller's stream.
+// Nothing here allocates, synchronizes or reads device memory.
+#include "../../include/mq.h"
+#include "mq_kernels.hpp"
+
+#include <stdlib.h>
+
+namespace {
+
+bool fmt_ok(int32_t f) { return f == MQ_NVFP4 || f == MQ_NVFP6; }
+
+int64_t squares(int32_t o0, int32_t o1, int32_t r, int32_t s)
+{
+    return (int64_t)o0 * o1 * ((r + 3) / 4) * ((s + 3) / 4);
+}
+
+bool qtensor_ok(const mq_qtensor *q)
+{
+    return q && q->o0 > 0 && q->o1 > 0 && q->r > 0 && q->s > 0 && fmt_ok(q->fmt) &&
+           q->role >= MQ_ROLE_ACT && q->role <= MQ_ROLE_GRAD && q->codes && q->scales &&
+           q->tscale;
+}
+
+// Geometry of a convolution, or false if it is not a valid convolution.
+bool conv_geom(const mq_conv *p, mq::ConvGeom *g)
+{
+    if (!p) return false;
+    if (p->N < 1 || p->Cin < 1 || p->H < 1 || p->W < 1 || p->Cout < 1 || p->Kh < 1 ||
+        p->Kw < 1 || p->stride_h < 1 || p->stride_w < 1 || p->pad_h < 0 || p->pad_w < 0)
+        return false;
+    if (p->H + 2 * p->pad_h < p->Kh || p->W + 2 * p->pad_w < p->Kw) return false;
+    g->N = p->N; g->Cin = p->Cin; g->H = p->H; g->W = p->W; g->Cout = p->Cout;
+    g->Kh = p->Kh; g->Kw = p->Kw; g->sh = p->stride_h; g->sw = p->stride_w;
+    g->ph = p->pad_h; g->pw = p->pad_w;
+    g->Ho = (p->H + 2 * p->pad_h - p->Kh) / p->stride_h + 1;
+    g->Wo = (p->W + 2 * p->pad_w - p->Kw) / p->stride_w + 1;
+    g->N4 = (p->N + 3) / 4; g->Cin4 = (p->Cin + 3) / 4; g->Cout4 = (p->Cout + 3) / 4;
+    return true;
+}
+
+// Limits of the implemented kernels: 32-bit index arithmetic inside the GEMM kernels.
+bool conv_supported(const mq::ConvGeom &g)
+{
+    const int64_t lim = (int64_t)1 << 30;
+    if ((int64_t)g.H * g.W * g.N4 >= lim / 4 || (int64_t)g.Ho * g.Wo * g.N4 >= lim / 4) return false;
+    if ((int64_t)g.Kh * g.Kw * (g.Cin4 > g.Cout4 ? g.Cin4 : g.Cout4) >= lim / 4) return false;
+    return true;
+}
+
+bool dims_are(const mq_qtensor *q, int32_t a, int32_t b, int32_t c, int32_t d, int32_t role)
+{
+    return q->o0 == a && q->o1 == b && q->r == c && q->s == d && q->role == role;
+}
+
+mq::QOperand operand(const mq_qtensor *q) { return {q->codes, q->scales, q->tscale}; }
+
+mq_status launch_status(hipError_t e) { return e == hipSuccess ? MQ_OK : MQ_ERR_LAUNCH; }
+
+} // namespace
+
+extern "C" {
+
+const char *mq_status_str(mq_status st)
+{
+    switch (st) {
+    case MQ_OK: return "MQ_OK";
+    case MQ_ERR_ARG: return "MQ_ERR_ARG: invalid argument";
+    case MQ_ERR_SHAPE: return "MQ_ERR_SHAPE: tensor shapes or formats do not match";
+    case MQ_ERR_UNSUPPORTED: return "MQ_ERR_UNSUPPORTED: outside the implemented set";
+    case MQ_ERR_WORKSPACE: return "MQ_ERR_WORKSPACE: workspace missing or too small";
+    case MQ_ERR_LAUNCH: return "MQ_ERR_LAUNCH: kernel launch failed";
+    }
+    return "unknown mq_status";
+}
+
+size_t mq_codes_bytes(int32_t o0, int32_t o1, int32_t r, int32_t s, int32_t fmt)
+{
+    if (o0 < 1 || o1 < 1 || r < 1 || s < 1 || !fmt_ok(fmt)) return 0;
+    return (size_t)squares(o0, o1, r, s) * (fmt == MQ_NVFP4 ? 8u : 12u);
+}
+
+size_t mq_scales_bytes(int32_t o0, int32_t o1, int32_t r, int32_t s)
+{
+    if (o0 < 1 || o1 < 1 || r < 1 || s < 1) return 0;
+    return (size_t)squares(o0, o1, r, s);
+}
+
+mq_status mq_relayout_cbf(const float *src, float *dst, int32_t N, int32_t C, int32_t H,
+                          int32_t W, int32_t inverse, hipStream_t stream)
+{
+    if (!src || !dst || N < 1 || C < 1 || H < 1 || W < 1 || (inverse != 0 && inverse != 1))
+        return MQ_ERR_ARG;
+    if (C > 65535) return MQ_ERR_UNSUPPORTED;
+    return launch_status(mq::launch_relayout_cbf(src, dst, N, C, H, W, inverse, stream));
+}
+
+mq_status mq_relayout_weight(const float *src, float *dst, int32_t Cout, int32_t Cin,
+                             int32_t Kh, int32_t Kw, int32_t inverse, hipStream_t stream)
+{
+    if (!src || !dst || Cout < 1 || Cin < 1 || Kh < 1 || Kw < 1 ||
+        (inverse != 0 && inverse != 1))
+        return MQ_ERR_ARG;
+    return launch_status(mq::launch_relayout_weight(src, dst, Cout, Cin, Kh, Kw, inverse, stream));
+}
+
+mq_status mq_quantize(const float *src, const mq_qtensor *dst, int32_t rnd, uint64_t seed,
+                      uint32_t *amax_ws, hipStream_t stream)
+{
+    if (!src || !qtensor_ok(dst) || !amax_ws || (rnd != MQ_RNE && rnd != MQ_SR)) return MQ_ERR_ARG;
+    return launch_status(mq::launch_quantize(src, (int64_t)dst->o0 * dst->o1, dst->r, dst->s,
+                                             dst->fmt, rnd, seed, dst->codes, dst->scales,
+                                             dst->tscale, amax_ws, stream));
+}
+
+mq_status mq_conv_fwd(const mq_conv *p, const mq_qtensor *x, const mq_qtensor *w, float *y,
+                      hipStream_t stream)
+{
+    mq::ConvGeom g;
+    if (!conv_geom(p, &g) || !qtensor_ok(x) || !qtensor_ok(w) || !y) return MQ_ERR_ARG;
+    if (!dims_are(x, p->H, p->W, p->Cin, p->N, MQ_ROLE_ACT) ||
+        !dims_are(w, p->Kh, p->Kw, p->Cout, p->Cin, MQ_ROLE_WEIGHT) || x->fmt != w->fmt)
+        return MQ_ERR_SHAPE;
+    if (!conv_supported(g)) return MQ_ERR_UNSUPPORTED;
+    return launch_status(mq::launch_conv_fwd(g, x->fmt, operand(x), operand(w), y, stream));
+}
+
+size_t mq_wgrad_workspace_bytes(const mq_conv *p)
+{
+    mq::ConvGeom g;
+    if (!conv_geom(p, &g)) return 0;
+    return mq::wgrad_workspace_bytes(g);
+}
+
+mq_status mq_conv_wgrad(const mq_conv *p, const mq_qtensor *gy, const mq_qtensor *x, float *gw,
+                        void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    mq::ConvGeom g;
+    if (!conv_geom(p, &g) || !qtensor_ok(gy) || !qtensor_ok(x) || !gw) return MQ_ERR_ARG;
+    if (!dims_are(gy, g.Ho, g.Wo, p->Cout, p->N, MQ_ROLE_GRAD) ||
+        !dims_are(x, p->H, p->W, p->Cin, p->N, MQ_ROLE_ACT) || gy->fmt != x->fmt)
+        return MQ_ERR_SHAPE;
+    if (!conv_supported(g)) return MQ_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < mq::wgrad_workspace_bytes(g)) return MQ_ERR_WORKSPACE;
+    return launch_status(mq::launch_conv_wgrad(g, x->fmt, operand(gy), operand(x), gw, ws,
+                                               ws_bytes, stream));
+}
+
+mq_status mq_conv_dgrad(const mq_conv *p, const mq_qtensor *w, const mq_qtensor *gy, float *gx,
+                        hipStream_t stream)
+{
+    mq::ConvGeom g;
+    if (!conv_geom(p, &g) || !qtensor_ok(w) || !qtensor_ok(gy) || !gx) return MQ_ERR_ARG;
+    if (!dims_are(w, p->Kh, p->Kw, p->Cout, p->Cin, MQ_ROLE_WEIGHT) ||
+        !dims_are(gy, g.Ho, g.Wo, p->Cout, p->N, MQ_ROLE_GRAD) || w->fmt != gy->fmt)
+        return MQ_ERR_SHAPE;
+    if (!conv_supported(g)) return MQ_ERR_UNSUPPORTED;
+    return launch_status(mq::launch_conv_dgrad(g, w->fmt, operand(w), operand(gy), gx, stream));
+}
+
+} // extern "C"

@@ -1,0 +1,137 @@
+// mq_device.hpp -- device helpers shared by the library's kernels (gfx950 only).
+//
+// Number formats of the NVFP4 / NVFP6 recipe (onedev.kr MicroQonv digest, section "How it
+// differs": E4M3 block scale, E2M1 elements; section "How it is used": E2M3 elements):
+//   E2M1 s|ee|m     bias 1, subnormal 0.5*m, largest 6
+//   E2M3 s|ee|mmm   bias 1, subnormal m/8,   largest 7.5
+//   E4M3 s|eeee|mmm bias 7, subnormal m*2^-9, largest 448 (0x7E), 0x7F = NaN
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mq {
+
+constexpr int kFP4 = 4;
+constexpr int kFP6 = 6;
+
+template <int FMT> struct Fmt;
+template <> struct Fmt<kFP4> {
+    static constexpr int kBits = 4;        // bits per code
+    static constexpr int kMant = 1;        // mantissa bits
+    static constexpr uint32_t kSign = 0x8; // sign bit of a code
+    static constexpr uint32_t kMaxMag = 7; // largest magnitude code
+    static constexpr int kBytesPerSquare = 8;
+    static constexpr float kEmax = 6.0f;
+    // Grid rounding on [0,2): code = 2a; [2,4): a + 2; [4, inf): a/2 + 4 (see quantize).
+    static constexpr float kScale0 = 2.0f;
+    static constexpr float kAdd1 = 2.0f, kAdd2 = 4.0f;
+};
+template <> struct Fmt<kFP6> {
+    static constexpr int kBits = 6;
+    static constexpr int kMant = 3;
+    static constexpr uint32_t kSign = 0x20;
+    static constexpr uint32_t kMaxMag = 31;
+    static constexpr int kBytesPerSquare = 12;
+    static constexpr float kEmax = 7.5f;
+    // [0,2): code = 8a; [2,4): 4a + 8; [4, inf): 2a + 16.
+    static constexpr float kScale0 = 8.0f;
+    static constexpr float kAdd1 = 8.0f, kAdd2 = 16.0f;
+};
+
+// Value of an E4M3 code (finite codes only; callers handle 0x7F separately).
+__device__ __forceinline__ float e4m3_to_float(uint32_t c)
+{
+    // Place eeee.mmm right below the fp32 exponent LSB: as a float this is the E4M3 value times
+    // 2^(1-127) * 2^(7-1)... i.e. value * 2^-120, exact also for E4M3 subnormals (they become fp32
+    // denormals). Rescale by 2^120.
+    uint32_t mag = c & 0x7Fu;
+    float v = __uint_as_float(mag << 20) * 0x1p120f;
+    return (c & 0x80u) ? -v : v;
+}
+
+// CastE4M3 of a non-negative, non-NaN fp32: round to nearest, ties to even, subnormals kept,
+// saturating at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float s)
+{
+    if (!(s < 448.0f)) return 0x7Eu;          // also +inf
+    if (s < 0x1p-6f) {                        // E4M3 subnormal range: m * 2^-9, m = 0..8
+        return (uint32_t)__builtin_rintf(s * 512.0f); // 8 -> code 8 = 2^-6, the first normal
+    }
+    uint32_t b = __float_as_uint(s);
+    // keep 3 mantissa bits, round-to-nearest-even on the 20 dropped bits
+    b += 0x7FFFFu + ((b >> 20) & 1u);
+    uint32_t e = (b >> 23) - 127u + 7u;
+    uint32_t m = (b >> 20) & 7u;
+    uint32_t c = (e << 3) | m;
+    return c > 0x7Eu ? 0x7Eu : c;
+}
+
+// Value of an element magnitude code: the code placed right under the fp32 exponent field is
+// the element value times 2^-126 (subnormal codes become fp32 denormals), so rescale by 2^126.
+template <int FMT>
+__device__ __forceinline__ float elem_mag_to_float(uint32_t mag)
+{
+    return __uint_as_float(mag << (23 - Fmt<FMT>::kMant)) * 0x1p126f;
+}
+
+// Nearest-even grid code of a = |q| (a >= 0, finite), saturating at the largest element.
+// On each of [0,2), [2,4), [4,inf) the grid is uniform, so the code is an affine function of
+// a rounded with rint (ties to even integer = ties to even code).
+template <int FMT>
+__device__ __forceinline__ uint32_t grid_rne(float a)
+{
+    using F = Fmt<FMT>;
+    float sc = a < 2.0f ? F::kScale0 : (a < 4.0f ? 0.5f * F::kScale0 : 0.25f * F::kScale0);
+    float ad = a < 2.0f ? 0.0f : (a < 4.0f ? F::kAdd1 : F::kAdd2);
+    float c = __builtin_rintf(a * sc) + ad;
+    c = fminf(c, (float)F::kMaxMag);
+    return (uint32_t)c;
+}
+
+// Stochastic grid rounding of a = |q|: from the lower neighbour up iff u16 < frac * 65536,
+// frac = (a - lo) / step (exact; lo is the grid value at or below a, step a power of two).
+template <int FMT>
+__device__ __forceinline__ uint32_t grid_sr(float a, uint32_t u16)
+{
+    using F = Fmt<FMT>;
+    if (a >= F::kEmax) return F::kMaxMag;
+    float sc = a < 2.0f ? F::kScale0 : (a < 4.0f ? 0.5f * F::kScale0 : 0.25f * F::kScale0);
+    float ad = a < 2.0f ? 0.0f : (a < 4.0f ? F::kAdd1 : F::kAdd2);
+    float fl = __builtin_floorf(a * sc);
+    float lo = fl / sc;                       // exact
+    float frac = (a - lo) * sc;               // exact: Sterbenz, power-of-two scale
+    uint32_t up = ((float)u16 < frac * 65536.0f) ? 1u : 0u;
+    return (uint32_t)(fl + ad) + up;
+}
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): multipliers 0xD2511F53 / 0xCD9E8D57,
+// Weyl increments 0x9E3779B9 / 0xBB67AE85.
+struct Philox4 {
+    uint32_t v[4];
+};
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                 uint32_t c3, uint32_t k0, uint32_t k1)
+{
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+        uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+        uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    Philox4 r;
+    r.v[0] = c0; r.v[1] = c1; r.v[2] = c2; r.v[3] = c3;
+    return r;
+}
+
+// bf16 bit pattern of an fp32 value that is exactly representable in bf16.
+__device__ __forceinline__ uint32_t bf16_bits_exact(float v) { return __float_as_uint(v) >> 16; }
+
+} // namespace mq

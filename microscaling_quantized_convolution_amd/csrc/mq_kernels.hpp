@@ -1,0 +1,38 @@
+// mq_kernels.hpp -- host-side launch entry points of the library's kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mq {
+
+hipError_t launch_relayout_cbf(const float *src, float *dst, int N, int C, int H, int W,
+                               int inverse, hipStream_t st);
+hipError_t launch_relayout_weight(const float *src, float *dst, int Cout, int Cin, int Kh,
+                                  int Kw, int inverse, hipStream_t st);
+hipError_t launch_quantize(const float *src, int64_t planes, int R, int S, int fmt, int rnd,
+                           uint64_t seed, uint8_t *codes, uint8_t *scales, float *tscale,
+                           uint32_t *amax_ws, hipStream_t st);
+
+// Convolution geometry shared by the GEMM kernels.
+struct ConvGeom {
+    int N, Cin, H, W, Cout, Kh, Kw, sh, sw, ph, pw, Ho, Wo;
+    int N4, Cin4, Cout4; // squares along N, Cin, Cout
+};
+
+struct QOperand {
+    const uint8_t *codes;
+    const uint8_t *scales;
+    const float *tscale;
+};
+
+size_t wgrad_workspace_bytes(const ConvGeom &g);
+hipError_t launch_conv_fwd(const ConvGeom &g, int fmt, QOperand x, QOperand w, float *y,
+                           hipStream_t st);
+hipError_t launch_conv_wgrad(const ConvGeom &g, int fmt, QOperand gy, QOperand x, float *gw,
+                             void *ws, size_t ws_bytes, hipStream_t st);
+hipError_t launch_conv_dgrad(const ConvGeom &g, int fmt, QOperand w, QOperand gy, float *gx,
+                             hipStream_t st);
+
+} // namespace mq

@@ -1,0 +1,224 @@
+// mq_quantize.hip -- tensor amax and square-block quantization (NVFP4 / NVFP6).
+//
+// Implements the quantizer of the onedev.kr MicroQonv digest, section "How it differs":
+//   T = amax / (448 * Emax); per 4x4 square B = CastE4M3(max|x_i| / (T * Emax));
+//   element code = Round(x_i / (B * T)), nearest-even for weights/activations, stochastic for
+//   gradients. Each tensor is quantized once; the square shares its scale along 4 elements in
+//   both of its dimensions, so the same codes serve the GEMMs that reduce along either one.
+//
+// Two kernels per tensor: amax (grid-stride max of |x| as uint bit patterns, wave reduction,
+// one atomicMax per workgroup) and quantize (one lane per 4x4 square).
+#include "mq_device.hpp"
+#include "mq_kernels.hpp"
+
+namespace mq {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ void zero_u32_kernel(uint32_t *p) { *p = 0u; }
+
+// Max over |x| as unsigned bit patterns: for non-negative floats the order of the bit patterns
+// is the numeric order, and NaN patterns sort above +inf, so a NaN anywhere wins.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+    return v;
+}
+
+__global__ void __launch_bounds__(256) amax_kernel(const float *__restrict__ x, int64_t n,
+                                                   uint32_t *__restrict__ out)
+{
+    uint32_t m = 0u;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool aligned = ((reinterpret_cast<uintptr_t>(x) & 15u) == 0);
+    if (aligned) {
+        const int64_t n4 = n >> 2;
+        const u32x4_t *x4 = reinterpret_cast<const u32x4_t *>(x);
+        for (int64_t j = i; j < n4; j += stride) {
+            u32x4_t v = __builtin_nontemporal_load(x4 + j);
+            m = max(m, max(max(v[0] & 0x7FFFFFFFu, v[1] & 0x7FFFFFFFu),
+                           max(v[2] & 0x7FFFFFFFu, v[3] & 0x7FFFFFFFu)));
+        }
+        for (int64_t j = (n4 << 2) + i; j < n; j += stride)
+            m = max(m, __float_as_uint(x[j]) & 0x7FFFFFFFu);
+    } else {
+        for (int64_t j = i; j < n; j += stride) m = max(m, __float_as_uint(x[j]) & 0x7FFFFFFFu);
+    }
+    m = wave_max_u32(m);
+    __shared__ uint32_t red[4];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    if (lane == 0) red[wid] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = red[0];
+        for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = max(r, red[w]);
+        // Skip the atomic when the running maximum already covers this block: one contended
+        // word otherwise serializes every workgroup.
+        if (r && r > __hip_atomic_load(out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            atomicMax(out, r);
+    }
+}
+
+struct QuantArgs {
+    const float *src;
+    uint8_t *codes;
+    uint8_t *scales;
+    float *tscale;
+    const uint32_t *amax_bits;
+    int64_t planes; // o0 * o1
+    int32_t R, S, R4, S4;
+    int64_t nsq;
+    uint32_t seed_lo, seed_hi;
+};
+
+// One lane per 4x4 square. FULL = every square lies entirely inside [R][S] and S % 4 == 0, so
+// the four rows are aligned float4 loads.
+template <int FMT, bool SR, bool FULL>
+__global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a)
+{
+    using F = Fmt<FMT>;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= a.nsq) return;
+
+    // Tensor scale from the amax pass.
+    const uint32_t abits = *a.amax_bits;
+    const bool nonfinite = abits >= 0x7F800000u;
+    const float T = __uint_as_float(abits) / (448.0f * F::kEmax);
+    if (t == 0) *a.tscale = nonfinite ? __uint_as_float(0x7FC00000u) : T;
+
+    const int s4 = (int)(t % a.S4);
+    const int64_t rest = t / a.S4;
+    const int r4 = (int)(rest % a.R4);
+    const int64_t plane = rest / a.R4;
+    const int64_t base = (plane * a.R + 4 * r4) * (int64_t)a.S + 4 * s4;
+
+    float x[16];
+    if (FULL) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f32x4_t v = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4_t *>(a.src + base + (int64_t)i * a.S));
+            x[4 * i + 0] = v[0]; x[4 * i + 1] = v[1]; x[4 * i + 2] = v[2]; x[4 * i + 3] = v[3];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bool in = (4 * r4 + i < a.R) && (4 * s4 + j < a.S);
+                x[4 * i + j] = in ? a.src[base + (int64_t)i * a.S + j] : 0.0f;
+            }
+    }
+
+    uint32_t code[16];
+    uint32_t bcode;
+    if (nonfinite) {
+        bcode = 0x7Fu;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) code[e] = 0u;
+    } else {
+        float bmax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) bmax = fmaxf(bmax, fabsf(x[e]));
+        const float TE = T * F::kEmax;
+        // T == 0 only for an all-zero (or vanishingly small) tensor: scales 0, codes 0.
+        bcode = (T == 0.0f) ? 0u : e4m3_rne_sat(bmax / TE);
+        const float B = e4m3_to_float(bcode);
+        const float D = B * T;
+        const bool zero = (bcode == 0u) || (D == 0.0f);
+        Philox4 r0, r1;
+        if (SR && !zero) {
+            const uint64_t j = 2u * (uint64_t)t;
+            r0 = philox4x32_10((uint32_t)j, (uint32_t)(j >> 32), 0u, 0u, a.seed_lo, a.seed_hi);
+            r1 = philox4x32_10((uint32_t)(j + 1), (uint32_t)((j + 1) >> 32), 0u, 0u, a.seed_lo,
+                               a.seed_hi);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            uint32_t c = 0u;
+            if (!zero) {
+                const float q = x[e] / D; // IEEE-correct division (hipcc default)
+                const float aq = fabsf(q);
+                uint32_t mag;
+                if (SR) {
+                    const uint32_t w = (e < 8) ? r0.v[(e & 7) >> 1] : r1.v[(e & 7) >> 1];
+                    const uint32_t u16 = (w >> (16 * (e & 1))) & 0xFFFFu;
+                    mag = grid_sr<FMT>(aq, u16);
+                } else {
+                    mag = grid_rne<FMT>(aq);
+                }
+                c = mag | ((__float_as_uint(x[e]) >> 31) ? F::kSign : 0u);
+            }
+            code[e] = c;
+        }
+        if (!FULL) { // padded slots hold code 0
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (!((4 * r4 + i < a.R) && (4 * s4 + j < a.S))) code[4 * i + j] = 0u;
+        }
+    }
+
+    a.scales[t] = (uint8_t)bcode;
+    if (FMT == kFP4) {
+        uint32_t w0 = 0u, w1 = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            w0 |= code[e] << (4 * e);
+            w1 |= code[e + 8] << (4 * e);
+        }
+        *reinterpret_cast<uint2 *>(a.codes + 8 * t) = make_uint2(w0, w1);
+    } else {
+        uint32_t w[3] = {0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int bit = 6 * e;
+            w[bit >> 5] |= code[e] << (bit & 31);
+            if ((bit & 31) > 26) w[(bit >> 5) + 1] |= code[e] >> (32 - (bit & 31));
+        }
+        uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes + 12 * t);
+        dst[0] = w[0]; dst[1] = w[1]; dst[2] = w[2];
+    }
+}
+
+template <int FMT, bool SR>
+static hipError_t launch_quant(const QuantArgs &a, bool full, hipStream_t st)
+{
+    const unsigned blocks = (unsigned)((a.nsq + 255) / 256);
+    if (full)
+        hipLaunchKernelGGL((quantize_kernel<FMT, SR, true>), dim3(blocks), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((quantize_kernel<FMT, SR, false>), dim3(blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize(const float *src, int64_t planes, int R, int S, int fmt, int rnd,
+                           uint64_t seed, uint8_t *codes, uint8_t *scales, float *tscale,
+                           uint32_t *amax_ws, hipStream_t st)
+{
+    const int64_t n = planes * (int64_t)R * S;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, st, amax_ws);
+    // at least 8 float4 per lane, at most 1024 workgroups (4 per CU)
+    int64_t want = (n / 4 + 2047) / 2048;
+    unsigned ablocks = (unsigned)(want < 1 ? 1 : (want > 1024 ? 1024 : want));
+    hipLaunchKernelGGL(amax_kernel, dim3(ablocks), dim3(256), 0, st, src, n, amax_ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    QuantArgs a;
+    a.src = src; a.codes = codes; a.scales = scales; a.tscale = tscale; a.amax_bits = amax_ws;
+    a.planes = planes; a.R = R; a.S = S; a.R4 = (R + 3) / 4; a.S4 = (S + 3) / 4;
+    a.nsq = planes * a.R4 * a.S4;
+    a.seed_lo = (uint32_t)seed; a.seed_hi = (uint32_t)(seed >> 32);
+    const bool full = (R % 4 == 0) && (S % 4 == 0) &&
+                      ((reinterpret_cast<uintptr_t>(src) & 15u) == 0);
+    if (fmt == kFP4)
+        return rnd ? launch_quant<kFP4, true>(a, full, st) : launch_quant<kFP4, false>(a, full, st);
+    return rnd ? launch_quant<kFP6, true>(a, full, st) : launch_quant<kFP6, false>(a, full, st);
+}
+
+} // namespace mq

@@ -1,0 +1,138 @@
+"""GPU parity of the three convolution GEMMs against the CPU oracle.
+
+Forward Y = W.X', weight gradient G_W = G_Y.X'^T and input gradient G_X' = W^T.G_Y (col2im
+fused), on channel-batch-first square-quantized tensors (onedev.kr MicroQonv digest, sections
+"How it works" and "How it differs"). Per element |gpu - oracle| <= 2^-10 * sum|w*x| (the
+GPU sums exact bf16 products in fp32), and exactly 0 where every term is 0.
+
+Small and mid-sized layers are compared element by element; the full-size workload layers are
+compared on random samples of outputs that the oracle evaluates one at a time.
+"""
+import numpy as np
+import pytest
+import torch
+
+import microscaling_quantized_convolution_amd as mq
+import oracle
+import workloads
+from gpu_parity import (assert_conv_close, assert_quant_equal, log, oracle_layer,
+                        run_gpu_layer)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = workloads.config1() + workloads.parity_layers()
+
+
+@pytest.mark.parametrize("layer", SMALL, ids=lambda l: l.name)
+def test_conv_parity_full_tensor(layer):
+    log("conv parity", layer.name)
+    gl = run_gpu_layer(layer)
+    ol = oracle_layer(layer)
+    assert_quant_equal(gl.qx, ol.q["x"], layer.fmt, "x")
+    assert_quant_equal(gl.qw, ol.q["w"], layer.fmt, "w")
+    assert_quant_equal(gl.qg, ol.q["g"], layer.fmt, "g")
+    p = layer.conv_tuple()
+    y, ya = oracle.conv_fwd(p, ol.deq["x"], ol.deq["w"])
+    gw, gwa = oracle.conv_wgrad(p, ol.deq["g"], ol.deq["x"])
+    gx, gxa = oracle.conv_dgrad(p, ol.deq["w"], ol.deq["g"])
+    assert_conv_close(gl.y.cpu().numpy(), y, ya, f"{layer.name} fwd")
+    assert_conv_close(gl.gw.cpu().numpy(), gw, gwa, f"{layer.name} wgrad")
+    assert_conv_close(gl.gx.cpu().numpy(), gx, gxa, f"{layer.name} dgrad")
+
+
+def _sample_idx(rng, shape, n):
+    return np.stack([rng.integers(0, d, n) for d in shape], 1).astype(np.int32)
+
+
+def _check_sampled(layer, nsamp=1500):
+    log("sampled conv parity", layer.name)
+    gl = run_gpu_layer(layer)
+    ol = oracle_layer(layer)
+    assert_quant_equal(gl.qx, ol.q["x"], layer.fmt, "x")
+    assert_quant_equal(gl.qw, ol.q["w"], layer.fmt, "w")
+    assert_quant_equal(gl.qg, ol.q["g"], layer.fmt, "g")
+    p = layer.conv_tuple()
+    rng = np.random.default_rng(hash(layer.name) % 2 ** 32)
+    Ho, Wo = layer.Ho, layer.Wo
+    yshape = (Ho, Wo, layer.Cout, layer.N)
+    wshape = (layer.Kh, layer.Kw, layer.Cout, layer.Cin)
+    xshape = (layer.H, layer.W, layer.Cin, layer.N)
+    for name, shape, fn, a, b, got in (
+            ("fwd", yshape, oracle.conv_fwd_at, ol.deq["x"], ol.deq["w"], gl.y),
+            ("wgrad", wshape, oracle.conv_wgrad_at, ol.deq["g"], ol.deq["x"], gl.gw),
+            ("dgrad", xshape, oracle.conv_dgrad_at, ol.deq["w"], ol.deq["g"], gl.gx)):
+        n = nsamp if name != "wgrad" else min(nsamp, 200)
+        idx = _sample_idx(rng, shape, n)
+        ref, refa = fn(p, a, b, idx)
+        g = got.cpu().numpy().reshape(shape)[tuple(idx.T)]
+        assert_conv_close(g, ref, refa, f"{layer.name} {name}")
+        assert np.isfinite(got.cpu().numpy()).all(), f"{layer.name} {name}: non-finite output"
+
+
+@pytest.mark.parametrize("cfg", ["c2", "c3"])
+def test_conv_parity_full_size_sampled(cfg):
+    for layer in workloads.CONFIGS[cfg]():
+        _check_sampled(layer)
+
+
+def test_conv_parity_yolo_stack_sampled():
+    for layer in workloads.config4():
+        _check_sampled(layer, nsamp=800)
+
+
+@pytest.mark.parametrize("which", [[0, 4], [5, 6, 9], [10, 11, 14], [15, 16, 18]])
+def test_conv_parity_resnet18_body_sampled(which):
+    layers = workloads.config5()
+    for i in which:
+        _check_sampled(layers[i], nsamp=600)
+
+
+def test_conv_deterministic():
+    layer = workloads.parity_layers()[6]
+    a = run_gpu_layer(layer)
+    b = run_gpu_layer(layer)
+    for t1, t2 in ((a.y, b.y), (a.gw, b.gw), (a.gx, b.gx)):
+        assert torch.equal(t1, t2)
+
+
+def test_conv_nan_propagates():
+    layer = workloads.parity_layers()[0]
+    x, w, g = workloads.make_tensors(layer)
+    x = x.copy()
+    x[0, 0, 0, 0] = np.nan
+    gl = run_gpu_layer(layer, tensors=(x, w, g))
+    assert torch.isnan(gl.y).all()
+    assert torch.isnan(gl.gw).all()
+    assert not torch.isnan(gl.gx).any()  # dgrad does not read X
+
+
+def test_conv_zero_weight_gives_exact_zero():
+    layer = workloads.parity_layers()[1]
+    x, w, g = workloads.make_tensors(layer)
+    gl = run_gpu_layer(layer, tensors=(x, np.zeros_like(w), g))
+    assert (gl.y == 0).all() and (gl.gx == 0).all()
+
+
+def test_conv_one_hot_weight_reads_im2col_column():
+    """A weight with one non-zero entry makes Y a copy of one im2col row: the on-chip im2col
+    gathers exactly the dequantized input (zero in the padding)."""
+    layer = workloads.ConvLayer("onehot", N=5, Cin=6, H=7, W=9, Cout=5, Kh=3, Kw=3, stride=2,
+                                pad=1, x_dist="normal", seed=21)
+    x, w, g = workloads.make_tensors(layer)
+    ol = oracle_layer(layer, tensors=(x, w, g))
+    for (co, ci, kh, kw) in ((0, 0, 0, 0), (3, 5, 2, 1), (4, 2, 1, 2)):
+        w1 = np.zeros_like(w)
+        w1[co, ci, kh, kw] = 1.0
+        gl = run_gpu_layer(layer, tensors=(x, w1, g))
+        y = gl.y.cpu().numpy().reshape(layer.Ho, layer.Wo, layer.Cout, layer.N)
+        xh = ol.deq["x"]
+        T_w = float(gl.qw.tscale.cpu().numpy()[0])
+        for ho in range(layer.Ho):
+            for wo in range(layer.Wo):
+                h, ww = ho * 2 - 1 + kh, wo * 2 - 1 + kw
+                exp = xh[h, ww, ci, :] if (0 <= h < layer.H and 0 <= ww < layer.W) else 0.0
+                # quantized one-hot weight = 6 * 448 * T_w with T_w = 1/2688 -> exactly 1
+                np.testing.assert_allclose(y[ho, wo, co, :], exp * (6 * 448 * T_w), rtol=2 ** -20,
+                                           atol=0)
+        others = [c for c in range(layer.Cout) if c != co]
+        assert (y[:, :, others, :] == 0).all()

@@ -1,0 +1,161 @@
+"""GPU parity of relayout and quantization: bit-exact against the CPU oracle.
+
+The quantizer follows the NVFP4 / NVFP6 recipe of the onedev.kr MicroQonv digest (section "How
+it differs"); the channel-batch-first relayout follows section "How it works". Codes, scales and
+the tensor scale must match the oracle byte for byte.
+"""
+import numpy as np
+import pytest
+import torch
+
+import microscaling_quantized_convolution_amd as mq
+import oracle
+import workloads
+from gpu_parity import assert_quant_equal, gpu_quantize, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [
+    (1, 1, 1, 1), (1, 1, 4, 4), (2, 3, 5, 7), (3, 2, 8, 12), (4, 4, 13, 2), (1, 7, 33, 9),
+    (6, 5, 16, 32), (2, 2, 64, 64), (5, 3, 17, 31),
+]
+
+
+@pytest.mark.parametrize("fmt", [4, 6])
+@pytest.mark.parametrize("rnd", [0, 1])
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("dist", ["normal", "relu", "t3"])
+def test_quantize_bit_exact(shape, fmt, rnd, dist):
+    log("quantize", shape, fmt, rnd, dist)
+    seed = 1234567 + 17 * rnd
+    x = workloads.random_array(shape, seed=sum(shape) + len(dist), dist=dist)
+    q = gpu_quantize(to_dev(x), shape, fmt, mq.MQ_ROLE_ACT, rnd, seed)
+    torch.cuda.synchronize()
+    assert_quant_equal(q, oracle.quantize(x, fmt, rnd, seed), fmt, f"{shape} {fmt} {rnd}")
+
+
+SPECIAL = {
+    "zeros": lambda s: np.zeros(s, np.float32),
+    "neg_zeros": lambda s: -np.zeros(s, np.float32),
+    "nan": lambda s: _with(workloads.random_array(s, 3), (0, 0, 1, 1), np.nan),
+    "inf": lambda s: _with(workloads.random_array(s, 3), (0, 1, 2, 0), np.inf),
+    "ninf": lambda s: _with(workloads.random_array(s, 3), (0, 1, 2, 0), -np.inf),
+    "tiny": lambda s: (workloads.random_array(s, 4) * np.float32(1e-38)).astype(np.float32),
+    "denormal": lambda s: (workloads.random_array(s, 5) * np.float32(1e-42)).astype(np.float32),
+    "huge": lambda s: (workloads.random_array(s, 6) * np.float32(1e37)).astype(np.float32),
+    "onehot": lambda s: _with(np.zeros(s, np.float32), (0, 0, 0, 0), 1.0),
+    "sparse_zero_squares": lambda s: _zero_some(workloads.random_array(s, 7)),
+    "ties": lambda s: _ties(s),
+}
+
+
+def _with(a, idx, v):
+    a = a.copy()
+    a[idx] = v
+    return a
+
+
+def _zero_some(a):
+    a = a.copy()
+    a[:, :, :4, :4] = 0.0
+    a[:, :, 4:8, :] = -0.0
+    return a
+
+
+def _ties(s):
+    # values whose quotients land exactly on grid midpoints (T = 1, B = 448 squares)
+    rng = np.random.default_rng(0)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 0.0625, 0.1875, 7.25, 6.75],
+                    np.float32)
+    a = rng.choice(mids, size=s).astype(np.float32) * 448
+    a.reshape(-1)[0] = 2688.0
+    return a * np.where(rng.random(s) < 0.5, -1, 1).astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", [4, 6])
+@pytest.mark.parametrize("rnd", [0, 1])
+@pytest.mark.parametrize("case", sorted(SPECIAL))
+def test_quantize_special_values(case, fmt, rnd):
+    shape = (2, 3, 9, 10)
+    log("quantize special", case, fmt, rnd)
+    x = SPECIAL[case](shape)
+    q = gpu_quantize(to_dev(x), shape, fmt, mq.MQ_ROLE_ACT, rnd, 99)
+    torch.cuda.synchronize()
+    assert_quant_equal(q, oracle.quantize(x, fmt, rnd, 99), fmt, case)
+
+
+def _layer_tensors(name):
+    out = []
+    for layer in workloads.CONFIGS[name]():
+        x, w, g = workloads.make_tensors(layer)
+        out.append((layer, x, w, g))
+    return out
+
+
+@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4", "c5"])
+def test_quantize_full_size_layers(cfg):
+    """Every tensor of the workload layers at full size, through GPU relayout + quantize."""
+    layers = workloads.CONFIGS[cfg]()
+    if cfg == "c5":
+        layers = layers[:2] + layers[4:7]  # one of each shape class keeps the run short
+    for layer in layers:
+        log("full-size quantize", layer.name)
+        x, w, g = workloads.make_tensors(layer)
+        N, Ci, H, W, Co, Kh, Kw = (layer.N, layer.Cin, layer.H, layer.W, layer.Cout, layer.Kh,
+                                   layer.Kw)
+        for name, a, shape, role, rnd, seed in (
+                ("x", x, (H, W, Ci, N), mq.MQ_ROLE_ACT, 0, 0),
+                ("w", w, (Kh, Kw, Co, Ci), mq.MQ_ROLE_WEIGHT, 0, 0),
+                ("g", g, (layer.Ho, layer.Wo, Co, N), mq.MQ_ROLE_GRAD, 1, layer.sr_seed)):
+            t = to_dev(a)
+            dst = torch.empty(a.size, dtype=torch.float32, device="cuda")
+            if name == "w":
+                mq.mq_relayout_weight(t, dst, Co, Ci, Kh, Kw, 0)
+                ref_src = oracle.oihw_to_tap_major(a)
+            else:
+                n_, c_, h_, w_ = a.shape
+                mq.mq_relayout_cbf(t, dst, n_, c_, h_, w_, 0)
+                ref_src = oracle.nchw_to_cbf(a)
+            torch.cuda.synchronize()
+            assert np.array_equal(dst.cpu().numpy().reshape(ref_src.shape), ref_src), \
+                f"{layer.name} {name}: relayout differs"
+            q = gpu_quantize(dst, shape, layer.fmt, role, rnd, seed)
+            torch.cuda.synchronize()
+            assert_quant_equal(q, oracle.quantize(ref_src, layer.fmt, rnd, seed), layer.fmt,
+                               f"{layer.name}.{name}")
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1), (3, 5, 7, 2), (2, 70, 9, 130), (64, 3, 1, 1)])
+def test_relayout_roundtrip(shape):
+    N, C, H, W = shape
+    x = workloads.random_array(shape, seed=8)
+    t = to_dev(x)
+    c = torch.empty(x.size, dtype=torch.float32, device="cuda")
+    back = torch.empty_like(c)
+    mq.mq_relayout_cbf(t, c, N, C, H, W, 0)
+    mq.mq_relayout_cbf(c, back, N, C, H, W, 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(c.cpu().numpy().reshape(H, W, C, N), oracle.nchw_to_cbf(x))
+    assert np.array_equal(back.cpu().numpy().reshape(shape), x)
+    w = workloads.random_array((C, N, 3, 2), seed=9)
+    tw = to_dev(w)
+    tm = torch.empty(w.size, dtype=torch.float32, device="cuda")
+    wb = torch.empty_like(tm)
+    mq.mq_relayout_weight(tw, tm, C, N, 3, 2, 0)
+    mq.mq_relayout_weight(tm, wb, C, N, 3, 2, 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(tm.cpu().numpy().reshape(3, 2, C, N), oracle.oihw_to_tap_major(w))
+    assert np.array_equal(wb.cpu().numpy().reshape(w.shape), w)
+
+
+def test_quantize_is_deterministic_and_seeded():
+    shape = (4, 4, 16, 16)
+    x = workloads.random_array(shape, seed=10)
+    t = to_dev(x)
+    a = gpu_quantize(t, shape, 4, mq.MQ_ROLE_GRAD, 1, 5)
+    b = gpu_quantize(t, shape, 4, mq.MQ_ROLE_GRAD, 1, 5)
+    c = gpu_quantize(t, shape, 4, mq.MQ_ROLE_GRAD, 1, 6)
+    torch.cuda.synchronize()
+    assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
+    assert not torch.equal(a.codes, c.codes)
+    assert torch.equal(a.scales, c.scales)
