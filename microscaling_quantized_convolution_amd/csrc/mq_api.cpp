@@ -123,6 +123,9 @@ mq_status mq_conv_fwd(const mq_conv *p, const mq_qtensor *x, const mq_qtensor *w
         !dims_are(w, p->Kh, p->Kw, p->Cout, p->Cin, MQ_ROLE_WEIGHT) || x->fmt != w->fmt)
         return MQ_ERR_SHAPE;
     if (!conv_supported(g)) return MQ_ERR_UNSUPPORTED;
+    if (mq::spatial_supported(g))
+        return launch_status(
+            mq::launch_conv_fwd_spatial(g, x->fmt, operand(x), operand(w), y, stream));
     return launch_status(mq::launch_conv_fwd(g, x->fmt, operand(x), operand(w), y, stream));
 }
 
@@ -130,7 +133,8 @@ size_t mq_wgrad_workspace_bytes(const mq_conv *p)
 {
     mq::ConvGeom g;
     if (!conv_geom(p, &g)) return 0;
-    return mq::wgrad_workspace_bytes(g);
+    return mq::wgrad_fast_supported(g) ? mq::wgrad_fast_workspace_bytes(g)
+                                        : mq::wgrad_workspace_bytes(g);
 }
 
 mq_status mq_conv_wgrad(const mq_conv *p, const mq_qtensor *gy, const mq_qtensor *x, float *gw,
@@ -142,6 +146,11 @@ mq_status mq_conv_wgrad(const mq_conv *p, const mq_qtensor *gy, const mq_qtensor
         !dims_are(x, p->H, p->W, p->Cin, p->N, MQ_ROLE_ACT) || gy->fmt != x->fmt)
         return MQ_ERR_SHAPE;
     if (!conv_supported(g)) return MQ_ERR_UNSUPPORTED;
+    if (mq::wgrad_fast_supported(g)) {
+        if (!ws || ws_bytes < mq::wgrad_fast_workspace_bytes(g)) return MQ_ERR_WORKSPACE;
+        return launch_status(mq::launch_conv_wgrad_fast(g, x->fmt, operand(gy), operand(x), gw,
+                                                        ws, ws_bytes, stream));
+    }
     if (!ws || ws_bytes < mq::wgrad_workspace_bytes(g)) return MQ_ERR_WORKSPACE;
     return launch_status(mq::launch_conv_wgrad(g, x->fmt, operand(gy), operand(x), gw, ws,
                                                ws_bytes, stream));
@@ -156,6 +165,9 @@ mq_status mq_conv_dgrad(const mq_conv *p, const mq_qtensor *w, const mq_qtensor 
         !dims_are(gy, g.Ho, g.Wo, p->Cout, p->N, MQ_ROLE_GRAD) || w->fmt != gy->fmt)
         return MQ_ERR_SHAPE;
     if (!conv_supported(g)) return MQ_ERR_UNSUPPORTED;
+    if (mq::spatial_supported(g))
+        return launch_status(
+            mq::launch_conv_dgrad_spatial(g, w->fmt, operand(w), operand(gy), gx, stream));
     return launch_status(mq::launch_conv_dgrad(g, w->fmt, operand(w), operand(gy), gx, stream));
 }
 

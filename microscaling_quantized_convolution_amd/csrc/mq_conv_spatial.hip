@@ -1,0 +1,375 @@
+// mq_conv_spatial.hip -- forward and input-gradient convolutions as halo-tiled implicit GEMMs.
+//
+// Forward Y = W . X' and input gradient G_X = col2im(W^T . G_Y) (onedev.kr MicroQonv digest,
+// section "How it differs") share one structure: an output pixel sums, over a set of taps, a
+// channel contraction of one weight tap with one input pixel of a channel-batch-first tensor
+// (section "How it works": per pixel all channels and batch elements are contiguous):
+//
+//   Out[i*sO + ah][j*sO + aw][m][n] = sum_{kh',kw'} sum_k A_tap[m][k] * In[i*SI + kh' + r0]
+//                                                                        [j*SI + kw' + c0][k][n]
+//   forward:            In = X,   A_tap = W[kh'][kw'],            SI = stride, r0 = -pad
+//   input grad, s = 1:  In = G_Y, A_tap = W[Kh-1-kh'][Kw-1-kw']^T, r0 = pad - Kh + 1
+//   input grad, s = 2:  one class per output parity (ah, aw); only the taps with
+//                       kh = ah + pad (mod 2) reach it, so the class is a dense stride-1
+//                       convolution with the kernel rows kh = ah + pad - 2*(r0 + kh') (no MFMA
+//                       work is spent on the zeros a transposed convolution would insert).
+//
+// A workgroup owns 64 rows (m) x PH x PW output pixels x 32 batch elements. Per 16-channel chunk
+// it decodes the weight taps and the input halo ((PH-1)*SI + Kh rows x (PW-1)*SI + Kw columns)
+// once into LDS as fp16 and every wave runs 32x32x16 fp16 MFMAs for its 64 x 4-pixel tile over
+// all taps; the halo is read once per chunk and reused by every tap, and the weight tile by
+// every pixel. The im2col matrix never exists outside registers.
+#include "mq_kernels.hpp"
+#include "mq_stage.hpp"
+
+namespace mq {
+
+struct SpatialClass {
+    int ah, aw;       // output offset of this class
+    int OHs, OWs;     // class sub-grid extent
+    int kh, kw;       // sub-kernel extent (0 = no tap reaches this class)
+    int r0, c0;       // input offset of sub-kernel tap (0,0)
+    int Ah, Bh, Aw, Bw; // weight tap row = Ah + Bh*kh', column = Aw + Bw*kw'
+    int tiles_w, tiles;  // pixel tiles along the sub-grid width, total pixel tiles
+};
+
+struct SpatialArgs {
+    const uint8_t *in_codes;
+    const uint8_t *in_scales;
+    const float *in_T;
+    int IH, IW, K4, N4;   // input squares [IH][IW][K4][N4]
+    const uint8_t *w_codes;
+    const uint8_t *w_scales;
+    const float *w_T;
+    int Kh, Kw, Cout4, Cin4; // weight squares [Kh*Kw][Cout4][Cin4]
+    float *out;
+    uint32_t out_bytes;
+    int OWf, M, N;        // output [..][OWf][M][N]
+    int M4, nblk;         // row squares, batch blocks of 32
+    int sO;
+    SpatialClass cls[4];
+};
+
+// A_KR: the weight square's first dimension (Cout) is the reduction (input gradient);
+// otherwise its second (Cin) is (forward). The input operand's squares always have the
+// reduction (channels) along their first dimension.
+//
+// Waves [0, NCW) consume: MFMAs on one LDS buffer. Waves [NCW, 2*NCW) produce: they load the
+// squares of the stage after next into registers and decode the next stage into the other LDS
+// buffer. Both sides meet at one barrier per stage, so a SIMD runs one MFMA wave and one decode
+// wave side by side.
+template <int FMT, bool A_KR, int SI, int PH, int PW>
+__global__ void __launch_bounds__(32 * PH * PW)
+conv_spatial_kernel(SpatialArgs a)
+{
+    constexpr int NCW = PH * PW / 4;  // consumer waves (4 pixels each)
+    constexpr int NP = 64 * NCW;      // producer threads
+    constexpr int KHM = 3, KWM = 3;
+    constexpr int HRM = (PH - 1) * SI + KHM, HCM = (PW - 1) * SI + KWM;
+    constexpr int WCOLS = 3 * SI + KWM; // halo columns one wave touches (4 pixels)
+    constexpr int ABYTES = KHM * KWM * 64 * 32, BBYTES = HRM * HCM * 32 * 32;
+    // items: weight (tap, m4) in [0, nA), halo (pixel, n4) in [nA64, nA64 + nB); nA64 rounds nA
+    // up to whole waves so that no wave runs both item kinds in one slot
+    constexpr int ITEMS = ((KHM * KWM * 16 + 63) / 64 * 64 + HRM * HCM * 8 + NP - 1) / NP;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][ABYTES + BBYTES];
+
+    const SpatialClass &cl = a.cls[blockIdx.z];
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
+    const int bx = blockIdx.x;
+    const int nb = bx % a.nblk;
+    const int tile = bx / a.nblk;
+    if (tile >= cl.tiles) return;
+    const int ti = tile / cl.tiles_w, tj = tile - ti * cl.tiles_w;
+    const int i0 = ti * PH, j0 = tj * PW;
+    const int m4_0 = blockIdx.y * 16;
+    const int kh = cl.kh, kw = cl.kw, ntap = kh * kw;
+    const int HR = (PH - 1) * SI + kh, HC = (PW - 1) * SI + kw;
+    const int nchunk = ntap > 0 ? (a.K4 + 3) / 4 : 0;
+
+    if (wave >= NCW) {
+        // ================= producer =================
+        const int ptid = tid - NP;
+        const int ih0 = i0 * SI + cl.r0, iw0 = j0 * SI + cl.c0;
+        const int nA = ntap * 16, nA64 = (nA + 63) & ~63, nAB = nA64 + HR * HC * 8;
+        constexpr int CB = (FMT == kFP4) ? 8 : 12;
+        const uint32_t in_sq = (uint32_t)a.IH * a.IW * a.K4 * a.N4;
+        const uint32_t w_sq = (uint32_t)a.Kh * a.Kw * a.Cout4 * a.Cin4;
+        const rsrc_t in_c = make_rsrc(a.in_codes, in_sq * CB), in_s = make_rsrc(a.in_scales, in_sq);
+        const rsrc_t w_c = make_rsrc(a.w_codes, w_sq * CB), w_s = make_rsrc(a.w_scales, w_sq);
+
+        // per slot: first square of chunk 0, the per-chunk step of that index, stride between
+        // the item's four squares, validity, and LDS row
+        uint32_t sq_base[ITEMS], sq_chunk[ITEMS], sq_step[ITEMS];
+        bool valid[ITEMS];
+        int row[ITEMS];
+    #pragma unroll
+        for (int q = 0; q < ITEMS; ++q) {
+            const int it = ptid + q * NP;
+            const int wit = wave_uniform(it & ~63);
+            sq_base[q] = 0; sq_chunk[q] = 0; sq_step[q] = 0; valid[q] = false; row[q] = 0;
+            if (wit < nA64) {
+                const int t = it >> 4, m4 = m4_0 + (it & 15);
+                const int tkh = t / kw, tkw = t - tkh * kw;
+                const int wtap = (cl.Ah + cl.Bh * tkh) * a.Kw + (cl.Aw + cl.Bw * tkw);
+                if (A_KR) {
+                    sq_base[q] = (uint32_t)wtap * a.Cout4 * a.Cin4 + m4;
+                    sq_step[q] = a.Cin4;
+                    sq_chunk[q] = 4u * a.Cin4;
+                } else {
+                    sq_base[q] = ((uint32_t)wtap * a.Cout4 + m4) * a.Cin4;
+                    sq_step[q] = 1;
+                    sq_chunk[q] = 4;
+                }
+                valid[q] = it < nA && m4 < a.M4;
+                row[q] = t * 64 + 4 * (it & 15);
+            } else if (wit < nAB) {
+                const int j = it - nA64, hp = j >> 3, n4 = nb * 8 + (j & 7);
+                const int hr = hp / HC, hc = hp - hr * HC;
+                const int ih = ih0 + hr, iw = iw0 + hc;
+                valid[q] = it < nAB && ih >= 0 && ih < a.IH && iw >= 0 && iw < a.IW && n4 < a.N4;
+                sq_base[q] = ((uint32_t)ih * a.IW + iw) * a.K4 * a.N4 + n4;
+                sq_step[q] = a.N4;
+                sq_chunk[q] = 4u * a.N4;
+                row[q] = hp * 32 + 4 * (j & 7);
+            }
+        }
+        RawItem<FMT> raw[ITEMS];
+        auto load = [&](int c) {
+            const int kvalid = a.K4 - 4 * c;
+            const uint32_t kmask = kvalid >= 4 ? 0xFu : ((1u << kvalid) - 1u);
+    #pragma unroll
+            for (int q = 0; q < ITEMS; ++q) {
+                const int wit = wave_uniform((ptid + q * NP) & ~63);
+                const uint32_t sq0 = sq_base[q] + (uint32_t)c * sq_chunk[q];
+                if (wit < nA64)
+                    load_item<FMT>(raw[q], w_c, w_s, sq0, sq_step[q], valid[q] ? kmask : 0u);
+                else if (wit < nAB)
+                    load_item<FMT>(raw[q], in_c, in_s, sq0, sq_step[q], valid[q] ? kmask : 0u);
+            }
+        };
+        auto store = [&](int buf) {
+    #pragma unroll
+            for (int q = 0; q < ITEMS; ++q) {
+                const int it = ptid + q * NP;
+                const int wit = wave_uniform(it & ~63);
+                if (wit < nA64) {
+                    if (it < nA) store_item<FMT, A_KR>(raw[q], lds[buf], row[q]);
+                } else if (wit < nAB) {
+                    if (it < nAB) store_item<FMT, true>(raw[q], lds[buf] + ABYTES, row[q]);
+                }
+            }
+        };
+
+        if (nchunk > 0) {
+            load(0);
+            store(0);
+            if (nchunk > 1) load(1);
+        }
+        __syncthreads();
+        for (int c = 0; c < nchunk; ++c) {
+            if (c + 1 < nchunk) {
+                store((c + 1) & 1);
+                if (c + 2 < nchunk) load(c + 2);
+            }
+            __syncthreads();
+        }
+        return;
+    }
+
+    // ================= consumer =================
+    // (the two roles take wave-uniform branches and pass the same number of barriers)
+    const int wr = wave / (PW / 4), wp = wave % (PW / 4); // consumer pixel row, pixel group
+    f32x16_t acc[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[u][j][r] = 0.0f;
+    const int half = lane >> 5, l32 = lane & 31;
+    __syncthreads();
+    for (int c = 0; c < nchunk; ++c) {
+        const uint8_t *As = lds[c & 1], *Bs = lds[c & 1] + ABYTES;
+#pragma unroll
+        for (int th = 0; th < KHM; ++th) {
+            if (th < kh) {
+                const int hr = wr * SI + th;
+                // every column of the wave's window is read (columns past the sub-kernel's
+                // extent stay inside the LDS buffer and are never used)
+                u32x4_t bf[WCOLS];
+#pragma unroll
+                for (int cc = 0; cc < WCOLS; ++cc) {
+                    const int hc = wp * 4 * SI + cc;
+                    bf[cc] = *reinterpret_cast<const u32x4_t *>(
+                        Bs + lds_row_off((hr * HC + hc) * 32 + l32, half));
+                }
+#pragma unroll
+                for (int tw = 0; tw < KWM; ++tw) {
+                    if (tw < kw) {
+                        const int t = th * kw + tw;
+                        const f16x8_t a0 = __builtin_bit_cast(
+                            f16x8_t, *reinterpret_cast<const u32x4_t *>(As + lds_row_off(t * 64 + l32, half)));
+                        const f16x8_t a1 = __builtin_bit_cast(
+                            f16x8_t, *reinterpret_cast<const u32x4_t *>(As + lds_row_off(t * 64 + 32 + l32, half)));
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const f16x8_t b = __builtin_bit_cast(f16x8_t, bf[j * SI + tw]);
+                            acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b, acc[0][j], 0, 0, 0);
+                            acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b, acc[1][j], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+        }
+            __syncthreads();
+    }
+
+    // ---- epilogue: scale by T_in * T_w and store fp32. Buffer stores: an element outside the
+    // output gets an out-of-range offset and is dropped; the row offset of each accumulator
+    // register is a wave-uniform constant passed as soffset. ----
+    const double sd = (double)*a.in_T * (double)*a.w_T;
+    const bool fsafe = scale_is_float_safe(sd);
+    const float sf = (float)sd;
+    const rsrc_t out_r = make_rsrc(a.out, a.out_bytes);
+    const int i = i0 + wr;
+    const int n = nb * 32 + l32;
+    const bool full_m = 4 * m4_0 + 64 <= a.M;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int jj = j0 + wp * 4 + j;
+        const bool pix_ok = i < cl.OHs && jj < cl.OWs && n < a.N;
+        const int oh = i * a.sO + cl.ah, ow = jj * a.sO + cl.aw;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int mrow = 4 * m4_0 + 32 * u + 4 * half; // row of register 0
+            const uint32_t vbase =
+                pix_ok ? ((((uint32_t)oh * a.OWf + ow) * a.M + mrow) * a.N + n) * 4u : kBad;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int dm = 8 * (r >> 2) + (r & 3);
+                const float v = fsafe ? acc[u][j][r] * sf : (float)((double)acc[u][j][r] * sd);
+                const uint32_t voff = (full_m || mrow + dm < a.M) ? vbase : kBad;
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), out_r,
+                                                      (int)voff, dm * a.N * 4, 0);
+            }
+        }
+    }
+}
+
+// ---- host side -----------------------------------------------------------------------------
+
+
+// Pixel tile per workgroup: 2 x 8 for stride-1 input walks, 1 x 8 for stride 2 (whose halo is
+// twice as wide), so that two LDS stage buffers fit.
+template <int SI> struct TileShape;
+template <> struct TileShape<1> { static constexpr int PH = 2, PW = 8; };
+template <> struct TileShape<2> { static constexpr int PH = 1, PW = 8; };
+
+static void set_tiles(SpatialClass &c, int PH, int PW)
+{
+    c.tiles_w = (c.OWs + PW - 1) / PW;
+    c.tiles = c.tiles_w * ((c.OHs + PH - 1) / PH);
+}
+
+bool spatial_supported(const ConvGeom &g)
+{
+    if (!(g.Kh <= 3 && g.Kw <= 3 && g.sh == g.sw && (g.sh == 1 || g.sh == 2) && g.ph < g.Kh &&
+          g.pw < g.Kw))
+        return false;
+    // 32-bit byte offsets below 2^31 for every operand and output
+    const uint64_t lim = 1ull << 31;
+    const uint64_t xs = (uint64_t)g.H * g.W * g.Cin4 * g.N4 * 12,
+                   gs = (uint64_t)g.Ho * g.Wo * g.Cout4 * g.N4 * 12,
+                   ws = (uint64_t)g.Kh * g.Kw * g.Cout4 * g.Cin4 * 12,
+                   ys = (uint64_t)g.Ho * g.Wo * g.Cout * g.N * 4,
+                   xo = (uint64_t)g.H * g.W * g.Cin * g.N * 4;
+    return xs < lim && gs < lim && ws < lim && ys < lim && xo < lim;
+}
+
+template <int FMT, bool A_KR, int SI>
+static hipError_t launch_spatial(SpatialArgs &a, int nclass, hipStream_t st)
+{
+    constexpr int PH = TileShape<SI>::PH, PW = TileShape<SI>::PW;
+    int max_tiles = 0;
+    for (int c = 0; c < nclass; ++c) {
+        set_tiles(a.cls[c], PH, PW);
+        if (a.cls[c].tiles > max_tiles) max_tiles = a.cls[c].tiles;
+    }
+    dim3 grid((unsigned)(max_tiles * a.nblk), (unsigned)((a.M4 + 15) / 16), (unsigned)nclass);
+    hipLaunchKernelGGL((conv_spatial_kernel<FMT, A_KR, SI, PH, PW>), grid, dim3(32 * PH * PW), 0,
+                       st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_conv_fwd_spatial(const ConvGeom &g, int fmt, QOperand x, QOperand w, float *y,
+                                   hipStream_t st)
+{
+    SpatialArgs a = {};
+    a.in_codes = x.codes; a.in_scales = x.scales; a.in_T = x.tscale;
+    a.IH = g.H; a.IW = g.W; a.K4 = g.Cin4; a.N4 = g.N4;
+    a.w_codes = w.codes; a.w_scales = w.scales; a.w_T = w.tscale;
+    a.Kh = g.Kh; a.Kw = g.Kw; a.Cout4 = g.Cout4; a.Cin4 = g.Cin4;
+    a.out = y; a.OWf = g.Wo; a.M = g.Cout; a.N = g.N; a.M4 = g.Cout4;
+    a.out_bytes = (uint32_t)((uint64_t)g.Ho * g.Wo * g.Cout * g.N * 4);
+    a.nblk = (g.N4 + 7) / 8; a.sO = 1;
+    SpatialClass &c = a.cls[0];
+    c.ah = c.aw = 0; c.OHs = g.Ho; c.OWs = g.Wo; c.kh = g.Kh; c.kw = g.Kw;
+    c.r0 = -g.ph; c.c0 = -g.pw; c.Ah = 0; c.Bh = 1; c.Aw = 0; c.Bw = 1;
+    if (fmt == kFP4)
+        return g.sh == 1 ? launch_spatial<kFP4, false, 1>(a, 1, st)
+                         : launch_spatial<kFP4, false, 2>(a, 1, st);
+    return g.sh == 1 ? launch_spatial<kFP6, false, 1>(a, 1, st)
+                     : launch_spatial<kFP6, false, 2>(a, 1, st);
+}
+
+// Sub-kernel of one output parity class of a stride-s input gradient along one dimension:
+// the kernel offsets k with (a + pad - k) divisible by s, as a dense range of input offsets.
+static void dgrad_class_dim(int a, int pad, int K, int s, int &cnt, int &r0, int &A, int &B)
+{
+    int kfirst = -1, klast = -1;
+    for (int k = 0; k < K; ++k)
+        if (((a + pad - k) % s + s) % s == 0) {
+            if (kfirst < 0) kfirst = k;
+            klast = k;
+        }
+    if (kfirst < 0) { cnt = 0; r0 = 0; A = 0; B = 0; return; }
+    cnt = (klast - kfirst) / s + 1;
+    r0 = (a + pad - klast) / s;   // smallest input offset (dh_min)
+    A = a + pad - s * r0;         // kernel row at sub-kernel index 0
+    B = -s;
+}
+
+hipError_t launch_conv_dgrad_spatial(const ConvGeom &g, int fmt, QOperand w, QOperand gy,
+                                     float *gx, hipStream_t st)
+{
+    SpatialArgs a = {};
+    a.in_codes = gy.codes; a.in_scales = gy.scales; a.in_T = gy.tscale;
+    a.IH = g.Ho; a.IW = g.Wo; a.K4 = g.Cout4; a.N4 = g.N4;
+    a.w_codes = w.codes; a.w_scales = w.scales; a.w_T = w.tscale;
+    a.Kh = g.Kh; a.Kw = g.Kw; a.Cout4 = g.Cout4; a.Cin4 = g.Cin4;
+    a.out = gx; a.OWf = g.W; a.M = g.Cin; a.N = g.N; a.M4 = g.Cin4;
+    a.out_bytes = (uint32_t)((uint64_t)g.H * g.W * g.Cin * g.N * 4);
+    a.nblk = (g.N4 + 7) / 8;
+    const int s = g.sh;
+    a.sO = s;
+    int nclass = 0;
+    for (int ah = 0; ah < s; ++ah)
+        for (int aw = 0; aw < s; ++aw) {
+            SpatialClass &c = a.cls[nclass++];
+            c.ah = ah; c.aw = aw;
+            c.OHs = (g.H - ah + s - 1) / s;
+            c.OWs = (g.W - aw + s - 1) / s;
+            if (s == 1) {
+                c.kh = g.Kh; c.kw = g.Kw;
+                c.r0 = g.ph - g.Kh + 1; c.c0 = g.pw - g.Kw + 1;
+                c.Ah = g.Kh - 1; c.Bh = -1; c.Aw = g.Kw - 1; c.Bw = -1;
+            } else {
+                dgrad_class_dim(ah, g.ph, g.Kh, s, c.kh, c.r0, c.Ah, c.Bh);
+                dgrad_class_dim(aw, g.pw, g.Kw, s, c.kw, c.c0, c.Aw, c.Bw);
+            }
+        }
+    if (fmt == kFP4) return launch_spatial<kFP4, true, 1>(a, nclass, st);
+    return launch_spatial<kFP6, true, 1>(a, nclass, st);
+}
+
+} // namespace mq

@@ -1,0 +1,305 @@
+// mq_conv_wgrad.hip -- weight-gradient GEMM G_W = G_Y . X'^T on channel-batch-first data.
+//
+// onedev.kr MicroQonv digest, section "How it differs": with G_{YfCout,N} (Cout x Hout*Wout*N)
+// the weight gradient is a GEMM whose reduction runs over output pixels and batch elements; in
+// the channel-batch-first layout (section "How it works") both operands are read along the batch
+// dimension N, which is the second side of every 4x4 square of G_Y and X, so neither operand
+// needs a transpose: a decoded square row is four consecutive reduction elements.
+//
+//   G_W[kh][kw][co][ci] = T_G * T_X * sum_{oh, ow, n} Gq[oh][ow][co][n]
+//                                        * Xq[oh*s - ph + kh][ow*s - pw + kw][ci][n]
+//
+// A workgroup owns one kernel row kh, 64 output channels, 64 input channels and every kw, and a
+// contiguous range of reduction stages; a stage is PW output pixels of one output row and 16 batch
+// elements. Per stage it decodes the G_Y strip (PW pixels) and the X row segment it meets
+// ((PW-1)*s + Kw pixels) once into LDS as fp16; each wave runs 32x32x16 fp16 MFMAs for a
+// 32 x 32 x Kw block. The fp32 partial block goes to the workspace, and a second kernel sums the
+// splits in a fixed order (deterministic) and applies the tensor scales.
+#include "mq_kernels.hpp"
+#include "mq_stage.hpp"
+
+namespace mq {
+
+namespace {
+
+constexpr int kRowBytes = 32; // 16 fp16 (one 16-element reduction step) per LDS row
+
+struct WgradArgs {
+    const uint8_t *g_codes, *g_scales; // squares [Ho][Wo][Cout4][N4]
+    const uint8_t *x_codes, *x_scales; // squares [H][W][Cin4][N4]
+    float *part;                       // [split][Kh*Kw][Cout][Cin] fp32 partial sums
+    int H, W, Ho, Wo, Cin, Cout, Cin4, Cout4, N4;
+    int Kh, Kw, sh, sw, ph, pw;
+    int owb, nch;          // pixel blocks per output row, 16-element batch chunks
+    int stages, per_split; // total stages, stages per split
+    int cot, cit;          // Cout / Cin tiles of 64
+    int64_t split_stride;  // floats per split
+};
+
+// Waves 0..3 consume (MFMAs on one LDS buffer); waves 4..7 produce (load the squares of the
+// stage after next, decode the next stage into the other buffer); one barrier per stage.
+// Output pixels per stage: 16 for stride 1, 8 for stride 2 (twice as wide an X segment), so that
+// two stage buffers fit in LDS.
+template <int SI> struct StagePixels { static constexpr int kPW = SI == 1 ? 8 : 8; };
+
+template <int FMT, int SI>
+__global__ void __launch_bounds__(512) conv_wgrad_kernel(WgradArgs a)
+{
+    constexpr int kPWg = StagePixels<SI>::kPW;
+    constexpr int KWM = 3;
+    constexpr int HCM = (kPWg - 1) * SI + KWM;
+    constexpr int GBYTES = kPWg * 64 * kRowBytes, XBYTES = HCM * 64 * kRowBytes;
+    constexpr int ITEMS = (kPWg * 16 + HCM * 16 + 255) / 256;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][GBYTES + XBYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
+    const int split = blockIdx.x;
+    int tile = blockIdx.y;
+    const int cit_i = tile % a.cit; tile /= a.cit;
+    const int cot_i = tile % a.cot;
+    const int kh = tile / a.cot;
+    const int co4_0 = cot_i * 16, ci4_0 = cit_i * 16;
+    const int kw = a.Kw;
+    const int HC = (kPWg - 1) * SI + kw;
+    const int st0 = split * a.per_split;
+    const int st1 = min(a.stages, st0 + a.per_split);
+    const int nst = st1 > st0 ? st1 - st0 : 0;
+
+    if (wave >= 4) {
+        // ================= producer =================
+        const int ptid = tid - 256;
+        const int nG = kPWg * 16, nGX = nG + HC * 16;
+        constexpr int CB = (FMT == kFP4) ? 8 : 12;
+        const uint32_t g_sq = (uint32_t)a.Ho * a.Wo * a.Cout4 * a.N4;
+        const uint32_t x_sq = (uint32_t)a.H * a.W * a.Cin4 * a.N4;
+        const rsrc_t g_c = make_rsrc(a.g_codes, g_sq * CB), g_s = make_rsrc(a.g_scales, g_sq);
+        const rsrc_t x_c = make_rsrc(a.x_codes, x_sq * CB), x_s = make_rsrc(a.x_scales, x_sq);
+        // Producer items: it < nG -> G_Y strip (pixel it/16, co4 it%16); else X segment (column,
+        // ci4). Each item spans the four batch squares 4*nc .. 4*nc+3 (consecutive in memory). nG is
+        // a whole number of waves, so no wave mixes the two kinds.
+        RawItem<FMT> raw[ITEMS];
+        auto load = [&](int st) {
+            const int nc = st % a.nch;
+            const int rest = st / a.nch;
+            const int ob = rest % a.owb;
+            const int oh = rest / a.owb;
+            const int ow0 = ob * kPWg;
+            const int ih = oh * SI - a.ph + kh;
+            const int iw0 = ow0 * SI - a.pw;
+            const int nvalid = a.N4 - 4 * nc;
+            const uint32_t nmask = nvalid >= 4 ? 0xFu : ((1u << nvalid) - 1u);
+    #pragma unroll
+            for (int q = 0; q < ITEMS; ++q) {
+                const int it = ptid + q * 256;
+                const int wit = wave_uniform(it & ~63);
+                if (wit < nG) {
+                    const int ow = ow0 + (it >> 4), co4 = co4_0 + (it & 15);
+                    const uint32_t sq0 = (((uint32_t)oh * a.Wo + ow) * a.Cout4 + co4) * a.N4 + 4 * nc;
+                    const uint32_t mask = (ow < a.Wo && co4 < a.Cout4) ? nmask : 0u;
+                    load_item<FMT>(raw[q], g_c, g_s, sq0, 1u, mask);
+                } else if (wit < nGX) {
+                    const int j = it - nG;
+                    const int iw = iw0 + (j >> 4), ci4 = ci4_0 + (j & 15);
+                    const uint32_t sq0 = (((uint32_t)ih * a.W + iw) * a.Cin4 + ci4) * a.N4 + 4 * nc;
+                    const bool in = it < nGX && ih >= 0 && ih < a.H && iw >= 0 && iw < a.W &&
+                                    ci4 < a.Cin4;
+                    load_item<FMT>(raw[q], x_c, x_s, sq0, 1u, in ? nmask : 0u);
+                }
+            }
+        };
+        auto store = [&](int buf) {
+    #pragma unroll
+            for (int q = 0; q < ITEMS; ++q) {
+                const int it = ptid + q * 256;
+                const int wit = wave_uniform(it & ~63);
+                if (wit < nG) store_item<FMT, false>(raw[q], lds[buf], (it >> 4) * 64 + 4 * (it & 15));
+                else if (wit < nGX && it < nGX) {
+                    const int j = it - nG;
+                    store_item<FMT, false>(raw[q], lds[buf] + GBYTES, (j >> 4) * 64 + 4 * (j & 15));
+                }
+            }
+        };
+
+        if (nst > 0) {
+            load(st0);
+            store(0);
+            if (nst > 1) load(st0 + 1);
+        }
+        __syncthreads();
+        for (int c = 0; c < nst; ++c) {
+            if (c + 1 < nst) {
+                store((c + 1) & 1);
+                if (c + 2 < nst) load(st0 + c + 2);
+            }
+            __syncthreads();
+        }
+        return;
+    }
+
+    // ================= consumer =================
+    // (the two roles take wave-uniform branches and pass the same number of barriers)
+    const int wm = wave & 1, wc = wave >> 1;
+    f32x16_t acc[KWM];
+#pragma unroll
+    for (int t = 0; t < KWM; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+    const int half = lane >> 5, l32 = lane & 31;
+    __syncthreads();
+    for (int c = 0; c < nst; ++c) {
+        const uint8_t *Gs = lds[c & 1], *Xs = lds[c & 1] + GBYTES;
+        // every X column of the buffer is read (columns past HC are never used)
+        u32x4_t xf[HCM];
+#pragma unroll
+        for (int cc = 0; cc < HCM; ++cc)
+            xf[cc] = *reinterpret_cast<const u32x4_t *>(Xs + lds_row_off(cc * 64 + wc * 32 + l32, half));
+#pragma unroll
+        for (int px = 0; px < kPWg; ++px) {
+            const f16x8_t gf = __builtin_bit_cast(
+                f16x8_t, *reinterpret_cast<const u32x4_t *>(Gs + lds_row_off(px * 64 + wm * 32 + l32, half)));
+#pragma unroll
+            for (int t = 0; t < KWM; ++t)
+                if (t < kw)
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        gf, __builtin_bit_cast(f16x8_t, xf[px * SI + t]), acc[t], 0, 0, 0);
+        }
+            __syncthreads();
+    }
+
+    // ---- partial block: part[split][kh*Kw + kw][co][ci] ----
+    float *out = a.part + (int64_t)split * a.split_stride;
+    const int ci = ci4_0 * 4 + wc * 32 + l32;
+#pragma unroll
+    for (int t = 0; t < KWM; ++t) {
+        if (t >= kw) continue;
+        float *o = out + (int64_t)(kh * kw + t) * a.Cout * a.Cin;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int co = co4_0 * 4 + wm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (co < a.Cout && ci < a.Cin) o[(int64_t)co * a.Cin + ci] = acc[t][r];
+        }
+    }
+}
+
+// out[i] = T_G * T_X * sum_{s = 0..S-1} part[s][i], summed in split order. A workgroup holds 64
+// consecutive i (as 16 float4) x 16 split groups; group g sums splits g, g+16, ... in order and
+// the 16 group sums are added in group order.
+__global__ void __launch_bounds__(256) wgrad_sum_kernel(const float *__restrict__ part, int S,
+                                                        int64_t stride, int64_t total,
+                                                        const float *tg, const float *tx,
+                                                        float *__restrict__ out)
+{
+    __shared__ float4 red[16][17];
+    const int v = threadIdx.x & 15, g = threadIdx.x >> 4;
+    const int64_t i4 = (int64_t)blockIdx.x * 16 + v; // float4 index
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    const bool vec = (total % 4 == 0) && (stride % 4 == 0);
+    if (vec && i4 * 4 < total) {
+        for (int z = g; z < S; z += 16) {
+            const float4 p = *reinterpret_cast<const float4 *>(part + z * stride + i4 * 4);
+            s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+        }
+    } else if (!vec) {
+        float e[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < 4; ++q) {
+            const int64_t i = i4 * 4 + q;
+            if (i < total)
+                for (int z = g; z < S; z += 16) e[q] += part[z * stride + i];
+        }
+        s = make_float4(e[0], e[1], e[2], e[3]);
+    }
+    red[g][v] = s;
+    __syncthreads();
+    if (g == 0) {
+        float4 t = red[0][v];
+        for (int q = 1; q < 16; ++q) {
+            const float4 p = red[q][v];
+            t.x += p.x; t.y += p.y; t.z += p.z; t.w += p.w;
+        }
+        const double sc = (double)*tg * (double)*tx;
+        const float r[4] = {t.x, t.y, t.z, t.w};
+        for (int q = 0; q < 4; ++q) {
+            const int64_t i = i4 * 4 + q;
+            if (i < total) out[i] = (float)((double)r[q] * sc);
+        }
+    }
+}
+
+struct Plan {
+    int owb, nch, stages, cot, cit, tiles, splits, per_split;
+    int64_t split_stride;
+    size_t bytes;
+};
+
+Plan plan(const ConvGeom &g)
+{
+    Plan p;
+    const int kPWg = g.sh == 1 ? StagePixels<1>::kPW : StagePixels<2>::kPW;
+    p.owb = (g.Wo + kPWg - 1) / kPWg;
+    p.nch = (g.N4 + 3) / 4;
+    p.stages = g.Ho * p.owb * p.nch;
+    p.cot = (g.Cout4 + 15) / 16;
+    p.cit = (g.Cin4 + 15) / 16;
+    p.tiles = g.Kh * p.cot * p.cit;
+    p.split_stride = (int64_t)g.Kh * g.Kw * g.Cout * g.Cin;
+    // enough workgroups to fill the GPU, but at most ~16 MB of partial sums
+    const int64_t out_bytes = p.split_stride * 4;
+    int64_t s = (256 + p.tiles - 1) / p.tiles; // one 8-wave workgroup per CU
+    int64_t cap = (16ll << 20) / (out_bytes > 0 ? out_bytes : 1);
+    if (cap < 1) cap = 1;
+    if (s > cap) s = cap;
+    if (s > p.stages) s = p.stages;
+    if (s < 1) s = 1;
+    p.per_split = (int)((p.stages + s - 1) / s);
+    p.splits = (p.stages + p.per_split - 1) / p.per_split;
+    p.bytes = (size_t)p.splits * (size_t)p.split_stride * 4;
+    return p;
+}
+
+} // namespace
+
+bool wgrad_fast_supported(const ConvGeom &g)
+{
+    if (g.Kw > 3 || g.sh != g.sw || (g.sh != 1 && g.sh != 2)) return false;
+    // 32-bit byte offsets below 2^31 for the operands and one split's partial block
+    const uint64_t lim = 1ull << 31;
+    const uint64_t xs = (uint64_t)g.H * g.W * g.Cin4 * g.N4 * 12,
+                   gs = (uint64_t)g.Ho * g.Wo * g.Cout4 * g.N4 * 12,
+                   ps = (uint64_t)g.Kh * g.Kw * g.Cout * g.Cin * 4;
+    return xs < lim && gs < lim && ps < lim;
+}
+
+size_t wgrad_fast_workspace_bytes(const ConvGeom &g) { return plan(g).bytes; }
+
+hipError_t launch_conv_wgrad_fast(const ConvGeom &g, int fmt, QOperand gy, QOperand x, float *gw,
+                                  void *ws, size_t ws_bytes, hipStream_t st)
+{
+    const Plan p = plan(g);
+    if (ws_bytes < p.bytes) return hipErrorInvalidValue;
+    WgradArgs a;
+    a.g_codes = gy.codes; a.g_scales = gy.scales; a.x_codes = x.codes; a.x_scales = x.scales;
+    a.part = reinterpret_cast<float *>(ws);
+    a.H = g.H; a.W = g.W; a.Ho = g.Ho; a.Wo = g.Wo; a.Cin = g.Cin; a.Cout = g.Cout;
+    a.Cin4 = g.Cin4; a.Cout4 = g.Cout4; a.N4 = g.N4;
+    a.Kh = g.Kh; a.Kw = g.Kw; a.sh = g.sh; a.sw = g.sw; a.ph = g.ph; a.pw = g.pw;
+    a.owb = p.owb; a.nch = p.nch; a.stages = p.stages; a.per_split = p.per_split;
+    a.cot = p.cot; a.cit = p.cit; a.split_stride = p.split_stride;
+    dim3 grid((unsigned)p.splits, (unsigned)p.tiles, 1);
+    if (fmt == kFP4) {
+        if (g.sh == 1) hipLaunchKernelGGL((conv_wgrad_kernel<kFP4, 1>), grid, dim3(512), 0, st, a);
+        else hipLaunchKernelGGL((conv_wgrad_kernel<kFP4, 2>), grid, dim3(512), 0, st, a);
+    } else {
+        if (g.sh == 1) hipLaunchKernelGGL((conv_wgrad_kernel<kFP6, 1>), grid, dim3(512), 0, st, a);
+        else hipLaunchKernelGGL((conv_wgrad_kernel<kFP6, 2>), grid, dim3(512), 0, st, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t total = p.split_stride;
+    const unsigned blocks = (unsigned)((total + 63) / 64);
+    hipLaunchKernelGGL(wgrad_sum_kernel, dim3(blocks), dim3(256), 0, st,
+                       reinterpret_cast<const float *>(ws), p.splits, p.split_stride, total,
+                       gy.tscale, x.tscale, gw);
+    return hipGetLastError();
+}
+
+} // namespace mq

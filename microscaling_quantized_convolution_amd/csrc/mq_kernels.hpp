@@ -35,4 +35,18 @@ hipError_t launch_conv_wgrad(const ConvGeom &g, int fmt, QOperand gy, QOperand x
 hipError_t launch_conv_dgrad(const ConvGeom &g, int fmt, QOperand w, QOperand gy, float *gx,
                              hipStream_t st);
 
+// Halo-tiled forward / input-gradient kernels (Kh, Kw <= 3, equal strides 1 or 2).
+bool spatial_supported(const ConvGeom &g);
+hipError_t launch_conv_fwd_spatial(const ConvGeom &g, int fmt, QOperand x, QOperand w, float *y,
+                                   hipStream_t st);
+hipError_t launch_conv_dgrad_spatial(const ConvGeom &g, int fmt, QOperand w, QOperand gy,
+                                     float *gx, hipStream_t st);
+
+// Split-K weight gradient with all kw taps of one kernel row per workgroup (Kw <= 3,
+// equal strides 1 or 2) and a deterministic split sum.
+bool wgrad_fast_supported(const ConvGeom &g);
+size_t wgrad_fast_workspace_bytes(const ConvGeom &g);
+hipError_t launch_conv_wgrad_fast(const ConvGeom &g, int fmt, QOperand gy, QOperand x, float *gw,
+                                  void *ws, size_t ws_bytes, hipStream_t st);
+
 } // namespace mq

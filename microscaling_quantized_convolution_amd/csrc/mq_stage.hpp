@@ -1,0 +1,119 @@
+// mq_stage.hpp -- register staging of quantized squares for the convolution kernels.
+//
+// A staging item is four squares that are consecutive along a GEMM's reduction dimension
+// (16 reduction elements) and share one 4-element column or row block. Items are loaded into
+// registers one stage ahead (so the global-load latency hides behind the current stage's MFMAs),
+// then decoded exactly to fp16 and written to LDS as four 16-element reduction rows.
+#pragma once
+
+#include "mq_decode.hpp"
+
+namespace mq {
+
+template <int FMT> struct RawItem {
+    static constexpr int kW = (FMT == kFP4) ? 2 : 3; // code words per square
+    uint32_t w[4][kW];
+    uint32_t sc; // four scale bytes, square k in byte k
+};
+
+// Buffer resources: raw (stride 0) descriptors whose range check makes every load at an offset
+// >= the buffer size return zero. kBad is such an offset for every buffer this library builds
+// (all are below 2^31 bytes).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kBad = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Load the four squares sq0 + k*step (k = 0..3) whose bit k of `mask` is set; the others read as
+// zero codes with a zero scale (out-of-range buffer offsets).
+template <int FMT>
+__device__ __forceinline__ void load_item(RawItem<FMT> &r, rsrc_t codes, rsrc_t scales,
+                                          uint32_t sq0, uint32_t step, uint32_t mask)
+{
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+    r.sc = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const bool on = (mask >> k) & 1u;
+        const uint32_t sq = sq0 + k * step;
+        const uint32_t coff = on ? sq * (uint32_t)(RawItem<FMT>::kW * 4) : kBad;
+        const uint32_t soff = on ? sq : kBad;
+        if constexpr (FMT == kFP4) {
+            const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(codes, (int)coff, 0, 0);
+            r.w[k][0] = v[0];
+            r.w[k][1] = v[1];
+        } else {
+            const u32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(codes, (int)coff, 0, 0);
+            r.w[k][0] = v[0];
+            r.w[k][1] = v[1];
+            r.w[k][2] = v[2];
+        }
+        r.sc |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(scales, (int)soff, 0, 0) << (8 * k);
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ void decode_raw(const RawItem<FMT> &r, int k, uint32_t (&d)[8])
+{
+    const uint32_t sc = (r.sc >> (8 * k)) & 0xFFu;
+    if constexpr (FMT == kFP4) decode_fp4_square(r.w[k][0], r.w[k][1], sc, d);
+    else decode_fp6_square(r.w[k][0], r.w[k][1], r.w[k][2], sc, d);
+}
+
+// LDS operand rows: 16 fp16 (32 bytes, two 16-byte units). The unit index row*2 + chunk is
+// XORed with (row/4) mod 8, a permutation inside each aligned group of four rows, so that both
+// MFMA operand reads (consecutive rows, one unit) and staging writes (rows four apart) spread
+// over eight distinct 16-byte bank groups per eight lanes.
+__device__ __forceinline__ int lds_row_off(int row, int chunk)
+{
+    return ((row * 2 + chunk) ^ ((row >> 2) & 7)) << 4;
+}
+
+// A value the caller knows to be equal across the wave, made visibly uniform to the compiler
+// (so that branches on it stay scalar and buffer descriptors chosen by it stay in SGPRs).
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Decode an item and write it as four LDS rows (row0 .. row0+3). KR: the squares' first
+// dimension is the reduction, so LDS row i takes square column i (a register transpose);
+// otherwise LDS row i takes square row i.
+template <int FMT, bool KR>
+__device__ __forceinline__ void store_item(const RawItem<FMT> &r, uint8_t *lds, int row0)
+{
+    uint32_t rows[4][8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t d[8];
+        decode_raw<FMT>(r, k, d);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (KR) {
+                square_column(d, i, rows[i][2 * k], rows[i][2 * k + 1]);
+            } else {
+                rows[i][2 * k] = d[2 * i];
+                rows[i][2 * k + 1] = d[2 * i + 1];
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<uint4 *>(lds + lds_row_off(row0 + i, 0)) =
+            make_uint4(rows[i][0], rows[i][1], rows[i][2], rows[i][3]);
+        *reinterpret_cast<uint4 *>(lds + lds_row_off(row0 + i, 1)) =
+            make_uint4(rows[i][4], rows[i][5], rows[i][6], rows[i][7]);
+    }
+}
+
+// fp32 epilogue scale T_a * T_b: one float when the product is a normal float (or zero / NaN /
+// inf), else the caller falls back to double arithmetic.
+__device__ __forceinline__ bool scale_is_float_safe(double s)
+{
+    const double a = s < 0 ? -s : s;
+    return a == 0.0 || !(a == a) || (a >= 1.1754943508222875e-38 && a <= 3.4028234663852886e38);
+}
+
+} // namespace mq
