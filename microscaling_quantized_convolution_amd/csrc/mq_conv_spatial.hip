@@ -97,79 +97,111 @@ conv_spatial_kernel(SpatialArgs a)
         const rsrc_t in_c = make_rsrc(a.in_codes, in_sq * CB), in_s = make_rsrc(a.in_scales, in_sq);
         const rsrc_t w_c = make_rsrc(a.w_codes, w_sq * CB), w_s = make_rsrc(a.w_scales, w_sq);
 
-        // per slot: first square of chunk 0, the per-chunk step of that index, stride between
-        // the item's four squares, validity, and LDS row
-        uint32_t sq_base[ITEMS], sq_chunk[ITEMS], sq_step[ITEMS];
-        bool valid[ITEMS];
-        int row[ITEMS];
-    #pragma unroll
+        // Items (all load four squares that are adjacent in memory):
+        //   weight, forward: (tap, m4), squares kc0..kc0+3 of Cin, stored as four LDS rows
+        //   weight, input gradient: (tap, kcl, m-group), squares 4g..4g+3 of Cin at Cout square
+        //       kc0+kcl, stored as 16 LDS rows x 4 reduction elements
+        //   halo: (pixel, kcl, n-group), squares 4g..4g+3 of N at channel square kc0+kcl
+        // per slot: first square at chunk 0, its per-chunk advance, static square validity,
+        // reduction block, LDS row
+        uint32_t sq_base[ITEMS], sq_chunk[ITEMS], vmask[ITEMS];
+        int kcl_of[ITEMS], row[ITEMS];
+        const bool w_aligned = (a.Cin4 & 3) == 0, in_aligned = (a.N4 & 3) == 0;
+#pragma unroll
         for (int q = 0; q < ITEMS; ++q) {
             const int it = ptid + q * NP;
             const int wit = wave_uniform(it & ~63);
-            sq_base[q] = 0; sq_chunk[q] = 0; sq_step[q] = 0; valid[q] = false; row[q] = 0;
+            sq_base[q] = 0; sq_chunk[q] = 0; vmask[q] = 0; kcl_of[q] = 0; row[q] = 0;
             if (wit < nA64) {
-                const int t = it >> 4, m4 = m4_0 + (it & 15);
+                const int t = it >> 4;
                 const int tkh = t / kw, tkw = t - tkh * kw;
                 const int wtap = (cl.Ah + cl.Bh * tkh) * a.Kw + (cl.Aw + cl.Bw * tkw);
                 if (A_KR) {
-                    sq_base[q] = (uint32_t)wtap * a.Cout4 * a.Cin4 + m4;
-                    sq_step[q] = a.Cin4;
+                    const int mg = it & 3, kcl = (it >> 2) & 3;
+                    const int m4 = m4_0 + 4 * mg;
+                    sq_base[q] = ((uint32_t)wtap * a.Cout4 + kcl) * a.Cin4 + m4;
                     sq_chunk[q] = 4u * a.Cin4;
+                    const int left = a.M4 - m4;
+                    vmask[q] = (it < nA && left > 0) ? (left >= 4 ? 0xFu : (1u << left) - 1u) : 0u;
+                    kcl_of[q] = kcl;
+                    row[q] = t * 64 + 16 * mg;
                 } else {
+                    const int m4 = m4_0 + (it & 15);
                     sq_base[q] = ((uint32_t)wtap * a.Cout4 + m4) * a.Cin4;
-                    sq_step[q] = 1;
                     sq_chunk[q] = 4;
+                    vmask[q] = (it < nA && m4 < a.M4) ? 0xFu : 0u;
+                    row[q] = t * 64 + 4 * (it & 15);
                 }
-                valid[q] = it < nA && m4 < a.M4;
-                row[q] = t * 64 + 4 * (it & 15);
             } else if (wit < nAB) {
-                const int j = it - nA64, hp = j >> 3, n4 = nb * 8 + (j & 7);
+                const int j = it - nA64, hp = j >> 3, g = j & 1, kcl = (j >> 1) & 3;
                 const int hr = hp / HC, hc = hp - hr * HC;
                 const int ih = ih0 + hr, iw = iw0 + hc;
-                valid[q] = it < nAB && ih >= 0 && ih < a.IH && iw >= 0 && iw < a.IW && n4 < a.N4;
-                sq_base[q] = ((uint32_t)ih * a.IW + iw) * a.K4 * a.N4 + n4;
-                sq_step[q] = a.N4;
+                const int n4 = nb * 8 + 4 * g;
+                const bool inside = it < nAB && ih >= 0 && ih < a.IH && iw >= 0 && iw < a.IW;
+                const int left = a.N4 - n4;
+                vmask[q] = (inside && left > 0) ? (left >= 4 ? 0xFu : (1u << left) - 1u) : 0u;
+                sq_base[q] = (((uint32_t)ih * a.IW + iw) * a.K4 + kcl) * a.N4 + n4;
                 sq_chunk[q] = 4u * a.N4;
-                row[q] = hp * 32 + 4 * (j & 7);
+                kcl_of[q] = kcl;
+                row[q] = hp * 32 + 16 * g;
             }
         }
-        RawItem<FMT> raw[ITEMS];
-        auto load = [&](int c) {
+        // Ring of kPF stages in registers: the loads of chunk c + kPF are issued while chunk c
+        // is consumed, so every load has kPF stage times to arrive.
+        constexpr int kPF = 3;
+        RawItem<FMT> raw[kPF][ITEMS];
+        auto load = [&](int c, RawItem<FMT>(&dst)[ITEMS]) {
             const int kvalid = a.K4 - 4 * c;
             const uint32_t kmask = kvalid >= 4 ? 0xFu : ((1u << kvalid) - 1u);
-    #pragma unroll
+#pragma unroll
             for (int q = 0; q < ITEMS; ++q) {
                 const int wit = wave_uniform((ptid + q * NP) & ~63);
                 const uint32_t sq0 = sq_base[q] + (uint32_t)c * sq_chunk[q];
-                if (wit < nA64)
-                    load_item<FMT>(raw[q], w_c, w_s, sq0, sq_step[q], valid[q] ? kmask : 0u);
-                else if (wit < nAB)
-                    load_item<FMT>(raw[q], in_c, in_s, sq0, sq_step[q], valid[q] ? kmask : 0u);
+                const bool kin = 4 * c + kcl_of[q] < a.K4;
+                if (wit < nA64) {
+                    if (A_KR) load_item_contig<FMT>(dst[q], w_c, w_s, sq0, kin ? vmask[q] : 0u, w_aligned);
+                    else load_item_contig<FMT>(dst[q], w_c, w_s, sq0, vmask[q] & kmask, w_aligned);
+                } else if (wit < nAB) {
+                    load_item_contig<FMT>(dst[q], in_c, in_s, sq0, kin ? vmask[q] : 0u, in_aligned);
+                }
             }
         };
-        auto store = [&](int buf) {
-    #pragma unroll
+        auto store = [&](int buf, const RawItem<FMT>(&src)[ITEMS]) {
+#pragma unroll
             for (int q = 0; q < ITEMS; ++q) {
                 const int it = ptid + q * NP;
                 const int wit = wave_uniform(it & ~63);
                 if (wit < nA64) {
-                    if (it < nA) store_item<FMT, A_KR>(raw[q], lds[buf], row[q]);
+                    if (it < nA) {
+                        if (A_KR) store_item_rows<FMT, true>(src[q], lds[buf], row[q], kcl_of[q]);
+                        else store_item<FMT, false>(src[q], lds[buf], row[q]);
+                    }
                 } else if (wit < nAB) {
-                    if (it < nAB) store_item<FMT, true>(raw[q], lds[buf] + ABYTES, row[q]);
+                    if (it < nAB) store_item_rows<FMT, true>(src[q], lds[buf] + ABYTES, row[q], kcl_of[q]);
                 }
             }
         };
-
+        auto rotate = [&]() {
+#pragma unroll
+            for (int d = 0; d + 1 < kPF; ++d)
+#pragma unroll
+                for (int q = 0; q < ITEMS; ++q) raw[d][q] = raw[d + 1][q];
+        };
+        // raw[d] holds chunk (next to store) + d
+#pragma unroll
+        for (int d = 0; d < kPF; ++d)
+            if (d < nchunk) load(d, raw[d]);
         if (nchunk > 0) {
-            load(0);
-            store(0);
-            if (nchunk > 1) load(1);
+            store(0, raw[0]);
+            rotate();
+            if (kPF < nchunk) load(kPF, raw[kPF - 1]);
         }
         __syncthreads();
         for (int c = 0; c < nchunk; ++c) {
             if (c + 1 < nchunk) {
-                store((c + 1) & 1);
-                if (c + 2 < nchunk) load(c + 2);
+                store((c + 1) & 1, raw[0]);
+                rotate();
+                if (c + 1 + kPF < nchunk) load(c + 1 + kPF, raw[kPF - 1]);
             }
             __syncthreads();
         }

@@ -40,7 +40,7 @@ struct WgradArgs {
 // stage after next, decode the next stage into the other buffer); one barrier per stage.
 // Output pixels per stage: 16 for stride 1, 8 for stride 2 (twice as wide an X segment), so that
 // two stage buffers fit in LDS.
-template <int SI> struct StagePixels { static constexpr int kPW = SI == 1 ? 8 : 8; };
+template <int SI> struct StagePixels { static constexpr int kPW = SI == 1 ? 16 : 8; };
 
 template <int FMT, int SI>
 __global__ void __launch_bounds__(512) conv_wgrad_kernel(WgradArgs a)
@@ -68,6 +68,7 @@ __global__ void __launch_bounds__(512) conv_wgrad_kernel(WgradArgs a)
     if (wave >= 4) {
         // ================= producer =================
         const int ptid = tid - 256;
+        const bool n_aligned = (a.N4 & 3) == 0;
         const int nG = kPWg * 16, nGX = nG + HC * 16;
         constexpr int CB = (FMT == kFP4) ? 8 : 12;
         const uint32_t g_sq = (uint32_t)a.Ho * a.Wo * a.Cout4 * a.N4;
@@ -77,8 +78,10 @@ __global__ void __launch_bounds__(512) conv_wgrad_kernel(WgradArgs a)
         // Producer items: it < nG -> G_Y strip (pixel it/16, co4 it%16); else X segment (column,
         // ci4). Each item spans the four batch squares 4*nc .. 4*nc+3 (consecutive in memory). nG is
         // a whole number of waves, so no wave mixes the two kinds.
-        RawItem<FMT> raw[ITEMS];
-        auto load = [&](int st) {
+        // ring of kPF stages in registers (loads issued kPF stage times ahead of their use)
+        constexpr int kPF = 3;
+        RawItem<FMT> raw[kPF][ITEMS];
+        auto load = [&](int st, RawItem<FMT>(&dst)[ITEMS]) {
             const int nc = st % a.nch;
             const int rest = st / a.nch;
             const int ob = rest % a.owb;
@@ -96,40 +99,50 @@ __global__ void __launch_bounds__(512) conv_wgrad_kernel(WgradArgs a)
                     const int ow = ow0 + (it >> 4), co4 = co4_0 + (it & 15);
                     const uint32_t sq0 = (((uint32_t)oh * a.Wo + ow) * a.Cout4 + co4) * a.N4 + 4 * nc;
                     const uint32_t mask = (ow < a.Wo && co4 < a.Cout4) ? nmask : 0u;
-                    load_item<FMT>(raw[q], g_c, g_s, sq0, 1u, mask);
+                    load_item_contig<FMT>(dst[q], g_c, g_s, sq0, mask, n_aligned);
                 } else if (wit < nGX) {
                     const int j = it - nG;
                     const int iw = iw0 + (j >> 4), ci4 = ci4_0 + (j & 15);
                     const uint32_t sq0 = (((uint32_t)ih * a.W + iw) * a.Cin4 + ci4) * a.N4 + 4 * nc;
                     const bool in = it < nGX && ih >= 0 && ih < a.H && iw >= 0 && iw < a.W &&
                                     ci4 < a.Cin4;
-                    load_item<FMT>(raw[q], x_c, x_s, sq0, 1u, in ? nmask : 0u);
+                    load_item_contig<FMT>(dst[q], x_c, x_s, sq0, in ? nmask : 0u, n_aligned);
                 }
             }
         };
-        auto store = [&](int buf) {
+        auto store = [&](int buf, const RawItem<FMT>(&src)[ITEMS]) {
     #pragma unroll
             for (int q = 0; q < ITEMS; ++q) {
                 const int it = ptid + q * 256;
                 const int wit = wave_uniform(it & ~63);
-                if (wit < nG) store_item<FMT, false>(raw[q], lds[buf], (it >> 4) * 64 + 4 * (it & 15));
+                if (wit < nG) store_item<FMT, false>(src[q], lds[buf], (it >> 4) * 64 + 4 * (it & 15));
                 else if (wit < nGX && it < nGX) {
                     const int j = it - nG;
-                    store_item<FMT, false>(raw[q], lds[buf] + GBYTES, (j >> 4) * 64 + 4 * (j & 15));
+                    store_item<FMT, false>(src[q], lds[buf] + GBYTES, (j >> 4) * 64 + 4 * (j & 15));
                 }
             }
         };
 
+        auto rotate = [&]() {
+#pragma unroll
+            for (int d = 0; d + 1 < kPF; ++d)
+#pragma unroll
+                for (int q = 0; q < ITEMS; ++q) raw[d][q] = raw[d + 1][q];
+        };
+#pragma unroll
+        for (int d = 0; d < kPF; ++d)
+            if (d < nst) load(st0 + d, raw[d]);
         if (nst > 0) {
-            load(st0);
-            store(0);
-            if (nst > 1) load(st0 + 1);
+            store(0, raw[0]);
+            rotate();
+            if (kPF < nst) load(st0 + kPF, raw[kPF - 1]);
         }
         __syncthreads();
         for (int c = 0; c < nst; ++c) {
             if (c + 1 < nst) {
-                store((c + 1) & 1);
-                if (c + 2 < nst) load(st0 + c + 2);
+                store((c + 1) & 1, raw[0]);
+                rotate();
+                if (c + 1 + kPF < nst) load(st0 + c + 1 + kPF, raw[kPF - 1]);
             }
             __syncthreads();
         }

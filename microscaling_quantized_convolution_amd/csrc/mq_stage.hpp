@@ -57,6 +57,46 @@ __device__ __forceinline__ void load_item(RawItem<FMT> &r, rsrc_t codes, rsrc_t 
     }
 }
 
+// Load four squares that are consecutive in memory (sq0 .. sq0+3) with wide loads: 32 (NVFP4) or
+// 48 (NVFP6) code bytes and, when `sc_aligned` (sq0 a multiple of 4 for every item), one 4-byte
+// scale load. Squares whose bit of `mask` is clear read as zero codes with a zero scale.
+template <int FMT>
+__device__ __forceinline__ void load_item_contig(RawItem<FMT> &r, rsrc_t codes, rsrc_t scales,
+                                                 uint32_t sq0, uint32_t mask, bool sc_aligned)
+{
+    const uint32_t coff = mask ? sq0 * (uint32_t)(RawItem<FMT>::kW * 4) : kBad;
+    if constexpr (FMT == kFP4) {
+        const u32x4_t v0 = __builtin_amdgcn_raw_buffer_load_b128(codes, (int)coff, 0, 0);
+        const u32x4_t v1 = __builtin_amdgcn_raw_buffer_load_b128(codes, (int)(coff + 16u), 0, 0);
+        r.w[0][0] = v0[0]; r.w[0][1] = v0[1]; r.w[1][0] = v0[2]; r.w[1][1] = v0[3];
+        r.w[2][0] = v1[0]; r.w[2][1] = v1[1]; r.w[3][0] = v1[2]; r.w[3][1] = v1[3];
+    } else {
+        const u32x4_t v0 = __builtin_amdgcn_raw_buffer_load_b128(codes, (int)coff, 0, 0);
+        const u32x4_t v1 = __builtin_amdgcn_raw_buffer_load_b128(codes, (int)(coff + 16u), 0, 0);
+        const u32x4_t v2 = __builtin_amdgcn_raw_buffer_load_b128(codes, (int)(coff + 32u), 0, 0);
+        r.w[0][0] = v0[0]; r.w[0][1] = v0[1]; r.w[0][2] = v0[2];
+        r.w[1][0] = v0[3]; r.w[1][1] = v1[0]; r.w[1][2] = v1[1];
+        r.w[2][0] = v1[2]; r.w[2][1] = v1[3]; r.w[2][2] = v2[0];
+        r.w[3][0] = v2[1]; r.w[3][1] = v2[2]; r.w[3][2] = v2[3];
+    }
+    if (sc_aligned) {
+        r.sc = __builtin_amdgcn_raw_buffer_load_b32(scales, (int)(mask ? sq0 : kBad), 0, 0);
+    } else {
+        r.sc = 0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            r.sc |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(scales, (int)(mask ? sq0 + k : kBad), 0, 0)
+                    << (8 * k);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (!((mask >> k) & 1u)) {
+#pragma unroll
+            for (int q = 0; q < RawItem<FMT>::kW; ++q) r.w[k][q] = 0u;
+            r.sc &= ~(0xFFu << (8 * k));
+        }
+}
+
 template <int FMT>
 __device__ __forceinline__ void decode_raw(const RawItem<FMT> &r, int k, uint32_t (&d)[8])
 {
@@ -105,6 +145,31 @@ __device__ __forceinline__ void store_item(const RawItem<FMT> &r, uint8_t *lds, 
             make_uint4(rows[i][0], rows[i][1], rows[i][2], rows[i][3]);
         *reinterpret_cast<uint4 *>(lds + lds_row_off(row0 + i, 1)) =
             make_uint4(rows[i][4], rows[i][5], rows[i][6], rows[i][7]);
+    }
+}
+
+// Decode an item whose four squares lie side by side along the rows of the LDS operand (the
+// reduction block kb = 4 elements is shared): square j fills LDS rows row0 + 4j .. row0 + 4j + 3
+// at reduction elements 4*kb .. 4*kb + 3 (8 bytes each). KR as in store_item.
+template <int FMT, bool KR>
+__device__ __forceinline__ void store_item_rows(const RawItem<FMT> &r, uint8_t *lds, int row0, int kb)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t d[8];
+        decode_raw<FMT>(r, j, d);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t p0, p1;
+            if (KR) {
+                square_column(d, i, p0, p1);
+            } else {
+                p0 = d[2 * i];
+                p1 = d[2 * i + 1];
+            }
+            *reinterpret_cast<uint2 *>(lds + lds_row_off(row0 + 4 * j + i, kb >> 1) + 8 * (kb & 1)) =
+                make_uint2(p0, p1);
+        }
     }
 }
 
