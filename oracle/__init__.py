@@ -10,9 +10,8 @@ the channel-batch-first layout (section "How it works"), the 2-D reshapes, the t
 the NVFP4 square-block recipe (section "How it differs"), NVFP6 (section "How it is used").
 
 Parity pins: every function here is pinned by a ``-m "not gpu"`` test against something other
-than itself (library casts, closed forms, invariants, brute force, torch float64 convolutions),
-except the exact Philox4x32-10 bit stream used by stochastic rounding, which is pinned only
-statistically (parity unpinned for the choice of random stream).
+than itself (library casts, closed forms, invariants, brute force, torch float64 convolutions,
+the published Philox4x32-10 known-answer vectors).
 """
 from __future__ import annotations
 
