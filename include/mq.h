@@ -66,7 +66,10 @@ typedef enum { MQ_RNE = 0, MQ_SR = 1 } mq_round;
  *   scales: 1 byte per square, E4M3 s|eeee|mmm (bias 7, subnormals, 0x7E = 448, 0x7F = NaN);
  *   tscale: one fp32, the tensor scale T.
  * Value of an element: decode(code) * decode(scale) * T.
- * fmt and role hold mq_format / mq_role values.
+ * fmt and role hold mq_format / mq_role values. codes must be 16-byte aligned, scales and tscale
+ * 4-byte aligned (device allocations are); other pointers give MQ_ERR_ARG. The convolutions may
+ * read the up to 3 bytes that follow the last scale byte in its aligned 4-byte word (never
+ * beyond it) and ignore them.
  */
 typedef struct {
     int32_t o0, o1, r, s;
@@ -142,7 +145,7 @@ mq_status mq_quantize(const float *src_dev, const mq_qtensor *dst, int32_t rnd, 
  * works"):
  *   Y[ho][wo][co][n] = T_W * T_X * sum_{kh,kw,ci} Wq[kh][kw][co][ci]
  *                                               * Xq[ho*sh - ph + kh][wo*sw - pw + kw][ci][n]
- * (zero outside the input), accumulated in fp32 from exact bf16 products.
+ * (zero outside the input), accumulated in fp32 from exact fp16 (or bf16) products.
  * x: MQ_ROLE_ACT tensor of shape (H, W, Cin, N); w: MQ_ROLE_WEIGHT tensor (Kh, Kw, Cout, Cin);
  * same format. y_dev: fp32 channel-batch-first [Hout][Wout][Cout][N], fully overwritten.
  * Errors: MQ_ERR_ARG, MQ_ERR_SHAPE (dims or formats disagree with p), MQ_ERR_UNSUPPORTED.

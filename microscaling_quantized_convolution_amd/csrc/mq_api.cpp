@@ -5,6 +5,7 @@
 #include "../../include/mq.h"
 #include "mq_kernels.hpp"
 
+#include <stdint.h>
 #include <stdlib.h>
 
 namespace {
@@ -16,11 +17,14 @@ int64_t squares(int32_t o0, int32_t o1, int32_t r, int32_t s)
     return (int64_t)o0 * o1 * ((r + 3) / 4) * ((s + 3) / 4);
 }
 
+// The kernels read codes with 16-byte loads and scales with aligned 4-byte loads (which may
+// cover up to 3 bytes past the last scale, always inside the same aligned word).
 bool qtensor_ok(const mq_qtensor *q)
 {
     return q && q->o0 > 0 && q->o1 > 0 && q->r > 0 && q->s > 0 && fmt_ok(q->fmt) &&
            q->role >= MQ_ROLE_ACT && q->role <= MQ_ROLE_GRAD && q->codes && q->scales &&
-           q->tscale;
+           q->tscale && ((uintptr_t)q->codes & 15u) == 0 && ((uintptr_t)q->scales & 3u) == 0 &&
+           ((uintptr_t)q->tscale & 3u) == 0;
 }
 
 // Geometry of a convolution, or false if it is not a valid convolution.

@@ -78,13 +78,16 @@ conv_spatial_kernel(SpatialArgs a)
     const int bx = blockIdx.x;
     const int nb = bx % a.nblk;
     const int tile = bx / a.nblk;
-    if (tile >= cl.tiles) return;
+    // A workgroup past its class's last tile loads and computes nothing, and its pixels fall
+    // outside the class grid. (No early return: every kernel argument is then fetched in one
+    // round trip instead of one per dependent branch.)
+    const bool live = tile < cl.tiles;
     const int ti = tile / cl.tiles_w, tj = tile - ti * cl.tiles_w;
     const int i0 = ti * PH, j0 = tj * PW;
     const int m4_0 = blockIdx.y * 16;
-    const int kh = cl.kh, kw = cl.kw, ntap = kh * kw;
+    const int kh = cl.kh * (int)live, kw = cl.kw * (int)live, ntap = kh * kw;
     const int HR = (PH - 1) * SI + kh, HC = (PW - 1) * SI + kw;
-    const int nchunk = ntap > 0 ? (a.K4 + 3) / 4 : 0;
+    const int nchunk = ((a.K4 + 3) / 4) * (ntap > 0 ? 1 : 0);
 
     if (wave >= NCW) {
         // ================= producer =================
@@ -94,8 +97,8 @@ conv_spatial_kernel(SpatialArgs a)
         constexpr int CB = (FMT == kFP4) ? 8 : 12;
         const uint32_t in_sq = (uint32_t)a.IH * a.IW * a.K4 * a.N4;
         const uint32_t w_sq = (uint32_t)a.Kh * a.Kw * a.Cout4 * a.Cin4;
-        const rsrc_t in_c = make_rsrc(a.in_codes, in_sq * CB), in_s = make_rsrc(a.in_scales, in_sq);
-        const rsrc_t w_c = make_rsrc(a.w_codes, w_sq * CB), w_s = make_rsrc(a.w_scales, w_sq);
+        const rsrc_t in_c = make_rsrc(a.in_codes, in_sq * CB), in_s = make_scale_rsrc(a.in_scales, in_sq);
+        const rsrc_t w_c = make_rsrc(a.w_codes, w_sq * CB), w_s = make_scale_rsrc(a.w_scales, w_sq);
 
         // Items (all load four squares that are adjacent in memory):
         //   weight, forward: (tap, m4), squares kc0..kc0+3 of Cin, stored as four LDS rows
@@ -106,7 +109,6 @@ conv_spatial_kernel(SpatialArgs a)
         // reduction block, LDS row
         uint32_t sq_base[ITEMS], sq_chunk[ITEMS], vmask[ITEMS];
         int kcl_of[ITEMS], row[ITEMS];
-        const bool w_aligned = (a.Cin4 & 3) == 0, in_aligned = (a.N4 & 3) == 0;
 #pragma unroll
         for (int q = 0; q < ITEMS; ++q) {
             const int it = ptid + q * NP;
@@ -137,7 +139,7 @@ conv_spatial_kernel(SpatialArgs a)
                 const int hr = hp / HC, hc = hp - hr * HC;
                 const int ih = ih0 + hr, iw = iw0 + hc;
                 const int n4 = nb * 8 + 4 * g;
-                const bool inside = it < nAB && ih >= 0 && ih < a.IH && iw >= 0 && iw < a.IW;
+                const bool inside = live && it < nAB && ih >= 0 && ih < a.IH && iw >= 0 && iw < a.IW;
                 const int left = a.N4 - n4;
                 vmask[q] = (inside && left > 0) ? (left >= 4 ? 0xFu : (1u << left) - 1u) : 0u;
                 sq_base[q] = (((uint32_t)ih * a.IW + iw) * a.K4 + kcl) * a.N4 + n4;
@@ -146,24 +148,22 @@ conv_spatial_kernel(SpatialArgs a)
                 row[q] = hp * 32 + 16 * g;
             }
         }
-        // Ring of kPF stages in registers: the loads of chunk c + kPF are issued while chunk c
-        // is consumed, so every load has kPF stage times to arrive.
-        constexpr int kPF = 3;
-        RawItem<FMT> raw[kPF][ITEMS];
+        // Two register stages: chunk c + 3 is loaded into the slot chunk c + 1 was just decoded
+        // from, so every load has two stage times to arrive. Loads are issued without branches,
+        // the same number per stage (a chunk past the end loads nothing: mask 0), and the loop is
+        // unrolled by two so that slots are never copied: the compiler's wait before a decode
+        // then covers exactly that chunk's loads.
+        RawItem<FMT> raw[2][ITEMS];
         auto load = [&](int c, RawItem<FMT>(&dst)[ITEMS]) {
             const int kvalid = a.K4 - 4 * c;
-            const uint32_t kmask = kvalid >= 4 ? 0xFu : ((1u << kvalid) - 1u);
+            const uint32_t kmask = kvalid >= 4 ? 0xFu : (kvalid > 0 ? (1u << kvalid) - 1u : 0u);
 #pragma unroll
             for (int q = 0; q < ITEMS; ++q) {
-                const int wit = wave_uniform((ptid + q * NP) & ~63);
+                const bool isA = wave_uniform((ptid + q * NP) & ~63) < nA64;
                 const uint32_t sq0 = sq_base[q] + (uint32_t)c * sq_chunk[q];
                 const bool kin = 4 * c + kcl_of[q] < a.K4;
-                if (wit < nA64) {
-                    if (A_KR) load_item_contig<FMT>(dst[q], w_c, w_s, sq0, kin ? vmask[q] : 0u, w_aligned);
-                    else load_item_contig<FMT>(dst[q], w_c, w_s, sq0, vmask[q] & kmask, w_aligned);
-                } else if (wit < nAB) {
-                    load_item_contig<FMT>(dst[q], in_c, in_s, sq0, kin ? vmask[q] : 0u, in_aligned);
-                }
+                const uint32_t m = (isA && !A_KR) ? (vmask[q] & kmask) : (kin ? vmask[q] : 0u);
+                load_item_contig<FMT>(dst[q], isA ? w_c : in_c, isA ? w_s : in_s, sq0, m);
             }
         };
         auto store = [&](int buf, const RawItem<FMT>(&src)[ITEMS]) {
@@ -181,30 +181,23 @@ conv_spatial_kernel(SpatialArgs a)
                 }
             }
         };
-        auto rotate = [&]() {
-#pragma unroll
-            for (int d = 0; d + 1 < kPF; ++d)
-#pragma unroll
-                for (int q = 0; q < ITEMS; ++q) raw[d][q] = raw[d + 1][q];
-        };
-        // raw[d] holds chunk (next to store) + d
-#pragma unroll
-        for (int d = 0; d < kPF; ++d)
-            if (d < nchunk) load(d, raw[d]);
-        if (nchunk > 0) {
-            store(0, raw[0]);
-            rotate();
-            if (kPF < nchunk) load(kPF, raw[kPF - 1]);
-        }
+        // step c: decode chunk c + 1 from slot (c + 1) & 1 into LDS buffer (c + 1) & 1, then
+        // load chunk c + 3 into that slot
+        load(0, raw[0]);
+        load(1, raw[1]);
+        store(0, raw[0]);
+        load(2, raw[0]);
         __syncthreads();
-        for (int c = 0; c < nchunk; ++c) {
-            if (c + 1 < nchunk) {
-                store((c + 1) & 1, raw[0]);
-                rotate();
-                if (c + 1 + kPF < nchunk) load(c + 1 + kPF, raw[kPF - 1]);
-            }
+        int c = 0;
+        for (; c + 1 < nchunk; c += 2) {
+            store(1, raw[1]);
+            load(c + 3, raw[1]);
+            __syncthreads();
+            if (c + 2 < nchunk) store(0, raw[0]);
+            load(c + 4, raw[0]);
             __syncthreads();
         }
+        if (c < nchunk) __syncthreads(); // last chunk: nothing left to decode
         return;
     }
 

@@ -68,19 +68,19 @@ __global__ void __launch_bounds__(512) conv_wgrad_kernel(WgradArgs a)
     if (wave >= 4) {
         // ================= producer =================
         const int ptid = tid - 256;
-        const bool n_aligned = (a.N4 & 3) == 0;
         const int nG = kPWg * 16, nGX = nG + HC * 16;
         constexpr int CB = (FMT == kFP4) ? 8 : 12;
         const uint32_t g_sq = (uint32_t)a.Ho * a.Wo * a.Cout4 * a.N4;
         const uint32_t x_sq = (uint32_t)a.H * a.W * a.Cin4 * a.N4;
-        const rsrc_t g_c = make_rsrc(a.g_codes, g_sq * CB), g_s = make_rsrc(a.g_scales, g_sq);
-        const rsrc_t x_c = make_rsrc(a.x_codes, x_sq * CB), x_s = make_rsrc(a.x_scales, x_sq);
+        const rsrc_t g_c = make_rsrc(a.g_codes, g_sq * CB), g_s = make_scale_rsrc(a.g_scales, g_sq);
+        const rsrc_t x_c = make_rsrc(a.x_codes, x_sq * CB), x_s = make_scale_rsrc(a.x_scales, x_sq);
         // Producer items: it < nG -> G_Y strip (pixel it/16, co4 it%16); else X segment (column,
         // ci4). Each item spans the four batch squares 4*nc .. 4*nc+3 (consecutive in memory). nG is
         // a whole number of waves, so no wave mixes the two kinds.
-        // ring of kPF stages in registers (loads issued kPF stage times ahead of their use)
-        constexpr int kPF = 3;
-        RawItem<FMT> raw[kPF][ITEMS];
+        // Two register stages: stage c + 3 is loaded into the slot stage c + 1 was just decoded
+        // from (two stage times ahead of its use). The loop is unrolled by two so that slots are
+        // never copied, which keeps the compiler's waits down to the stage being decoded.
+        RawItem<FMT> raw[2][ITEMS];
         auto load = [&](int st, RawItem<FMT>(&dst)[ITEMS]) {
             const int nc = st % a.nch;
             const int rest = st / a.nch;
@@ -90,24 +90,23 @@ __global__ void __launch_bounds__(512) conv_wgrad_kernel(WgradArgs a)
             const int ih = oh * SI - a.ph + kh;
             const int iw0 = ow0 * SI - a.pw;
             const int nvalid = a.N4 - 4 * nc;
-            const uint32_t nmask = nvalid >= 4 ? 0xFu : ((1u << nvalid) - 1u);
+            // a stage past the end of this split loads nothing (mask 0), so that every stage
+            // issues the same loads without branches and each decode waits for its own stage only
+            const uint32_t nmask = st >= st1 ? 0u : nvalid >= 4 ? 0xFu : ((1u << nvalid) - 1u);
     #pragma unroll
             for (int q = 0; q < ITEMS; ++q) {
                 const int it = ptid + q * 256;
-                const int wit = wave_uniform(it & ~63);
-                if (wit < nG) {
-                    const int ow = ow0 + (it >> 4), co4 = co4_0 + (it & 15);
-                    const uint32_t sq0 = (((uint32_t)oh * a.Wo + ow) * a.Cout4 + co4) * a.N4 + 4 * nc;
-                    const uint32_t mask = (ow < a.Wo && co4 < a.Cout4) ? nmask : 0u;
-                    load_item_contig<FMT>(dst[q], g_c, g_s, sq0, mask, n_aligned);
-                } else if (wit < nGX) {
-                    const int j = it - nG;
-                    const int iw = iw0 + (j >> 4), ci4 = ci4_0 + (j & 15);
-                    const uint32_t sq0 = (((uint32_t)ih * a.W + iw) * a.Cin4 + ci4) * a.N4 + 4 * nc;
-                    const bool in = it < nGX && ih >= 0 && ih < a.H && iw >= 0 && iw < a.W &&
-                                    ci4 < a.Cin4;
-                    load_item_contig<FMT>(dst[q], x_c, x_s, sq0, in ? nmask : 0u, n_aligned);
-                }
+                const bool isG = wave_uniform(it & ~63) < nG;
+                const int ow = ow0 + (it >> 4), co4 = co4_0 + (it & 15);
+                const uint32_t sqg = (((uint32_t)oh * a.Wo + ow) * a.Cout4 + co4) * a.N4 + 4 * nc;
+                const uint32_t mg = (ow < a.Wo && co4 < a.Cout4) ? nmask : 0u;
+                const int j = it - nG;
+                const int iw = iw0 + (j >> 4), ci4 = ci4_0 + (j & 15);
+                const uint32_t sqx = (((uint32_t)ih * a.W + iw) * a.Cin4 + ci4) * a.N4 + 4 * nc;
+                const bool in = it < nGX && ih >= 0 && ih < a.H && iw >= 0 && iw < a.W &&
+                                ci4 < a.Cin4;
+                load_item_contig<FMT>(dst[q], isG ? g_c : x_c, isG ? g_s : x_s, isG ? sqg : sqx,
+                                      isG ? mg : (in ? nmask : 0u));
             }
         };
         auto store = [&](int buf, const RawItem<FMT>(&src)[ITEMS]) {
@@ -123,29 +122,21 @@ __global__ void __launch_bounds__(512) conv_wgrad_kernel(WgradArgs a)
             }
         };
 
-        auto rotate = [&]() {
-#pragma unroll
-            for (int d = 0; d + 1 < kPF; ++d)
-#pragma unroll
-                for (int q = 0; q < ITEMS; ++q) raw[d][q] = raw[d + 1][q];
-        };
-#pragma unroll
-        for (int d = 0; d < kPF; ++d)
-            if (d < nst) load(st0 + d, raw[d]);
-        if (nst > 0) {
-            store(0, raw[0]);
-            rotate();
-            if (kPF < nst) load(st0 + kPF, raw[kPF - 1]);
-        }
+        load(st0, raw[0]);
+        load(st0 + 1, raw[1]);
+        store(0, raw[0]);
+        load(st0 + 2, raw[0]);
         __syncthreads();
-        for (int c = 0; c < nst; ++c) {
-            if (c + 1 < nst) {
-                store((c + 1) & 1, raw[0]);
-                rotate();
-                if (c + 1 + kPF < nst) load(st0 + c + 1 + kPF, raw[kPF - 1]);
-            }
+        int c = 0;
+        for (; c + 1 < nst; c += 2) {
+            store(1, raw[1]);
+            load(st0 + c + 3, raw[1]);
+            __syncthreads();
+            if (c + 2 < nst) store(0, raw[0]);
+            load(st0 + c + 4, raw[0]);
             __syncthreads();
         }
+        if (c < nst) __syncthreads(); // last stage: nothing left to decode
         return;
     }
 

@@ -13,7 +13,9 @@ namespace mq {
 template <int FMT> struct RawItem {
     static constexpr int kW = (FMT == kFP4) ? 2 : 3; // code words per square
     uint32_t w[4][kW];
-    uint32_t sc; // four scale bytes, square k in byte k
+    uint32_t sc, sh; // scale bytes: square k is byte k + b of the 64-bit pair (sh:sc)
+    uint32_t m;      // bits 0-3: square k is real (a clear bit decodes as zeros whatever was
+                     // loaded); bits 8-9: the byte offset b
 };
 
 // Buffer resources: raw (stride 0) descriptors whose range check makes every load at an offset
@@ -28,6 +30,15 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
                                              0x00020000);
 }
 
+// Scale bytes are read as aligned 4-byte words. The range check drops a whole word that reaches
+// past the end, which would lose the last real scales, so the range is rounded up to whole
+// words: the scale array is 4-byte aligned, so its last word lies inside the memory page of its
+// last byte, and the extra bytes only ever belong to squares that are masked off.
+__device__ __forceinline__ rsrc_t make_scale_rsrc(const uint8_t *base, uint32_t nsquares)
+{
+    return make_rsrc(base, (nsquares + 3u) & ~3u);
+}
+
 // Load the four squares sq0 + k*step (k = 0..3) whose bit k of `mask` is set; the others read as
 // zero codes with a zero scale (out-of-range buffer offsets).
 template <int FMT>
@@ -37,6 +48,8 @@ __device__ __forceinline__ void load_item(RawItem<FMT> &r, rsrc_t codes, rsrc_t 
     typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
     typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
     r.sc = 0u;
+    r.sh = 0u;
+    r.m = 0xFu;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const bool on = (mask >> k) & 1u;
@@ -58,11 +71,13 @@ __device__ __forceinline__ void load_item(RawItem<FMT> &r, rsrc_t codes, rsrc_t 
 }
 
 // Load four squares that are consecutive in memory (sq0 .. sq0+3) with wide loads: 32 (NVFP4) or
-// 48 (NVFP6) code bytes and, when `sc_aligned` (sq0 a multiple of 4 for every item), one 4-byte
-// scale load. Squares whose bit of `mask` is clear read as zero codes with a zero scale.
+// 48 (NVFP6) code bytes, and the four scale bytes as the two aligned words that hold them.
+// Squares whose bit of `mask` is clear decode as zeros (their scale is replaced by 0 at decode
+// time). The code has no branch and never touches the loaded data, so no load waits before its
+// value is decoded (a data-dependent select or a branch join would make the compiler wait).
 template <int FMT>
 __device__ __forceinline__ void load_item_contig(RawItem<FMT> &r, rsrc_t codes, rsrc_t scales,
-                                                 uint32_t sq0, uint32_t mask, bool sc_aligned)
+                                                 uint32_t sq0, uint32_t mask)
 {
     const uint32_t coff = mask ? sq0 * (uint32_t)(RawItem<FMT>::kW * 4) : kBad;
     if constexpr (FMT == kFP4) {
@@ -79,28 +94,18 @@ __device__ __forceinline__ void load_item_contig(RawItem<FMT> &r, rsrc_t codes, 
         r.w[2][0] = v1[2]; r.w[2][1] = v1[3]; r.w[2][2] = v2[0];
         r.w[3][0] = v2[1]; r.w[3][1] = v2[2]; r.w[3][2] = v2[3];
     }
-    if (sc_aligned) {
-        r.sc = __builtin_amdgcn_raw_buffer_load_b32(scales, (int)(mask ? sq0 : kBad), 0, 0);
-    } else {
-        r.sc = 0u;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            r.sc |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(scales, (int)(mask ? sq0 + k : kBad), 0, 0)
-                    << (8 * k);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        if (!((mask >> k) & 1u)) {
-#pragma unroll
-            for (int q = 0; q < RawItem<FMT>::kW; ++q) r.w[k][q] = 0u;
-            r.sc &= ~(0xFFu << (8 * k));
-        }
+    const uint32_t a4 = sq0 & ~3u;
+    r.sc = __builtin_amdgcn_raw_buffer_load_b32(scales, (int)(mask ? a4 : kBad), 0, 0);
+    r.sh = __builtin_amdgcn_raw_buffer_load_b32(scales, (int)(mask ? a4 + 4u : kBad), 0, 0);
+    r.m = mask | ((sq0 & 3u) << 8);
 }
 
 template <int FMT>
 __device__ __forceinline__ void decode_raw(const RawItem<FMT> &r, int k, uint32_t (&d)[8])
 {
-    const uint32_t sc = (r.sc >> (8 * k)) & 0xFFu;
+    // a zero scale decodes every element of the square to +-0 (element formats have no NaN)
+    const uint32_t s4 = __builtin_amdgcn_alignbyte(r.sh, r.sc, (r.m >> 8) & 3u);
+    const uint32_t sc = ((r.m >> k) & 1u) ? (s4 >> (8 * k)) & 0xFFu : 0u;
     if constexpr (FMT == kFP4) decode_fp4_square(r.w[k][0], r.w[k][1], sc, d);
     else decode_fp6_square(r.w[k][0], r.w[k][1], r.w[k][2], sc, d);
 }

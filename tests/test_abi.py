@@ -69,6 +69,11 @@ def test_validation_errors_without_gpu():
     assert L.mq_quantize(y, ctypes.byref(bad), 0, 0, y, s0) == mq.MQ_ERR_ARG
     nul = _fake_q((8, 8, 16, 2), null=True)
     assert L.mq_quantize(y, ctypes.byref(nul), 0, 0, y, s0) == mq.MQ_ERR_ARG
+    # misaligned codes (16 B) or scales (4 B) -> MQ_ERR_ARG
+    mis = mq.mq_qtensor(8, 8, 16, 2, mq.MQ_NVFP4, mq.MQ_ROLE_ACT, 0x1008, 0x1000, 0x1000)
+    assert L.mq_quantize(y, ctypes.byref(mis), 0, 0, y, s0) == mq.MQ_ERR_ARG
+    mis = mq.mq_qtensor(8, 8, 16, 2, mq.MQ_NVFP4, mq.MQ_ROLE_ACT, 0x1000, 0x1002, 0x1000)
+    assert L.mq_conv_fwd(ctypes.byref(conv), ctypes.byref(mis), ctypes.byref(w), y, s0) == mq.MQ_ERR_ARG
     assert L.mq_conv_fwd(ctypes.byref(conv), ctypes.byref(x), ctypes.byref(w), None, s0) == mq.MQ_ERR_ARG
     # shape / role / format mismatches -> MQ_ERR_SHAPE
     assert L.mq_conv_fwd(ctypes.byref(conv), ctypes.byref(w), ctypes.byref(x), y, s0) == mq.MQ_ERR_SHAPE
