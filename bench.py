@@ -7,14 +7,24 @@ first) and W (OIHW -> tap-major), quantize X and W (round-to-nearest) and G_Y (s
 seed every step), then the forward, weight-gradient and input-gradient GEMMs. Inputs are resident
 in HBM before the timed region starts.
 
-Prints one JSON line. `value` is the step's conv throughput (3 GEMMs' algorithmic flops / step
-time); `per_op` holds each op's time, GB/s or TFLOP/s and roofline fraction; `roofline` covers the
-op that takes the most time in the step, timed with HIP events around each of its launches
-inside the timed steps; `cpu_baseline` times the CPU oracle on a bounded sample (rank 0, N=1).
+The timed steps call the C ABI back to back on one stream (arguments marshalled once, so the
+GPU, not the host, sets the pace), with HIP events on that stream around every launch of the op
+that takes the longest (`roofline`). `--graph` replays one HIP graph per step instead (split
+around that op so the events stay outside the graphs). `per_op` times each op alone as a graph
+of back-to-back launches. `cpu_baseline` times the CPU oracle on a bounded sample (rank 0, N=1).
+
+`roofline.traffic` is the HBM traffic of that op per launch from rocprofv3 FETCH_SIZE and
+WRITE_SIZE counters (profiles/c2_pmc_traffic.txt), scaled by what the same counters read for a
+plain copy of known size; it is null when the kernel sources differ from the ones counted.
+`--summarize-pmc FETCH_DB WRITE_DB` writes that file's body from two rocprofv3 --pmc databases.
+
+Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -24,7 +34,20 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
-BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA, TFLOP/s (256 CU x 2.4 GHz x 4096)
+MFMA_PEAK_TFLOPS = 2516.6    # MI355X dense fp16/bf16 MFMA, TFLOP/s (256 CU x 2.4 GHz x 4096)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c2_pmc_traffic.txt")
+CALIB_ELEMS = 1 << 26        # plain copy for counter calibration: 256 MiB read + 256 MiB written
+
+# which kernels make up each op (rocprofv3 kernel names start with these)
+OP_KERNELS = {
+    "relayout_x": ["mq::transpose_kernel"], "relayout_w": ["mq::transpose_kernel"],
+    "quantize_x": ["mq::zero_u32_kernel", "mq::amax_kernel", "void mq::quantize_kernel"],
+    "quantize_w": ["mq::zero_u32_kernel", "mq::amax_kernel", "void mq::quantize_kernel"],
+    "quantize_g": ["mq::zero_u32_kernel", "mq::amax_kernel", "void mq::quantize_kernel"],
+    "conv_fwd": ["void mq::conv_spatial_kernel<4, false"],
+    "conv_wgrad": ["void mq::conv_wgrad_kernel", "mq::wgrad_sum_kernel"],
+    "conv_dgrad": ["void mq::conv_spatial_kernel<4, true"],
+}
 
 
 def parse():
@@ -32,98 +55,127 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--op-reps", type=int, default=50, help="reps per op for the breakdown")
+    ap.add_argument("--op-reps", type=int, default=20, help="launches per op for the breakdown")
+    ap.add_argument("--eager", action="store_true",
+                    help="time plain launches (the default; kept for the profiling commands)")
+    ap.add_argument("--graph", action="store_true", help="time HIP graph replays of the steps")
+    ap.add_argument("--roofline-op", default=None,
+                    help="op the roofline covers (default: the one with the longest per-op time)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-n", type=int, default=32,
                     help="batch elements of the layer the CPU oracle runs on")
     ap.add_argument("--calib-copy", action="store_true",
-                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="print the traffic summary from two rocprofv3 --pmc databases")
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "microscaling_quantized_convolution_amd",
+                                           "csrc", "*"))):
+        if p.endswith((".hip", ".hpp", ".cpp")):
+            h.update(os.path.basename(p).encode())
+            with open(p, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(op: str):
+    """HBM bytes per launch of `op` from the committed counter summary, or None if there is none
+    or it was taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith((" ", "#", "|")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha256") != kernel_source_hash():
+        return None
+    v = kv.get(f"traffic_bytes_per_launch.{op}")
+    return None if v is None else int(float(v))
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the hot path here is single-device; "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import microscaling_quantized_convolution_amd as mq
+    from microscaling_quantized_convolution_amd.step import LayerStep
     import workloads
 
     layer = workloads.config2()[0]
     N, Ci, H, W, Co, Kh, Kw = (layer.N, layer.Cin, layer.H, layer.W, layer.Cout, layer.Kh,
                                layer.Kw)
     Ho, Wo = layer.Ho, layer.Wo
-    p = layer.conv_tuple()
     fmt = layer.fmt
     dev = "cuda:0"
     torch.cuda.set_device(0)
 
     x, w, g = workloads.make_tensors(layer)
-    xt = torch.from_numpy(x).to(dev)
-    wt = torch.from_numpy(w).to(dev)
     gc = torch.empty(g.size, dtype=torch.float32, device=dev)
     # G_Y arrives channel-batch-first (it is the next layer's input-gradient output)
     mq.mq_relayout_cbf(torch.from_numpy(g).to(dev), gc, N, Co, Ho, Wo, 0)
-    xc = torch.empty(x.size, dtype=torch.float32, device=dev)
-    wc = torch.empty(w.size, dtype=torch.float32, device=dev)
-    amax = torch.empty(4, dtype=torch.int32, device=dev)
-    qx = mq.QTensor(H, W, Ci, N, fmt, mq.MQ_ROLE_ACT, dev)
-    qw = mq.QTensor(Kh, Kw, Co, Ci, fmt, mq.MQ_ROLE_WEIGHT, dev)
-    qg = mq.QTensor(Ho, Wo, Co, N, fmt, mq.MQ_ROLE_GRAD, dev)
-    y = torch.empty(Ho * Wo * Co * N, dtype=torch.float32, device=dev)
-    gw = torch.empty(Kh * Kw * Co * Ci, dtype=torch.float32, device=dev)
-    gx = torch.empty(H * W * Ci * N, dtype=torch.float32, device=dev)
-    ws = torch.empty(mq.mq_wgrad_workspace_bytes(p), dtype=torch.uint8, device=dev)
-    a0, a1, a2 = amax[0:1], amax[1:2], amax[2:3]
-
-    ops = {
-        "relayout_x": lambda s: mq.mq_relayout_cbf(xt, xc, N, Ci, H, W, 0),
-        "relayout_w": lambda s: mq.mq_relayout_weight(wt, wc, Co, Ci, Kh, Kw, 0),
-        "quantize_x": lambda s: mq.mq_quantize(xc, qx, mq.MQ_RNE, 0, a0),
-        "quantize_w": lambda s: mq.mq_quantize(wc, qw, mq.MQ_RNE, 0, a1),
-        "quantize_g": lambda s: mq.mq_quantize(gc, qg, mq.MQ_SR, 1 + s, a2),
-        "conv_fwd": lambda s: mq.mq_conv_fwd(p, qx, qw, y),
-        "conv_wgrad": lambda s: mq.mq_conv_wgrad(p, qg, qx, gw, ws),
-        "conv_dgrad": lambda s: mq.mq_conv_dgrad(p, qw, qg, gx),
-    }
+    st = LayerStep(layer.conv_tuple(), fmt, torch.from_numpy(x).to(dev),
+                   torch.from_numpy(w).to(dev), gc, sr_seed_base=layer.sr_seed)
+    ops = st.ops
+    stream = torch.cuda.Stream()
 
     flops = layer.gemm_flops()
     sq = lambda o0, o1, r, s_: o0 * o1 * ((r + 3) // 4) * ((s_ + 3) // 4)
     qbytes = lambda shape: sq(*shape) * (8 if fmt == 4 else 12) + sq(*shape)  # codes + scales
     nx, nw, ng = x.size, w.size, g.size
     qx_b, qw_b, qg_b = qbytes((H, W, Ci, N)), qbytes((Kh, Kw, Co, Ci)), qbytes((Ho, Wo, Co, N))
-    # algorithmic bytes: quantize = amax read + quantize read + codes/scales written
+    # algorithmic bytes: relayout 8 B/el; quantize = amax read + quantize read + codes/scales
     alg = {
         "relayout_x": ("hbm", 8 * nx), "relayout_w": ("hbm", 8 * nw),
         "quantize_x": ("hbm", 8 * nx + qx_b), "quantize_w": ("hbm", 8 * nw + qw_b),
         "quantize_g": ("hbm", 8 * ng + qg_b),
-        "conv_fwd": ("mfma", flops), "conv_wgrad": ("mfma", flops), "conv_dgrad": ("mfma", flops),
+        "conv_fwd": ("gemm", flops), "conv_wgrad": ("gemm", flops), "conv_dgrad": ("gemm", flops),
     }
+    # conv: quantized operands read once + fp32 result written once
     conv_bytes = {"conv_fwd": qx_b + qw_b + 4 * Ho * Wo * Co * N,
                   "conv_wgrad": qg_b + qx_b + 4 * Kh * Kw * Co * Ci,
                   "conv_dgrad": qw_b + qg_b + 4 * H * W * Ci * N}
+    ridge = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 
-    def step(s):
-        for f in ops.values():
-            f(s)
+    def capture(fns):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=stream):
+            for f in fns:
+                f()
+        return gr
 
-    # ---- per-op breakdown (each op back to back, events on the launch stream) ----
-    for s in range(max(args.warmup, 1)):
-        step(s)
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # ---- warm-up (eager) ----
+    with torch.cuda.stream(stream):
+        for s in range(max(args.warmup, 1)):
+            st.run(s)
     torch.cuda.synchronize()
+
+    # ---- per-op breakdown: each op alone, `op_reps` launches back to back ----
     per_op = {}
     for name, f in ops.items():
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        f(0)
-        e0.record()
-        for r in range(args.op_reps):
-            f(r)
-        e1.record()
+        with torch.cuda.stream(stream):
+            gr = capture([lambda r=r: f(r) for r in range(args.op_reps)])
+            gr.replay()
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            gr.replay()
+            e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.op_reps
         kind, amount = alg[name]
@@ -135,29 +187,63 @@ def main():
             tf = amount / (ms * 1e-3) / 1e12
             gbs = conv_bytes[name] / (ms * 1e-3) / 1e9
             per_op[name] = {"ms": round(ms, 5), "TFLOP_s": round(tf, 1),
-                            "frac_mfma_bf16": round(tf / BF16_PEAK_TFLOPS, 4),
+                            "frac_mfma": round(tf / MFMA_PEAK_TFLOPS, 4),
                             "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                            "alg_flops": amount, "alg_bytes": conv_bytes[name]}
-    dominant = max(per_op, key=lambda k: per_op[k]["ms"])
+                            "alg_flops": amount, "alg_bytes": conv_bytes[name],
+                            "bound": "mfma" if amount / conv_bytes[name] >= ridge else "hbm"}
+    dominant = args.roofline_op or max(per_op, key=lambda k: per_op[k]["ms"])
+    names = list(ops)
+    di = names.index(dominant)
 
-    # ---- timed steps, with events around every launch of the dominant op ----
+    # ---- timed steps: pre-ops, the dominant op between two events, post-ops ----
+    total = args.warmup + args.steps
+    calls = st.direct_calls(stream)
+    if not args.graph:
+        plan = None
+    else:
+        plan = []
+        for s in range(total):
+            fs = [lambda f=ops[n], s=s: f(s) for n in names]
+            plan.append((capture(fs[:di]) if di > 0 else None, capture([fs[di]]),
+                         capture(fs[di + 1:]) if di + 1 < len(fs) else None))
+        torch.cuda.synchronize()
+
+    def run_step(s, e_in=None, e_out=None):
+        if plan is None:
+            for n in names[:di]:
+                calls[n](s)
+            if e_in is not None:
+                e_in.record(stream)
+            calls[dominant](s)
+            if e_out is not None:
+                e_out.record(stream)
+            for n in names[di + 1:]:
+                calls[n](s)
+        else:
+            pre, dom, post = plan[s]
+            if pre is not None:
+                pre.replay()
+            if e_in is not None:
+                e_in.record(stream)
+            dom.replay()
+            if e_out is not None:
+                e_out.record(stream)
+            if post is not None:
+                post.replay()
+
+    with torch.cuda.stream(stream):
+        for s in range(args.warmup):
+            run_step(s)
     torch.cuda.synchronize()
-    dom_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    dom_ev = [(ev(), ev()) for _ in range(args.steps)]
+    t0, t1 = ev(), ev()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t0.record()
-    for s in range(args.steps):
-        for name, f in ops.items():
-            if name == dominant:
-                dom_ev[s][0].record()
-                f(args.warmup + s)
-                dom_ev[s][1].record()
-            else:
-                f(args.warmup + s)
-    t1.record()
+    with torch.cuda.stream(stream):
+        t0.record(stream)
+        for s in range(args.steps):
+            run_step(args.warmup + s, *dom_ev[s])
+        t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / args.steps
@@ -167,22 +253,20 @@ def main():
     if kind == "hbm":
         ach = amount / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    elif amount / conv_bytes[dominant] >= ridge:
+        ach = amount / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
     else:
-        # the convolution GEMMs at this shape: arithmetic intensity decides the bound
-        ai = amount / conv_bytes[dominant]
-        ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-        if ai >= ridge:
-            ach = amount / (dom_ms * 1e-3) / 1e12
-            roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s"}
-        else:
-            ach = conv_bytes[dominant] / (dom_ms * 1e-3) / 1e9
-            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s"}
+        ach = conv_bytes[dominant] / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
-    roof["kernel"] = dominant
+    roof["traffic"] = read_traffic(dominant)
+    roof["op"] = dominant
+    roof["kernels"] = OP_KERNELS[dominant]
     roof["ms_per_launch"] = round(dom_ms, 5)
+    roof["alg_per_launch"] = amount if roof["bound"] != "hbm" or kind == "hbm" \
+        else conv_bytes[dominant]
 
     result = {
         "metric": "quant GB/s (% HBM peak) + conv fwd/wgrad/dgrad TFLOP/s (% bf16 MFMA) per layer",
@@ -193,30 +277,32 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "wall_s_timed": round(wall, 4),
+        "timing": "HIP graph replay per step" if args.graph else "back-to-back launches",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4-e2m1/e4m3 codes, bf16 MFMA, fp32 accumulate",
+        "dtype": "fp16",
         "data": "synthetic (seeded numpy PCG64; X=ReLU(N(0,1)), W Kaiming-normal, G_Y~N(0,1e-3))",
-        "config": {"workload": "resnet-3x3-s1p1 N=32 Cin=Cout=64 56x56 NVFP4: relayout + "
-                               "quantize x3 + conv fwd/wgrad/dgrad",
+        "config": {"workload": "resnet-3x3-s1p1 N=32 Cin=Cout=64 56x56 NVFP4: relayout x2, "
+                               "quantize x3 (RNE, RNE, SR), conv fwd/wgrad/dgrad",
                    "N": N, "Cin": Ci, "Cout": Co, "H": H, "W": W, "K": Kh, "stride": 1, "pad": 1,
-                   "format": "NVFP4"},
+                   "format": "NVFP4 (E2M1 codes, E4M3 4x4-square scales, fp32 tensor scale)",
+                   "mfma": "fp16 operands decoded exactly, fp32 accumulate"},
         "per_op": per_op,
         "roofline": roof,
     }
 
     if args.calib_copy:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
-        dst = torch.empty_like(src)
-        src.fill_(1.0)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        import torch as _t
+        src = _t.full((CALIB_ELEMS,), 1.0, dtype=_t.float32, device=dev)
+        dst = _t.empty_like(src)
+        _t.cuda.synchronize()
+        e0, e1 = ev(), ev()
         e0.record()
-        dst.copy_(src)
+        _t.neg(src, out=dst)
         e1.record()
-        torch.cuda.synchronize()
-        result["calib_copy"] = {"bytes_each_way": src.numel() * 4,
+        _t.cuda.synchronize()
+        result["calib_copy"] = {"bytes_read": CALIB_ELEMS * 4, "bytes_written": CALIB_ELEMS * 4,
                                 "ms": round(e0.elapsed_time(e1), 4)}
 
     if not args.no_cpu_baseline:
@@ -254,6 +340,65 @@ def cpu_baseline(layer, nsample: int):
             "sample": f"same layer with N={nsample} of {layer.N} batch elements: relayout, "
                       f"3 quantizations, dequantization, explicit-im2col fwd/wgrad/dgrad in "
                       f"double; flops of the sample's three GEMMs / wall time"}
+
+
+def _short(name: str) -> str:
+    """Kernel name without its parameter list."""
+    if name.endswith(")"):
+        depth = 0
+        for i in range(len(name) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(name[i], 0)
+            if depth == 0:
+                return name[:i]
+    return name
+
+
+def _pmc_per_kernel(db: str, counter: str):
+    """Mean per dispatch of `counter` (summed over its instances) per kernel name."""
+    import collections
+    import sqlite3
+    con = sqlite3.connect(db)
+    cols = [r[1] for r in con.execute("pragma table_info(counters_collection)")]
+    ki, ci, vi, di = (cols.index(c) for c in ("kernel_name", "counter_name", "value",
+                                              "dispatch_id"))
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for row in con.execute("select * from counters_collection"):
+        if row[ci] == counter:
+            per[_short(row[ki])][row[di]] += row[vi]
+    return {k: (sum(d.values()) / len(d), len(d)) for k, d in per.items()}
+
+
+def summarize_pmc(fetch_db: str, write_db: str):
+    """Traffic summary (key: value lines) from a FETCH_SIZE run and a WRITE_SIZE run of
+    `bench.py --eager --calib-copy`; the counters are KiB per dispatch."""
+    fetch = _pmc_per_kernel(fetch_db, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_db, "WRITE_SIZE")
+    copy = [k for k in fetch if "neg_kernel" in k]
+    if not copy:
+        raise SystemExit("no calibration copy kernel in the FETCH_SIZE database")
+    ck = copy[0]
+    f_cal = fetch[ck][0] * 1024 / (CALIB_ELEMS * 4)
+    w_cal = write[ck][0] * 1024 / (CALIB_ELEMS * 4) if ck in write else 1.0
+    print(f"kernel_sources_sha256: {kernel_source_hash()}")
+    print(f"calibration_kernel: {ck[:90]}")
+    print(f"calibration_fetch_factor: {f_cal:.4f}")
+    print(f"calibration_write_factor: {w_cal:.4f}")
+    print("#")
+    print("# kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (calibrated)")
+    per_kernel = {}
+    for k in sorted(fetch):
+        fk = fetch[k][0]
+        wk = write.get(k, (0.0, 0))[0]
+        b = fk * 1024 / f_cal + wk * 1024 / w_cal
+        per_kernel[k] = b
+        print(f"| {k[:90]} | {fetch[k][1]} | {fk:.1f} | {wk:.1f} | {b:.0f} |")
+    # per op (relayout_x/w and quantize_x/w/g share kernel names with different sizes, so only
+    # the convolutions, whose kernels are distinct, get a per-op figure)
+    for op in ("conv_fwd", "conv_wgrad", "conv_dgrad"):
+        tot = sum(b for k, b in per_kernel.items()
+                  if any(k.replace("(anonymous namespace)::", "").startswith(p)
+                         for p in OP_KERNELS[op]))
+        print(f"traffic_bytes_per_launch.{op}: {tot:.0f}")
 
 
 if __name__ == "__main__":

@@ -133,11 +133,15 @@ mq_status mq_relayout_weight(const float *src_dev, float *dst_dev, int32_t Cout,
  *          channel-batch-first layout).
  * dst:     host struct describing the destination; dst->codes, dst->scales, dst->tscale are
  *          device buffers of mq_codes_bytes / mq_scales_bytes / 4 bytes.
- * amax_ws_dev: one device uint32 of scratch (overwritten).
- * Errors: MQ_ERR_ARG (null pointer, bad enum, non-positive dims).
+ * amax_ws_dev / amax_ws_bytes: device scratch of at least MQ_QUANTIZE_WS_BYTES bytes, 4-byte
+ *          aligned, for the amax pass's partial maxima (overwritten; calls on one stream may
+ *          share it, calls that can run concurrently must not).
+ * Errors: MQ_ERR_ARG (null pointer, bad enum, non-positive dims, misaligned pointer),
+ *         MQ_ERR_WORKSPACE (amax_ws_dev null or smaller than MQ_QUANTIZE_WS_BYTES).
  */
+#define MQ_QUANTIZE_WS_BYTES 1024
 mq_status mq_quantize(const float *src_dev, const mq_qtensor *dst, int32_t rnd, uint64_t seed,
-                      uint32_t *amax_ws_dev, hipStream_t stream);
+                      uint32_t *amax_ws_dev, size_t amax_ws_bytes, hipStream_t stream);
 
 /*
  * mq_conv_fwd: forward GEMM Y = W . X' (onedev.kr digest, section "How it differs") with the

@@ -20,6 +20,7 @@ MQ_OK, MQ_ERR_ARG, MQ_ERR_SHAPE, MQ_ERR_UNSUPPORTED, MQ_ERR_WORKSPACE, MQ_ERR_LA
 MQ_NVFP4, MQ_NVFP6 = 4, 6
 MQ_ROLE_ACT, MQ_ROLE_WEIGHT, MQ_ROLE_GRAD = 0, 1, 2
 MQ_RNE, MQ_SR = 0, 1
+MQ_QUANTIZE_WS_BYTES = 1024  # amax workspace of mq_quantize
 
 EXPORTS = (
     "mq_status_str", "mq_codes_bytes", "mq_scales_bytes", "mq_relayout_cbf",
@@ -60,7 +61,7 @@ def _load() -> ctypes.CDLL:
     L.mq_scales_bytes.argtypes = [i32] * 4
     L.mq_relayout_cbf.argtypes = [P, P, i32, i32, i32, i32, i32, P]
     L.mq_relayout_weight.argtypes = [P, P, i32, i32, i32, i32, i32, P]
-    L.mq_quantize.argtypes = [P, ctypes.POINTER(mq_qtensor), i32, u64, P, P]
+    L.mq_quantize.argtypes = [P, ctypes.POINTER(mq_qtensor), i32, u64, P, sz, P]
     L.mq_conv_fwd.argtypes = [ctypes.POINTER(mq_conv), ctypes.POINTER(mq_qtensor),
                               ctypes.POINTER(mq_qtensor), P, P]
     L.mq_wgrad_workspace_bytes.restype = sz
@@ -146,11 +147,17 @@ def mq_relayout_weight(src: torch.Tensor, dst: torch.Tensor, Cout: int, Cin: int
                                    _stream(stream)), "mq_relayout_weight")
 
 
+def quantize_workspace(device: Union[str, torch.device] = "cuda") -> torch.Tensor:
+    """Device scratch for mq_quantize's amax pass."""
+    return torch.empty(MQ_QUANTIZE_WS_BYTES, dtype=torch.uint8, device=device)
+
+
 def mq_quantize(src: torch.Tensor, dst: QTensor, rnd: int, seed: int, amax_ws: torch.Tensor,
                 stream=None):
     q = dst.struct()
+    nbytes = amax_ws.numel() * amax_ws.element_size()
     _check(_lib.mq_quantize(_ptr(src), ctypes.byref(q), rnd, seed & (2 ** 64 - 1),
-                            _ptr(amax_ws), _stream(stream)), "mq_quantize")
+                            _ptr(amax_ws), nbytes, _stream(stream)), "mq_quantize")
 
 
 def mq_conv_fwd(p: ConvLike, x: QTensor, w: QTensor, y: torch.Tensor, stream=None):

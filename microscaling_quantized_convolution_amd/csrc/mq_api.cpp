@@ -110,9 +110,11 @@ mq_status mq_relayout_weight(const float *src, float *dst, int32_t Cout, int32_t
 }
 
 mq_status mq_quantize(const float *src, const mq_qtensor *dst, int32_t rnd, uint64_t seed,
-                      uint32_t *amax_ws, hipStream_t stream)
+                      uint32_t *amax_ws, size_t amax_ws_bytes, hipStream_t stream)
 {
-    if (!src || !qtensor_ok(dst) || !amax_ws || (rnd != MQ_RNE && rnd != MQ_SR)) return MQ_ERR_ARG;
+    if (!src || !qtensor_ok(dst) || (rnd != MQ_RNE && rnd != MQ_SR)) return MQ_ERR_ARG;
+    if (!amax_ws || amax_ws_bytes < MQ_QUANTIZE_WS_BYTES) return MQ_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(amax_ws) & 3u) != 0) return MQ_ERR_ARG;
     return launch_status(mq::launch_quantize(src, (int64_t)dst->o0 * dst->o1, dst->r, dst->s,
                                              dst->fmt, rnd, seed, dst->codes, dst->scales,
                                              dst->tscale, amax_ws, stream));

@@ -11,6 +11,8 @@ hipError_t launch_relayout_cbf(const float *src, float *dst, int N, int C, int H
                                int inverse, hipStream_t st);
 hipError_t launch_relayout_weight(const float *src, float *dst, int Cout, int Cin, int Kh,
                                   int Kw, int inverse, hipStream_t st);
+// amax_ws: kAmaxParts words of partial maxima
+constexpr int kAmaxParts = 256;
 hipError_t launch_quantize(const float *src, int64_t planes, int R, int S, int fmt, int rnd,
                            uint64_t seed, uint8_t *codes, uint8_t *scales, float *tscale,
                            uint32_t *amax_ws, hipStream_t st);

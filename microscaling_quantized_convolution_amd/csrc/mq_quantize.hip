@@ -6,8 +6,10 @@
 //   gradients. Each tensor is quantized once; the square shares its scale along 4 elements in
 //   both of its dimensions, so the same codes serve the GEMMs that reduce along either one.
 //
-// Two kernels per tensor: amax (grid-stride max of |x| as uint bit patterns, wave reduction,
-// one atomicMax per workgroup) and quantize (one lane per 4x4 square).
+// Two kernels per tensor: amax (grid-stride max of |x| as uint bit patterns, one partial maximum
+// per workgroup) and quantize (each workgroup first reduces the partial maxima to the tensor's
+// amax, then one lane per 4x4 square). No atomics and no memset: every call writes all the
+// partials it reads.
 #include "mq_device.hpp"
 #include "mq_kernels.hpp"
 
@@ -15,8 +17,6 @@ namespace mq {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-__global__ void zero_u32_kernel(uint32_t *p) { *p = 0u; }
 
 // Max over |x| as unsigned bit patterns: for non-negative floats the order of the bit patterns
 // is the numeric order, and NaN patterns sort above +inf, so a NaN anywhere wins.
@@ -27,39 +27,54 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     return v;
 }
 
-__global__ void __launch_bounds__(256) amax_kernel(const float *__restrict__ x, int64_t n,
-                                                   uint32_t *__restrict__ out)
+__device__ __forceinline__ uint32_t absmax4(u32x4_t v)
+{
+    return max(max(v[0] & 0x7FFFFFFFu, v[1] & 0x7FFFFFFFu), max(v[2] & 0x7FFFFFFFu, v[3] & 0x7FFFFFFFu));
+}
+
+// Maximum over the 64-lane waves of a workgroup of kThreads lanes (every lane gets it).
+template <int kThreads>
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *red)
+{
+    v = wave_max_u32(v);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    if (lane == 0) red[wid] = v;
+    __syncthreads();
+    uint32_t r = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) r = max(r, red[w]);
+    return r;
+}
+
+constexpr int kAmaxThreads = 512;
+
+// Partial maxima: workgroup b writes max |x| over its grid-stride share to part[b]. Eight
+// independent 16-byte loads per lane are in flight at a time, enough to cover HBM latency.
+__global__ void __launch_bounds__(kAmaxThreads) amax_kernel(const float *__restrict__ x, int64_t n,
+                                                            uint32_t *__restrict__ part)
 {
     uint32_t m = 0u;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const bool aligned = ((reinterpret_cast<uintptr_t>(x) & 15u) == 0);
-    if (aligned) {
+    const int64_t nt = (int64_t)gridDim.x * kAmaxThreads;
+    const int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+    int64_t tail = 0;
+    if ((reinterpret_cast<uintptr_t>(x) & 15u) == 0) {
         const int64_t n4 = n >> 2;
         const u32x4_t *x4 = reinterpret_cast<const u32x4_t *>(x);
-        for (int64_t j = i; j < n4; j += stride) {
-            u32x4_t v = __builtin_nontemporal_load(x4 + j);
-            m = max(m, max(max(v[0] & 0x7FFFFFFFu, v[1] & 0x7FFFFFFFu),
-                           max(v[2] & 0x7FFFFFFFu, v[3] & 0x7FFFFFFFu)));
+        int64_t j = i;
+        for (; j + 7 * nt < n4; j += 8 * nt) {
+            u32x4_t v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = x4[j + k * nt]; // cached: quantize reads x next
+#pragma unroll
+            for (int k = 0; k < 8; ++k) m = max(m, absmax4(v[k]));
         }
-        for (int64_t j = (n4 << 2) + i; j < n; j += stride)
-            m = max(m, __float_as_uint(x[j]) & 0x7FFFFFFFu);
-    } else {
-        for (int64_t j = i; j < n; j += stride) m = max(m, __float_as_uint(x[j]) & 0x7FFFFFFFu);
+        for (; j < n4; j += nt) m = max(m, absmax4(x4[j]));
+        tail = n4 << 2;
     }
-    m = wave_max_u32(m);
-    __shared__ uint32_t red[4];
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    if (lane == 0) red[wid] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t r = red[0];
-        for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = max(r, red[w]);
-        // Skip the atomic when the running maximum already covers this block: one contended
-        // word otherwise serializes every workgroup.
-        if (r && r > __hip_atomic_load(out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-            atomicMax(out, r);
-    }
+    for (int64_t j = tail + i; j < n; j += nt) m = max(m, __float_as_uint(x[j]) & 0x7FFFFFFFu);
+    __shared__ uint32_t red[kAmaxThreads / 64];
+    m = block_max_u32<kAmaxThreads>(m, red);
+    if (threadIdx.x == 0) part[blockIdx.x] = m;
 }
 
 struct QuantArgs {
@@ -67,7 +82,8 @@ struct QuantArgs {
     uint8_t *codes;
     uint8_t *scales;
     float *tscale;
-    const uint32_t *amax_bits;
+    const uint32_t *amax_part; // partial maxima of |x| bit patterns
+    int32_t nparts;            // <= 256
     int64_t planes; // o0 * o1
     int32_t R, S, R4, S4;
     int64_t nsq;
@@ -81,10 +97,12 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a)
 {
     using F = Fmt<FMT>;
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= a.nsq) return;
 
-    // Tensor scale from the amax pass.
-    const uint32_t abits = *a.amax_bits;
+    // Tensor scale: reduce the amax pass's partial maxima (every lane of the workgroup).
+    __shared__ uint32_t red[4];
+    const uint32_t abits =
+        block_max_u32<256>(threadIdx.x < a.nparts ? a.amax_part[threadIdx.x] : 0u, red);
+    if (t >= a.nsq) return;
     const bool nonfinite = abits >= 0x7F800000u;
     const float T = __uint_as_float(abits) / (448.0f * F::kEmax);
     if (t == 0) *a.tscale = nonfinite ? __uint_as_float(0x7FC00000u) : T;
@@ -201,16 +219,16 @@ hipError_t launch_quantize(const float *src, int64_t planes, int R, int S, int f
                            uint32_t *amax_ws, hipStream_t st)
 {
     const int64_t n = planes * (int64_t)R * S;
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, st, amax_ws);
-    // at least 8 float4 per lane, at most 1024 workgroups (4 per CU)
-    int64_t want = (n / 4 + 2047) / 2048;
-    unsigned ablocks = (unsigned)(want < 1 ? 1 : (want > 1024 ? 1024 : want));
-    hipLaunchKernelGGL(amax_kernel, dim3(ablocks), dim3(256), 0, st, src, n, amax_ws);
+    // at least 8 float4 per lane where the tensor allows, at most kAmaxParts workgroups
+    const int64_t want = (n / 4 + 8 * kAmaxThreads - 1) / (8 * kAmaxThreads);
+    const int parts = (int)(want < 1 ? 1 : (want > kAmaxParts ? kAmaxParts : want));
+    hipLaunchKernelGGL(amax_kernel, dim3(parts), dim3(kAmaxThreads), 0, st, src, n, amax_ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
     QuantArgs a;
-    a.src = src; a.codes = codes; a.scales = scales; a.tscale = tscale; a.amax_bits = amax_ws;
+    a.src = src; a.codes = codes; a.scales = scales; a.tscale = tscale;
+    a.amax_part = amax_ws; a.nparts = parts;
     a.planes = planes; a.R = R; a.S = S; a.R4 = (R + 3) / 4; a.S4 = (S + 3) / 4;
     a.nsq = planes * a.R4 * a.S4;
     a.seed_lo = (uint32_t)seed; a.seed_hi = (uint32_t)(seed >> 32);

@@ -40,7 +40,7 @@ def to_dev(a: np.ndarray, dev="cuda") -> torch.Tensor:
 
 def gpu_quantize(src_cbf: torch.Tensor, shape, fmt, role, rnd, seed, dev="cuda"):
     q = mq.QTensor(*shape, fmt, role, dev)
-    ws = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = mq.quantize_workspace(dev)
     mq.mq_quantize(src_cbf, q, rnd, seed, ws)
     return q
 
