@@ -137,7 +137,8 @@ mq_status mq_relayout_weight(const float *src_dev, float *dst_dev, int32_t Cout,
  *          aligned, for the amax pass's partial maxima (overwritten; calls on one stream may
  *          share it, calls that can run concurrently must not).
  * Errors: MQ_ERR_ARG (null pointer, bad enum, non-positive dims, misaligned pointer),
- *         MQ_ERR_WORKSPACE (amax_ws_dev null or smaller than MQ_QUANTIZE_WS_BYTES).
+ *         MQ_ERR_WORKSPACE (amax_ws_dev null or smaller than MQ_QUANTIZE_WS_BYTES),
+ *         MQ_ERR_UNSUPPORTED (2^31 squares or more).
  */
 #define MQ_QUANTIZE_WS_BYTES 1024
 mq_status mq_quantize(const float *src_dev, const mq_qtensor *dst, int32_t rnd, uint64_t seed,

@@ -114,6 +114,7 @@ mq_status mq_quantize(const float *src, const mq_qtensor *dst, int32_t rnd, uint
 {
     if (!src || !qtensor_ok(dst) || (rnd != MQ_RNE && rnd != MQ_SR)) return MQ_ERR_ARG;
     if (!amax_ws || amax_ws_bytes < MQ_QUANTIZE_WS_BYTES) return MQ_ERR_WORKSPACE;
+    if (squares(dst->o0, dst->o1, dst->r, dst->s) >= ((int64_t)1 << 31)) return MQ_ERR_UNSUPPORTED;
     if ((reinterpret_cast<uintptr_t>(amax_ws) & 3u) != 0) return MQ_ERR_ARG;
     return launch_status(mq::launch_quantize(src, (int64_t)dst->o0 * dst->o1, dst->r, dst->s,
                                              dst->fmt, rnd, seed, dst->codes, dst->scales,

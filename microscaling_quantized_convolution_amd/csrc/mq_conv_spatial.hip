@@ -58,7 +58,10 @@ struct SpatialArgs {
 // squares of the stage after next into registers and decode the next stage into the other LDS
 // buffer. Both sides meet at one barrier per stage, so a SIMD runs one MFMA wave and one decode
 // wave side by side.
-template <int FMT, bool A_KR, int SI, int PH, int PW>
+// KF = 3: every workgroup's class has the full 3 x 3 taps (compile-time tap loops, so the
+// consumer's LDS reads for later taps can be issued ahead of earlier taps' MFMAs); KF = 0: the
+// class's sub-kernel extent is read at run time.
+template <int FMT, bool A_KR, int SI, int PH, int PW, int KF>
 __global__ void __launch_bounds__(32 * PH * PW)
 conv_spatial_kernel(SpatialArgs a)
 {
@@ -85,7 +88,8 @@ conv_spatial_kernel(SpatialArgs a)
     const int ti = tile / cl.tiles_w, tj = tile - ti * cl.tiles_w;
     const int i0 = ti * PH, j0 = tj * PW;
     const int m4_0 = blockIdx.y * 16;
-    const int kh = cl.kh * (int)live, kw = cl.kw * (int)live, ntap = kh * kw;
+    const int kh = KF ? KF : cl.kh * (int)live, kw = KF ? KF : cl.kw * (int)live;
+    const int ntap = kh * kw;
     const int HR = (PH - 1) * SI + kh, HC = (PW - 1) * SI + kw;
     const int nchunk = ((a.K4 + 3) / 4) * (ntap > 0 ? 1 : 0);
 
@@ -321,8 +325,14 @@ static hipError_t launch_spatial(SpatialArgs &a, int nclass, hipStream_t st)
         if (a.cls[c].tiles > max_tiles) max_tiles = a.cls[c].tiles;
     }
     dim3 grid((unsigned)(max_tiles * a.nblk), (unsigned)((a.M4 + 15) / 16), (unsigned)nclass);
-    hipLaunchKernelGGL((conv_spatial_kernel<FMT, A_KR, SI, PH, PW>), grid, dim3(32 * PH * PW), 0,
-                       st, a);
+    const bool full3 = nclass == 1 && a.cls[0].kh == 3 && a.cls[0].kw == 3 &&
+                       a.cls[0].tiles * a.nblk == (int)grid.x;
+    if (full3)
+        hipLaunchKernelGGL((conv_spatial_kernel<FMT, A_KR, SI, PH, PW, 3>), grid,
+                           dim3(32 * PH * PW), 0, st, a);
+    else
+        hipLaunchKernelGGL((conv_spatial_kernel<FMT, A_KR, SI, PH, PW, 0>), grid,
+                           dim3(32 * PH * PW), 0, st, a);
     return hipGetLastError();
 }
 

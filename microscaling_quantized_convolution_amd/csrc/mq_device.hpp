@@ -95,14 +95,14 @@ template <int FMT>
 __device__ __forceinline__ uint32_t grid_sr(float a, uint32_t u16)
 {
     using F = Fmt<FMT>;
-    if (a >= F::kEmax) return F::kMaxMag;
     float sc = a < 2.0f ? F::kScale0 : (a < 4.0f ? 0.5f * F::kScale0 : 0.25f * F::kScale0);
     float ad = a < 2.0f ? 0.0f : (a < 4.0f ? F::kAdd1 : F::kAdd2);
     float fl = __builtin_floorf(a * sc);
-    float lo = fl / sc;                       // exact
+    float lo = fl * (1.0f / sc);              // exact: sc is a power of two
     float frac = (a - lo) * sc;               // exact: Sterbenz, power-of-two scale
     uint32_t up = ((float)u16 < frac * 65536.0f) ? 1u : 0u;
-    return (uint32_t)(fl + ad) + up;
+    const uint32_t c = (uint32_t)(fl + ad) + up;
+    return a >= F::kEmax ? F::kMaxMag : c;   // at or above the largest element: saturate
 }
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): multipliers 0xD2511F53 / 0xCD9E8D57,

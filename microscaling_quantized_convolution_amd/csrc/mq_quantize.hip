@@ -47,6 +47,7 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *red)
 }
 
 constexpr int kAmaxThreads = 512;
+constexpr int64_t kQuantBlocks = 1024;
 
 // Partial maxima: workgroup b writes max |x| over its grid-stride share to part[b]. Eight
 // independent 16-byte loads per lane are in flight at a time, enough to cover HBM latency.
@@ -96,70 +97,123 @@ template <int FMT, bool SR, bool FULL>
 __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a)
 {
     using F = Fmt<FMT>;
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-
     // Tensor scale: reduce the amax pass's partial maxima (every lane of the workgroup).
     __shared__ uint32_t red[4];
     const uint32_t abits =
         block_max_u32<256>(threadIdx.x < a.nparts ? a.amax_part[threadIdx.x] : 0u, red);
-    if (t >= a.nsq) return;
     const bool nonfinite = abits >= 0x7F800000u;
     const float T = __uint_as_float(abits) / (448.0f * F::kEmax);
-    if (t == 0) *a.tscale = nonfinite ? __uint_as_float(0x7FC00000u) : T;
+    // square indices fit in 31 bits (checked at launch)
+    const int t0 = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (t0 == 0) *a.tscale = nonfinite ? __uint_as_float(0x7FC00000u) : T;
+    const int nsq = (int)a.nsq;
+    if (t0 >= nsq) return;
+    const int stride = (int)(gridDim.x * blockDim.x);
 
-    const int s4 = (int)(t % a.S4);
-    const int64_t rest = t / a.S4;
-    const int r4 = (int)(rest % a.R4);
-    const int64_t plane = rest / a.R4;
-    const int64_t base = (plane * a.R + 4 * r4) * (int64_t)a.S + 4 * s4;
-
-    float x[16];
-    if (FULL) {
+    // Square t = (plane * R4 + r4) * S4 + s4, stepped by `stride` with carries instead of
+    // divisions: the step is (dp, dr, ds) in the same mixed radix.
+    struct Pos { int plane, r4, s4; };
+    const int ds = stride % a.S4, dr = (stride / a.S4) % a.R4, dp = stride / a.S4 / a.R4;
+    auto advance = [&](Pos p) {
+        p.s4 += ds;
+        const int c1 = p.s4 >= a.S4;
+        p.s4 -= c1 ? a.S4 : 0;
+        p.r4 += dr + c1;
+        const int c2 = p.r4 >= a.R4;
+        p.r4 -= c2 ? a.R4 : 0;
+        p.plane += dp + c2;
+        return p;
+    };
+    // Square p's 16 elements, row-major; slots outside [R][S] read as 0.
+    auto load = [&](Pos p, float (&x)[16]) {
+        const int s4 = p.s4, r4 = p.r4;
+        const int64_t base = ((int64_t)p.plane * a.R + 4 * r4) * (int64_t)a.S + 4 * s4;
+        if (FULL) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f32x4_t v = __builtin_nontemporal_load(
-                reinterpret_cast<const f32x4_t *>(a.src + base + (int64_t)i * a.S));
-            x[4 * i + 0] = v[0]; x[4 * i + 1] = v[1]; x[4 * i + 2] = v[2]; x[4 * i + 3] = v[3];
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                bool in = (4 * r4 + i < a.R) && (4 * s4 + j < a.S);
-                x[4 * i + j] = in ? a.src[base + (int64_t)i * a.S + j] : 0.0f;
+            for (int i = 0; i < 4; ++i) {
+                f32x4_t v = __builtin_nontemporal_load(
+                    reinterpret_cast<const f32x4_t *>(a.src + base + (int64_t)i * a.S));
+                x[4 * i + 0] = v[0]; x[4 * i + 1] = v[1]; x[4 * i + 2] = v[2]; x[4 * i + 3] = v[3];
             }
-    }
-
-    uint32_t code[16];
-    uint32_t bcode;
-    if (nonfinite) {
-        bcode = 0x7Fu;
+        } else {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) code[e] = 0u;
-    } else {
-        float bmax = 0.0f;
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) bmax = fmaxf(bmax, fabsf(x[e]));
-        const float TE = T * F::kEmax;
-        // T == 0 only for an all-zero (or vanishingly small) tensor: scales 0, codes 0.
-        bcode = (T == 0.0f) ? 0u : e4m3_rne_sat(bmax / TE);
-        const float B = e4m3_to_float(bcode);
-        const float D = B * T;
-        const bool zero = (bcode == 0u) || (D == 0.0f);
-        Philox4 r0, r1;
-        if (SR && !zero) {
-            const uint64_t j = 2u * (uint64_t)t;
-            r0 = philox4x32_10((uint32_t)j, (uint32_t)(j >> 32), 0u, 0u, a.seed_lo, a.seed_hi);
-            r1 = philox4x32_10((uint32_t)(j + 1), (uint32_t)((j + 1) >> 32), 0u, 0u, a.seed_lo,
-                               a.seed_hi);
+                for (int j = 0; j < 4; ++j) {
+                    bool in = (4 * r4 + i < a.R) && (4 * s4 + j < a.S);
+                    x[4 * i + j] = in ? a.src[base + (int64_t)i * a.S + j] : 0.0f;
+                }
         }
+    };
+
+    // Grid-stride over squares with the next square's loads in flight while this one is
+    // quantized (the last step reloads its own square, so every step issues the same loads).
+    Pos pos = {t0 / a.S4 / a.R4, (t0 / a.S4) % a.R4, t0 % a.S4};
+    float xn[16];
+    load(pos, xn);
+    for (int t = t0; t < nsq; t += stride) {
+        float x[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            uint32_t c = 0u;
+        for (int e = 0; e < 16; ++e) x[e] = xn[e];
+        const Pos cur = pos;
+        const bool more = t + stride < nsq;
+        if (more) pos = advance(pos);
+        load(pos, xn); // the last step reloads its own square
+        const int s4 = cur.s4, r4 = cur.r4;
+        uint32_t code[16];
+        uint32_t bcode;
+        if (nonfinite) {
+            bcode = 0x7Fu;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) code[e] = 0u;
+        } else {
+            float bmax = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) bmax = fmaxf(bmax, fabsf(x[e]));
+            const float TE = T * F::kEmax;
+            // T == 0 only for an all-zero (or vanishingly small) tensor: scales 0, codes 0.
+            bcode = (T == 0.0f) ? 0u : e4m3_rne_sat(bmax / TE);
+            const float B = e4m3_to_float(bcode);
+            const float D = B * T;
+            const bool zero = (bcode == 0u) || (D == 0.0f);
+            // x / D for 16 elements from one reciprocal: with rD = RN(1/D), q0 = RN(x * rD) and the
+            // exact residual x - q0 * D, RN(q0 + residual * rD) is the correctly rounded quotient
+            // (Markstein's theorem) as long as nothing underflows: D within 2^+-64 and
+            // |x / D| >= 2^-20 (or x = 0). A square with any other element (a tiny one, whose code
+            // only the round-up draw of stochastic rounding could tell apart) divides instead.
+            float q[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) q[e] = 0.0f;
             if (!zero) {
-                const float q = x[e] / D; // IEEE-correct division (hipcc default)
-                const float aq = fabsf(q);
+                const float rD = 1.0f / D;
+                const float Dlo = D * 0x1p-20f;
+                bool slow = !(D >= 0x1p-64f && D <= 0x1p64f);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float ax = fabsf(x[e]);
+                    slow |= (ax < Dlo) && (ax != 0.0f);
+                }
+                if (slow) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) q[e] = x[e] / D; // IEEE division
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const float q0 = x[e] * rD;
+                        q[e] = __builtin_fmaf(__builtin_fmaf(-q0, D, x[e]), rD, q0);
+                    }
+                }
+            }
+            Philox4 r0 = {}, r1 = {};
+            if (SR && !zero) {
+                const uint64_t j = 2u * (uint64_t)t;
+                r0 = philox4x32_10((uint32_t)j, (uint32_t)(j >> 32), 0u, 0u, a.seed_lo, a.seed_hi);
+                r1 = philox4x32_10((uint32_t)(j + 1), (uint32_t)((j + 1) >> 32), 0u, 0u, a.seed_lo,
+                                   a.seed_hi);
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float aq = fabsf(q[e]);
                 uint32_t mag;
                 if (SR) {
                     const uint32_t w = (e < 8) ? r0.v[(e & 7) >> 1] : r1.v[(e & 7) >> 1];
@@ -168,45 +222,47 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a)
                 } else {
                     mag = grid_rne<FMT>(aq);
                 }
-                c = mag | ((__float_as_uint(x[e]) >> 31) ? F::kSign : 0u);
+                const uint32_t c = mag | ((__float_as_uint(x[e]) >> 31) ? F::kSign : 0u);
+                code[e] = zero ? 0u : c; // a zero scale holds +0 codes
             }
-            code[e] = c;
-        }
-        if (!FULL) { // padded slots hold code 0
+            if (!FULL) { // padded slots hold code 0
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (!((4 * r4 + i < a.R) && (4 * s4 + j < a.S))) code[4 * i + j] = 0u;
+                    for (int j = 0; j < 4; ++j)
+                        if (!((4 * r4 + i < a.R) && (4 * s4 + j < a.S))) code[4 * i + j] = 0u;
+            }
         }
-    }
 
-    a.scales[t] = (uint8_t)bcode;
-    if (FMT == kFP4) {
-        uint32_t w0 = 0u, w1 = 0u;
+        a.scales[t] = (uint8_t)bcode;
+        if (FMT == kFP4) {
+            uint32_t w0 = 0u, w1 = 0u;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            w0 |= code[e] << (4 * e);
-            w1 |= code[e + 8] << (4 * e);
-        }
-        *reinterpret_cast<uint2 *>(a.codes + 8 * t) = make_uint2(w0, w1);
-    } else {
-        uint32_t w[3] = {0u, 0u, 0u};
+            for (int e = 0; e < 8; ++e) {
+                w0 |= code[e] << (4 * e);
+                w1 |= code[e + 8] << (4 * e);
+            }
+            *reinterpret_cast<uint2 *>(a.codes + 8 * (int64_t)t) = make_uint2(w0, w1);
+        } else {
+            uint32_t w[3] = {0u, 0u, 0u};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int bit = 6 * e;
-            w[bit >> 5] |= code[e] << (bit & 31);
-            if ((bit & 31) > 26) w[(bit >> 5) + 1] |= code[e] >> (32 - (bit & 31));
+            for (int e = 0; e < 16; ++e) {
+                const int bit = 6 * e;
+                w[bit >> 5] |= code[e] << (bit & 31);
+                if ((bit & 31) > 26) w[(bit >> 5) + 1] |= code[e] >> (32 - (bit & 31));
+            }
+            uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes + 12 * (int64_t)t);
+            dst[0] = w[0]; dst[1] = w[1]; dst[2] = w[2];
         }
-        uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes + 12 * t);
-        dst[0] = w[0]; dst[1] = w[1]; dst[2] = w[2];
     }
 }
 
 template <int FMT, bool SR>
 static hipError_t launch_quant(const QuantArgs &a, bool full, hipStream_t st)
 {
-    const unsigned blocks = (unsigned)((a.nsq + 255) / 256);
+    // a few grid-stride steps per lane (4 workgroups of 256 lanes per CU) when the tensor is big
+    const int64_t want = (a.nsq + 255) / 256;
+    const unsigned blocks = (unsigned)(want < kQuantBlocks ? want : kQuantBlocks);
     if (full)
         hipLaunchKernelGGL((quantize_kernel<FMT, SR, true>), dim3(blocks), dim3(256), 0, st, a);
     else
@@ -218,6 +274,8 @@ hipError_t launch_quantize(const float *src, int64_t planes, int R, int S, int f
                            uint64_t seed, uint8_t *codes, uint8_t *scales, float *tscale,
                            uint32_t *amax_ws, hipStream_t st)
 {
+    if (planes * ((R + 3) / 4) * (int64_t)((S + 3) / 4) >= ((int64_t)1 << 31))
+        return hipErrorInvalidValue; // square indices are 31-bit
     const int64_t n = planes * (int64_t)R * S;
     // at least 8 float4 per lane where the tensor allows, at most kAmaxParts workgroups
     const int64_t want = (n / 4 + 8 * kAmaxThreads - 1) / (8 * kAmaxThreads);
@@ -230,7 +288,7 @@ hipError_t launch_quantize(const float *src, int64_t planes, int R, int S, int f
     a.src = src; a.codes = codes; a.scales = scales; a.tscale = tscale;
     a.amax_part = amax_ws; a.nparts = parts;
     a.planes = planes; a.R = R; a.S = S; a.R4 = (R + 3) / 4; a.S4 = (S + 3) / 4;
-    a.nsq = planes * a.R4 * a.S4;
+    a.nsq = planes * a.R4 * a.S4; // below 2^31 (the API rejects larger tensors)
     a.seed_lo = (uint32_t)seed; a.seed_hi = (uint32_t)(seed >> 32);
     const bool full = (R % 4 == 0) && (S % 4 == 0) &&
                       ((reinterpret_cast<uintptr_t>(src) & 15u) == 0);
