@@ -61,12 +61,14 @@ struct SpatialArgs {
 // KF = 3: every workgroup's class has the full 3 x 3 taps (compile-time tap loops, so the
 // consumer's LDS reads for later taps can be issued ahead of earlier taps' MFMAs); KF = 0: the
 // class's sub-kernel extent is read at run time.
-template <int FMT, bool A_KR, int SI, int PH, int PW, int KF>
-__global__ void __launch_bounds__(32 * PH * PW)
+// MW: 32-row blocks per consumer wave (2: a wave owns all 64 rows of 4 pixels; 1: two waves
+// share 4 pixels, 32 rows each, so that small pixel tiles still give four MFMA waves).
+template <int FMT, bool A_KR, int SI, int PH, int PW, int MW, int KF>
+__global__ void __launch_bounds__(32 * PH * PW * (2 / MW))
 conv_spatial_kernel(SpatialArgs a)
 {
-    constexpr int NCW = PH * PW / 4;  // consumer waves (4 pixels each)
-    constexpr int NP = 64 * NCW;      // producer threads
+    constexpr int NCW = PH * PW / 4 * (2 / MW); // consumer waves (4 pixels x 32*MW rows each)
+    constexpr int NP = 64 * NCW;                // producer threads
     constexpr int KHM = 3, KWM = 3;
     constexpr int HRM = (PH - 1) * SI + KHM, HCM = (PW - 1) * SI + KWM;
     constexpr int WCOLS = 3 * SI + KWM; // halo columns one wave touches (4 pixels)
@@ -207,10 +209,12 @@ conv_spatial_kernel(SpatialArgs a)
 
     // ================= consumer =================
     // (the two roles take wave-uniform branches and pass the same number of barriers)
-    const int wr = wave / (PW / 4), wp = wave % (PW / 4); // consumer pixel row, pixel group
-    f32x16_t acc[2][4];
+    constexpr int WM = 2 / MW;                        // waves per 4-pixel group
+    const int wm = wave % WM, wpix = wave / WM;       // row block, pixel group
+    const int wr = wpix / (PW / 4), wp = wpix % (PW / 4); // consumer pixel row, pixel group
+    f32x16_t acc[MW][4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < MW; ++u)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -236,21 +240,24 @@ conv_spatial_kernel(SpatialArgs a)
                 for (int tw = 0; tw < KWM; ++tw) {
                     if (tw < kw) {
                         const int t = th * kw + tw;
-                        const f16x8_t a0 = __builtin_bit_cast(
-                            f16x8_t, *reinterpret_cast<const u32x4_t *>(As + lds_row_off(t * 64 + l32, half)));
-                        const f16x8_t a1 = __builtin_bit_cast(
-                            f16x8_t, *reinterpret_cast<const u32x4_t *>(As + lds_row_off(t * 64 + 32 + l32, half)));
+                        f16x8_t av[MW];
+#pragma unroll
+                        for (int u = 0; u < MW; ++u)
+                            av[u] = __builtin_bit_cast(
+                                f16x8_t, *reinterpret_cast<const u32x4_t *>(
+                                             As + lds_row_off(t * 64 + 32 * (wm * MW + u) + l32, half)));
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             const f16x8_t b = __builtin_bit_cast(f16x8_t, bf[j * SI + tw]);
-                            acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b, acc[0][j], 0, 0, 0);
-                            acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b, acc[1][j], 0, 0, 0);
+#pragma unroll
+                            for (int u = 0; u < MW; ++u)
+                                acc[u][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[u], b, acc[u][j], 0, 0, 0);
                         }
                     }
                 }
             }
         }
-            __syncthreads();
+        __syncthreads();
     }
 
     // ---- epilogue: scale by T_in * T_w and store fp32. Buffer stores: an element outside the
@@ -269,8 +276,8 @@ conv_spatial_kernel(SpatialArgs a)
         const bool pix_ok = i < cl.OHs && jj < cl.OWs && n < a.N;
         const int oh = i * a.sO + cl.ah, ow = jj * a.sO + cl.aw;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int mrow = 4 * m4_0 + 32 * u + 4 * half; // row of register 0
+        for (int u = 0; u < MW; ++u) {
+            const int mrow = 4 * m4_0 + 32 * (wm * MW + u) + 4 * half;
             const uint32_t vbase =
                 pix_ok ? ((((uint32_t)oh * a.OWf + ow) * a.M + mrow) * a.N + n) * 4u : kBad;
 #pragma unroll
@@ -291,8 +298,8 @@ conv_spatial_kernel(SpatialArgs a)
 // Pixel tile per workgroup: 2 x 8 for stride-1 input walks, 1 x 8 for stride 2 (whose halo is
 // twice as wide), so that two LDS stage buffers fit.
 template <int SI> struct TileShape;
-template <> struct TileShape<1> { static constexpr int PH = 2, PW = 8; };
-template <> struct TileShape<2> { static constexpr int PH = 1, PW = 8; };
+template <> struct TileShape<1> { static constexpr int PH = 2, PW = 8, MW = 2; };
+template <> struct TileShape<2> { static constexpr int PH = 1, PW = 8, MW = 1; };
 
 static void set_tiles(SpatialClass &c, int PH, int PW)
 {
@@ -318,7 +325,8 @@ bool spatial_supported(const ConvGeom &g)
 template <int FMT, bool A_KR, int SI>
 static hipError_t launch_spatial(SpatialArgs &a, int nclass, hipStream_t st)
 {
-    constexpr int PH = TileShape<SI>::PH, PW = TileShape<SI>::PW;
+    constexpr int PH = TileShape<SI>::PH, PW = TileShape<SI>::PW, MW = TileShape<SI>::MW;
+    constexpr int THREADS = 32 * PH * PW * (2 / MW);
     int max_tiles = 0;
     for (int c = 0; c < nclass; ++c) {
         set_tiles(a.cls[c], PH, PW);
@@ -328,11 +336,11 @@ static hipError_t launch_spatial(SpatialArgs &a, int nclass, hipStream_t st)
     const bool full3 = nclass == 1 && a.cls[0].kh == 3 && a.cls[0].kw == 3 &&
                        a.cls[0].tiles * a.nblk == (int)grid.x;
     if (full3)
-        hipLaunchKernelGGL((conv_spatial_kernel<FMT, A_KR, SI, PH, PW, 3>), grid,
-                           dim3(32 * PH * PW), 0, st, a);
+        hipLaunchKernelGGL((conv_spatial_kernel<FMT, A_KR, SI, PH, PW, MW, 3>), grid,
+                           dim3(THREADS), 0, st, a);
     else
-        hipLaunchKernelGGL((conv_spatial_kernel<FMT, A_KR, SI, PH, PW, 0>), grid,
-                           dim3(32 * PH * PW), 0, st, a);
+        hipLaunchKernelGGL((conv_spatial_kernel<FMT, A_KR, SI, PH, PW, MW, 0>), grid,
+                           dim3(THREADS), 0, st, a);
     return hipGetLastError();
 }
 

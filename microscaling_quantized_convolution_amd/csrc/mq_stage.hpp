@@ -100,14 +100,25 @@ __device__ __forceinline__ void load_item_contig(RawItem<FMT> &r, rsrc_t codes, 
     r.m = mask | ((sq0 & 3u) << 8);
 }
 
+// The four squares' scales as fp16 (squares 0,1 in sc[0], 2,3 in sc[1]); a square whose bit of
+// the item mask is clear gets scale 0, so it decodes to zeros whatever codes were loaded.
 template <int FMT>
-__device__ __forceinline__ void decode_raw(const RawItem<FMT> &r, int k, uint32_t (&d)[8])
+__device__ __forceinline__ void item_scales(const RawItem<FMT> &r, f16x2_t (&sc)[2])
 {
-    // a zero scale decodes every element of the square to +-0 (element formats have no NaN)
     const uint32_t s4 = __builtin_amdgcn_alignbyte(r.sh, r.sc, (r.m >> 8) & 3u);
-    const uint32_t sc = ((r.m >> k) & 1u) ? (s4 >> (8 * k)) & 0xFFu : 0u;
-    if constexpr (FMT == kFP4) decode_fp4_square(r.w[k][0], r.w[k][1], sc, d);
-    else decode_fp6_square(r.w[k][0], r.w[k][1], r.w[k][2], sc, d);
+    // bit k of the mask -> 0xFF in byte k
+    const uint32_t keep = (((r.m & 0xFu) * 0x00204081u) & 0x01010101u) * 0xFFu;
+    sc[0] = e4m3_pair_to_f16<false>(s4 & keep);
+    sc[1] = e4m3_pair_to_f16<true>(s4 & keep);
+}
+
+template <int FMT>
+__device__ __forceinline__ void decode_raw(const RawItem<FMT> &r, const f16x2_t (&sc)[2], int k,
+                                           uint32_t (&d)[8])
+{
+    const _Float16 B = sc[k >> 1][k & 1];
+    if constexpr (FMT == kFP4) decode_fp4_square(r.w[k][0], r.w[k][1], B, d);
+    else decode_fp6_square(r.w[k][0], r.w[k][1], r.w[k][2], B, d);
 }
 
 // LDS operand rows: 16 fp16 (32 bytes, two 16-byte units). The unit index row*2 + chunk is
@@ -130,10 +141,12 @@ template <int FMT, bool KR>
 __device__ __forceinline__ void store_item(const RawItem<FMT> &r, uint8_t *lds, int row0)
 {
     uint32_t rows[4][8];
+    f16x2_t sc[2];
+    item_scales<FMT>(r, sc);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         uint32_t d[8];
-        decode_raw<FMT>(r, k, d);
+        decode_raw<FMT>(r, sc, k, d);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (KR) {
@@ -159,10 +172,12 @@ __device__ __forceinline__ void store_item(const RawItem<FMT> &r, uint8_t *lds, 
 template <int FMT, bool KR>
 __device__ __forceinline__ void store_item_rows(const RawItem<FMT> &r, uint8_t *lds, int row0, int kb)
 {
+    f16x2_t sc[2];
+    item_scales<FMT>(r, sc);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         uint32_t d[8];
-        decode_raw<FMT>(r, j, d);
+        decode_raw<FMT>(r, sc, j, d);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             uint32_t p0, p1;
