@@ -10,8 +10,9 @@
 //                                        * Xq[oh*s - ph + kh][ow*s - pw + kw][ci][n]
 //
 // A workgroup owns one kernel row kh, 64 output channels, 64 input channels and every kw, and a
-// contiguous range of reduction stages; a stage is PW output pixels of one output row and 16 batch
-// elements. Per stage it decodes the G_Y strip (PW pixels) and the X row segment it meets
+// contiguous range of reduction stages; a stage is PW output pixels of one output row and 32 batch
+// elements (eight batch squares, 256 contiguous code bytes per pixel and channel square for NVFP4).
+// Per stage it decodes the G_Y strip (PW pixels) and the X row segment it meets
 // ((PW-1)*s + Kw pixels) once into LDS as fp16; each wave runs 32x32x16 fp16 MFMAs for a
 // 32 x 32 x Kw block. The fp32 partial block goes to the workspace, and a second kernel sums the
 // splits in a fixed order (deterministic) and applies the tensor scales.
@@ -30,26 +31,32 @@ struct WgradArgs {
     float *part;                       // [split][Kh*Kw][Cout][Cin] fp32 partial sums
     int H, W, Ho, Wo, Cin, Cout, Cin4, Cout4, N4;
     int Kh, Kw, sh, sw, ph, pw;
-    int owb, nch;          // pixel blocks per output row, 16-element batch chunks
+    int owb, nch;          // pixel blocks per output row, 32-element batch chunks
     int stages, per_split; // total stages, stages per split
     int cot, cit;          // Cout / Cin tiles of 64
+    int splits, tiles;     // reduction splits, (kh, Cout tile, Cin tile) tiles
     int64_t split_stride;  // floats per split
 };
 
 // Waves 0..3 consume (MFMAs on one LDS buffer); waves 4..7 produce (load the squares of the
 // stage after next, decode the next stage into the other buffer); one barrier per stage.
-// Output pixels per stage: 16 for stride 1, 8 for stride 2 (twice as wide an X segment), so that
-// two stage buffers fit in LDS.
-template <int SI> struct StagePixels { static constexpr int kPW = SI == 1 ? 16 : 8; };
+// KS: 16-element reduction steps per stage and pixel: 2 (32 batch elements, eight batch
+// squares) when the batch has at least eight squares, else 1 (four squares: the whole batch of a
+// pixel and channel square is then 32 contiguous bytes, so neighbouring lanes stay contiguous).
+// Output pixels per stage: 16 / KS for stride 1, 8 / KS for stride 2 (twice as wide an X
+// segment), so that two stage buffers fit in LDS.
+template <int SI, int KS> struct StagePixels { static constexpr int kPW = (SI == 1 ? 16 : 8) / KS; };
+inline int stage_ks(int N4) { return N4 >= 8 ? 2 : 1; }
 
-template <int FMT, int SI>
+// KF: the kernel width Kw when fixed at compile time (1 or 3), 0 = read at run time.
+template <int FMT, int SI, int KF, int kKS>
 __global__ void __launch_bounds__(512) conv_wgrad_kernel(WgradArgs a)
 {
-    constexpr int kPWg = StagePixels<SI>::kPW;
-    constexpr int KWM = 3;
+    constexpr int kPWg = StagePixels<SI, kKS>::kPW;
+    constexpr int KWM = KF ? KF : 3;
     constexpr int HCM = (kPWg - 1) * SI + KWM;
-    constexpr int GBYTES = kPWg * 64 * kRowBytes, XBYTES = HCM * 64 * kRowBytes;
-    constexpr int ITEMS = (kPWg * 16 + HCM * 16 + 255) / 256;
+    constexpr int GBYTES = kPWg * kKS * 64 * kRowBytes, XBYTES = HCM * kKS * 64 * kRowBytes;
+    constexpr int ITEMS = (kPWg * 16 * kKS + HCM * 16 * kKS + 255) / 256;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][GBYTES + XBYTES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
@@ -59,7 +66,7 @@ __global__ void __launch_bounds__(512) conv_wgrad_kernel(WgradArgs a)
     const int cot_i = tile % a.cot;
     const int kh = tile / a.cot;
     const int co4_0 = cot_i * 16, ci4_0 = cit_i * 16;
-    const int kw = a.Kw;
+    const int kw = KF ? KF : a.Kw;
     const int HC = (kPWg - 1) * SI + kw;
     const int st0 = split * a.per_split;
     const int st1 = min(a.stages, st0 + a.per_split);
@@ -68,15 +75,17 @@ __global__ void __launch_bounds__(512) conv_wgrad_kernel(WgradArgs a)
     if (wave >= 4) {
         // ================= producer =================
         const int ptid = tid - 256;
-        const int nG = kPWg * 16, nGX = nG + HC * 16;
+        const int nG = kPWg * 16 * kKS, nGX = nG + HC * 16 * kKS;
         constexpr int CB = (FMT == kFP4) ? 8 : 12;
         const uint32_t g_sq = (uint32_t)a.Ho * a.Wo * a.Cout4 * a.N4;
         const uint32_t x_sq = (uint32_t)a.H * a.W * a.Cin4 * a.N4;
         const rsrc_t g_c = make_rsrc(a.g_codes, g_sq * CB), g_s = make_scale_rsrc(a.g_scales, g_sq);
         const rsrc_t x_c = make_rsrc(a.x_codes, x_sq * CB), x_s = make_scale_rsrc(a.x_scales, x_sq);
-        // Producer items: it < nG -> G_Y strip (pixel it/16, co4 it%16); else X segment (column,
-        // ci4). Each item spans the four batch squares 4*nc .. 4*nc+3 (consecutive in memory). nG is
-        // a whole number of waves, so no wave mixes the two kinds.
+        // Producer items: it < nG -> G_Y strip (pixel, co4, batch half); else X segment (column,
+        // ci4, batch half). With KS = 2 bit 0 picks the half of the stage's eight batch squares,
+        // four squares (consecutive in memory) per item, so neighbouring lanes read neighbouring
+        // 32-byte pieces of one pixel's [channel square][batch square] block. nG is a whole
+        // number of waves, so no wave mixes the two kinds.
         // Two register stages: stage c + 3 is loaded into the slot stage c + 1 was just decoded
         // from (two stage times ahead of its use). The loop is unrolled by two so that slots are
         // never copied, which keeps the compiler's waits down to the stage being decoded.
@@ -89,20 +98,25 @@ __global__ void __launch_bounds__(512) conv_wgrad_kernel(WgradArgs a)
             const int ow0 = ob * kPWg;
             const int ih = oh * SI - a.ph + kh;
             const int iw0 = ow0 * SI - a.pw;
-            const int nvalid = a.N4 - 4 * nc;
-            // a stage past the end of this split loads nothing (mask 0), so that every stage
-            // issues the same loads without branches and each decode waits for its own stage only
-            const uint32_t nmask = st >= st1 ? 0u : nvalid >= 4 ? 0xFu : ((1u << nvalid) - 1u);
+            constexpr int SH = kKS == 2 ? 1 : 0; // item index bits below the channel square
     #pragma unroll
             for (int q = 0; q < ITEMS; ++q) {
                 const int it = ptid + q * 256;
                 const bool isG = wave_uniform(it & ~63) < nG;
-                const int ow = ow0 + (it >> 4), co4 = co4_0 + (it & 15);
-                const uint32_t sqg = (((uint32_t)oh * a.Wo + ow) * a.Cout4 + co4) * a.N4 + 4 * nc;
+                const int nh = it & (kKS - 1); // nG is even, so X items keep the same bit
+                // a stage past the end of this split loads nothing (mask 0), so that every stage
+                // issues the same loads without branches and each decode waits for its own stage
+                const int nvalid = a.N4 - 4 * (kKS * nc + nh);
+                const uint32_t nmask =
+                    st >= st1 || nvalid <= 0 ? 0u : nvalid >= 4 ? 0xFu : ((1u << nvalid) - 1u);
+                const int ow = ow0 + (it >> (4 + SH)), co4 = co4_0 + ((it >> SH) & 15);
+                const uint32_t sqg =
+                    (((uint32_t)oh * a.Wo + ow) * a.Cout4 + co4) * a.N4 + 4 * (kKS * nc + nh);
                 const uint32_t mg = (ow < a.Wo && co4 < a.Cout4) ? nmask : 0u;
                 const int j = it - nG;
-                const int iw = iw0 + (j >> 4), ci4 = ci4_0 + (j & 15);
-                const uint32_t sqx = (((uint32_t)ih * a.W + iw) * a.Cin4 + ci4) * a.N4 + 4 * nc;
+                const int iw = iw0 + (j >> (4 + SH)), ci4 = ci4_0 + ((j >> SH) & 15);
+                const uint32_t sqx =
+                    (((uint32_t)ih * a.W + iw) * a.Cin4 + ci4) * a.N4 + 4 * (kKS * nc + nh);
                 const bool in = it < nGX && ih >= 0 && ih < a.H && iw >= 0 && iw < a.W &&
                                 ci4 < a.Cin4;
                 load_item_contig<FMT>(dst[q], isG ? g_c : x_c, isG ? g_s : x_s, isG ? sqg : sqx,
@@ -114,10 +128,17 @@ __global__ void __launch_bounds__(512) conv_wgrad_kernel(WgradArgs a)
             for (int q = 0; q < ITEMS; ++q) {
                 const int it = ptid + q * 256;
                 const int wit = wave_uniform(it & ~63);
-                if (wit < nG) store_item<FMT, false>(src[q], lds[buf], (it >> 4) * 64 + 4 * (it & 15));
+                // LDS rows: [pixel or column][reduction step][64 channels]
+                constexpr int SH = kKS == 2 ? 1 : 0;
+                if (wit < nG)
+                    store_item<FMT, false>(src[q], lds[buf],
+                                           ((it >> (4 + SH)) * kKS + (it & (kKS - 1))) * 64 +
+                                               4 * ((it >> SH) & 15));
                 else if (wit < nGX && it < nGX) {
                     const int j = it - nG;
-                    store_item<FMT, false>(src[q], lds[buf] + GBYTES, (j >> 4) * 64 + 4 * (j & 15));
+                    store_item<FMT, false>(src[q], lds[buf] + GBYTES,
+                                           ((j >> (4 + SH)) * kKS + (j & (kKS - 1))) * 64 +
+                                               4 * ((j >> SH) & 15));
                 }
             }
         };
@@ -152,22 +173,27 @@ __global__ void __launch_bounds__(512) conv_wgrad_kernel(WgradArgs a)
     __syncthreads();
     for (int c = 0; c < nst; ++c) {
         const uint8_t *Gs = lds[c & 1], *Xs = lds[c & 1] + GBYTES;
-        // every X column of the buffer is read (columns past HC are never used)
-        u32x4_t xf[HCM];
 #pragma unroll
-        for (int cc = 0; cc < HCM; ++cc)
-            xf[cc] = *reinterpret_cast<const u32x4_t *>(Xs + lds_row_off(cc * 64 + wc * 32 + l32, half));
+        for (int ks = 0; ks < kKS; ++ks) {
+            // every X column of the buffer is read (columns past HC are never used)
+            u32x4_t xf[HCM];
 #pragma unroll
-        for (int px = 0; px < kPWg; ++px) {
-            const f16x8_t gf = __builtin_bit_cast(
-                f16x8_t, *reinterpret_cast<const u32x4_t *>(Gs + lds_row_off(px * 64 + wm * 32 + l32, half)));
+            for (int cc = 0; cc < HCM; ++cc)
+                xf[cc] = *reinterpret_cast<const u32x4_t *>(
+                    Xs + lds_row_off((cc * kKS + ks) * 64 + wc * 32 + l32, half));
 #pragma unroll
-            for (int t = 0; t < KWM; ++t)
-                if (t < kw)
-                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        gf, __builtin_bit_cast(f16x8_t, xf[px * SI + t]), acc[t], 0, 0, 0);
+            for (int px = 0; px < kPWg; ++px) {
+                const f16x8_t gf = __builtin_bit_cast(
+                    f16x8_t, *reinterpret_cast<const u32x4_t *>(
+                                 Gs + lds_row_off((px * kKS + ks) * 64 + wm * 32 + l32, half)));
+#pragma unroll
+                for (int t = 0; t < KWM; ++t)
+                    if (t < kw)
+                        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            gf, __builtin_bit_cast(f16x8_t, xf[px * SI + t]), acc[t], 0, 0, 0);
+            }
         }
-            __syncthreads();
+        __syncthreads();
     }
 
     // ---- partial block: part[split][kh*Kw + kw][co][ci] ----
@@ -238,9 +264,10 @@ struct Plan {
 Plan plan(const ConvGeom &g)
 {
     Plan p;
-    const int kPWg = g.sh == 1 ? StagePixels<1>::kPW : StagePixels<2>::kPW;
+    const int ks = stage_ks(g.N4);
+    const int kPWg = (g.sh == 1 ? 16 : 8) / ks;
     p.owb = (g.Wo + kPWg - 1) / kPWg;
-    p.nch = (g.N4 + 3) / 4;
+    p.nch = (g.N4 + 4 * ks - 1) / (4 * ks);
     p.stages = g.Ho * p.owb * p.nch;
     p.cot = (g.Cout4 + 15) / 16;
     p.cit = (g.Cin4 + 15) / 16;
@@ -275,6 +302,30 @@ bool wgrad_fast_supported(const ConvGeom &g)
 
 size_t wgrad_fast_workspace_bytes(const ConvGeom &g) { return plan(g).bytes; }
 
+template <int FMT, int SI, int KS>
+static void launch_wgrad_ks(const ConvGeom &g, dim3 grid, const WgradArgs &a, hipStream_t st)
+{
+    if (g.Kw == 3)
+        hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 3, KS>), grid, dim3(512), 0, st, a);
+    else if (g.Kw == 1)
+        hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 1, KS>), grid, dim3(512), 0, st, a);
+    else hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 0, KS>), grid, dim3(512), 0, st, a);
+}
+
+template <int FMT, int SI>
+static void launch_wgrad_si(const ConvGeom &g, dim3 grid, const WgradArgs &a, hipStream_t st)
+{
+    if (stage_ks(g.N4) == 2) launch_wgrad_ks<FMT, SI, 2>(g, grid, a, st);
+    else launch_wgrad_ks<FMT, SI, 1>(g, grid, a, st);
+}
+
+template <int FMT>
+static void launch_wgrad_fmt(const ConvGeom &g, dim3 grid, const WgradArgs &a, hipStream_t st)
+{
+    if (g.sh == 1) launch_wgrad_si<FMT, 1>(g, grid, a, st);
+    else launch_wgrad_si<FMT, 2>(g, grid, a, st);
+}
+
 hipError_t launch_conv_wgrad_fast(const ConvGeom &g, int fmt, QOperand gy, QOperand x, float *gw,
                                   void *ws, size_t ws_bytes, hipStream_t st)
 {
@@ -288,14 +339,10 @@ hipError_t launch_conv_wgrad_fast(const ConvGeom &g, int fmt, QOperand gy, QOper
     a.Kh = g.Kh; a.Kw = g.Kw; a.sh = g.sh; a.sw = g.sw; a.ph = g.ph; a.pw = g.pw;
     a.owb = p.owb; a.nch = p.nch; a.stages = p.stages; a.per_split = p.per_split;
     a.cot = p.cot; a.cit = p.cit; a.split_stride = p.split_stride;
+    a.splits = p.splits; a.tiles = p.tiles;
     dim3 grid((unsigned)p.splits, (unsigned)p.tiles, 1);
-    if (fmt == kFP4) {
-        if (g.sh == 1) hipLaunchKernelGGL((conv_wgrad_kernel<kFP4, 1>), grid, dim3(512), 0, st, a);
-        else hipLaunchKernelGGL((conv_wgrad_kernel<kFP4, 2>), grid, dim3(512), 0, st, a);
-    } else {
-        if (g.sh == 1) hipLaunchKernelGGL((conv_wgrad_kernel<kFP6, 1>), grid, dim3(512), 0, st, a);
-        else hipLaunchKernelGGL((conv_wgrad_kernel<kFP6, 2>), grid, dim3(512), 0, st, a);
-    }
+    if (fmt == kFP4) launch_wgrad_fmt<kFP4>(g, grid, a, st);
+    else launch_wgrad_fmt<kFP6>(g, grid, a, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t total = p.split_stride;
