@@ -95,26 +95,48 @@ size_t mq_codes_bytes(int32_t o0, int32_t o1, int32_t r, int32_t s, int32_t fmt)
 size_t mq_scales_bytes(int32_t o0, int32_t o1, int32_t r, int32_t s);
 
 /*
+ * Tensor-amax workspace (mq_quantize, and optionally the relayouts): device scratch of at least
+ * MQ_QUANTIZE_WS_BYTES bytes, 4-byte aligned. Word 0 holds the number P of partial maxima,
+ * words 1..P the partials (max |x| per part of the tensor, as fp32 bit patterns). Calls on one
+ * stream may share a workspace; calls that can run concurrently must not.
+ */
+#define MQ_QUANTIZE_WS_BYTES 8192
+
+/*
  * mq_relayout_cbf: NCHW fp32 <-> channel-batch-first fp32.
  * Channel-batch-first X_{Cin,N} (onedev.kr digest, section "How it works"): for each pixel
  * (h, w) all channels and all batch elements are contiguous; here [H][W][C][N], N fastest.
  *   inverse = 0: dst[h][w][c][n] = src[n][c][h][w]
  *   inverse = 1: dst[n][c][h][w] = src[h][w][c][n]
  * src_dev, dst_dev: N*C*H*W floats each, must not overlap.
- * Errors: MQ_ERR_ARG for null pointers or non-positive sizes.
+ * amax_ws_dev: null, or a tensor-amax workspace that receives the partial maxima of the tensor
+ *          (the relayout reads every element anyway), so that mq_quantize of dst_dev can pass
+ *          MQ_QUANTIZE_AMAX_READY and skip its own pass over the tensor. amax_ws_bytes is
+ *          ignored when amax_ws_dev is null.
+ * Errors: MQ_ERR_ARG for null pointers, non-positive sizes or a misaligned workspace;
+ *         MQ_ERR_WORKSPACE for a workspace below MQ_QUANTIZE_WS_BYTES; MQ_ERR_UNSUPPORTED for
+ *         C > 65535.
  */
 mq_status mq_relayout_cbf(const float *src_dev, float *dst_dev, int32_t N, int32_t C, int32_t H,
-                          int32_t W, int32_t inverse, hipStream_t stream);
+                          int32_t W, int32_t inverse, uint32_t *amax_ws_dev, size_t amax_ws_bytes,
+                          hipStream_t stream);
 
 /*
  * mq_relayout_weight: OIHW fp32 <-> tap-major [Kh][Kw][Cout][Cin] fp32, the layout of the 2-D
  * weight matrix W_{fCout,Cin} (Cout x Kh*Kw*Cin; onedev.kr digest, section "How it differs")
  * with one Cout x Cin block per tap.
  *   inverse = 0: dst[kh][kw][co][ci] = src[co][ci][kh][kw];  inverse = 1: the reverse.
- * Errors: MQ_ERR_ARG for null pointers or non-positive sizes.
+ * amax_ws_dev, amax_ws_bytes: as for mq_relayout_cbf.
+ * Errors: MQ_ERR_ARG for null pointers, non-positive sizes or a misaligned workspace;
+ *         MQ_ERR_WORKSPACE for a workspace below MQ_QUANTIZE_WS_BYTES.
  */
 mq_status mq_relayout_weight(const float *src_dev, float *dst_dev, int32_t Cout, int32_t Cin,
-                             int32_t Kh, int32_t Kw, int32_t inverse, hipStream_t stream);
+                             int32_t Kh, int32_t Kw, int32_t inverse, uint32_t *amax_ws_dev,
+                             size_t amax_ws_bytes, hipStream_t stream);
+
+/* mq_quantize flag: amax_ws_dev already holds the partial maxima of this tensor's values (from a
+ * relayout that wrote src_dev, earlier on the same stream); the amax pass is skipped. */
+#define MQ_QUANTIZE_AMAX_READY 1u
 
 /*
  * mq_quantize: quantize one fp32 tensor, exactly once, with the NVFP4 / NVFP6 recipe of the
@@ -133,16 +155,16 @@ mq_status mq_relayout_weight(const float *src_dev, float *dst_dev, int32_t Cout,
  *          channel-batch-first layout).
  * dst:     host struct describing the destination; dst->codes, dst->scales, dst->tscale are
  *          device buffers of mq_codes_bytes / mq_scales_bytes / 4 bytes.
- * amax_ws_dev / amax_ws_bytes: device scratch of at least MQ_QUANTIZE_WS_BYTES bytes, 4-byte
- *          aligned, for the amax pass's partial maxima (overwritten; calls on one stream may
- *          share it, calls that can run concurrently must not).
- * Errors: MQ_ERR_ARG (null pointer, bad enum, non-positive dims, misaligned pointer),
+ * amax_ws_dev / amax_ws_bytes: a tensor-amax workspace (overwritten unless flags has
+ *          MQ_QUANTIZE_AMAX_READY, then read).
+ * flags:   0 or MQ_QUANTIZE_AMAX_READY.
+ * Errors: MQ_ERR_ARG (null pointer, bad enum or flag, non-positive dims, misaligned pointer),
  *         MQ_ERR_WORKSPACE (amax_ws_dev null or smaller than MQ_QUANTIZE_WS_BYTES),
  *         MQ_ERR_UNSUPPORTED (2^31 squares or more).
  */
-#define MQ_QUANTIZE_WS_BYTES 1024
 mq_status mq_quantize(const float *src_dev, const mq_qtensor *dst, int32_t rnd, uint64_t seed,
-                      uint32_t *amax_ws_dev, size_t amax_ws_bytes, hipStream_t stream);
+                      uint32_t *amax_ws_dev, size_t amax_ws_bytes, uint32_t flags,
+                      hipStream_t stream);
 
 /*
  * mq_conv_fwd: forward GEMM Y = W . X' (onedev.kr digest, section "How it differs") with the

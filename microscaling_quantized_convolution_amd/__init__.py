@@ -20,7 +20,8 @@ MQ_OK, MQ_ERR_ARG, MQ_ERR_SHAPE, MQ_ERR_UNSUPPORTED, MQ_ERR_WORKSPACE, MQ_ERR_LA
 MQ_NVFP4, MQ_NVFP6 = 4, 6
 MQ_ROLE_ACT, MQ_ROLE_WEIGHT, MQ_ROLE_GRAD = 0, 1, 2
 MQ_RNE, MQ_SR = 0, 1
-MQ_QUANTIZE_WS_BYTES = 1024  # amax workspace of mq_quantize
+MQ_QUANTIZE_WS_BYTES = 8192  # tensor-amax workspace (mq_quantize, relayouts)
+MQ_QUANTIZE_AMAX_READY = 1   # mq_quantize flag: the workspace already holds this tensor's amax
 
 EXPORTS = (
     "mq_status_str", "mq_codes_bytes", "mq_scales_bytes", "mq_relayout_cbf",
@@ -59,9 +60,9 @@ def _load() -> ctypes.CDLL:
     L.mq_codes_bytes.argtypes = [i32] * 5
     L.mq_scales_bytes.restype = sz
     L.mq_scales_bytes.argtypes = [i32] * 4
-    L.mq_relayout_cbf.argtypes = [P, P, i32, i32, i32, i32, i32, P]
-    L.mq_relayout_weight.argtypes = [P, P, i32, i32, i32, i32, i32, P]
-    L.mq_quantize.argtypes = [P, ctypes.POINTER(mq_qtensor), i32, u64, P, sz, P]
+    L.mq_relayout_cbf.argtypes = [P, P, i32, i32, i32, i32, i32, P, sz, P]
+    L.mq_relayout_weight.argtypes = [P, P, i32, i32, i32, i32, i32, P, sz, P]
+    L.mq_quantize.argtypes = [P, ctypes.POINTER(mq_qtensor), i32, u64, P, sz, ctypes.c_uint32, P]
     L.mq_conv_fwd.argtypes = [ctypes.POINTER(mq_conv), ctypes.POINTER(mq_qtensor),
                               ctypes.POINTER(mq_qtensor), P, P]
     L.mq_wgrad_workspace_bytes.restype = sz
@@ -135,16 +136,22 @@ def mq_scales_bytes(o0, o1, r, s) -> int:
     return int(_lib.mq_scales_bytes(o0, o1, r, s))
 
 
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def mq_relayout_cbf(src: torch.Tensor, dst: torch.Tensor, N: int, C: int, H: int, W: int,
-                    inverse: int = 0, stream=None):
-    _check(_lib.mq_relayout_cbf(_ptr(src), _ptr(dst), N, C, H, W, inverse, _stream(stream)),
-           "mq_relayout_cbf")
+                    inverse: int = 0, amax_ws: Optional[torch.Tensor] = None, stream=None):
+    _check(_lib.mq_relayout_cbf(_ptr(src), _ptr(dst), N, C, H, W, inverse, _ptr(amax_ws),
+                                _nbytes(amax_ws), _stream(stream)), "mq_relayout_cbf")
 
 
 def mq_relayout_weight(src: torch.Tensor, dst: torch.Tensor, Cout: int, Cin: int, Kh: int,
-                       Kw: int, inverse: int = 0, stream=None):
+                       Kw: int, inverse: int = 0, amax_ws: Optional[torch.Tensor] = None,
+                       stream=None):
     _check(_lib.mq_relayout_weight(_ptr(src), _ptr(dst), Cout, Cin, Kh, Kw, inverse,
-                                   _stream(stream)), "mq_relayout_weight")
+                                   _ptr(amax_ws), _nbytes(amax_ws), _stream(stream)),
+           "mq_relayout_weight")
 
 
 def quantize_workspace(device: Union[str, torch.device] = "cuda") -> torch.Tensor:
@@ -153,11 +160,11 @@ def quantize_workspace(device: Union[str, torch.device] = "cuda") -> torch.Tenso
 
 
 def mq_quantize(src: torch.Tensor, dst: QTensor, rnd: int, seed: int, amax_ws: torch.Tensor,
-                stream=None):
+                flags: int = 0, stream=None):
     q = dst.struct()
-    nbytes = amax_ws.numel() * amax_ws.element_size()
     _check(_lib.mq_quantize(_ptr(src), ctypes.byref(q), rnd, seed & (2 ** 64 - 1),
-                            _ptr(amax_ws), nbytes, _stream(stream)), "mq_quantize")
+                            _ptr(amax_ws), _nbytes(amax_ws), flags, _stream(stream)),
+           "mq_quantize")
 
 
 def mq_conv_fwd(p: ConvLike, x: QTensor, w: QTensor, y: torch.Tensor, stream=None):

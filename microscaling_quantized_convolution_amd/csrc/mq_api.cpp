@@ -62,6 +62,14 @@ mq::QOperand operand(const mq_qtensor *q) { return {q->codes, q->scales, q->tsca
 
 mq_status launch_status(hipError_t e) { return e == hipSuccess ? MQ_OK : MQ_ERR_LAUNCH; }
 
+// Optional amax workspace of a relayout: null, or at least MQ_QUANTIZE_WS_BYTES, 4-byte aligned.
+mq_status amax_ws_check(const uint32_t *ws, size_t bytes)
+{
+    if (!ws) return MQ_OK;
+    if (bytes < MQ_QUANTIZE_WS_BYTES) return MQ_ERR_WORKSPACE;
+    return (reinterpret_cast<uintptr_t>(ws) & 3u) ? MQ_ERR_ARG : MQ_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -92,33 +100,42 @@ size_t mq_scales_bytes(int32_t o0, int32_t o1, int32_t r, int32_t s)
 }
 
 mq_status mq_relayout_cbf(const float *src, float *dst, int32_t N, int32_t C, int32_t H,
-                          int32_t W, int32_t inverse, hipStream_t stream)
+                          int32_t W, int32_t inverse, uint32_t *amax_ws, size_t amax_ws_bytes,
+                          hipStream_t stream)
 {
     if (!src || !dst || N < 1 || C < 1 || H < 1 || W < 1 || (inverse != 0 && inverse != 1))
         return MQ_ERR_ARG;
     if (C > 65535) return MQ_ERR_UNSUPPORTED;
-    return launch_status(mq::launch_relayout_cbf(src, dst, N, C, H, W, inverse, stream));
+    const mq_status ws = amax_ws_check(amax_ws, amax_ws_bytes);
+    if (ws != MQ_OK) return ws;
+    return launch_status(mq::launch_relayout_cbf(src, dst, N, C, H, W, inverse, amax_ws, stream));
 }
 
 mq_status mq_relayout_weight(const float *src, float *dst, int32_t Cout, int32_t Cin,
-                             int32_t Kh, int32_t Kw, int32_t inverse, hipStream_t stream)
+                             int32_t Kh, int32_t Kw, int32_t inverse, uint32_t *amax_ws,
+                             size_t amax_ws_bytes, hipStream_t stream)
 {
     if (!src || !dst || Cout < 1 || Cin < 1 || Kh < 1 || Kw < 1 ||
         (inverse != 0 && inverse != 1))
         return MQ_ERR_ARG;
-    return launch_status(mq::launch_relayout_weight(src, dst, Cout, Cin, Kh, Kw, inverse, stream));
+    const mq_status ws = amax_ws_check(amax_ws, amax_ws_bytes);
+    if (ws != MQ_OK) return ws;
+    return launch_status(mq::launch_relayout_weight(src, dst, Cout, Cin, Kh, Kw, inverse, amax_ws,
+                                                    stream));
 }
 
 mq_status mq_quantize(const float *src, const mq_qtensor *dst, int32_t rnd, uint64_t seed,
-                      uint32_t *amax_ws, size_t amax_ws_bytes, hipStream_t stream)
+                      uint32_t *amax_ws, size_t amax_ws_bytes, uint32_t flags, hipStream_t stream)
 {
     if (!src || !qtensor_ok(dst) || (rnd != MQ_RNE && rnd != MQ_SR)) return MQ_ERR_ARG;
+    if (flags & ~(uint32_t)MQ_QUANTIZE_AMAX_READY) return MQ_ERR_ARG;
     if (!amax_ws || amax_ws_bytes < MQ_QUANTIZE_WS_BYTES) return MQ_ERR_WORKSPACE;
     if (squares(dst->o0, dst->o1, dst->r, dst->s) >= ((int64_t)1 << 31)) return MQ_ERR_UNSUPPORTED;
     if ((reinterpret_cast<uintptr_t>(amax_ws) & 3u) != 0) return MQ_ERR_ARG;
     return launch_status(mq::launch_quantize(src, (int64_t)dst->o0 * dst->o1, dst->r, dst->s,
                                              dst->fmt, rnd, seed, dst->codes, dst->scales,
-                                             dst->tscale, amax_ws, stream));
+                                             dst->tscale, amax_ws,
+                                             (flags & MQ_QUANTIZE_AMAX_READY) != 0, stream));
 }
 
 mq_status mq_conv_fwd(const mq_conv *p, const mq_qtensor *x, const mq_qtensor *w, float *y,

@@ -225,9 +225,18 @@ __global__ void __launch_bounds__(256) wgrad_sum_kernel(const float *__restrict_
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     const bool vec = (total % 4 == 0) && (stride % 4 == 0);
     if (vec && i4 * 4 < total) {
-        for (int z = g; z < S; z += 16) {
-            const float4 p = *reinterpret_cast<const float4 *>(part + z * stride + i4 * 4);
-            s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+        // eight loads in flight per batch, added in split order afterwards
+        for (int z0 = g; z0 < S; z0 += 16 * 8) {
+            float4 p[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int z = z0 + 16 * k;
+                p[k] = z < S ? *reinterpret_cast<const float4 *>(part + z * stride + i4 * 4)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (z0 + 16 * k < S) { s.x += p[k].x; s.y += p[k].y; s.z += p[k].z; s.w += p[k].w; }
         }
     } else if (!vec) {
         float e[4] = {0.f, 0.f, 0.f, 0.f};

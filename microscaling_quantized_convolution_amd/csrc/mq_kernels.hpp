@@ -7,15 +7,17 @@
 
 namespace mq {
 
+// Tensor-amax workspace: word 0 = number of partial maxima P (1..kAmaxParts), words 1..P = the
+// partials (max |x| as fp32 bit patterns). Written by the amax pass or by a relayout that is
+// given the workspace (amax_ws non-null), read by the quantize kernel.
+constexpr int kAmaxParts = 1024;
 hipError_t launch_relayout_cbf(const float *src, float *dst, int N, int C, int H, int W,
-                               int inverse, hipStream_t st);
+                               int inverse, uint32_t *amax_ws, hipStream_t st);
 hipError_t launch_relayout_weight(const float *src, float *dst, int Cout, int Cin, int Kh,
-                                  int Kw, int inverse, hipStream_t st);
-// amax_ws: kAmaxParts words of partial maxima
-constexpr int kAmaxParts = 256;
+                                  int Kw, int inverse, uint32_t *amax_ws, hipStream_t st);
 hipError_t launch_quantize(const float *src, int64_t planes, int R, int S, int fmt, int rnd,
                            uint64_t seed, uint8_t *codes, uint8_t *scales, float *tscale,
-                           uint32_t *amax_ws, hipStream_t st);
+                           uint32_t *amax_ws, bool amax_ready, hipStream_t st);
 
 // Convolution geometry shared by the GEMM kernels.
 struct ConvGeom {

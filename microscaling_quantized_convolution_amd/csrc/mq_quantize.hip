@@ -8,8 +8,9 @@
 //
 // Two kernels per tensor: amax (grid-stride max of |x| as uint bit patterns, one partial maximum
 // per workgroup) and quantize (each workgroup first reduces the partial maxima to the tensor's
-// amax, then one lane per 4x4 square). No atomics and no memset: every call writes all the
-// partials it reads.
+// amax, then one lane per 4x4 square). No atomics and no memset: the workspace holds the number
+// of partials in word 0 and the partials after it, all written by the pass that produces them
+// (this amax kernel, or a relayout that already moved the tensor, which then saves a full read).
 #include "mq_device.hpp"
 #include "mq_kernels.hpp"
 
@@ -49,10 +50,11 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *red)
 constexpr int kAmaxThreads = 512;
 constexpr int64_t kQuantBlocks = 1024;
 
-// Partial maxima: workgroup b writes max |x| over its grid-stride share to part[b]. Eight
-// independent 16-byte loads per lane are in flight at a time, enough to cover HBM latency.
+// Partial maxima: workgroup b writes max |x| over its grid-stride share to ws[1 + b]; ws[0] is the
+// number of workgroups. Eight independent 16-byte loads per lane are in flight at a time, enough
+// to cover HBM latency.
 __global__ void __launch_bounds__(kAmaxThreads) amax_kernel(const float *__restrict__ x, int64_t n,
-                                                            uint32_t *__restrict__ part)
+                                                            uint32_t *__restrict__ ws)
 {
     uint32_t m = 0u;
     const int64_t nt = (int64_t)gridDim.x * kAmaxThreads;
@@ -75,7 +77,10 @@ __global__ void __launch_bounds__(kAmaxThreads) amax_kernel(const float *__restr
     for (int64_t j = tail + i; j < n; j += nt) m = max(m, __float_as_uint(x[j]) & 0x7FFFFFFFu);
     __shared__ uint32_t red[kAmaxThreads / 64];
     m = block_max_u32<kAmaxThreads>(m, red);
-    if (threadIdx.x == 0) part[blockIdx.x] = m;
+    if (threadIdx.x == 0) {
+        ws[1 + blockIdx.x] = m;
+        if (blockIdx.x == 0) ws[0] = gridDim.x;
+    }
 }
 
 struct QuantArgs {
@@ -83,8 +88,7 @@ struct QuantArgs {
     uint8_t *codes;
     uint8_t *scales;
     float *tscale;
-    const uint32_t *amax_part; // partial maxima of |x| bit patterns
-    int32_t nparts;            // <= 256
+    const uint32_t *amax_ws;   // [0]: count P <= kAmaxParts, [1..P]: partial maxima of |x| bits
     int64_t planes; // o0 * o1
     int32_t R, S, R4, S4;
     int64_t nsq;
@@ -97,10 +101,16 @@ template <int FMT, bool SR, bool FULL>
 __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a)
 {
     using F = Fmt<FMT>;
-    // Tensor scale: reduce the amax pass's partial maxima (every lane of the workgroup).
+    // Tensor scale: reduce the partial maxima (every lane of the workgroup).
     __shared__ uint32_t red[4];
-    const uint32_t abits =
-        block_max_u32<256>(threadIdx.x < a.nparts ? a.amax_part[threadIdx.x] : 0u, red);
+    const uint32_t np = min(a.amax_ws[0], (uint32_t)kAmaxParts);
+    uint32_t pm = 0u;
+#pragma unroll
+    for (int k = 0; k < kAmaxParts / 256; ++k) {
+        const uint32_t i = threadIdx.x + 256u * k;
+        pm = max(pm, i < np ? a.amax_ws[1 + i] : 0u);
+    }
+    const uint32_t abits = block_max_u32<256>(pm, red);
     const bool nonfinite = abits >= 0x7F800000u;
     const float T = __uint_as_float(abits) / (448.0f * F::kEmax);
     // square indices fit in 31 bits (checked at launch)
@@ -272,7 +282,7 @@ static hipError_t launch_quant(const QuantArgs &a, bool full, hipStream_t st)
 
 hipError_t launch_quantize(const float *src, int64_t planes, int R, int S, int fmt, int rnd,
                            uint64_t seed, uint8_t *codes, uint8_t *scales, float *tscale,
-                           uint32_t *amax_ws, hipStream_t st)
+                           uint32_t *amax_ws, bool amax_ready, hipStream_t st)
 {
     if (planes * ((R + 3) / 4) * (int64_t)((S + 3) / 4) >= ((int64_t)1 << 31))
         return hipErrorInvalidValue; // square indices are 31-bit
@@ -280,13 +290,15 @@ hipError_t launch_quantize(const float *src, int64_t planes, int R, int S, int f
     // at least 8 float4 per lane where the tensor allows, at most kAmaxParts workgroups
     const int64_t want = (n / 4 + 8 * kAmaxThreads - 1) / (8 * kAmaxThreads);
     const int parts = (int)(want < 1 ? 1 : (want > kAmaxParts ? kAmaxParts : want));
-    hipLaunchKernelGGL(amax_kernel, dim3(parts), dim3(kAmaxThreads), 0, st, src, n, amax_ws);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (!amax_ready) {
+        hipLaunchKernelGGL(amax_kernel, dim3(parts), dim3(kAmaxThreads), 0, st, src, n, amax_ws);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
 
     QuantArgs a;
     a.src = src; a.codes = codes; a.scales = scales; a.tscale = tscale;
-    a.amax_part = amax_ws; a.nparts = parts;
+    a.amax_ws = amax_ws;
     a.planes = planes; a.R = R; a.S = S; a.R4 = (R + 3) / 4; a.S4 = (S + 3) / 4;
     a.nsq = planes * a.R4 * a.S4; // below 2^31 (the API rejects larger tensors)
     a.seed_lo = (uint32_t)seed; a.seed_hi = (uint32_t)(seed >> 32);

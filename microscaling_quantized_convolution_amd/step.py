@@ -3,9 +3,12 @@
 Device buffers for one layer (fp32 inputs, their channel-batch-first copies, the three quantized
 tensors, the outputs and the weight-gradient workspace) and the calls of one pass, in order:
 
-  relayout_x   X NCHW -> CBF                     quantize_x  X (round to nearest)
-  relayout_w   W OIHW -> tap-major               quantize_w  W (round to nearest)
+  relayout_x   X NCHW -> CBF (+ amax partials)   quantize_x  X (round to nearest)
+  relayout_w   W OIHW -> tap-major (+ amax)      quantize_w  W (round to nearest)
   quantize_g   G_Y (stochastic, seed per pass)   conv_fwd / conv_wgrad / conv_dgrad
+
+The relayouts write the tensor-amax partials of X and W, so their quantizations skip the amax
+pass (MQ_QUANTIZE_AMAX_READY); G_Y's quantization runs its own.
 
 G_Y is taken as already channel-batch-first (it is the next layer's input-gradient output).
 Every call goes through the C ABI on the current stream; nothing here computes.
@@ -17,8 +20,8 @@ from typing import Callable, Dict
 
 import torch
 
-from . import (MQ_QUANTIZE_WS_BYTES, MQ_ROLE_ACT, MQ_ROLE_GRAD, MQ_ROLE_WEIGHT, MQ_RNE, MQ_SR,
-               QTensor, conv_struct,
+from . import (MQ_QUANTIZE_AMAX_READY, MQ_QUANTIZE_WS_BYTES, MQ_ROLE_ACT, MQ_ROLE_GRAD,
+               MQ_ROLE_WEIGHT, MQ_RNE, MQ_SR, QTensor, conv_struct,
                mq_conv_dgrad, mq_conv_fwd, mq_conv_wgrad, mq_quantize, mq_relayout_cbf,
                mq_relayout_weight, mq_wgrad_workspace_bytes, out_hw)
 
@@ -51,11 +54,14 @@ class LayerStep:
         a0, a1, a2 = (self.amax[i * nws:(i + 1) * nws] for i in range(3))
         p = self.p
         self.ops: Dict[str, Callable[[int], None]] = OrderedDict([
-            ("relayout_x", lambda s: mq_relayout_cbf(self.x, self.xc, c.N, c.Cin, c.H, c.W, 0)),
+            ("relayout_x", lambda s: mq_relayout_cbf(self.x, self.xc, c.N, c.Cin, c.H, c.W, 0,
+                                                     amax_ws=a0)),
             ("relayout_w", lambda s: mq_relayout_weight(self.w, self.wc, c.Cout, c.Cin, c.Kh,
-                                                        c.Kw, 0)),
-            ("quantize_x", lambda s: mq_quantize(self.xc, self.qx, MQ_RNE, 0, a0)),
-            ("quantize_w", lambda s: mq_quantize(self.wc, self.qw, MQ_RNE, 0, a1)),
+                                                        c.Kw, 0, amax_ws=a1)),
+            ("quantize_x", lambda s: mq_quantize(self.xc, self.qx, MQ_RNE, 0, a0,
+                                                 MQ_QUANTIZE_AMAX_READY)),
+            ("quantize_w", lambda s: mq_quantize(self.wc, self.qw, MQ_RNE, 0, a1,
+                                                 MQ_QUANTIZE_AMAX_READY)),
             ("quantize_g", lambda s: mq_quantize(self.gc, self.qg, MQ_SR,
                                                  self.sr_seed_base + s, a2)),
             ("conv_fwd", lambda s: mq_conv_fwd(p, self.qx, self.qw, self.y)),
@@ -90,11 +96,14 @@ class LayerStep:
                 raise MQError(st, name)
 
         fixed = {
-            "relayout_x": (L.mq_relayout_cbf, (P(self.x), P(self.xc), c.N, c.Cin, c.H, c.W, 0, hs)),
+            "relayout_x": (L.mq_relayout_cbf, (P(self.x), P(self.xc), c.N, c.Cin, c.H, c.W, 0,
+                                               a[0], wsb, hs)),
             "relayout_w": (L.mq_relayout_weight, (P(self.w), P(self.wc), c.Cout, c.Cin, c.Kh,
-                                                  c.Kw, 0, hs)),
-            "quantize_x": (L.mq_quantize, (P(self.xc), bx, MQ_RNE, 0, a[0], wsb, hs)),
-            "quantize_w": (L.mq_quantize, (P(self.wc), bw, MQ_RNE, 0, a[1], wsb, hs)),
+                                                  c.Kw, 0, a[1], wsb, hs)),
+            "quantize_x": (L.mq_quantize, (P(self.xc), bx, MQ_RNE, 0, a[0], wsb,
+                                           MQ_QUANTIZE_AMAX_READY, hs)),
+            "quantize_w": (L.mq_quantize, (P(self.wc), bw, MQ_RNE, 0, a[1], wsb,
+                                           MQ_QUANTIZE_AMAX_READY, hs)),
             "conv_fwd": (L.mq_conv_fwd, (conv, bx, bw, P(self.y), hs)),
             "conv_wgrad": (L.mq_conv_wgrad, (conv, bg, bx, P(self.gw), P(self.ws), nws, hs)),
             "conv_dgrad": (L.mq_conv_dgrad, (conv, bw, bg, P(self.gx), hs)),
@@ -104,7 +113,7 @@ class LayerStep:
             if name == "quantize_g":
                 gsrc = P(self.gc)
                 out[name] = lambda s, f=L.mq_quantize, g=gsrc: chk(
-                    f(g, bg, MQ_SR, (self.sr_seed_base + s) & (2 ** 64 - 1), a[2], wsb, hs),
+                    f(g, bg, MQ_SR, (self.sr_seed_base + s) & (2 ** 64 - 1), a[2], wsb, 0, hs),
                     "mq_quantize")
             else:
                 f, args = fixed[name]

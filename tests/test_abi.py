@@ -59,21 +59,25 @@ def test_validation_errors_without_gpu():
     y = ctypes.c_void_p(0x2000)
     s0 = ctypes.c_void_p(0)
     # null pointers / bad enums -> MQ_ERR_ARG
-    assert L.mq_relayout_cbf(None, y, 1, 1, 1, 1, 0, s0) == mq.MQ_ERR_ARG
-    assert L.mq_relayout_cbf(y, y, 1, 0, 1, 1, 0, s0) == mq.MQ_ERR_ARG
-    assert L.mq_relayout_cbf(y, y, 1, 1, 1, 1, 2, s0) == mq.MQ_ERR_ARG
-    assert L.mq_relayout_weight(y, None, 1, 1, 1, 1, 0, s0) == mq.MQ_ERR_ARG
     ws = mq.MQ_QUANTIZE_WS_BYTES
-    assert L.mq_quantize(y, ctypes.byref(x), 2, 0, y, ws, s0) == mq.MQ_ERR_ARG
-    assert L.mq_quantize(y, ctypes.byref(x), 0, 0, None, ws, s0) == mq.MQ_ERR_WORKSPACE
-    assert L.mq_quantize(y, ctypes.byref(x), 0, 0, y, ws - 4, s0) == mq.MQ_ERR_WORKSPACE
+    assert L.mq_relayout_cbf(None, y, 1, 1, 1, 1, 0, None, 0, s0) == mq.MQ_ERR_ARG
+    assert L.mq_relayout_cbf(y, y, 1, 0, 1, 1, 0, None, 0, s0) == mq.MQ_ERR_ARG
+    assert L.mq_relayout_cbf(y, y, 1, 1, 1, 1, 2, None, 0, s0) == mq.MQ_ERR_ARG
+    assert L.mq_relayout_cbf(y, y, 1, 1, 1, 1, 0, y, ws - 1, s0) == mq.MQ_ERR_WORKSPACE
+    assert L.mq_relayout_cbf(y, y, 1, 1, 1, 1, 0, ctypes.c_void_p(0x2002), ws, s0) == mq.MQ_ERR_ARG
+    assert L.mq_relayout_weight(y, None, 1, 1, 1, 1, 0, None, 0, s0) == mq.MQ_ERR_ARG
+    assert L.mq_relayout_weight(y, y, 1, 1, 1, 1, 0, y, 16, s0) == mq.MQ_ERR_WORKSPACE
+    assert L.mq_quantize(y, ctypes.byref(x), 2, 0, y, ws, 0, s0) == mq.MQ_ERR_ARG
+    assert L.mq_quantize(y, ctypes.byref(x), 0, 0, y, ws, 2, s0) == mq.MQ_ERR_ARG  # unknown flag
+    assert L.mq_quantize(y, ctypes.byref(x), 0, 0, None, ws, 0, s0) == mq.MQ_ERR_WORKSPACE
+    assert L.mq_quantize(y, ctypes.byref(x), 0, 0, y, ws - 4, 0, s0) == mq.MQ_ERR_WORKSPACE
     bad = _fake_q((8, 8, 16, 2), fmt=5)
-    assert L.mq_quantize(y, ctypes.byref(bad), 0, 0, y, ws, s0) == mq.MQ_ERR_ARG
+    assert L.mq_quantize(y, ctypes.byref(bad), 0, 0, y, ws, 0, s0) == mq.MQ_ERR_ARG
     nul = _fake_q((8, 8, 16, 2), null=True)
-    assert L.mq_quantize(y, ctypes.byref(nul), 0, 0, y, ws, s0) == mq.MQ_ERR_ARG
+    assert L.mq_quantize(y, ctypes.byref(nul), 0, 0, y, ws, 0, s0) == mq.MQ_ERR_ARG
     # misaligned codes (16 B) or scales (4 B) -> MQ_ERR_ARG
     mis = mq.mq_qtensor(8, 8, 16, 2, mq.MQ_NVFP4, mq.MQ_ROLE_ACT, 0x1008, 0x1000, 0x1000)
-    assert L.mq_quantize(y, ctypes.byref(mis), 0, 0, y, ws, s0) == mq.MQ_ERR_ARG
+    assert L.mq_quantize(y, ctypes.byref(mis), 0, 0, y, ws, 0, s0) == mq.MQ_ERR_ARG
     mis = mq.mq_qtensor(8, 8, 16, 2, mq.MQ_NVFP4, mq.MQ_ROLE_ACT, 0x1000, 0x1002, 0x1000)
     assert L.mq_conv_fwd(ctypes.byref(conv), ctypes.byref(mis), ctypes.byref(w), y, s0) == mq.MQ_ERR_ARG
     assert L.mq_conv_fwd(ctypes.byref(conv), ctypes.byref(x), ctypes.byref(w), None, s0) == mq.MQ_ERR_ARG
@@ -102,3 +106,5 @@ def test_header_constants_match_binding():
     hdr = open(os.path.join(ROOT, "include", "mq.h")).read()
     m = re.search(r"#define MQ_QUANTIZE_WS_BYTES (\d+)", hdr)
     assert m and int(m.group(1)) == mq.MQ_QUANTIZE_WS_BYTES
+    m = re.search(r"#define MQ_QUANTIZE_AMAX_READY (\d+)u", hdr)
+    assert m and int(m.group(1)) == mq.MQ_QUANTIZE_AMAX_READY

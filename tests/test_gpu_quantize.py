@@ -159,3 +159,37 @@ def test_quantize_is_deterministic_and_seeded():
     assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
     assert not torch.equal(a.codes, c.codes)
     assert torch.equal(a.scales, c.scales)
+
+
+FUSED_CASES = [
+    ("normal", (3, 7, 5, 9)), ("relu", (32, 64, 14, 14)), ("t3", (4, 12, 9, 10)),
+    ("nan", (2, 3, 9, 10)), ("zeros", (2, 3, 9, 10)), ("denormal", (2, 3, 9, 10)),
+]
+
+
+@pytest.mark.parametrize("fmt", [4, 6])
+@pytest.mark.parametrize("case,shape", FUSED_CASES)
+def test_relayout_amax_then_quantize(case, shape, fmt):
+    """The relayouts can write the tensor-amax partials; quantizing with MQ_QUANTIZE_AMAX_READY
+    then skips the amax pass and must give the same bytes as the oracle."""
+    log("relayout+amax", case, shape, fmt)
+    N, C, H, W = shape
+    x = SPECIAL[case](shape) if case in SPECIAL else workloads.random_array(shape, 21, dist=case)
+    ws = mq.quantize_workspace()
+    t = to_dev(x)
+    xc = torch.empty(x.size, dtype=torch.float32, device="cuda")
+    mq.mq_relayout_cbf(t, xc, N, C, H, W, 0, amax_ws=ws)
+    for rnd in (0, 1):
+        q = mq.QTensor(H, W, C, N, fmt, mq.MQ_ROLE_ACT)
+        mq.mq_quantize(xc, q, rnd, 77, ws, mq.MQ_QUANTIZE_AMAX_READY)
+        torch.cuda.synchronize()
+        assert_quant_equal(q, oracle.quantize(oracle.nchw_to_cbf(x), fmt, rnd, 77), fmt,
+                           f"cbf {case} {rnd}")
+    # weights: OIHW (Cout, Cin, Kh, Kw) = shape
+    wt = torch.empty(x.size, dtype=torch.float32, device="cuda")
+    mq.mq_relayout_weight(t, wt, N, C, H, W, 0, amax_ws=ws)
+    q = mq.QTensor(H, W, N, C, fmt, mq.MQ_ROLE_WEIGHT)
+    mq.mq_quantize(wt, q, 0, 0, ws, mq.MQ_QUANTIZE_AMAX_READY)
+    torch.cuda.synchronize()
+    assert_quant_equal(q, oracle.quantize(oracle.oihw_to_tap_major(x), fmt, 0, 0), fmt,
+                       f"weight {case}")
