@@ -23,6 +23,8 @@ template <int FMT> struct RawItem {
 // (all are below 2^31 bytes).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t kBad = 0x80000000u;
+// cache-policy operand of buffer stores: the non-temporal bit (gfx950)
+constexpr int kStoreNT = 2;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
