@@ -137,10 +137,12 @@ def main():
     qbytes = lambda shape: sq(*shape) * (8 if fmt == 4 else 12) + sq(*shape)  # codes + scales
     nx, nw, ng = x.size, w.size, g.size
     qx_b, qw_b, qg_b = qbytes((H, W, Ci, N)), qbytes((Kh, Kw, Co, Ci)), qbytes((Ho, Wo, Co, N))
-    # algorithmic bytes: relayout 8 B/el; quantize = amax read + quantize read + codes/scales
+    # algorithmic bytes: relayout 8 B/el (its amax partials ride along); quantize of X and W
+    # (amax ready from the relayout) = one read + codes/scales; quantize of G_Y = amax read +
+    # quantize read + codes/scales
     alg = {
         "relayout_x": ("hbm", 8 * nx), "relayout_w": ("hbm", 8 * nw),
-        "quantize_x": ("hbm", 8 * nx + qx_b), "quantize_w": ("hbm", 8 * nw + qw_b),
+        "quantize_x": ("hbm", 4 * nx + qx_b), "quantize_w": ("hbm", 4 * nw + qw_b),
         "quantize_g": ("hbm", 8 * ng + qg_b),
         "conv_fwd": ("gemm", flops), "conv_wgrad": ("gemm", flops), "conv_dgrad": ("gemm", flops),
     }
