@@ -97,9 +97,9 @@ __device__ __forceinline__ uint32_t grid_sr(float a, uint32_t u16)
     using F = Fmt<FMT>;
     float sc = a < 2.0f ? F::kScale0 : (a < 4.0f ? 0.5f * F::kScale0 : 0.25f * F::kScale0);
     float ad = a < 2.0f ? 0.0f : (a < 4.0f ? F::kAdd1 : F::kAdd2);
-    float fl = __builtin_floorf(a * sc);
-    float lo = fl * (1.0f / sc);              // exact: sc is a power of two
-    float frac = (a - lo) * sc;               // exact: Sterbenz, power-of-two scale
+    const float x = a * sc;                   // exact: sc is a power of two
+    const float fl = __builtin_floorf(x);
+    const float frac = x - fl;                // exact (Sterbenz for x >= 1; fl = 0 below)
     uint32_t up = ((float)u16 < frac * 65536.0f) ? 1u : 0u;
     const uint32_t c = (uint32_t)(fl + ad) + up;
     return a >= F::kEmax ? F::kMaxMag : c;   // at or above the largest element: saturate
