@@ -96,15 +96,18 @@ __global__ void __launch_bounds__(256) transpose4_kernel(TransposeArgs p)
     __shared__ uint32_t red[4];
     const int tid = threadIdx.x;
     uint32_t m = 0u;
-    for (int64_t t = blockIdx.x; t < p.ntiles; t += gridDim.x) {
+    // tile t -> (channel, a0, b0)
+    auto coords = [&](int64_t t, int &c, int &a0, int &b0) {
         const int bt = (int)(t % p.tilesB);
         const int64_t rest = t / p.tilesB;
-        const int at = (int)(rest % p.tilesA);
-        const int c = (int)(rest / p.tilesA);
-        const int a0 = at * TA, b0 = bt * TB;
+        a0 = (int)(rest % p.tilesA) * TA;
+        c = (int)(rest / p.tilesA);
+        b0 = bt * TB;
+    };
+    auto load = [&](int64_t t, f32x4v (&v)[4]) {
+        int c, a0, b0;
+        coords(t, c, a0, b0);
         const float *s = p.src + c * p.src_cs;
-        float *d = p.dst + c * p.dst_cs;
-        f32x4v v[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int idx = tid + 256 * k, ra = idx / (TB / 4), cb = idx % (TB / 4);
@@ -113,6 +116,13 @@ __global__ void __launch_bounds__(256) transpose4_kernel(TransposeArgs p)
                                               reinterpret_cast<const f32x4v *>(s + a * p.src_ld + b))
                                         : f32x4v{0.f, 0.f, 0.f, 0.f};
         }
+    };
+    // the next tile's loads are issued as soon as this tile is in LDS, so they overlap the
+    // LDS reads and global stores of this tile
+    f32x4v v[4];
+    int64_t t = blockIdx.x;
+    if (t < p.ntiles) load(t, v);
+    for (; t < p.ntiles; t += gridDim.x) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int idx = tid + 256 * k, ra = idx / (TB / 4), cb = idx % (TB / 4);
@@ -123,6 +133,11 @@ __global__ void __launch_bounds__(256) transpose4_kernel(TransposeArgs p)
                                max(abs_bits(v[k][2]), abs_bits(v[k][3]))));
         }
         __syncthreads();
+        const int64_t tn = t + gridDim.x;
+        if (tn < p.ntiles) load(tn, v);
+        int c, a0, b0;
+        coords(t, c, a0, b0);
+        float *d = p.dst + c * p.dst_cs;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int idx = tid + 256 * k, rb = idx / (TA / 4), ca = idx % (TA / 4);
