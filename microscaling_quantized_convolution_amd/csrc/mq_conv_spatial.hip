@@ -220,6 +220,7 @@ conv_spatial_kernel(SpatialArgs a)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[u][j][r] = 0.0f;
     const int half = lane >> 5, l32 = lane & 31;
+    const int loff = lds_row_off(l32, half);
     __syncthreads();
     for (int c = 0; c < nchunk; ++c) {
         const uint8_t *As = lds[c & 1], *Bs = lds[c & 1] + ABYTES;
@@ -234,7 +235,7 @@ conv_spatial_kernel(SpatialArgs a)
                 for (int cc = 0; cc < WCOLS; ++cc) {
                     const int hc = wp * 4 * SI + cc;
                     bf[cc] = *reinterpret_cast<const u32x4_t *>(
-                        Bs + lds_row_off((hr * HC + hc) * 32 + l32, half));
+                        Bs + lds_row_off32((hr * HC + hc) * 32, loff));
                 }
 #pragma unroll
                 for (int tw = 0; tw < KWM; ++tw) {
@@ -245,7 +246,7 @@ conv_spatial_kernel(SpatialArgs a)
                         for (int u = 0; u < MW; ++u)
                             av[u] = __builtin_bit_cast(
                                 f16x8_t, *reinterpret_cast<const u32x4_t *>(
-                                             As + lds_row_off(t * 64 + 32 * (wm * MW + u) + l32, half)));
+                                             As + lds_row_off32(t * 64 + 32 * (wm * MW + u), loff)));
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             const f16x8_t b = __builtin_bit_cast(f16x8_t, bf[j * SI + tw]);

@@ -170,6 +170,7 @@ __global__ void __launch_bounds__(512) conv_wgrad_kernel(WgradArgs a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
     const int half = lane >> 5, l32 = lane & 31;
+    const int loff = lds_row_off(l32, half);
     __syncthreads();
     for (int c = 0; c < nst; ++c) {
         const uint8_t *Gs = lds[c & 1], *Xs = lds[c & 1] + GBYTES;
@@ -180,12 +181,12 @@ __global__ void __launch_bounds__(512) conv_wgrad_kernel(WgradArgs a)
 #pragma unroll
             for (int cc = 0; cc < HCM; ++cc)
                 xf[cc] = *reinterpret_cast<const u32x4_t *>(
-                    Xs + lds_row_off((cc * kKS + ks) * 64 + wc * 32 + l32, half));
+                    Xs + lds_row_off32((cc * kKS + ks) * 64 + wc * 32, loff));
 #pragma unroll
             for (int px = 0; px < kPWg; ++px) {
                 const f16x8_t gf = __builtin_bit_cast(
                     f16x8_t, *reinterpret_cast<const u32x4_t *>(
-                                 Gs + lds_row_off((px * kKS + ks) * 64 + wm * 32 + l32, half)));
+                                 Gs + lds_row_off32((px * kKS + ks) * 64 + wm * 32, loff)));
 #pragma unroll
                 for (int t = 0; t < KWM; ++t)
                     if (t < kw)

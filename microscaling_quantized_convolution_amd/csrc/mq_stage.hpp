@@ -123,13 +123,24 @@ __device__ __forceinline__ void decode_raw(const RawItem<FMT> &r, const f16x2_t 
     else decode_fp6_square(r.w[k][0], r.w[k][1], r.w[k][2], B, d);
 }
 
-// LDS operand rows: 16 fp16 (32 bytes, two 16-byte units). The unit index row*2 + chunk is
-// XORed with (row/4) mod 8, a permutation inside each aligned group of four rows, so that both
-// MFMA operand reads (consecutive rows, one unit) and staging writes (rows four apart) spread
-// over eight distinct 16-byte bank groups per eight lanes.
+// LDS operand rows: 16 fp16 (32 bytes, two 16-byte units). Bits 0-2 of the unit index
+// row*2 + chunk are XORed with a function of the row (a permutation inside each aligned group of
+// four rows) chosen so that every access pattern of the convolution kernels spreads over distinct
+// banks: MFMA operand reads (16 consecutive rows per group of 16 lanes need 16 distinct units
+// modulo 16), 16-byte staging writes of rows four apart (8 lanes, distinct units modulo 8) and
+// 8-byte staging writes of rows 16 and 32 apart.
 __device__ __forceinline__ int lds_row_off(int row, int chunk)
 {
-    return ((row * 2 + chunk) ^ ((row >> 2) & 7)) << 4;
+    const int x = ((row >> 3) & 1) | ((((row >> 2) ^ (row >> 5)) & 1) << 1) |
+                  ((((row >> 4) ^ (row >> 6)) & 1) << 2);
+    return ((row * 2 + chunk) ^ x) << 4;
+}
+
+// The same offset for row R + r with R a multiple of 32, from lane_off = lds_row_off(r, chunk)
+// (r < 32): the swizzle is linear over XOR, and R contributes only through its bits 5 and 6.
+__device__ __forceinline__ int lds_row_off32(int R, int lane_off)
+{
+    return (R << 5) + (lane_off ^ (R & 96));
 }
 
 // A value the caller knows to be equal across the wave, made visibly uniform to the compiler
@@ -159,23 +170,28 @@ __device__ __forceinline__ void store_item(const RawItem<FMT> &r, uint8_t *lds, 
             }
         }
     }
+    // rows row0 .. row0+3 share one swizzle (row0 is a multiple of 4): unit u of row i is at
+    // P ^ ((2i + u) << 4)
+    const int P = lds_row_off(row0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<uint4 *>(lds + lds_row_off(row0 + i, 0)) =
+        *reinterpret_cast<uint4 *>(lds + (P ^ ((2 * i) << 4))) =
             make_uint4(rows[i][0], rows[i][1], rows[i][2], rows[i][3]);
-        *reinterpret_cast<uint4 *>(lds + lds_row_off(row0 + i, 1)) =
+        *reinterpret_cast<uint4 *>(lds + (P ^ ((2 * i + 1) << 4))) =
             make_uint4(rows[i][4], rows[i][5], rows[i][6], rows[i][7]);
     }
 }
 
 // Decode an item whose four squares lie side by side along the rows of the LDS operand (the
 // reduction block kb = 4 elements is shared): square j fills LDS rows row0 + 4j .. row0 + 4j + 3
-// at reduction elements 4*kb .. 4*kb + 3 (8 bytes each). KR as in store_item.
+// at reduction elements 4*kb .. 4*kb + 3 (8 bytes each). row0 is a multiple of 16. KR as in
+// store_item.
 template <int FMT, bool KR>
 __device__ __forceinline__ void store_item_rows(const RawItem<FMT> &r, uint8_t *lds, int row0, int kb)
 {
     f16x2_t sc[2];
     item_scales<FMT>(r, sc);
+    const int Q = lds_row_off(row0, kb >> 1) + 8 * (kb & 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         uint32_t d[8];
@@ -189,8 +205,11 @@ __device__ __forceinline__ void store_item_rows(const RawItem<FMT> &r, uint8_t *
                 p0 = d[2 * i];
                 p1 = d[2 * i + 1];
             }
-            *reinterpret_cast<uint2 *>(lds + lds_row_off(row0 + 4 * j + i, kb >> 1) + 8 * (kb & 1)) =
-                make_uint2(p0, p1);
+            // row0 is a multiple of 16: rows row0 + s differ from row0 in the swizzle only by
+            // the bits that s sets (bit 3 and bit 2 of the row move unit bits 0 and 1)
+            const int s4 = 4 * j + i;
+            const int K = (2 * s4) ^ ((s4 >> 3) & 1) ^ (((s4 >> 2) & 1) << 1);
+            *reinterpret_cast<uint2 *>(lds + (Q ^ (K << 4))) = make_uint2(p0, p1);
         }
     }
 }
