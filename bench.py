@@ -68,6 +68,13 @@ def parse():
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="print the traffic summary from two rocprofv3 --pmc databases")
+    ap.add_argument("--config", default=None, choices=["c1", "c2", "c3", "c4", "c5"],
+                    help="time the hot path of every layer of a workload (one step = every "
+                         "layer once) instead of the single 3x3 layer")
+    ap.add_argument("--network", default=None, choices=["resnet18"],
+                    help="time a full training step of ResNet-18 (19 body convolutions on the "
+                         "library, the rest in PyTorch fp32)")
+    ap.add_argument("--batch", type=int, default=128, help="batch size of --network")
     return ap.parse_args()
 
 
@@ -108,6 +115,12 @@ def main():
         print("bench.py measures one GPU only: the hot path here is single-device; "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.network:
+        run_network(args)
+        return
+    if args.config:
+        run_config(args)
+        return
 
     import torch
 
@@ -310,6 +323,164 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layer, args.cpu_sample_n)
 
+    print(json.dumps(result), flush=True)
+
+
+def _time_graph(fns, reps: int, stream) -> float:
+    """Milliseconds per pass of `fns` (called in order), from one HIP graph of `reps` passes."""
+    import torch
+    with torch.cuda.stream(stream):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=stream):
+            for r in range(reps):
+                for f in fns:
+                    f(r)
+        gr.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        gr.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def run_config(args):
+    """Every layer of a workload through the hot path: one step = each layer's relayouts, three
+    quantizations and three GEMMs once (layers that repeat a shape are timed once and counted
+    with their multiplicity). Per layer and op: time, rate and fraction of the bound."""
+    import collections
+
+    import numpy as np
+    import torch
+
+    from microscaling_quantized_convolution_amd.step import LayerStep
+    import workloads
+
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    layers = workloads.CONFIGS[args.config]()
+    groups = collections.OrderedDict()
+    for l in layers:
+        groups.setdefault(l.conv_tuple() + (l.fmt,), []).append(l)
+    stream = torch.cuda.Stream()
+    ridge = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    per_layer, step_ms, flops_total = [], 0.0, 0
+    for key, ls in groups.items():
+        l = ls[0]
+        x, w, g = workloads.make_tensors(l)
+        gc = torch.empty(g.size, dtype=torch.float32, device=dev)
+        import microscaling_quantized_convolution_amd as mq
+        mq.mq_relayout_cbf(torch.from_numpy(g).to(dev), gc, l.N, l.Cout, l.Ho, l.Wo, 0)
+        st = LayerStep(l.conv_tuple(), l.fmt, torch.from_numpy(x).to(dev),
+                       torch.from_numpy(w).to(dev), gc, sr_seed_base=l.sr_seed)
+        del x, w, g
+        calls = st.direct_calls(stream)
+        for s_ in range(max(args.warmup, 1)):
+            for f in calls.values():
+                f(s_)
+        torch.cuda.synchronize()
+        eb = 0.5625 if l.fmt == 4 else 0.8125
+        nx, nw, ng = l.N * l.Cin * l.H * l.W, l.Cout * l.Cin * l.Kh * l.Kw, l.N * l.Cout * l.Ho * l.Wo
+        fl = l.gemm_flops()
+        byt = {"relayout_x": 8 * nx, "relayout_w": 8 * nw, "quantize_x": 4 * nx + eb * nx,
+               "quantize_w": 4 * nw + eb * nw, "quantize_g": 8 * ng + eb * ng,
+               "conv_fwd": eb * (nx + nw) + 4 * ng, "conv_wgrad": eb * (nx + ng) + 4 * nw,
+               "conv_dgrad": eb * (nw + ng) + 4 * nx}
+        ops = {}
+        for name, f in calls.items():
+            ms = _time_graph([f], args.op_reps, stream)
+            gbs = byt[name] / (ms * 1e-3) / 1e9
+            if name.startswith("conv"):
+                tf = fl / (ms * 1e-3) / 1e12
+                mfma = fl / byt[name] >= ridge
+                ops[name] = {"ms": round(ms, 5), "TFLOP_s": round(tf, 1), "GB_s": round(gbs, 1),
+                             "bound": "mfma" if mfma else "hbm",
+                             "frac": round(tf / MFMA_PEAK_TFLOPS if mfma else
+                                           gbs / HBM_PEAK_GBS, 4)}
+            else:
+                ops[name] = {"ms": round(ms, 5), "GB_s": round(gbs, 1),
+                             "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        fns = list(calls.values())
+        ms_layer = _time_graph(fns, max(2, args.op_reps // 4), stream)
+        step_ms += ms_layer * len(ls)
+        flops_total += 3 * fl * len(ls)
+        per_layer.append({"layers": [x_.name for x_ in ls], "shape": {
+            "N": l.N, "Cin": l.Cin, "Cout": l.Cout, "H": l.H, "W": l.W, "K": l.Kh,
+            "stride": l.stride, "pad": l.pad, "format": f"NVFP{l.fmt}"},
+            "ms_layer_step": round(ms_layer, 5), "per_op": ops})
+        del st, calls, gc
+        torch.cuda.empty_cache()
+    result = {
+        "metric": "quant GB/s (% HBM peak) + conv fwd/wgrad/dgrad TFLOP/s (% bf16 MFMA) per layer",
+        "value": round(flops_total / (step_ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "ms_per_step": round(step_ms, 5),
+        "timing": "per layer: one HIP graph of back-to-back layer steps; the step is the sum "
+                  "over the workload's layers with their multiplicity",
+        "higher_is_better": True,
+        "dtype": "fp16",
+        "data": "synthetic (seeded numpy PCG64, the workload's value distributions)",
+        "config": {"workload": f"{args.config}: {len(layers)} layers, relayout x2, quantize x3, "
+                               f"conv fwd/wgrad/dgrad each"},
+        "per_layer": per_layer,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def run_network(args):
+    """One ResNet-18 training step (forward, cross-entropy on random labels, backward, SGD with
+    momentum) at 224x224 on synthetic uniform images: the 19 body convolutions go through the
+    library (each of X, W, G_Y quantized once per step), the stem, batch norms, activations,
+    residual adds, pooling and classifier stay fp32 PyTorch."""
+    import torch
+
+    from microscaling_quantized_convolution_amd.nn import ResNet18MQ
+    import workloads
+
+    torch.cuda.set_device(0)
+    torch.manual_seed(0)
+    B = args.batch
+    model = ResNet18MQ(num_classes=1000).cuda()
+    opt = torch.optim.SGD(model.parameters(), lr=0.01, momentum=0.9)
+    x = torch.rand(B, 3, 224, 224, device="cuda")
+    labels = torch.randint(0, 1000, (B,), device="cuda")
+
+    def step():
+        opt.zero_grad(set_to_none=True)
+        loss = torch.nn.functional.cross_entropy(model(x), labels)
+        loss.backward()
+        opt.step()
+        return loss
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        loss = step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    body_flops = 3 * sum(l.gemm_flops() for l in workloads.config5()) * B // 128
+    result = {
+        "metric": "ResNet-18 training step with NVFP4 body convolutions",
+        "value": round(B / (ms * 1e-3), 1),
+        "unit": "images/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "dtype": "fp16 MFMA on quantized body convs; fp32 elsewhere",
+        "data": "synthetic (uniform [0,1) images, random labels)",
+        "config": {"workload": f"resnet18 N={B} 224x224: 19 body convs on the library, "
+                               f"stem/BN/ReLU/pool/FC fp32 PyTorch, SGD momentum"},
+        "body_gemm_flops_per_step": body_flops,
+        "body_gemm_tflops_over_step": round(body_flops / (ms * 1e-3) / 1e12, 2),
+        "final_loss": round(float(loss.detach()), 4),
+    }
     print(json.dumps(result), flush=True)
 
 

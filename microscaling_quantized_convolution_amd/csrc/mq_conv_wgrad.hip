@@ -283,15 +283,29 @@ Plan plan(const ConvGeom &g)
     p.cit = (g.Cin4 + 15) / 16;
     p.tiles = g.Kh * p.cot * p.cit;
     p.split_stride = (int64_t)g.Kh * g.Kw * g.Cout * g.Cin;
-    // enough workgroups to fill the GPU, but at most ~16 MB of partial sums
+    // Split count: a workgroup holds one CU (its LDS), so tiles * splits workgroups run in
+    // ceil(tiles * splits / 256) rounds of per_split stages. Pick the count with the least
+    // modelled time: rounds * per_split stages (about 1.9 us each) plus the partial sums that
+    // every split writes and the sum kernel reads back (at about 5 TB/s); at most ~16 MB of
+    // partial sums. Ties keep the smaller count.
     const int64_t out_bytes = p.split_stride * 4;
-    int64_t s = (256 + p.tiles - 1) / p.tiles; // one 8-wave workgroup per CU
     int64_t cap = (16ll << 20) / (out_bytes > 0 ? out_bytes : 1);
     if (cap < 1) cap = 1;
-    if (s > cap) s = cap;
-    if (s > p.stages) s = p.stages;
-    if (s < 1) s = 1;
-    p.per_split = (int)((p.stages + s - 1) / s);
+    if (cap > p.stages) cap = p.stages;
+    int64_t best_per = p.stages;
+    double best = -1.0;
+    for (int64_t s = 1; s <= cap; ++s) {
+        const int64_t per = (p.stages + s - 1) / s;
+        const int64_t splits = (p.stages + per - 1) / per;
+        if (splits != s) continue; // the same split as a smaller s
+        const int64_t rounds = (p.tiles * splits + 255) / 256;
+        const double t = 1.9 * (double)(rounds * per) + 2.0 * (double)(splits * out_bytes) / 5e6;
+        if (best < 0.0 || t < best) {
+            best = t;
+            best_per = per;
+        }
+    }
+    p.per_split = (int)best_per;
     p.splits = (p.stages + p.per_split - 1) / p.per_split;
     p.bytes = (size_t)p.splits * (size_t)p.split_stride * 4;
     return p;
