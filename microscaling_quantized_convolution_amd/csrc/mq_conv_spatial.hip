@@ -299,7 +299,8 @@ conv_spatial_kernel(SpatialArgs a)
 
 
 // Pixel tile per workgroup: 2 x 8 for stride-1 input walks, 1 x 8 for stride 2 (whose halo is
-// twice as wide), so that two LDS stage buffers fit.
+// twice as wide), so that two LDS stage buffers fit. A stride-1 walk over a small map also takes
+// the 1 x 8 tile when the 2 x 8 tiles would leave many CUs idle (see launch_spatial).
 template <int SI> struct TileShape;
 template <> struct TileShape<1> { static constexpr int PH = 2, PW = 8, MW = 2; };
 template <> struct TileShape<2> { static constexpr int PH = 1, PW = 8, MW = 1; };
@@ -325,10 +326,9 @@ bool spatial_supported(const ConvGeom &g)
     return xs < lim && gs < lim && ws < lim && ys < lim && xo < lim;
 }
 
-template <int FMT, bool A_KR, int SI>
-static hipError_t launch_spatial(SpatialArgs &a, int nclass, hipStream_t st)
+template <int FMT, bool A_KR, int SI, int PH, int PW, int MW>
+static hipError_t launch_spatial_tiles(SpatialArgs &a, int nclass, hipStream_t st)
 {
-    constexpr int PH = TileShape<SI>::PH, PW = TileShape<SI>::PW, MW = TileShape<SI>::MW;
     constexpr int THREADS = 32 * PH * PW * (2 / MW);
     int max_tiles = 0;
     for (int c = 0; c < nclass; ++c) {
@@ -345,6 +345,33 @@ static hipError_t launch_spatial(SpatialArgs &a, int nclass, hipStream_t st)
         hipLaunchKernelGGL((conv_spatial_kernel<FMT, A_KR, SI, PH, PW, MW, 0>), grid,
                            dim3(THREADS), 0, st, a);
     return hipGetLastError();
+}
+
+// Workgroups of either tile shape take one CU each (their LDS), so a grid runs in
+// ceil(workgroups / 256) rounds. A 1 x 8 workgroup does half the MFMA work of a 2 x 8 one in
+// about 0.6 of its time (the stage overheads stay); the shape with the smaller modelled time
+// (rounds x time per workgroup) is taken.
+static int spatial_grid_wgs(const SpatialArgs &a, int nclass, int PH, int PW)
+{
+    int max_tiles = 0;
+    for (int c = 0; c < nclass; ++c) {
+        const SpatialClass &k = a.cls[c];
+        const int t = ((k.OWs + PW - 1) / PW) * ((k.OHs + PH - 1) / PH);
+        if (t > max_tiles) max_tiles = t;
+    }
+    return max_tiles * a.nblk * ((a.M4 + 15) / 16) * nclass;
+}
+
+template <int FMT, bool A_KR, int SI>
+static hipError_t launch_spatial(SpatialArgs &a, int nclass, hipStream_t st)
+{
+    constexpr int PH = TileShape<SI>::PH, PW = TileShape<SI>::PW, MW = TileShape<SI>::MW;
+    if constexpr (SI == 1) {
+        const int w2 = spatial_grid_wgs(a, nclass, 2, 8), w1 = spatial_grid_wgs(a, nclass, 1, 8);
+        const double t2 = 1.0 * ((w2 + 255) / 256), t1 = 0.6 * ((w1 + 255) / 256);
+        if (t1 < t2) return launch_spatial_tiles<FMT, A_KR, SI, 1, 8, 1>(a, nclass, st);
+    }
+    return launch_spatial_tiles<FMT, A_KR, SI, PH, PW, MW>(a, nclass, st);
 }
 
 hipError_t launch_conv_fwd_spatial(const ConvGeom &g, int fmt, QOperand x, QOperand w, float *y,
