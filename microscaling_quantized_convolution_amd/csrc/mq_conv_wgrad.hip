@@ -38,7 +38,7 @@ struct WgradArgs {
     int64_t split_stride;  // floats per split
 };
 
-// Waves 0..3 consume (MFMAs on one LDS buffer); waves 4..7 produce (load the squares of the
+// Waves 0..3 consume (MFMAs on one LDS buffer); waves 4..11 produce (load the squares of the
 // stage after next, decode the next stage into the other buffer); one barrier per stage.
 // KS: 16-element reduction steps per stage and pixel: 2 (32 batch elements, eight batch
 // squares) when the batch has at least eight squares, else 1 (four squares: the whole batch of a
@@ -46,17 +46,21 @@ struct WgradArgs {
 // Output pixels per stage: 16 / KS for stride 1, 8 / KS for stride 2 (twice as wide an X
 // segment), so that two stage buffers fit in LDS.
 template <int SI, int KS> struct StagePixels { static constexpr int kPW = (SI == 1 ? 16 : 8) / KS; };
+// Producer threads: two waves per SIMD, so that one wave's decode overlaps the other's LDS
+// writes and load issue (one producer wave per SIMD left each stage producer-bound).
+constexpr int kNP = 512;
+constexpr int kWgradThreads = 256 + kNP;
 inline int stage_ks(int N4) { return N4 >= 8 ? 2 : 1; }
 
 // KF: the kernel width Kw when fixed at compile time (1 or 3), 0 = read at run time.
 template <int FMT, int SI, int KF, int kKS>
-__global__ void __launch_bounds__(512) conv_wgrad_kernel(WgradArgs a)
+__global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
 {
     constexpr int kPWg = StagePixels<SI, kKS>::kPW;
     constexpr int KWM = KF ? KF : 3;
     constexpr int HCM = (kPWg - 1) * SI + KWM;
     constexpr int GBYTES = kPWg * kKS * 64 * kRowBytes, XBYTES = HCM * kKS * 64 * kRowBytes;
-    constexpr int ITEMS = (kPWg * 16 * kKS + HCM * 16 * kKS + 255) / 256;
+    constexpr int ITEMS = (kPWg * 16 * kKS + HCM * 16 * kKS + kNP - 1) / kNP;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][GBYTES + XBYTES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
@@ -101,7 +105,7 @@ __global__ void __launch_bounds__(512) conv_wgrad_kernel(WgradArgs a)
             constexpr int SH = kKS == 2 ? 1 : 0; // item index bits below the channel square
     #pragma unroll
             for (int q = 0; q < ITEMS; ++q) {
-                const int it = ptid + q * 256;
+                const int it = ptid + q * kNP;
                 const bool isG = wave_uniform(it & ~63) < nG;
                 const int nh = it & (kKS - 1); // nG is even, so X items keep the same bit
                 // a stage past the end of this split loads nothing (mask 0), so that every stage
@@ -126,7 +130,7 @@ __global__ void __launch_bounds__(512) conv_wgrad_kernel(WgradArgs a)
         auto store = [&](int buf, const RawItem<FMT>(&src)[ITEMS]) {
     #pragma unroll
             for (int q = 0; q < ITEMS; ++q) {
-                const int it = ptid + q * 256;
+                const int it = ptid + q * kNP;
                 const int wit = wave_uniform(it & ~63);
                 // LDS rows: [pixel or column][reduction step][64 channels]
                 constexpr int SH = kKS == 2 ? 1 : 0;
@@ -330,10 +334,10 @@ template <int FMT, int SI, int KS>
 static void launch_wgrad_ks(const ConvGeom &g, dim3 grid, const WgradArgs &a, hipStream_t st)
 {
     if (g.Kw == 3)
-        hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 3, KS>), grid, dim3(512), 0, st, a);
+        hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 3, KS>), grid, dim3(kWgradThreads), 0, st, a);
     else if (g.Kw == 1)
-        hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 1, KS>), grid, dim3(512), 0, st, a);
-    else hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 0, KS>), grid, dim3(512), 0, st, a);
+        hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 1, KS>), grid, dim3(kWgradThreads), 0, st, a);
+    else hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 0, KS>), grid, dim3(kWgradThreads), 0, st, a);
 }
 
 template <int FMT, int SI>
