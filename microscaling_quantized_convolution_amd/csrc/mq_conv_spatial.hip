@@ -63,7 +63,7 @@ struct SpatialArgs {
 // class's sub-kernel extent is read at run time.
 // MW: 32-row blocks per consumer wave (2: a wave owns all 64 rows of 4 pixels; 1: two waves
 // share 4 pixels, 32 rows each, so that small pixel tiles still give four MFMA waves).
-template <int FMT, bool A_KR, int SI, int PH, int PW, int MW, int KF>
+template <int FMT, bool A_KR, int SI, int PH, int PW, int MW, int KF, bool PERSIST>
 __global__ void __launch_bounds__(32 * PH * PW * (2 / MW))
 conv_spatial_kernel(SpatialArgs a)
 {
@@ -80,25 +80,57 @@ conv_spatial_kernel(SpatialArgs a)
 
     const SpatialClass &cl = a.cls[blockIdx.z];
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
-    const int bx = blockIdx.x;
-    const int nb = bx % a.nblk;
-    const int tile = bx / a.nblk;
-    // A workgroup past its class's last tile loads and computes nothing, and its pixels fall
-    // outside the class grid. (No early return: every kernel argument is then fetched in one
-    // round trip instead of one per dependent branch.)
-    const bool live = tile < cl.tiles;
-    const int ti = tile / cl.tiles_w, tj = tile - ti * cl.tiles_w;
-    const int i0 = ti * PH, j0 = tj * PW;
-    const int m4_0 = blockIdx.y * 16;
-    const int kh = KF ? KF : cl.kh * (int)live, kw = KF ? KF : cl.kw * (int)live;
+    // Work items of this class: (M block of 64 rows, pixel tile, batch block), batch block
+    // fastest. Workgroup b takes items b, b + gridDim.x, ...; its chunks form one stream
+    // (item-major), so the producer runs into the next item while the consumers write the
+    // current one's output.
+    const int nmb = (a.M4 + 15) / 16;
+    const int tiles_h = cl.tiles / (cl.tiles_w > 0 ? cl.tiles_w : 1);
+    const int T = cl.tiles * a.nblk * nmb;
+    const int P = (int)gridDim.x, b = (int)blockIdx.x;
+    // PERSIST: each workgroup loops over several items; otherwise one item per workgroup
+    const int nmine = b < T ? (PERSIST ? (T - 1 - b) / P + 1 : 1) : 0;
+    // Item w = ((mb * tiles_h + ti) * tiles_w + tj) * nblk + nb, stepped by P in that mixed radix
+    // with carries (no division per item).
+    struct ItemPos { int nb, tj, ti, mb; };
+    ItemPos step_p;
+    {
+        int r = P;
+        step_p.nb = r % a.nblk; r /= a.nblk;
+        step_p.tj = r % cl.tiles_w; r /= cl.tiles_w;
+        step_p.ti = r % tiles_h; r /= tiles_h;
+        step_p.mb = r;
+    }
+    ItemPos first;
+    {
+        int r = b;
+        first.nb = r % a.nblk; r /= a.nblk;
+        first.tj = r % cl.tiles_w; r /= cl.tiles_w;
+        first.ti = r % tiles_h; r /= tiles_h;
+        first.mb = r;
+    }
+    auto advance = [&](ItemPos p) {
+        p.nb += step_p.nb;
+        int c = p.nb >= a.nblk;
+        p.nb -= c ? a.nblk : 0;
+        p.tj += step_p.tj + c;
+        c = p.tj >= cl.tiles_w;
+        p.tj -= c ? cl.tiles_w : 0;
+        p.ti += step_p.ti + c;
+        c = p.ti >= tiles_h;
+        p.ti -= c ? tiles_h : 0;
+        p.mb += step_p.mb + c;
+        return p;
+    };
+    const int kh = KF ? KF : cl.kh, kw = KF ? KF : cl.kw;
     const int ntap = kh * kw;
     const int HR = (PH - 1) * SI + kh, HC = (PW - 1) * SI + kw;
     const int nchunk = ((a.K4 + 3) / 4) * (ntap > 0 ? 1 : 0);
+    const int G = nmine * nchunk; // chunk steps of this workgroup
 
     if (wave >= NCW) {
         // ================= producer =================
         const int ptid = tid - NP;
-        const int ih0 = i0 * SI + cl.r0, iw0 = j0 * SI + cl.c0;
         const int nA = ntap * 16, nA64 = (nA + 63) & ~63, nAB = nA64 + HR * HC * 8;
         constexpr int CB = (FMT == kFP4) ? 8 : 12;
         const uint32_t in_sq = (uint32_t)a.IH * a.IW * a.K4 * a.N4;
@@ -111,65 +143,115 @@ conv_spatial_kernel(SpatialArgs a)
         //   weight, input gradient: (tap, kcl, m-group), squares 4g..4g+3 of Cin at Cout square
         //       kc0+kcl, stored as 16 LDS rows x 4 reduction elements
         //   halo: (pixel, kcl, n-group), squares 4g..4g+3 of N at channel square kc0+kcl
-        // per slot: first square at chunk 0, its per-chunk advance, static square validity,
-        // reduction block, LDS row
-        uint32_t sq_base[ITEMS], sq_chunk[ITEMS], vmask[ITEMS];
-        int kcl_of[ITEMS], row[ITEMS];
+        // per slot, the parts that do not depend on the work item: weight square base and row
+        // offset within the M block, or halo row/column and batch offset; the reduction block;
+        // whether the slot holds an item at all; the LDS row
+        int base0[ITEMS], off1[ITEMS], hrow[ITEMS], hcol[ITEMS], kcl_of[ITEMS], row[ITEMS];
+        bool used[ITEMS];
 #pragma unroll
         for (int q = 0; q < ITEMS; ++q) {
             const int it = ptid + q * NP;
             const int wit = wave_uniform(it & ~63);
-            sq_base[q] = 0; sq_chunk[q] = 0; vmask[q] = 0; kcl_of[q] = 0; row[q] = 0;
+            base0[q] = 0; off1[q] = 0; hrow[q] = 0; hcol[q] = 0; kcl_of[q] = 0; row[q] = 0;
+            used[q] = false;
             if (wit < nA64) {
                 const int t = it >> 4;
                 const int tkh = t / kw, tkw = t - tkh * kw;
                 const int wtap = (cl.Ah + cl.Bh * tkh) * a.Kw + (cl.Aw + cl.Bw * tkw);
+                used[q] = it < nA;
                 if (A_KR) {
                     const int mg = it & 3, kcl = (it >> 2) & 3;
-                    const int m4 = m4_0 + 4 * mg;
-                    sq_base[q] = ((uint32_t)wtap * a.Cout4 + kcl) * a.Cin4 + m4;
-                    sq_chunk[q] = 4u * a.Cin4;
-                    const int left = a.M4 - m4;
-                    vmask[q] = (it < nA && left > 0) ? (left >= 4 ? 0xFu : (1u << left) - 1u) : 0u;
+                    base0[q] = (wtap * a.Cout4 + kcl) * a.Cin4 + 4 * mg;
+                    off1[q] = 4 * mg;
                     kcl_of[q] = kcl;
                     row[q] = t * 64 + 16 * mg;
                 } else {
-                    const int m4 = m4_0 + (it & 15);
-                    sq_base[q] = ((uint32_t)wtap * a.Cout4 + m4) * a.Cin4;
-                    sq_chunk[q] = 4;
-                    vmask[q] = (it < nA && m4 < a.M4) ? 0xFu : 0u;
+                    base0[q] = (wtap * a.Cout4 + (it & 15)) * a.Cin4;
+                    off1[q] = it & 15;
                     row[q] = t * 64 + 4 * (it & 15);
                 }
             } else if (wit < nAB) {
                 const int j = it - nA64, hp = j >> 3, g = j & 1, kcl = (j >> 1) & 3;
-                const int hr = hp / HC, hc = hp - hr * HC;
-                const int ih = ih0 + hr, iw = iw0 + hc;
-                const int n4 = nb * 8 + 4 * g;
-                const bool inside = live && it < nAB && ih >= 0 && ih < a.IH && iw >= 0 && iw < a.IW;
-                const int left = a.N4 - n4;
-                vmask[q] = (inside && left > 0) ? (left >= 4 ? 0xFu : (1u << left) - 1u) : 0u;
-                sq_base[q] = (((uint32_t)ih * a.IW + iw) * a.K4 + kcl) * a.N4 + n4;
-                sq_chunk[q] = 4u * a.N4;
+                hrow[q] = hp / HC;
+                hcol[q] = hp - hrow[q] * HC;
+                off1[q] = 4 * g;
                 kcl_of[q] = kcl;
+                used[q] = it < nAB;
                 row[q] = hp * 32 + 16 * g;
             }
         }
-        // Two register stages: chunk c + 3 is loaded into the slot chunk c + 1 was just decoded
-        // from, so every load has two stage times to arrive. Loads are issued without branches,
-        // the same number per stage (a chunk past the end loads nothing: mask 0), and the loop is
-        // unrolled by two so that slots are never copied: the compiler's wait before a decode
-        // then covers exactly that chunk's loads.
+        // Two register stages: chunk g + 3 of the stream is loaded into the slot chunk g + 1 was
+        // just decoded from, so every load has two stage times to arrive. Loads are issued
+        // without branches, the same number per stage (a chunk past the end loads nothing:
+        // mask 0), and the loop is unrolled by two so that slots are never copied: the
+        // compiler's wait before a decode then covers exactly that chunk's loads.
         RawItem<FMT> raw[2][ITEMS];
-        auto load = [&](int c, RawItem<FMT>(&dst)[ITEMS]) {
+        // Per slot: first square of an item's chunk 0 and its static validity, for the item
+        // `p`. With one item per workgroup it is set once; in the persistent case it is
+        // recomputed for every load (without a branch: a branch here makes the compiler wait for
+        // every load in flight).
+        auto geometry = [&](ItemPos p, uint32_t (&sqb)[ITEMS], uint32_t (&vm)[ITEMS]) {
+            const int nb = p.nb, m4_0 = p.mb * 16;
+            const int ih0 = p.ti * PH * SI + cl.r0, iw0 = p.tj * PW * SI + cl.c0;
+#pragma unroll
+            for (int q = 0; q < ITEMS; ++q) {
+                const bool isA = wave_uniform((ptid + q * NP) & ~63) < nA64;
+                if (isA && !A_KR) {
+                    sqb[q] = (uint32_t)base0[q] + (uint32_t)m4_0 * a.Cin4;
+                    vm[q] = (used[q] && m4_0 + off1[q] < a.M4) ? 0xFu : 0u;
+                } else if (isA) {
+                    const int left = a.M4 - m4_0 - off1[q];
+                    sqb[q] = (uint32_t)base0[q] + (uint32_t)m4_0;
+                    vm[q] = (used[q] && left > 0) ? (left >= 4 ? 0xFu : (1u << left) - 1u) : 0u;
+                } else {
+                    const int ih = ih0 + hrow[q], iw = iw0 + hcol[q];
+                    const int n4 = nb * 8 + off1[q];
+                    const bool inside = used[q] && ih >= 0 && ih < a.IH && iw >= 0 && iw < a.IW;
+                    const int left = a.N4 - n4;
+                    sqb[q] = (((uint32_t)ih * a.IW + iw) * a.K4 + kcl_of[q]) * a.N4 + n4;
+                    vm[q] = (inside && left > 0) ? (left >= 4 ? 0xFu : (1u << left) - 1u) : 0u;
+                }
+            }
+        };
+        uint32_t sq_chunk[ITEMS], sq_base[ITEMS], vmask[ITEMS];
+#pragma unroll
+        for (int q = 0; q < ITEMS; ++q) {
+            const bool isA = wave_uniform((ptid + q * NP) & ~63) < nA64;
+            sq_chunk[q] = isA ? (A_KR ? 4u * a.Cin4 : 4u) : 4u * a.N4;
+        }
+        geometry(first, sq_base, vmask);
+        // the item and chunk of the next load (loads go through the stream in order)
+        int lp_nb = first.nb, lp_tj = first.tj, lp_ti = first.ti, lp_mb = first.mb;
+        int lc = 0;
+        auto load = [&](int gs, RawItem<FMT>(&dst)[ITEMS]) {
+            const bool valid = gs < G;
+            int c = gs;
+            uint32_t sqb[ITEMS], vm[ITEMS];
+            if constexpr (PERSIST) {
+                const ItemPos cur = {lp_nb, lp_tj, lp_ti, lp_mb};
+                geometry(cur, sqb, vm);
+                c = lc;
+                const bool wrap = lc + 1 >= nchunk;
+                const ItemPos nx = advance(cur);
+                lc = wrap ? 0 : lc + 1;
+                lp_nb = wrap ? nx.nb : lp_nb;
+                lp_tj = wrap ? nx.tj : lp_tj;
+                lp_ti = wrap ? nx.ti : lp_ti;
+                lp_mb = wrap ? nx.mb : lp_mb;
+            } else {
+#pragma unroll
+                for (int q = 0; q < ITEMS; ++q) { sqb[q] = sq_base[q]; vm[q] = vmask[q]; }
+            }
             const int kvalid = a.K4 - 4 * c;
             const uint32_t kmask = kvalid >= 4 ? 0xFu : (kvalid > 0 ? (1u << kvalid) - 1u : 0u);
 #pragma unroll
             for (int q = 0; q < ITEMS; ++q) {
                 const bool isA = wave_uniform((ptid + q * NP) & ~63) < nA64;
-                const uint32_t sq0 = sq_base[q] + (uint32_t)c * sq_chunk[q];
+                const uint32_t sq0 = sqb[q] + (uint32_t)c * sq_chunk[q];
                 const bool kin = 4 * c + kcl_of[q] < a.K4;
-                const uint32_t m = (isA && !A_KR) ? (vmask[q] & kmask) : (kin ? vmask[q] : 0u);
-                load_item_contig<FMT>(dst[q], isA ? w_c : in_c, isA ? w_s : in_s, sq0, m);
+                const uint32_t m = (isA && !A_KR) ? (vm[q] & kmask) : (kin ? vm[q] : 0u);
+                load_item_contig<FMT>(dst[q], isA ? w_c : in_c, isA ? w_s : in_s, sq0,
+                                      valid ? m : 0u);
             }
         };
         auto store = [&](int buf, const RawItem<FMT>(&src)[ITEMS]) {
@@ -187,23 +269,23 @@ conv_spatial_kernel(SpatialArgs a)
                 }
             }
         };
-        // step c: decode chunk c + 1 from slot (c + 1) & 1 into LDS buffer (c + 1) & 1, then
-        // load chunk c + 3 into that slot
+        // step g: decode chunk g + 1 from slot (g + 1) & 1 into LDS buffer (g + 1) & 1, then
+        // load chunk g + 3 into that slot
         load(0, raw[0]);
         load(1, raw[1]);
         store(0, raw[0]);
         load(2, raw[0]);
         __syncthreads();
-        int c = 0;
-        for (; c + 1 < nchunk; c += 2) {
+        int gs = 0;
+        for (; gs + 1 < G; gs += 2) {
             store(1, raw[1]);
-            load(c + 3, raw[1]);
+            load(gs + 3, raw[1]);
             __syncthreads();
-            if (c + 2 < nchunk) store(0, raw[0]);
-            load(c + 4, raw[0]);
+            if (gs + 2 < G) store(0, raw[0]);
+            load(gs + 4, raw[0]);
             __syncthreads();
         }
-        if (c < nchunk) __syncthreads(); // last chunk: nothing left to decode
+        if (gs < G) __syncthreads(); // last chunk: nothing left to decode
         return;
     }
 
@@ -212,84 +294,90 @@ conv_spatial_kernel(SpatialArgs a)
     constexpr int WM = 2 / MW;                        // waves per 4-pixel group
     const int wm = wave % WM, wpix = wave / WM;       // row block, pixel group
     const int wr = wpix / (PW / 4), wp = wpix % (PW / 4); // consumer pixel row, pixel group
-    f32x16_t acc[MW][4];
-#pragma unroll
-    for (int u = 0; u < MW; ++u)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[u][j][r] = 0.0f;
     const int half = lane >> 5, l32 = lane & 31;
     const int loff = lds_row_off(l32, half);
-    __syncthreads();
-    for (int c = 0; c < nchunk; ++c) {
-        const uint8_t *As = lds[c & 1], *Bs = lds[c & 1] + ABYTES;
-#pragma unroll
-        for (int th = 0; th < KHM; ++th) {
-            if (th < kh) {
-                const int hr = wr * SI + th;
-                // every column of the wave's window is read (columns past the sub-kernel's
-                // extent stay inside the LDS buffer and are never used)
-                u32x4_t bf[WCOLS];
-#pragma unroll
-                for (int cc = 0; cc < WCOLS; ++cc) {
-                    const int hc = wp * 4 * SI + cc;
-                    bf[cc] = *reinterpret_cast<const u32x4_t *>(
-                        Bs + lds_row_off32((hr * HC + hc) * 32, loff));
-                }
-#pragma unroll
-                for (int tw = 0; tw < KWM; ++tw) {
-                    if (tw < kw) {
-                        const int t = th * kw + tw;
-                        f16x8_t av[MW];
-#pragma unroll
-                        for (int u = 0; u < MW; ++u)
-                            av[u] = __builtin_bit_cast(
-                                f16x8_t, *reinterpret_cast<const u32x4_t *>(
-                                             As + lds_row_off32(t * 64 + 32 * (wm * MW + u), loff)));
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const f16x8_t b = __builtin_bit_cast(f16x8_t, bf[j * SI + tw]);
-#pragma unroll
-                            for (int u = 0; u < MW; ++u)
-                                acc[u][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[u], b, acc[u][j], 0, 0, 0);
-                        }
-                    }
-                }
-            }
-        }
-        __syncthreads();
-    }
-
-    // ---- epilogue: scale by T_in * T_w and store fp32. Buffer stores: an element outside the
-    // output gets an out-of-range offset and is dropped; the row offset of each accumulator
-    // register is a wave-uniform constant passed as soffset. ----
+    // Epilogue of every item: scale by T_in * T_w and store fp32. Buffer stores: an element
+    // outside the output gets an out-of-range offset and is dropped; the row offset of each
+    // accumulator register is a wave-uniform constant passed as soffset. The stores of one item
+    // drain while the MFMAs of the next run.
     const double sd = (double)*a.in_T * (double)*a.w_T;
     const bool fsafe = scale_is_float_safe(sd);
     const float sf = (float)sd;
     const rsrc_t out_r = make_rsrc(a.out, a.out_bytes);
-    const int i = i0 + wr;
-    const int n = nb * 32 + l32;
-    const bool full_m = 4 * m4_0 + 64 <= a.M;
+    __syncthreads();
+    int gc = 0; // chunk of the stream: LDS buffer gc & 1
+    ItemPos cp = first;
+    for (int k = 0; k < nmine; ++k, cp = advance(cp)) {
+        const int nb = cp.nb, i0 = cp.ti * PH, j0 = cp.tj * PW, m4_0 = cp.mb * 16;
+        f32x16_t acc[MW][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int jj = j0 + wp * 4 + j;
-        const bool pix_ok = i < cl.OHs && jj < cl.OWs && n < a.N;
-        const int oh = i * a.sO + cl.ah, ow = jj * a.sO + cl.aw;
+        for (int u = 0; u < MW; ++u)
 #pragma unroll
-        for (int u = 0; u < MW; ++u) {
-            const int mrow = 4 * m4_0 + 32 * (wm * MW + u) + 4 * half;
-            const uint32_t vbase =
-                pix_ok ? ((((uint32_t)oh * a.OWf + ow) * a.M + mrow) * a.N + n) * 4u : kBad;
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int dm = 8 * (r >> 2) + (r & 3);
-                const float v = fsafe ? acc[u][j][r] * sf : (float)((double)acc[u][j][r] * sd);
-                const uint32_t voff = (full_m || mrow + dm < a.M) ? vbase : kBad;
-                // non-temporal: the output is not read again by this pass (streaming writes
-                // measured ~10% faster than cached ones for this write-bound epilogue)
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), out_r,
-                                                      (int)voff, dm * a.N * 4, kStoreNT);
+                for (int r = 0; r < 16; ++r) acc[u][j][r] = 0.0f;
+        for (int c = 0; c < nchunk; ++c, ++gc) {
+            const uint8_t *As = lds[gc & 1], *Bs = lds[gc & 1] + ABYTES;
+#pragma unroll
+            for (int th = 0; th < KHM; ++th) {
+                if (th < kh) {
+                    const int hr = wr * SI + th;
+                    // every column of the wave's window is read (columns past the sub-kernel's
+                    // extent stay inside the LDS buffer and are never used)
+                    u32x4_t bf[WCOLS];
+#pragma unroll
+                    for (int cc = 0; cc < WCOLS; ++cc) {
+                        const int hc = wp * 4 * SI + cc;
+                        bf[cc] = *reinterpret_cast<const u32x4_t *>(
+                            Bs + lds_row_off32((hr * HC + hc) * 32, loff));
+                    }
+#pragma unroll
+                    for (int tw = 0; tw < KWM; ++tw) {
+                        if (tw < kw) {
+                            const int t = th * kw + tw;
+                            f16x8_t av[MW];
+#pragma unroll
+                            for (int u = 0; u < MW; ++u)
+                                av[u] = __builtin_bit_cast(
+                                    f16x8_t, *reinterpret_cast<const u32x4_t *>(
+                                                 As + lds_row_off32(t * 64 + 32 * (wm * MW + u), loff)));
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const f16x8_t b = __builtin_bit_cast(f16x8_t, bf[j * SI + tw]);
+#pragma unroll
+                                for (int u = 0; u < MW; ++u)
+                                    acc[u][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[u], b, acc[u][j], 0, 0, 0);
+                            }
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        }
+
+        const int i = i0 + wr;
+        const int n = nb * 32 + l32;
+        const bool full_m = 4 * m4_0 + 64 <= a.M;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int jj = j0 + wp * 4 + j;
+            const bool pix_ok = i < cl.OHs && jj < cl.OWs && n < a.N;
+            const int oh = i * a.sO + cl.ah, ow = jj * a.sO + cl.aw;
+#pragma unroll
+            for (int u = 0; u < MW; ++u) {
+                const int mrow = 4 * m4_0 + 32 * (wm * MW + u) + 4 * half;
+                const uint32_t vbase =
+                    pix_ok ? ((((uint32_t)oh * a.OWf + ow) * a.M + mrow) * a.N + n) * 4u : kBad;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int dm = 8 * (r >> 2) + (r & 3);
+                    const float v = fsafe ? acc[u][j][r] * sf : (float)((double)acc[u][j][r] * sd);
+                    const uint32_t voff = (full_m || mrow + dm < a.M) ? vbase : kBad;
+                    // non-temporal: the output is not read again by this pass (streaming writes
+                    // measured ~10% faster than cached ones for this write-bound epilogue)
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), out_r,
+                                                          (int)voff, dm * a.N * 4, kStoreNT);
+                }
             }
         }
     }
@@ -330,27 +418,37 @@ template <int FMT, bool A_KR, int SI, int PH, int PW, int MW>
 static hipError_t launch_spatial_tiles(SpatialArgs &a, int nclass, hipStream_t st)
 {
     constexpr int THREADS = 32 * PH * PW * (2 / MW);
-    int max_tiles = 0;
+    int max_items = 0;
     for (int c = 0; c < nclass; ++c) {
         set_tiles(a.cls[c], PH, PW);
-        if (a.cls[c].tiles > max_tiles) max_tiles = a.cls[c].tiles;
+        const int items = a.cls[c].tiles * a.nblk * ((a.M4 + 15) / 16);
+        if (items > max_items) max_items = items;
     }
-    dim3 grid((unsigned)(max_tiles * a.nblk), (unsigned)((a.M4 + 15) / 16), (unsigned)nclass);
-    const bool full3 = nclass == 1 && a.cls[0].kh == 3 && a.cls[0].kw == 3 &&
-                       a.cls[0].tiles * a.nblk == (int)grid.x;
-    if (full3)
-        hipLaunchKernelGGL((conv_spatial_kernel<FMT, A_KR, SI, PH, PW, MW, 3>), grid,
-                           dim3(THREADS), 0, st, a);
-    else
-        hipLaunchKernelGGL((conv_spatial_kernel<FMT, A_KR, SI, PH, PW, MW, 0>), grid,
-                           dim3(THREADS), 0, st, a);
+    // One class with at least 2.5 items per CU: 256 workgroups (one per CU, their LDS), each
+    // looping over items, so that one prologue serves several items and each item's output
+    // writes overlap the next item's MFMAs. With fewer items the per-chunk bookkeeping of the
+    // loop measured slower than the hardware's own dispatch of one workgroup per item, which
+    // every other case uses (also several classes, the input gradient at stride 2, whose
+    // classes differ in work per item).
+    const bool persist = nclass == 1 && max_items >= 640;
+    const int P = persist ? 256 : max_items;
+    dim3 grid((unsigned)(P > 0 ? P : 1), 1, (unsigned)nclass);
+    const bool full3 = nclass == 1 && a.cls[0].kh == 3 && a.cls[0].kw == 3;
+#define MQ_SPATIAL_LAUNCH(KFV, PV)                                                              \
+    hipLaunchKernelGGL((conv_spatial_kernel<FMT, A_KR, SI, PH, PW, MW, KFV, PV>), grid,          \
+                       dim3(THREADS), 0, st, a)
+    if (full3 && persist) MQ_SPATIAL_LAUNCH(3, true);
+    else if (full3) MQ_SPATIAL_LAUNCH(3, false);
+    else if (persist) MQ_SPATIAL_LAUNCH(0, true);
+    else MQ_SPATIAL_LAUNCH(0, false);
+#undef MQ_SPATIAL_LAUNCH
     return hipGetLastError();
 }
 
-// Workgroups of either tile shape take one CU each (their LDS), so a grid runs in
-// ceil(workgroups / 256) rounds. A 1 x 8 workgroup does half the MFMA work of a 2 x 8 one in
-// about 0.6 of its time (the stage overheads stay); the shape with the smaller modelled time
-// (rounds x time per workgroup) is taken.
+// Work items of either tile shape: the launch runs at most 256 workgroups (one per CU, their
+// LDS), so the busiest workgroup takes ceil(items / 256) items. A 1 x 8 item does half the MFMA
+// work of a 2 x 8 one in about 0.6 of its time (the per-chunk overheads stay); the shape with
+// the smaller modelled time (items per workgroup x time per item) is taken.
 static int spatial_grid_wgs(const SpatialArgs &a, int nclass, int PH, int PW)
 {
     int max_tiles = 0;

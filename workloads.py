@@ -189,4 +189,9 @@ def parity_layers() -> List[ConvLayer]:
                   x_dist="relu", seed=107, sr_seed=13),
         ConvLayer("p.5x5s1p2", N=4, Cin=8, H=10, W=10, Cout=12, Kh=5, Kw=5, stride=1, pad=2,
                   x_dist="normal", seed=108, sr_seed=14),
+        # more pixel tiles than the GPU has CUs: workgroups loop over several work items
+        ConvLayer("p.many.s1", N=8, Cin=8, H=66, W=70, Cout=12, Kh=3, Kw=3, stride=1, pad=1,
+                  x_dist="relu", seed=109, sr_seed=15),
+        ConvLayer("p.many.s2", N=4, Cin=8, H=100, W=100, Cout=8, Kh=3, Kw=3, stride=2, pad=1,
+                  x_dist="normal", seed=110, sr_seed=16),
     ]
