@@ -31,6 +31,7 @@ struct SpatialClass {
     int r0, c0;       // input offset of sub-kernel tap (0,0)
     int Ah, Bh, Aw, Bw; // weight tap row = Ah + Bh*kh', column = Aw + Bw*kw'
     int tiles_w, tiles;  // pixel tiles along the sub-grid width, total pixel tiles
+    int P, b0;           // workgroups of this class and the first one's index in the grid
 };
 
 struct SpatialArgs {
@@ -47,6 +48,7 @@ struct SpatialArgs {
     int OWf, M, N;        // output [..][OWf][M][N]
     int M4, nblk;         // row squares, batch blocks of 32
     int sO;
+    int nclass;
     SpatialClass cls[4];
 };
 
@@ -78,16 +80,21 @@ conv_spatial_kernel(SpatialArgs a)
     constexpr int ITEMS = ((KHM * KWM * 16 + 63) / 64 * 64 + HRM * HCM * 8 + NP - 1) / NP;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][ABYTES + BBYTES];
 
-    const SpatialClass &cl = a.cls[blockIdx.z];
+    // The grid holds the workgroups of every class back to back (class k from cls[k].b0 on).
+    const int bx = (int)blockIdx.x;
+    int z = 0;
+#pragma unroll
+    for (int k = 1; k < 4; ++k) z = (k < a.nclass && bx >= a.cls[k].b0) ? k : z;
+    const SpatialClass &cl = a.cls[z];
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
     // Work items of this class: (M block of 64 rows, pixel tile, batch block), batch block
-    // fastest. Workgroup b takes items b, b + gridDim.x, ...; its chunks form one stream
-    // (item-major), so the producer runs into the next item while the consumers write the
-    // current one's output.
+    // fastest. Workgroup b of the class's P takes items b, b + P, ...; its chunks form one
+    // stream (item-major), so the producer runs into the next item while the consumers write
+    // the current one's output.
     const int nmb = (a.M4 + 15) / 16;
     const int tiles_h = cl.tiles / (cl.tiles_w > 0 ? cl.tiles_w : 1);
     const int T = cl.tiles * a.nblk * nmb;
-    const int P = (int)gridDim.x, b = (int)blockIdx.x;
+    const int P = cl.P, b = bx - cl.b0;
     // PERSIST: each workgroup loops over several items; otherwise one item per workgroup
     const int nmine = b < T ? (PERSIST ? (T - 1 - b) / P + 1 : 1) : 0;
     // Item w = ((mb * tiles_h + ti) * tiles_w + tj) * nblk + nb, stepped by P in that mixed radix
@@ -418,21 +425,39 @@ template <int FMT, bool A_KR, int SI, int PH, int PW, int MW>
 static hipError_t launch_spatial_tiles(SpatialArgs &a, int nclass, hipStream_t st)
 {
     constexpr int THREADS = 32 * PH * PW * (2 / MW);
-    int max_items = 0;
+    int items[4] = {0, 0, 0, 0}, total = 0;
+    double work[4] = {0, 0, 0, 0}, total_work = 0;
     for (int c = 0; c < nclass; ++c) {
         set_tiles(a.cls[c], PH, PW);
-        const int items = a.cls[c].tiles * a.nblk * ((a.M4 + 15) / 16);
-        if (items > max_items) max_items = items;
+        items[c] = a.cls[c].tiles * a.nblk * ((a.M4 + 15) / 16);
+        total += items[c];
+        // per item: MFMA work in taps plus the per-chunk staging (the halo is decoded whatever
+        // the tap count) and the output write, about six taps' worth
+        work[c] = (double)items[c] * (a.cls[c].kh * a.cls[c].kw + 6);
+        total_work += work[c];
     }
-    // One class with at least 2.5 items per CU: 256 workgroups (one per CU, their LDS), each
-    // looping over items, so that one prologue serves several items and each item's output
-    // writes overlap the next item's MFMAs. With fewer items the per-chunk bookkeeping of the
-    // loop measured slower than the hardware's own dispatch of one workgroup per item, which
-    // every other case uses (also several classes, the input gradient at stride 2, whose
-    // classes differ in work per item).
-    const bool persist = nclass == 1 && max_items >= 640;
-    const int P = persist ? 256 : max_items;
-    dim3 grid((unsigned)(P > 0 ? P : 1), 1, (unsigned)nclass);
+    // With at least 2.5 items per CU (4 when the classes of a stride-2 input gradient share the
+    // CUs: their items differ in cost): 256 persistent workgroups (one per CU, their LDS),
+    // shared among the classes by their work, each looping over items of its class, so that one
+    // prologue serves several items and each item's output writes overlap the next item's
+    // MFMAs. With fewer items the per-chunk bookkeeping of the loop, or an uneven split among
+    // classes, measured slower than the hardware's own dispatch of one workgroup per item,
+    // which is used then.
+    const bool persist = total >= (nclass == 1 ? 640 : 1024);
+    int nwg = 0;
+    for (int c = 0; c < nclass; ++c) {
+        int P = items[c];
+        if (persist) {
+            P = (int)(256.0 * work[c] / total_work);
+            P = P < 1 ? 1 : (P > items[c] ? items[c] : P);
+        }
+        a.cls[c].P = P;
+        a.cls[c].b0 = nwg;
+        nwg += P;
+    }
+    a.nclass = nclass;
+    if (nwg == 0) return hipSuccess;
+    dim3 grid((unsigned)nwg, 1, 1);
     const bool full3 = nclass == 1 && a.cls[0].kh == 3 && a.cls[0].kw == 3;
 #define MQ_SPATIAL_LAUNCH(KFV, PV)                                                              \
     hipLaunchKernelGGL((conv_spatial_kernel<FMT, A_KR, SI, PH, PW, MW, KFV, PV>), grid,          \
