@@ -3,8 +3,9 @@
 
 One step = one pass of the whole hot path over one batch of synthetic input, for the ResNet-style
 3x3 layer (N=32, Cin=Cout=64, 56x56, stride 1, pad 1, NVFP4): relayout X (NCHW -> channel-batch
-first) and W (OIHW -> tap-major), quantize X and W (round-to-nearest) and G_Y (stochastic, a new
-seed every step), then the forward, weight-gradient and input-gradient GEMMs. Inputs are resident
+first) and quantize it (round-to-nearest), quantize W from OIHW into its tap-major squares
+(round-to-nearest, one call), quantize G_Y (stochastic, a new seed every step), then the forward,
+weight-gradient and input-gradient GEMMs. Inputs are resident
 in HBM before the timed region starts.
 
 The timed steps call the C ABI back to back on one stream (arguments marshalled once, so the
@@ -40,10 +41,11 @@ CALIB_ELEMS = 1 << 26        # plain copy for counter calibration: 256 MiB read 
 
 # which kernels make up each op (rocprofv3 kernel names start with these)
 OP_KERNELS = {
-    "relayout_x": ["mq::transpose_kernel"], "relayout_w": ["mq::transpose_kernel"],
-    "quantize_x": ["mq::zero_u32_kernel", "mq::amax_kernel", "void mq::quantize_kernel"],
-    "quantize_w": ["mq::zero_u32_kernel", "mq::amax_kernel", "void mq::quantize_kernel"],
-    "quantize_g": ["mq::zero_u32_kernel", "mq::amax_kernel", "void mq::quantize_kernel"],
+    "relayout_x": ["void mq::transpose4_kernel", "void mq::transpose_kernel"],
+    "quantize_x": ["void mq::quantize_kernel"],
+    "quantize_w": ["void mq::quantize_weight_small_kernel", "mq::amax_kernel",
+                   "void mq::quantize_kernel"],
+    "quantize_g": ["mq::amax_kernel", "void mq::quantize_kernel"],
     "conv_fwd": ["void mq::conv_spatial_kernel<4, false"],
     "conv_wgrad": ["void mq::conv_wgrad_kernel", "mq::wgrad_sum_kernel"],
     "conv_dgrad": ["void mq::conv_spatial_kernel<4, true"],
@@ -75,6 +77,9 @@ def parse():
                     help="time a full training step of ResNet-18 (19 body convolutions on the "
                          "library, the rest in PyTorch fp32)")
     ap.add_argument("--batch", type=int, default=128, help="batch size of --network")
+    ap.add_argument("--inference", action="store_true",
+                    help="with --config: the inference path only (relayout and quantize X, "
+                         "conv fwd; the weights are quantized once before timing)")
     return ap.parse_args()
 
 
@@ -154,7 +159,7 @@ def main():
     # (amax ready from the relayout) = one read + codes/scales; quantize of G_Y = amax read +
     # quantize read + codes/scales
     alg = {
-        "relayout_x": ("hbm", 8 * nx), "relayout_w": ("hbm", 8 * nw),
+        "relayout_x": ("hbm", 8 * nx),
         "quantize_x": ("hbm", 4 * nx + qx_b), "quantize_w": ("hbm", 4 * nw + qw_b),
         "quantize_g": ("hbm", 8 * ng + qg_b),
         "conv_fwd": ("gemm", flops), "conv_wgrad": ("gemm", flops), "conv_dgrad": ("gemm", flops),
@@ -298,8 +303,8 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic (seeded numpy PCG64; X=ReLU(N(0,1)), W Kaiming-normal, G_Y~N(0,1e-3))",
-        "config": {"workload": "resnet-3x3-s1p1 N=32 Cin=Cout=64 56x56 NVFP4: relayout x2, "
-                               "quantize x3 (RNE, RNE, SR), conv fwd/wgrad/dgrad",
+        "config": {"workload": "resnet-3x3-s1p1 N=32 Cin=Cout=64 56x56 NVFP4: relayout X, "
+                               "quantize X, W, G_Y (RNE, RNE, SR), conv fwd/wgrad/dgrad",
                    "N": N, "Cin": Ci, "Cout": Co, "H": H, "W": W, "K": Kh, "stride": 1, "pad": 1,
                    "format": "NVFP4 (E2M1 codes, E4M3 4x4-square scales, fp32 tensor scale)",
                    "mfma": "fp16 operands decoded exactly, fp32 accumulate"},
@@ -379,6 +384,9 @@ def run_config(args):
             for f in calls.values():
                 f(s_)
         torch.cuda.synchronize()
+        if args.inference:  # W stays quantized from the warm-up: activations only
+            calls = collections.OrderedDict((k, calls[k]) for k in
+                                            ("relayout_x", "quantize_x", "conv_fwd"))
         eb = 0.5625 if l.fmt == 4 else 0.8125
         nx, nw, ng = l.N * l.Cin * l.H * l.W, l.Cout * l.Cin * l.Kh * l.Kw, l.N * l.Cout * l.Ho * l.Wo
         fl = l.gemm_flops()
@@ -403,7 +411,7 @@ def run_config(args):
         fns = list(calls.values())
         ms_layer = _time_graph(fns, max(2, args.op_reps // 4), stream)
         step_ms += ms_layer * len(ls)
-        flops_total += 3 * fl * len(ls)
+        flops_total += (1 if args.inference else 3) * fl * len(ls)
         per_layer.append({"layers": [x_.name for x_ in ls], "shape": {
             "N": l.N, "Cin": l.Cin, "Cout": l.Cout, "H": l.H, "W": l.W, "K": l.Kh,
             "stride": l.stride, "pad": l.pad, "format": f"NVFP{l.fmt}"},
@@ -421,8 +429,11 @@ def run_config(args):
         "higher_is_better": True,
         "dtype": "fp16",
         "data": "synthetic (seeded numpy PCG64, the workload's value distributions)",
-        "config": {"workload": f"{args.config}: {len(layers)} layers, relayout x2, quantize x3, "
-                               f"conv fwd/wgrad/dgrad each"},
+        "config": {"workload": (f"{args.config} inference: {len(layers)} layers, relayout and "
+                                f"quantize X, conv fwd each (weights quantized once)")
+                   if args.inference else
+                   (f"{args.config}: {len(layers)} layers, relayout X, quantize X/W/G_Y, "
+                    f"conv fwd/wgrad/dgrad each")},
         "per_layer": per_layer,
     }
     print(json.dumps(result), flush=True)

@@ -167,6 +167,26 @@ mq_status mq_quantize(const float *src_dev, const mq_qtensor *dst, int32_t rnd, 
                       hipStream_t stream);
 
 /*
+ * mq_quantize_weight: quantize an OIHW fp32 weight straight into the tap-major quantized layout
+ * [Kh][Kw][Cout][Cin] of the 2-D weight matrix (onedev.kr digest, section "How it differs"),
+ * with the same amax, T, square scales and codes as mq_relayout_weight followed by mq_quantize
+ * on its output (the recipe above), without writing the fp32 tap-major copy. A weight of at
+ * most 40448 elements takes one launch of one workgroup (the tensor staged in LDS); a larger one
+ * runs the amax pass into amax_ws_dev and a quantizer that gathers from OIHW.
+ * w_oihw_dev: Cout*Cin*Kh*Kw floats, [co][ci][kh][kw].
+ * dst:     role MQ_ROLE_WEIGHT with (o0, o1, r, s) = (Kh, Kw, Cout, Cin).
+ * rnd, seed: as for mq_quantize.
+ * amax_ws_dev / amax_ws_bytes: a tensor-amax workspace (overwritten; untouched for a small
+ *          weight, but required either way).
+ * Errors: MQ_ERR_ARG (null pointer, bad enum, misaligned pointer), MQ_ERR_SHAPE (dst role not
+ *         MQ_ROLE_WEIGHT), MQ_ERR_WORKSPACE (workspace null or smaller than
+ *         MQ_QUANTIZE_WS_BYTES), MQ_ERR_UNSUPPORTED (2^31 squares or more).
+ */
+mq_status mq_quantize_weight(const float *w_oihw_dev, const mq_qtensor *dst, int32_t rnd,
+                             uint64_t seed, uint32_t *amax_ws_dev, size_t amax_ws_bytes,
+                             hipStream_t stream);
+
+/*
  * mq_conv_fwd: forward GEMM Y = W . X' (onedev.kr digest, section "How it differs") with the
  * im2col matrix X' formed on chip from the channel-batch-first quantized X (section "How it
  * works"):

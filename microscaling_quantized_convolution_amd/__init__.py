@@ -25,7 +25,8 @@ MQ_QUANTIZE_AMAX_READY = 1   # mq_quantize flag: the workspace already holds thi
 
 EXPORTS = (
     "mq_status_str", "mq_codes_bytes", "mq_scales_bytes", "mq_relayout_cbf",
-    "mq_relayout_weight", "mq_quantize", "mq_conv_fwd", "mq_wgrad_workspace_bytes",
+    "mq_relayout_weight", "mq_quantize", "mq_quantize_weight", "mq_conv_fwd",
+    "mq_wgrad_workspace_bytes",
     "mq_conv_wgrad", "mq_conv_dgrad",
 )
 
@@ -63,6 +64,7 @@ def _load() -> ctypes.CDLL:
     L.mq_relayout_cbf.argtypes = [P, P, i32, i32, i32, i32, i32, P, sz, P]
     L.mq_relayout_weight.argtypes = [P, P, i32, i32, i32, i32, i32, P, sz, P]
     L.mq_quantize.argtypes = [P, ctypes.POINTER(mq_qtensor), i32, u64, P, sz, ctypes.c_uint32, P]
+    L.mq_quantize_weight.argtypes = [P, ctypes.POINTER(mq_qtensor), i32, u64, P, sz, P]
     L.mq_conv_fwd.argtypes = [ctypes.POINTER(mq_conv), ctypes.POINTER(mq_qtensor),
                               ctypes.POINTER(mq_qtensor), P, P]
     L.mq_wgrad_workspace_bytes.restype = sz
@@ -165,6 +167,16 @@ def mq_quantize(src: torch.Tensor, dst: QTensor, rnd: int, seed: int, amax_ws: t
     _check(_lib.mq_quantize(_ptr(src), ctypes.byref(q), rnd, seed & (2 ** 64 - 1),
                             _ptr(amax_ws), _nbytes(amax_ws), flags, _stream(stream)),
            "mq_quantize")
+
+
+def mq_quantize_weight(w_oihw: torch.Tensor, dst: QTensor, rnd: int, seed: int,
+                       amax_ws: torch.Tensor, stream=None):
+    """OIHW fp32 weight -> quantized tap-major weight (same result as mq_relayout_weight then
+    mq_quantize, without the fp32 copy)."""
+    q = dst.struct()
+    _check(_lib.mq_quantize_weight(_ptr(w_oihw), ctypes.byref(q), rnd, seed & (2 ** 64 - 1),
+                                   _ptr(amax_ws), _nbytes(amax_ws), _stream(stream)),
+           "mq_quantize_weight")
 
 
 def mq_conv_fwd(p: ConvLike, x: QTensor, w: QTensor, y: torch.Tensor, stream=None):

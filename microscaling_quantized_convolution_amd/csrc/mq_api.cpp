@@ -138,6 +138,19 @@ mq_status mq_quantize(const float *src, const mq_qtensor *dst, int32_t rnd, uint
                                              (flags & MQ_QUANTIZE_AMAX_READY) != 0, stream));
 }
 
+mq_status mq_quantize_weight(const float *w, const mq_qtensor *dst, int32_t rnd, uint64_t seed,
+                             uint32_t *amax_ws, size_t amax_ws_bytes, hipStream_t stream)
+{
+    if (!w || !qtensor_ok(dst) || (rnd != MQ_RNE && rnd != MQ_SR)) return MQ_ERR_ARG;
+    if (dst->role != MQ_ROLE_WEIGHT) return MQ_ERR_SHAPE;
+    if (!amax_ws || amax_ws_bytes < MQ_QUANTIZE_WS_BYTES) return MQ_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(amax_ws) & 3u) != 0) return MQ_ERR_ARG;
+    if (squares(dst->o0, dst->o1, dst->r, dst->s) >= ((int64_t)1 << 31)) return MQ_ERR_UNSUPPORTED;
+    return launch_status(mq::launch_quantize_weight(w, dst->r, dst->s, dst->o0, dst->o1, dst->fmt,
+                                                    rnd, seed, dst->codes, dst->scales,
+                                                    dst->tscale, amax_ws, stream));
+}
+
 mq_status mq_conv_fwd(const mq_conv *p, const mq_qtensor *x, const mq_qtensor *w, float *y,
                       hipStream_t stream)
 {

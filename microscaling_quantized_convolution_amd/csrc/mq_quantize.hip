@@ -95,9 +95,107 @@ struct QuantArgs {
     uint32_t seed_lo, seed_hi;
 };
 
+// One square: 16 values in row-major order (slots outside the tensor hold 0) -> the E4M3
+// scale byte (returned) and 16 codes (sign | magnitude). T is the tensor scale; nonfinite: the
+// tensor amax is Inf or NaN (scale 0x7F, codes 0). r0, r1: the square's Philox draws (SR only).
+template <int FMT, bool SR>
+__device__ __forceinline__ uint32_t quantize_square(const float (&x)[16], float T, bool nonfinite,
+                                                    const Philox4 &r0, const Philox4 &r1,
+                                                    uint32_t (&code)[16])
+{
+    using F = Fmt<FMT>;
+    uint32_t bcode;
+    if (nonfinite) {
+        bcode = 0x7Fu;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) code[e] = 0u;
+    } else {
+        float bmax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) bmax = fmaxf(bmax, fabsf(x[e]));
+        const float TE = T * F::kEmax;
+        // T == 0 only for an all-zero (or vanishingly small) tensor: scales 0, codes 0.
+        bcode = (T == 0.0f) ? 0u : e4m3_rne_sat(bmax / TE);
+        const float B = e4m3_to_float(bcode);
+        const float D = B * T;
+        const bool zero = (bcode == 0u) || (D == 0.0f);
+        // x / D for 16 elements from one reciprocal: with rD = RN(1/D), q0 = RN(x * rD) and the
+        // exact residual x - q0 * D, RN(q0 + residual * rD) is the correctly rounded quotient
+        // (Markstein's theorem) as long as nothing underflows: D within 2^+-64 and
+        // |x / D| >= 2^-20 (or x = 0). A square with any other element (a tiny one, whose code
+        // only the round-up draw of stochastic rounding could tell apart) divides instead.
+        float q[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) q[e] = 0.0f;
+        if (!zero) {
+            const float rD = 1.0f / D;
+            const float Dlo = D * 0x1p-20f;
+            bool slow = !(D >= 0x1p-64f && D <= 0x1p64f);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float ax = fabsf(x[e]);
+                slow |= (ax < Dlo) && (ax != 0.0f);
+            }
+            if (slow) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) q[e] = x[e] / D; // IEEE division
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float q0 = x[e] * rD;
+                    q[e] = __builtin_fmaf(__builtin_fmaf(-q0, D, x[e]), rD, q0);
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float aq = fabsf(q[e]);
+            uint32_t mag;
+            if (SR) {
+                const uint32_t w = (e < 8) ? r0.v[(e & 7) >> 1] : r1.v[(e & 7) >> 1];
+                const uint32_t u16 = (w >> (16 * (e & 1))) & 0xFFFFu;
+                mag = grid_sr<FMT>(aq, u16);
+            } else {
+                mag = grid_rne<FMT>(aq);
+            }
+            const uint32_t c = mag | ((__float_as_uint(x[e]) >> 31) ? F::kSign : 0u);
+            code[e] = zero ? 0u : c; // a zero scale holds +0 codes
+        }
+    }
+    return bcode;
+}
+
+// Pack 16 codes of square t: 8 bytes (NVFP4, element e in nibble e) or 12 bytes (NVFP6,
+// element e at bits 6e .. 6e+5 of the 96-bit little-endian word).
+template <int FMT>
+__device__ __forceinline__ void store_square_codes(uint8_t *codes, int64_t t, const uint32_t (&code)[16])
+{
+    if (FMT == kFP4) {
+        uint32_t w0 = 0u, w1 = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            w0 |= code[e] << (4 * e);
+            w1 |= code[e + 8] << (4 * e);
+        }
+        *reinterpret_cast<uint2 *>(codes + 8 * t) = make_uint2(w0, w1);
+    } else {
+        uint32_t w[3] = {0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int bit = 6 * e;
+            w[bit >> 5] |= code[e] << (bit & 31);
+            if ((bit & 31) > 26) w[(bit >> 5) + 1] |= code[e] >> (32 - (bit & 31));
+        }
+        uint32_t *dst = reinterpret_cast<uint32_t *>(codes + 12 * t);
+        dst[0] = w[0]; dst[1] = w[1]; dst[2] = w[2];
+    }
+}
+
 // One lane per 4x4 square. FULL = every square lies entirely inside [R][S] and S % 4 == 0, so
-// the four rows are aligned float4 loads.
-template <int FMT, bool SR, bool FULL>
+// the four rows are aligned float4 loads. OIHW: the source is a weight in OIHW order (plane =
+// kh*Kw + kw, R = Cout, S = Cin): element (plane, r, s) is read from src[(r*S + s)*planes +
+// plane], so the tap-major fp32 copy is never written.
+template <int FMT, bool SR, bool FULL, bool OIHW = false>
 __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a)
 {
     using F = Fmt<FMT>;
@@ -138,7 +236,16 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a)
     auto load = [&](Pos p, float (&x)[16]) {
         const int s4 = p.s4, r4 = p.r4;
         const int64_t base = ((int64_t)p.plane * a.R + 4 * r4) * (int64_t)a.S + 4 * s4;
-        if (FULL) {
+        if (OIHW) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 4 * r4 + i, c = 4 * s4 + j;
+                    const bool in = r < a.R && c < a.S;
+                    x[4 * i + j] = in ? a.src[((int64_t)r * a.S + c) * a.planes + p.plane] : 0.0f;
+                }
+        } else if (FULL) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 f32x4_t v = __builtin_nontemporal_load(
@@ -169,101 +276,28 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a)
         const bool more = t + stride < nsq;
         if (more) pos = advance(pos);
         load(pos, xn); // the last step reloads its own square
+        // The square's random bits do not depend on its values: drawn here, the Philox rounds
+        // run while the square's loads are still in flight.
+        Philox4 r0 = {}, r1 = {};
+        if (SR) {
+            const uint64_t j = 2u * (uint64_t)t;
+            r0 = philox4x32_10((uint32_t)j, (uint32_t)(j >> 32), 0u, 0u, a.seed_lo, a.seed_hi);
+            r1 = philox4x32_10((uint32_t)(j + 1), (uint32_t)((j + 1) >> 32), 0u, 0u, a.seed_lo,
+                               a.seed_hi);
+        }
         const int s4 = cur.s4, r4 = cur.r4;
         uint32_t code[16];
-        uint32_t bcode;
-        if (nonfinite) {
-            bcode = 0x7Fu;
+        const uint32_t bcode = quantize_square<FMT, SR>(x, T, nonfinite, r0, r1, code);
+        if (!FULL) { // padded slots hold code 0
 #pragma unroll
-            for (int e = 0; e < 16; ++e) code[e] = 0u;
-        } else {
-            float bmax = 0.0f;
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) bmax = fmaxf(bmax, fabsf(x[e]));
-            const float TE = T * F::kEmax;
-            // T == 0 only for an all-zero (or vanishingly small) tensor: scales 0, codes 0.
-            bcode = (T == 0.0f) ? 0u : e4m3_rne_sat(bmax / TE);
-            const float B = e4m3_to_float(bcode);
-            const float D = B * T;
-            const bool zero = (bcode == 0u) || (D == 0.0f);
-            // x / D for 16 elements from one reciprocal: with rD = RN(1/D), q0 = RN(x * rD) and the
-            // exact residual x - q0 * D, RN(q0 + residual * rD) is the correctly rounded quotient
-            // (Markstein's theorem) as long as nothing underflows: D within 2^+-64 and
-            // |x / D| >= 2^-20 (or x = 0). A square with any other element (a tiny one, whose code
-            // only the round-up draw of stochastic rounding could tell apart) divides instead.
-            float q[16];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) q[e] = 0.0f;
-            if (!zero) {
-                const float rD = 1.0f / D;
-                const float Dlo = D * 0x1p-20f;
-                bool slow = !(D >= 0x1p-64f && D <= 0x1p64f);
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float ax = fabsf(x[e]);
-                    slow |= (ax < Dlo) && (ax != 0.0f);
-                }
-                if (slow) {
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) q[e] = x[e] / D; // IEEE division
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const float q0 = x[e] * rD;
-                        q[e] = __builtin_fmaf(__builtin_fmaf(-q0, D, x[e]), rD, q0);
-                    }
-                }
-            }
-            Philox4 r0 = {}, r1 = {};
-            if (SR && !zero) {
-                const uint64_t j = 2u * (uint64_t)t;
-                r0 = philox4x32_10((uint32_t)j, (uint32_t)(j >> 32), 0u, 0u, a.seed_lo, a.seed_hi);
-                r1 = philox4x32_10((uint32_t)(j + 1), (uint32_t)((j + 1) >> 32), 0u, 0u, a.seed_lo,
-                                   a.seed_hi);
-            }
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float aq = fabsf(q[e]);
-                uint32_t mag;
-                if (SR) {
-                    const uint32_t w = (e < 8) ? r0.v[(e & 7) >> 1] : r1.v[(e & 7) >> 1];
-                    const uint32_t u16 = (w >> (16 * (e & 1))) & 0xFFFFu;
-                    mag = grid_sr<FMT>(aq, u16);
-                } else {
-                    mag = grid_rne<FMT>(aq);
-                }
-                const uint32_t c = mag | ((__float_as_uint(x[e]) >> 31) ? F::kSign : 0u);
-                code[e] = zero ? 0u : c; // a zero scale holds +0 codes
-            }
-            if (!FULL) { // padded slots hold code 0
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (!((4 * r4 + i < a.R) && (4 * s4 + j < a.S))) code[4 * i + j] = 0u;
-            }
+                for (int j = 0; j < 4; ++j)
+                    if (!((4 * r4 + i < a.R) && (4 * s4 + j < a.S))) code[4 * i + j] = 0u;
         }
 
         a.scales[t] = (uint8_t)bcode;
-        if (FMT == kFP4) {
-            uint32_t w0 = 0u, w1 = 0u;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                w0 |= code[e] << (4 * e);
-                w1 |= code[e + 8] << (4 * e);
-            }
-            *reinterpret_cast<uint2 *>(a.codes + 8 * (int64_t)t) = make_uint2(w0, w1);
-        } else {
-            uint32_t w[3] = {0u, 0u, 0u};
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int bit = 6 * e;
-                w[bit >> 5] |= code[e] << (bit & 31);
-                if ((bit & 31) > 26) w[(bit >> 5) + 1] |= code[e] >> (32 - (bit & 31));
-            }
-            uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes + 12 * (int64_t)t);
-            dst[0] = w[0]; dst[1] = w[1]; dst[2] = w[2];
-        }
+        store_square_codes<FMT>(a.codes, t, code);
     }
 }
 
@@ -278,6 +312,115 @@ static hipError_t launch_quant(const QuantArgs &a, bool full, hipStream_t st)
     else
         hipLaunchKernelGGL((quantize_kernel<FMT, SR, false>), dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
+}
+
+// A small weight (at most kSmallWeight floats), from OIHW fp32 to quantized tap-major squares in
+// one launch: every workgroup reduces the whole tensor's amax itself (1024 lanes, a few 16-byte
+// loads each; no step across workgroups, no workspace), then its first kSmallSquares lanes
+// quantize one square each, gathered from OIHW, with the same arithmetic as quantize_kernel.
+constexpr int kSmallWeight = 65536;
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallSquares = 64;
+
+template <int FMT, bool SR>
+__global__ void __launch_bounds__(kSmallThreads) quantize_weight_small_kernel(QuantArgs a)
+{
+    using F = Fmt<FMT>;
+    __shared__ uint32_t red[kSmallThreads / 64];
+    const int n = (int)(a.planes * a.R * a.S);
+    uint32_t m = 0u;
+    int tail = 0;
+    if ((reinterpret_cast<uintptr_t>(a.src) & 15u) == 0) {
+        const int n4 = n >> 2;
+        const u32x4_t *x4 = reinterpret_cast<const u32x4_t *>(a.src);
+        int j = threadIdx.x;
+        for (; j + 7 * kSmallThreads < n4; j += 8 * kSmallThreads) {
+            u32x4_t v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = x4[j + k * kSmallThreads];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) m = max(m, absmax4(v[k]));
+        }
+        for (; j < n4; j += kSmallThreads) m = max(m, absmax4(x4[j]));
+        tail = n4 << 2;
+    }
+    for (int j = tail + threadIdx.x; j < n; j += kSmallThreads)
+        m = max(m, __float_as_uint(a.src[j]) & 0x7FFFFFFFu);
+    const uint32_t abits = block_max_u32<kSmallThreads>(m, red);
+    const bool nonfinite = abits >= 0x7F800000u;
+    const float T = __uint_as_float(abits) / (448.0f * F::kEmax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.tscale = nonfinite ? __uint_as_float(0x7FC00000u) : T;
+    const int t = (int)blockIdx.x * kSmallSquares + (int)threadIdx.x;
+    if (threadIdx.x >= kSmallSquares || t >= (int)a.nsq) return;
+    const int planes = (int)a.planes;
+    const int s4 = t % a.S4, r4 = (t / a.S4) % a.R4, plane = t / a.S4 / a.R4;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * r4 + i, c = 4 * s4 + j;
+            const bool in = r < a.R && c < a.S;
+            x[4 * i + j] = in ? a.src[(r * a.S + c) * planes + plane] : 0.0f;
+        }
+    Philox4 r0 = {}, r1 = {};
+    if (SR) {
+        const uint64_t jj = 2u * (uint64_t)t;
+        r0 = philox4x32_10((uint32_t)jj, (uint32_t)(jj >> 32), 0u, 0u, a.seed_lo, a.seed_hi);
+        r1 = philox4x32_10((uint32_t)(jj + 1), (uint32_t)((jj + 1) >> 32), 0u, 0u, a.seed_lo,
+                           a.seed_hi);
+    }
+    uint32_t code[16];
+    const uint32_t bcode = quantize_square<FMT, SR>(x, T, nonfinite, r0, r1, code);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (!((4 * r4 + i < a.R) && (4 * s4 + j < a.S))) code[4 * i + j] = 0u;
+    a.scales[t] = (uint8_t)bcode;
+    store_square_codes<FMT>(a.codes, t, code);
+}
+
+template <int FMT, bool SR>
+static hipError_t launch_quant_weight(const QuantArgs &a, uint32_t *amax_ws, hipStream_t st)
+{
+    const int64_t n = a.planes * a.R * a.S;
+    if (n <= kSmallWeight) {
+        hipLaunchKernelGGL((quantize_weight_small_kernel<FMT, SR>),
+                           dim3((unsigned)((a.nsq + kSmallSquares - 1) / kSmallSquares)),
+                           dim3(kSmallThreads), 0, st, a);
+        return hipGetLastError();
+    }
+    // larger: the amax pass over the OIHW array (same values), then the gathering quantizer
+    const int64_t want = (n / 4 + 8 * kAmaxThreads - 1) / (8 * kAmaxThreads);
+    const int parts = (int)(want < 1 ? 1 : (want > kAmaxParts ? kAmaxParts : want));
+    hipLaunchKernelGGL(amax_kernel, dim3(parts), dim3(kAmaxThreads), 0, st, a.src, n, amax_ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    QuantArgs b = a;
+    b.amax_ws = amax_ws;
+    const int64_t wantq = (a.nsq + 255) / 256;
+    const unsigned blocks = (unsigned)(wantq < kQuantBlocks ? wantq : kQuantBlocks);
+    hipLaunchKernelGGL((quantize_kernel<FMT, SR, false, true>), dim3(blocks), dim3(256), 0, st, b);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_weight(const float *src, int Cout, int Cin, int Kh, int Kw, int fmt,
+                                  int rnd, uint64_t seed, uint8_t *codes, uint8_t *scales,
+                                  float *tscale, uint32_t *amax_ws, hipStream_t st)
+{
+    QuantArgs a;
+    a.src = src; a.codes = codes; a.scales = scales; a.tscale = tscale;
+    a.amax_ws = amax_ws;
+    a.planes = (int64_t)Kh * Kw; a.R = Cout; a.S = Cin; a.R4 = (Cout + 3) / 4; a.S4 = (Cin + 3) / 4;
+    a.nsq = a.planes * a.R4 * a.S4;
+    if (a.nsq >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    a.seed_lo = (uint32_t)seed; a.seed_hi = (uint32_t)(seed >> 32);
+    if (fmt == kFP4)
+        return rnd ? launch_quant_weight<kFP4, true>(a, amax_ws, st)
+                   : launch_quant_weight<kFP4, false>(a, amax_ws, st);
+    return rnd ? launch_quant_weight<kFP6, true>(a, amax_ws, st)
+               : launch_quant_weight<kFP6, false>(a, amax_ws, st);
 }
 
 hipError_t launch_quantize(const float *src, int64_t planes, int R, int S, int fmt, int rnd,

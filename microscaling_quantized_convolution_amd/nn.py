@@ -5,7 +5,7 @@ through the library, following the onedev.kr MicroQonv digest (sections "How it 
 differs"):
 
   forward   X (NCHW) -> channel-batch-first copy (+ amax partials) -> quantize once (RNE)
-            W (OIHW) -> tap-major copy (+ amax partials)            -> quantize once (RNE)
+            W (OIHW) -> quantized tap-major squares in one call       (quantize once, RNE)
             Y = conv_fwd(Xq, Wq), back to NCHW
   backward  G_Y (NCHW) -> channel-batch-first copy (+ amax partials) -> quantize once (SR)
             G_W = conv_wgrad(G_Yq, Xq) (the forward's Xq is kept, not re-quantized)
@@ -34,8 +34,8 @@ from torch import nn
 
 from . import (MQ_NVFP4, MQ_QUANTIZE_AMAX_READY, MQ_QUANTIZE_WS_BYTES, MQ_ROLE_ACT, MQ_ROLE_GRAD,
                MQ_ROLE_WEIGHT, MQ_RNE, MQ_SR, QTensor, mq_conv_dgrad, mq_conv_fwd,
-               mq_conv_wgrad, mq_quantize, mq_relayout_cbf, mq_relayout_weight,
-               mq_wgrad_workspace_bytes, out_hw)
+               mq_conv_wgrad, mq_quantize, mq_quantize_weight, mq_relayout_cbf,
+               mq_relayout_weight, mq_wgrad_workspace_bytes, out_hw)
 
 
 def _check_input(t: torch.Tensor, what: str, ndim: int = 4):
@@ -45,12 +45,10 @@ def _check_input(t: torch.Tensor, what: str, ndim: int = 4):
 
 
 def quantize_weight(weight: torch.Tensor, fmt: int, ws: torch.Tensor) -> QTensor:
-    """OIHW fp32 weight -> quantized tap-major weight (relayout with amax, then RNE)."""
+    """OIHW fp32 weight -> quantized tap-major weight (RNE), one library call."""
     Cout, Cin, Kh, Kw = weight.shape
-    wc = torch.empty(Kh * Kw * Cout * Cin, dtype=torch.float32, device=weight.device)
-    mq_relayout_weight(weight, wc, Cout, Cin, Kh, Kw, 0, amax_ws=ws)
     qw = QTensor(Kh, Kw, Cout, Cin, fmt, MQ_ROLE_WEIGHT, weight.device)
-    mq_quantize(wc, qw, MQ_RNE, 0, ws, MQ_QUANTIZE_AMAX_READY)
+    mq_quantize_weight(weight, qw, MQ_RNE, 0, ws)
     return qw
 
 

@@ -4,11 +4,12 @@ Device buffers for one layer (fp32 inputs, their channel-batch-first copies, the
 tensors, the outputs and the weight-gradient workspace) and the calls of one pass, in order:
 
   relayout_x   X NCHW -> CBF (+ amax partials)   quantize_x  X (round to nearest)
-  relayout_w   W OIHW -> tap-major (+ amax)      quantize_w  W (round to nearest)
+  quantize_w   W OIHW -> quantized tap-major squares (round to nearest), one call
   quantize_g   G_Y (stochastic, seed per pass)   conv_fwd / conv_wgrad / conv_dgrad
 
-The relayouts write the tensor-amax partials of X and W, so their quantizations skip the amax
-pass (MQ_QUANTIZE_AMAX_READY); G_Y's quantization runs its own.
+The relayout of X writes its tensor-amax partials, so X's quantization skips the amax pass
+(MQ_QUANTIZE_AMAX_READY). W goes from OIHW to its quantized tap-major layout in one call
+(mq_quantize_weight: no fp32 tap-major copy). G_Y's quantization runs its own amax pass.
 
 G_Y is taken as already channel-batch-first (it is the next layer's input-gradient output).
 Every call goes through the C ABI on the current stream; nothing here computes.
@@ -22,8 +23,8 @@ import torch
 
 from . import (MQ_QUANTIZE_AMAX_READY, MQ_QUANTIZE_WS_BYTES, MQ_ROLE_ACT, MQ_ROLE_GRAD,
                MQ_ROLE_WEIGHT, MQ_RNE, MQ_SR, QTensor, conv_struct,
-               mq_conv_dgrad, mq_conv_fwd, mq_conv_wgrad, mq_quantize, mq_relayout_cbf,
-               mq_relayout_weight, mq_wgrad_workspace_bytes, out_hw)
+               mq_conv_dgrad, mq_conv_fwd, mq_conv_wgrad, mq_quantize, mq_quantize_weight,
+               mq_relayout_cbf, mq_wgrad_workspace_bytes, out_hw)
 
 
 class LayerStep:
@@ -40,7 +41,6 @@ class LayerStep:
         self.x, self.w, self.gc = x, w, g_cbf
         f32 = dict(dtype=torch.float32, device=dev)
         self.xc = torch.empty(c.H * c.W * c.Cin * c.N, **f32)
-        self.wc = torch.empty(c.Kh * c.Kw * c.Cout * c.Cin, **f32)
         nws = MQ_QUANTIZE_WS_BYTES
         self.amax = torch.empty(3 * nws, dtype=torch.uint8, device=dev)
         self.qx = QTensor(c.H, c.W, c.Cin, c.N, fmt, MQ_ROLE_ACT, dev)
@@ -56,12 +56,9 @@ class LayerStep:
         self.ops: Dict[str, Callable[[int], None]] = OrderedDict([
             ("relayout_x", lambda s: mq_relayout_cbf(self.x, self.xc, c.N, c.Cin, c.H, c.W, 0,
                                                      amax_ws=a0)),
-            ("relayout_w", lambda s: mq_relayout_weight(self.w, self.wc, c.Cout, c.Cin, c.Kh,
-                                                        c.Kw, 0, amax_ws=a1)),
             ("quantize_x", lambda s: mq_quantize(self.xc, self.qx, MQ_RNE, 0, a0,
                                                  MQ_QUANTIZE_AMAX_READY)),
-            ("quantize_w", lambda s: mq_quantize(self.wc, self.qw, MQ_RNE, 0, a1,
-                                                 MQ_QUANTIZE_AMAX_READY)),
+            ("quantize_w", lambda s: mq_quantize_weight(self.w, self.qw, MQ_RNE, 0, a1)),
             ("quantize_g", lambda s: mq_quantize(self.gc, self.qg, MQ_SR,
                                                  self.sr_seed_base + s, a2)),
             ("conv_fwd", lambda s: mq_conv_fwd(p, self.qx, self.qw, self.y)),
@@ -98,12 +95,9 @@ class LayerStep:
         fixed = {
             "relayout_x": (L.mq_relayout_cbf, (P(self.x), P(self.xc), c.N, c.Cin, c.H, c.W, 0,
                                                a[0], wsb, hs)),
-            "relayout_w": (L.mq_relayout_weight, (P(self.w), P(self.wc), c.Cout, c.Cin, c.Kh,
-                                                  c.Kw, 0, a[1], wsb, hs)),
             "quantize_x": (L.mq_quantize, (P(self.xc), bx, MQ_RNE, 0, a[0], wsb,
                                            MQ_QUANTIZE_AMAX_READY, hs)),
-            "quantize_w": (L.mq_quantize, (P(self.wc), bw, MQ_RNE, 0, a[1], wsb,
-                                           MQ_QUANTIZE_AMAX_READY, hs)),
+            "quantize_w": (L.mq_quantize_weight, (P(self.w), bw, MQ_RNE, 0, a[1], wsb, hs)),
             "conv_fwd": (L.mq_conv_fwd, (conv, bx, bw, P(self.y), hs)),
             "conv_wgrad": (L.mq_conv_wgrad, (conv, bg, bx, P(self.gw), P(self.ws), nws, hs)),
             "conv_dgrad": (L.mq_conv_dgrad, (conv, bw, bg, P(self.gx), hs)),

@@ -193,3 +193,46 @@ def test_relayout_amax_then_quantize(case, shape, fmt):
     torch.cuda.synchronize()
     assert_quant_equal(q, oracle.quantize(oracle.oihw_to_tap_major(x), fmt, 0, 0), fmt,
                        f"weight {case}")
+
+
+# ---- weights straight from OIHW (mq_quantize_weight) -------------------------------------
+
+WEIGHT_SHAPES = [  # (Cout, Cin, Kh, Kw): small (one launch) and large (amax pass + gather)
+    (1, 1, 1, 1), (5, 3, 3, 3), (16, 16, 3, 3), (24, 20, 3, 3), (64, 64, 3, 3), (17, 13, 1, 1),
+    (36, 70, 5, 5), (128, 128, 3, 3), (130, 67, 3, 3), (256, 64, 1, 1),
+]
+
+
+@pytest.mark.parametrize("fmt", [4, 6])
+@pytest.mark.parametrize("rnd", [0, 1])
+@pytest.mark.parametrize("wshape", WEIGHT_SHAPES)
+def test_quantize_weight_from_oihw(wshape, fmt, rnd):
+    Co, Ci, Kh, Kw = wshape
+    log("quantize_weight", wshape, fmt, rnd)
+    w = workloads.random_array(wshape, seed=Co * 7 + Ci, dist="kaiming", fan_in=Ci * Kh * Kw)
+    seed = 99 + rnd
+    q = mq.QTensor(Kh, Kw, Co, Ci, fmt, mq.MQ_ROLE_WEIGHT, "cuda")
+    ws = mq.quantize_workspace("cuda")
+    mq.mq_quantize_weight(to_dev(w), q, rnd, seed, ws)
+    torch.cuda.synchronize()
+    ref = oracle.quantize(oracle.oihw_to_tap_major(w), fmt, rnd, seed)
+    assert_quant_equal(q, ref, fmt, f"{wshape} {fmt} {rnd}")
+
+
+@pytest.mark.parametrize("wshape", [(64, 64, 3, 3), (128, 128, 3, 3)])
+def test_quantize_weight_special_values(wshape):
+    Co, Ci, Kh, Kw = wshape
+    for name, w in (("zeros", np.zeros(wshape, np.float32)),
+                    ("inf", _with(workloads.random_array(wshape, 5), (1, 2, 0, 1), np.inf))):
+        q = mq.QTensor(Kh, Kw, Co, Ci, 4, mq.MQ_ROLE_WEIGHT, "cuda")
+        mq.mq_quantize_weight(to_dev(w), q, 0, 0, mq.quantize_workspace("cuda"))
+        torch.cuda.synchronize()
+        ref = oracle.quantize(oracle.oihw_to_tap_major(w), 4, 0, 0)
+        assert_quant_equal(q, ref, 4, f"{wshape} {name}")
+
+
+def test_quantize_weight_rejects_wrong_role():
+    q = mq.QTensor(3, 3, 8, 8, 4, mq.MQ_ROLE_ACT, "cuda")
+    w = torch.zeros(8, 8, 3, 3, device="cuda")
+    with pytest.raises(mq.MQError):
+        mq.mq_quantize_weight(w, q, 0, 0, mq.quantize_workspace("cuda"))
