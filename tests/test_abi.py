@@ -75,6 +75,13 @@ def test_validation_errors_without_gpu():
     assert L.mq_quantize(y, ctypes.byref(bad), 0, 0, y, ws, 0, s0) == mq.MQ_ERR_ARG
     nul = _fake_q((8, 8, 16, 2), null=True)
     assert L.mq_quantize(y, ctypes.byref(nul), 0, 0, y, ws, 0, s0) == mq.MQ_ERR_ARG
+    # weights straight from OIHW
+    assert L.mq_quantize_weight(None, ctypes.byref(w), 0, 0, y, ws, s0) == mq.MQ_ERR_ARG
+    assert L.mq_quantize_weight(y, ctypes.byref(w), 3, 0, y, ws, s0) == mq.MQ_ERR_ARG
+    assert L.mq_quantize_weight(y, ctypes.byref(x), 0, 0, y, ws, s0) == mq.MQ_ERR_SHAPE  # role
+    assert L.mq_quantize_weight(y, ctypes.byref(w), 0, 0, None, ws, s0) == mq.MQ_ERR_WORKSPACE
+    assert L.mq_quantize_weight(y, ctypes.byref(w), 0, 0, y, ws - 1, s0) == mq.MQ_ERR_WORKSPACE
+    assert L.mq_quantize_weight(y, ctypes.byref(w), 0, 0, ctypes.c_void_p(0x2002), ws, s0) == mq.MQ_ERR_ARG
     # misaligned codes (16 B) or scales (4 B) -> MQ_ERR_ARG
     mis = mq.mq_qtensor(8, 8, 16, 2, mq.MQ_NVFP4, mq.MQ_ROLE_ACT, 0x1008, 0x1000, 0x1000)
     assert L.mq_quantize(y, ctypes.byref(mis), 0, 0, y, ws, 0, s0) == mq.MQ_ERR_ARG
