@@ -171,8 +171,9 @@ mq_status mq_quantize(const float *src_dev, const mq_qtensor *dst, int32_t rnd, 
  * [Kh][Kw][Cout][Cin] of the 2-D weight matrix (onedev.kr digest, section "How it differs"),
  * with the same amax, T, square scales and codes as mq_relayout_weight followed by mq_quantize
  * on its output (the recipe above), without writing the fp32 tap-major copy. A weight of at
- * most 40448 elements takes one launch of one workgroup (the tensor staged in LDS); a larger one
- * runs the amax pass into amax_ws_dev and a quantizer that gathers from OIHW.
+ * most 65536 elements takes one launch (every workgroup reduces the whole tensor's amax itself,
+ * then quantizes its share of the squares); a larger one runs the amax pass into amax_ws_dev and
+ * a quantizer that gathers from OIHW.
  * w_oihw_dev: Cout*Cin*Kh*Kw floats, [co][ci][kh][kw].
  * dst:     role MQ_ROLE_WEIGHT with (o0, o1, r, s) = (Kh, Kw, Cout, Cin).
  * rnd, seed: as for mq_quantize.

@@ -20,8 +20,8 @@ hipError_t launch_quantize(const float *src, int64_t planes, int R, int S, int f
                            uint32_t *amax_ws, bool amax_ready, hipStream_t st);
 // OIHW fp32 weight [Cout][Cin][Kh][Kw] -> quantized tap-major squares [Kh][Kw][Cout][Cin], the
 // same codes, scales and T as launch_relayout_weight followed by launch_quantize, without the
-// fp32 copy (one launch of one workgroup, the tensor staged in LDS, for a weight of at most
-// 40448 elements; else the amax pass in amax_ws and a quantizer that gathers from OIHW).
+// fp32 copy (one launch for a weight of at most 65536 elements, every workgroup reducing the
+// whole amax itself; else the amax pass in amax_ws and a quantizer that gathers from OIHW).
 hipError_t launch_quantize_weight(const float *src, int Cout, int Cin, int Kh, int Kw, int fmt,
                                   int rnd, uint64_t seed, uint8_t *codes, uint8_t *scales,
                                   float *tscale, uint32_t *amax_ws, hipStream_t st);
