@@ -94,11 +94,18 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
         // from (two stage times ahead of its use). The loop is unrolled by two so that slots are
         // never copied, which keeps the compiler's waits down to the stage being decoded.
         RawItem<FMT> raw[2][ITEMS];
+        // (batch chunk, pixel block, output row) of the next load's stage: loads go through the
+        // stages in order, so the position is stepped with carries instead of divided out
+        int l_nc = st0 % a.nch, l_ob = (st0 / a.nch) % a.owb, l_oh = st0 / a.nch / a.owb;
         auto load = [&](int st, RawItem<FMT>(&dst)[ITEMS]) {
-            const int nc = st % a.nch;
-            const int rest = st / a.nch;
-            const int ob = rest % a.owb;
-            const int oh = rest / a.owb;
+            const int nc = l_nc, ob = l_ob, oh = l_oh;
+            {
+                const bool c1 = l_nc + 1 >= a.nch;
+                l_nc = c1 ? 0 : l_nc + 1;
+                const bool c2 = c1 && l_ob + 1 >= a.owb;
+                l_ob = c1 ? (c2 ? 0 : l_ob + 1) : l_ob;
+                l_oh += c2 ? 1 : 0;
+            }
             const int ow0 = ob * kPWg;
             const int ih = oh * SI - a.ph + kh;
             const int iw0 = ow0 * SI - a.pw;
