@@ -95,20 +95,82 @@ struct QuantArgs {
     uint32_t seed_lo, seed_hi;
 };
 
-// One square: 16 values in row-major order (slots outside the tensor hold 0) -> the E4M3
-// scale byte (returned) and 16 codes (sign | magnitude). T is the tensor scale; nonfinite: the
-// tensor amax is Inf or NaN (scale 0x7F, codes 0). r0, r1: the square's Philox draws (SR only).
+// Round-to-nearest-even grid codes of 16 finite quotients q (sign | magnitude, packed as stored:
+// NVFP4 element e in nibble e of w[0..1], NVFP6 element e at bits 6e .. 6e+5 of w[0..2]). The
+// gfx950 conversions with scale 1.0 round to nearest, ties to even, and saturate at the largest
+// element (6 or 7.5): the same codes as grid_rne with the sign of q, for every finite fp32 input
+// of either sign (checked exhaustively on the device).
+template <int FMT>
+__device__ __forceinline__ void pack_rne(const float (&q)[16], uint32_t (&w)[3])
+{
+    if constexpr (FMT == kFP4) {
+        // byte k of a word: element 2k in the low nibble, 2k + 1 in the high one
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t v = 0u;
+            v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, q[8 * h + 0], q[8 * h + 1], 1.0f, 0);
+            v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, q[8 * h + 2], q[8 * h + 3], 1.0f, 1);
+            v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, q[8 * h + 4], q[8 * h + 5], 1.0f, 2);
+            v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, q[8 * h + 6], q[8 * h + 7], 1.0f, 3);
+            w[h] = v;
+        }
+        w[2] = 0u;
+    } else {
+        // The 32-value conversion puts a[i] in 6-bit field 2i and b[i] in field 2i + 1: even
+        // elements in a, odd ones in b give the fields in element order (fields 16..31, from
+        // the zero upper halves, are dropped). Its result may not overlap its sources while it
+        // runs, hence the early-clobber output.
+        typedef float f32x16_v __attribute__((ext_vector_type(16)));
+        typedef uint32_t u32x6_v __attribute__((ext_vector_type(6)));
+        f32x16_v a, b;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            a[i] = q[2 * i];
+            b[i] = q[2 * i + 1];
+            a[8 + i] = 0.0f;
+            b[8 + i] = 0.0f;
+        }
+        u32x6_v v;
+        asm("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, 1.0" : "=&v"(v) : "v"(a), "v"(b));
+        w[0] = v[0]; w[1] = v[1]; w[2] = v[2];
+    }
+}
+
+// Pack 16 codes (sign | magnitude) as stored, the layout of pack_rne.
+template <int FMT>
+__device__ __forceinline__ void pack_codes(const uint32_t (&code)[16], uint32_t (&w)[3])
+{
+    w[0] = w[1] = w[2] = 0u;
+    if (FMT == kFP4) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            w[0] |= code[e] << (4 * e);
+            w[1] |= code[e + 8] << (4 * e);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int bit = 6 * e;
+            w[bit >> 5] |= code[e] << (bit & 31);
+            if ((bit & 31) > 26) w[(bit >> 5) + 1] |= code[e] >> (32 - (bit & 31));
+        }
+    }
+}
+
+// One square: 16 values in row-major order (slots outside the tensor hold +0, which always gets
+// code 0) -> the E4M3 scale byte (returned) and the square's packed codes w (8 bytes NVFP4,
+// 12 bytes NVFP6). T is the tensor scale; nonfinite: the tensor amax is Inf or NaN (scale 0x7F,
+// codes 0). r0, r1: the square's Philox draws (SR only).
 template <int FMT, bool SR>
 __device__ __forceinline__ uint32_t quantize_square(const float (&x)[16], float T, bool nonfinite,
                                                     const Philox4 &r0, const Philox4 &r1,
-                                                    uint32_t (&code)[16])
+                                                    uint32_t (&w)[3])
 {
     using F = Fmt<FMT>;
     uint32_t bcode;
     if (nonfinite) {
         bcode = 0x7Fu;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) code[e] = 0u;
+        w[0] = w[1] = w[2] = 0u;
     } else {
         float bmax = 0.0f;
 #pragma unroll
@@ -122,19 +184,23 @@ __device__ __forceinline__ uint32_t quantize_square(const float (&x)[16], float 
         // x / D for 16 elements from one reciprocal: with rD = RN(1/D), q0 = RN(x * rD) and the
         // exact residual x - q0 * D, RN(q0 + residual * rD) is the correctly rounded quotient
         // (Markstein's theorem) as long as nothing underflows: D within 2^+-64 and
-        // |x / D| >= 2^-20 (or x = 0). A square with any other element (a tiny one, whose code
-        // only the round-up draw of stochastic rounding could tell apart) divides instead.
+        // |x / D| >= 2^-20 (or x = 0). A square with any other element divides instead under
+        // stochastic rounding, where a tiny quotient's code depends on its exact value (the
+        // round-up draw). Nearest rounding sends every |q| below 2^-20 to a zero code of q's
+        // sign, which the reciprocal form keeps, so there only D's range is checked.
         float q[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) q[e] = 0.0f;
+        for (int e = 0; e < 16; ++e) q[e] = 0.0f; // zero scale: +0 codes
         if (!zero) {
             const float rD = 1.0f / D;
             const float Dlo = D * 0x1p-20f;
             bool slow = !(D >= 0x1p-64f && D <= 0x1p64f);
+            if (SR) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float ax = fabsf(x[e]);
-                slow |= (ax < Dlo) && (ax != 0.0f);
+                for (int e = 0; e < 16; ++e) {
+                    const float ax = fabsf(x[e]);
+                    slow |= (ax < Dlo) && (ax != 0.0f);
+                }
             }
             if (slow) {
 #pragma unroll
@@ -147,45 +213,31 @@ __device__ __forceinline__ uint32_t quantize_square(const float (&x)[16], float 
                 }
             }
         }
+        if (SR) {
+            uint32_t code[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const float aq = fabsf(q[e]);
-            uint32_t mag;
-            if (SR) {
-                const uint32_t w = (e < 8) ? r0.v[(e & 7) >> 1] : r1.v[(e & 7) >> 1];
-                const uint32_t u16 = (w >> (16 * (e & 1))) & 0xFFFFu;
-                mag = grid_sr<FMT>(aq, u16);
-            } else {
-                mag = grid_rne<FMT>(aq);
+            for (int e = 0; e < 16; ++e) {
+                const uint32_t rw = (e < 8) ? r0.v[(e & 7) >> 1] : r1.v[(e & 7) >> 1];
+                const uint32_t u16 = (rw >> (16 * (e & 1))) & 0xFFFFu;
+                const uint32_t c = grid_sr<FMT>(fabsf(q[e]), u16) |
+                                   ((__float_as_uint(x[e]) >> 31) ? F::kSign : 0u);
+                code[e] = zero ? 0u : c; // a zero scale holds +0 codes
             }
-            const uint32_t c = mag | ((__float_as_uint(x[e]) >> 31) ? F::kSign : 0u);
-            code[e] = zero ? 0u : c; // a zero scale holds +0 codes
+            pack_codes<FMT>(code, w);
+        } else {
+            pack_rne<FMT>(q, w);
         }
     }
     return bcode;
 }
 
-// Pack 16 codes of square t: 8 bytes (NVFP4, element e in nibble e) or 12 bytes (NVFP6,
-// element e at bits 6e .. 6e+5 of the 96-bit little-endian word).
+// Store square t's packed codes: 8 bytes (NVFP4) or 12 bytes (NVFP6).
 template <int FMT>
-__device__ __forceinline__ void store_square_codes(uint8_t *codes, int64_t t, const uint32_t (&code)[16])
+__device__ __forceinline__ void store_square_codes(uint8_t *codes, int64_t t, const uint32_t (&w)[3])
 {
     if (FMT == kFP4) {
-        uint32_t w0 = 0u, w1 = 0u;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            w0 |= code[e] << (4 * e);
-            w1 |= code[e + 8] << (4 * e);
-        }
-        *reinterpret_cast<uint2 *>(codes + 8 * t) = make_uint2(w0, w1);
+        *reinterpret_cast<uint2 *>(codes + 8 * t) = make_uint2(w[0], w[1]);
     } else {
-        uint32_t w[3] = {0u, 0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int bit = 6 * e;
-            w[bit >> 5] |= code[e] << (bit & 31);
-            if ((bit & 31) > 26) w[(bit >> 5) + 1] |= code[e] >> (32 - (bit & 31));
-        }
         uint32_t *dst = reinterpret_cast<uint32_t *>(codes + 12 * t);
         dst[0] = w[0]; dst[1] = w[1]; dst[2] = w[2];
     }
@@ -272,7 +324,6 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a)
         float x[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) x[e] = xn[e];
-        const Pos cur = pos;
         const bool more = t + stride < nsq;
         if (more) pos = advance(pos);
         load(pos, xn); // the last step reloads its own square
@@ -285,19 +336,10 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a)
             r1 = philox4x32_10((uint32_t)(j + 1), (uint32_t)((j + 1) >> 32), 0u, 0u, a.seed_lo,
                                a.seed_hi);
         }
-        const int s4 = cur.s4, r4 = cur.r4;
-        uint32_t code[16];
-        const uint32_t bcode = quantize_square<FMT, SR>(x, T, nonfinite, r0, r1, code);
-        if (!FULL) { // padded slots hold code 0
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (!((4 * r4 + i < a.R) && (4 * s4 + j < a.S))) code[4 * i + j] = 0u;
-        }
-
+        uint32_t w[3];
+        const uint32_t bcode = quantize_square<FMT, SR>(x, T, nonfinite, r0, r1, w);
         a.scales[t] = (uint8_t)bcode;
-        store_square_codes<FMT>(a.codes, t, code);
+        store_square_codes<FMT>(a.codes, t, w);
     }
 }
 
@@ -370,15 +412,10 @@ __global__ void __launch_bounds__(kSmallThreads) quantize_weight_small_kernel(Qu
         r1 = philox4x32_10((uint32_t)(jj + 1), (uint32_t)((jj + 1) >> 32), 0u, 0u, a.seed_lo,
                            a.seed_hi);
     }
-    uint32_t code[16];
-    const uint32_t bcode = quantize_square<FMT, SR>(x, T, nonfinite, r0, r1, code);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (!((4 * r4 + i < a.R) && (4 * s4 + j < a.S))) code[4 * i + j] = 0u;
+    uint32_t w[3];
+    const uint32_t bcode = quantize_square<FMT, SR>(x, T, nonfinite, r0, r1, w);
     a.scales[t] = (uint8_t)bcode;
-    store_square_codes<FMT>(a.codes, t, code);
+    store_square_codes<FMT>(a.codes, t, w);
 }
 
 template <int FMT, bool SR>
