@@ -2,10 +2,10 @@
 """Benchmark of the quantize-once convolution hot path on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input, for the ResNet-style
-3x3 layer (N=32, Cin=Cout=64, 56x56, stride 1, pad 1, NVFP4): relayout X (NCHW -> channel-batch
-first) and quantize it (round-to-nearest), quantize W from OIHW into its tap-major squares
-(round-to-nearest, one call), quantize G_Y (stochastic, a new seed every step), then the forward,
-weight-gradient and input-gradient GEMMs. Inputs are resident
+3x3 layer (N=32, Cin=Cout=64, 56x56, stride 1, pad 1, NVFP4): quantize X from NCHW into its
+channel-batch-first squares (round-to-nearest; amax pass + one quantizing pass), quantize W from
+OIHW into its tap-major squares (round-to-nearest, one call), quantize G_Y (stochastic, a new seed
+every step), then the forward, weight-gradient and input-gradient GEMMs. Inputs are resident
 in HBM before the timed region starts.
 
 The timed steps call the C ABI back to back on one stream (arguments marshalled once, so the
@@ -41,8 +41,7 @@ CALIB_ELEMS = 1 << 26        # plain copy for counter calibration: 256 MiB read 
 
 # which kernels make up each op (rocprofv3 kernel names start with these)
 OP_KERNELS = {
-    "relayout_x": ["void mq::transpose4_kernel", "void mq::transpose_kernel"],
-    "quantize_x": ["void mq::quantize_kernel"],
+    "quantize_x": ["mq::amax_kernel", "void mq::quantize_nchw_kernel"],
     "quantize_w": ["void mq::quantize_weight_small_kernel", "mq::amax_kernel",
                    "void mq::quantize_kernel"],
     "quantize_g": ["mq::amax_kernel", "void mq::quantize_kernel"],
@@ -78,7 +77,7 @@ def parse():
                          "library, the rest in PyTorch fp32)")
     ap.add_argument("--batch", type=int, default=128, help="batch size of --network")
     ap.add_argument("--inference", action="store_true",
-                    help="with --config: the inference path only (relayout and quantize X, "
+                    help="with --config: the inference path only (quantize X from NCHW, "
                          "conv fwd; the weights are quantized once before timing)")
     return ap.parse_args()
 
@@ -155,12 +154,10 @@ def main():
     qbytes = lambda shape: sq(*shape) * (8 if fmt == 4 else 12) + sq(*shape)  # codes + scales
     nx, nw, ng = x.size, w.size, g.size
     qx_b, qw_b, qg_b = qbytes((H, W, Ci, N)), qbytes((Kh, Kw, Co, Ci)), qbytes((Ho, Wo, Co, N))
-    # algorithmic bytes: relayout 8 B/el (its amax partials ride along); quantize of X and W
-    # (amax ready from the relayout) = one read + codes/scales; quantize of G_Y = amax read +
-    # quantize read + codes/scales
+    # algorithmic bytes: quantize of X and G_Y = amax read + quantize read + codes/scales;
+    # quantize of W = one read + codes/scales
     alg = {
-        "relayout_x": ("hbm", 8 * nx),
-        "quantize_x": ("hbm", 4 * nx + qx_b), "quantize_w": ("hbm", 4 * nw + qw_b),
+        "quantize_x": ("hbm", 8 * nx + qx_b), "quantize_w": ("hbm", 4 * nw + qw_b),
         "quantize_g": ("hbm", 8 * ng + qg_b),
         "conv_fwd": ("gemm", flops), "conv_wgrad": ("gemm", flops), "conv_dgrad": ("gemm", flops),
     }
@@ -303,8 +300,8 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic (seeded numpy PCG64; X=ReLU(N(0,1)), W Kaiming-normal, G_Y~N(0,1e-3))",
-        "config": {"workload": "resnet-3x3-s1p1 N=32 Cin=Cout=64 56x56 NVFP4: relayout X, "
-                               "quantize X, W, G_Y (RNE, RNE, SR), conv fwd/wgrad/dgrad",
+        "config": {"workload": "resnet-3x3-s1p1 N=32 Cin=Cout=64 56x56 NVFP4: quantize X "
+                               "(from NCHW), W, G_Y (RNE, RNE, SR), conv fwd/wgrad/dgrad",
                    "N": N, "Cin": Ci, "Cout": Co, "H": H, "W": W, "K": Kh, "stride": 1, "pad": 1,
                    "format": "NVFP4 (E2M1 codes, E4M3 4x4-square scales, fp32 tensor scale)",
                    "mfma": "fp16 operands decoded exactly, fp32 accumulate"},
@@ -350,7 +347,7 @@ def _time_graph(fns, reps: int, stream) -> float:
 
 
 def run_config(args):
-    """Every layer of a workload through the hot path: one step = each layer's relayouts, three
+    """Every layer of a workload through the hot path: one step = each layer's three
     quantizations and three GEMMs once (layers that repeat a shape are timed once and counted
     with their multiplicity). Per layer and op: time, rate and fraction of the bound."""
     import collections
@@ -386,11 +383,11 @@ def run_config(args):
         torch.cuda.synchronize()
         if args.inference:  # W stays quantized from the warm-up: activations only
             calls = collections.OrderedDict((k, calls[k]) for k in
-                                            ("relayout_x", "quantize_x", "conv_fwd"))
+                                            ("quantize_x", "conv_fwd"))
         eb = 0.5625 if l.fmt == 4 else 0.8125
         nx, nw, ng = l.N * l.Cin * l.H * l.W, l.Cout * l.Cin * l.Kh * l.Kw, l.N * l.Cout * l.Ho * l.Wo
         fl = l.gemm_flops()
-        byt = {"relayout_x": 8 * nx, "relayout_w": 8 * nw, "quantize_x": 4 * nx + eb * nx,
+        byt = {"quantize_x": 8 * nx + eb * nx,
                "quantize_w": 4 * nw + eb * nw, "quantize_g": 8 * ng + eb * ng,
                "conv_fwd": eb * (nx + nw) + 4 * ng, "conv_wgrad": eb * (nx + ng) + 4 * nw,
                "conv_dgrad": eb * (nw + ng) + 4 * nx}
@@ -429,10 +426,10 @@ def run_config(args):
         "higher_is_better": True,
         "dtype": "fp16",
         "data": "synthetic (seeded numpy PCG64, the workload's value distributions)",
-        "config": {"workload": (f"{args.config} inference: {len(layers)} layers, relayout and "
-                                f"quantize X, conv fwd each (weights quantized once)")
+        "config": {"workload": (f"{args.config} inference: {len(layers)} layers, quantize X "
+                                f"(from NCHW), conv fwd each (weights quantized once)")
                    if args.inference else
-                   (f"{args.config}: {len(layers)} layers, relayout X, quantize X/W/G_Y, "
+                   (f"{args.config}: {len(layers)} layers, quantize X (from NCHW), W, G_Y, "
                     f"conv fwd/wgrad/dgrad each")},
         "per_layer": per_layer,
     }
@@ -581,7 +578,7 @@ def summarize_pmc(fetch_db: str, write_db: str):
         b = fk * 1024 / f_cal + wk * 1024 / w_cal
         per_kernel[k] = b
         print(f"| {k[:90]} | {fetch[k][1]} | {fk:.1f} | {wk:.1f} | {b:.0f} |")
-    # per op (relayout_x/w and quantize_x/w/g share kernel names with different sizes, so only
+    # per op (quantize_x/w/g share kernel names with different sizes, so only
     # the convolutions, whose kernels are distinct, get a per-op figure)
     for op in ("conv_fwd", "conv_wgrad", "conv_dgrad"):
         tot = sum(b for k, b in per_kernel.items()

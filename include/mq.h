@@ -167,6 +167,27 @@ mq_status mq_quantize(const float *src_dev, const mq_qtensor *dst, int32_t rnd, 
                       hipStream_t stream);
 
 /*
+ * mq_quantize_nchw: quantize an NCHW fp32 activation or output gradient straight into its
+ * channel-batch-first quantized layout (onedev.kr digest, section "How it works": the layout
+ * change happens before quantization, which then runs once, section "How it differs"). The
+ * codes, scales and T are those of mq_relayout_cbf (inverse = 0) followed by mq_quantize on its
+ * output, with the same recipe, rounding and random draws (square t of the channel-batch-first
+ * tensor), without writing the fp32 channel-batch-first copy: an amax pass over src_dev (unless
+ * flags has MQ_QUANTIZE_AMAX_READY), then one quantizing pass that reads NCHW and writes squares.
+ * src_dev: N*C*H*W floats [n][c][h][w] with (H, W, C, N) = (dst->o0, dst->o1, dst->r, dst->s).
+ * dst:     role MQ_ROLE_ACT or MQ_ROLE_GRAD, buffers as for mq_quantize.
+ * amax_ws_dev / amax_ws_bytes / flags: as for mq_quantize (the partial maxima may come from any
+ *          layout of the same values).
+ * Errors: MQ_ERR_ARG (null pointer, bad enum or flag, non-positive dims, misaligned pointer),
+ *         MQ_ERR_SHAPE (role MQ_ROLE_WEIGHT), MQ_ERR_WORKSPACE (as for mq_quantize),
+ *         MQ_ERR_UNSUPPORTED (the source zero-padded to whole squares, 16*ceil(N/4)*ceil(C/4)*H*W
+ *         floats, reaches 2^31 bytes).
+ */
+mq_status mq_quantize_nchw(const float *src_dev, const mq_qtensor *dst, int32_t rnd, uint64_t seed,
+                           uint32_t *amax_ws_dev, size_t amax_ws_bytes, uint32_t flags,
+                           hipStream_t stream);
+
+/*
  * mq_quantize_weight: quantize an OIHW fp32 weight straight into the tap-major quantized layout
  * [Kh][Kw][Cout][Cin] of the 2-D weight matrix (onedev.kr digest, section "How it differs"),
  * with the same amax, T, square scales and codes as mq_relayout_weight followed by mq_quantize

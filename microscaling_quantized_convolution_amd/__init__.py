@@ -25,7 +25,7 @@ MQ_QUANTIZE_AMAX_READY = 1   # mq_quantize flag: the workspace already holds thi
 
 EXPORTS = (
     "mq_status_str", "mq_codes_bytes", "mq_scales_bytes", "mq_relayout_cbf",
-    "mq_relayout_weight", "mq_quantize", "mq_quantize_weight", "mq_conv_fwd",
+    "mq_relayout_weight", "mq_quantize", "mq_quantize_nchw", "mq_quantize_weight", "mq_conv_fwd",
     "mq_wgrad_workspace_bytes",
     "mq_conv_wgrad", "mq_conv_dgrad",
 )
@@ -52,7 +52,7 @@ class mq_conv(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
-                          f"python -m microscaling_quantized_convolution_amd._build")
+                          f"python microscaling_quantized_convolution_amd/_build.py")
     L = ctypes.CDLL(LIB_PATH)
     P, i32, u64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
     L.mq_status_str.restype = ctypes.c_char_p
@@ -64,6 +64,8 @@ def _load() -> ctypes.CDLL:
     L.mq_relayout_cbf.argtypes = [P, P, i32, i32, i32, i32, i32, P, sz, P]
     L.mq_relayout_weight.argtypes = [P, P, i32, i32, i32, i32, i32, P, sz, P]
     L.mq_quantize.argtypes = [P, ctypes.POINTER(mq_qtensor), i32, u64, P, sz, ctypes.c_uint32, P]
+    L.mq_quantize_nchw.argtypes = [P, ctypes.POINTER(mq_qtensor), i32, u64, P, sz,
+                                   ctypes.c_uint32, P]
     L.mq_quantize_weight.argtypes = [P, ctypes.POINTER(mq_qtensor), i32, u64, P, sz, P]
     L.mq_conv_fwd.argtypes = [ctypes.POINTER(mq_conv), ctypes.POINTER(mq_qtensor),
                               ctypes.POINTER(mq_qtensor), P, P]
@@ -167,6 +169,16 @@ def mq_quantize(src: torch.Tensor, dst: QTensor, rnd: int, seed: int, amax_ws: t
     _check(_lib.mq_quantize(_ptr(src), ctypes.byref(q), rnd, seed & (2 ** 64 - 1),
                             _ptr(amax_ws), _nbytes(amax_ws), flags, _stream(stream)),
            "mq_quantize")
+
+
+def mq_quantize_nchw(src_nchw: torch.Tensor, dst: QTensor, rnd: int, seed: int,
+                     amax_ws: torch.Tensor, flags: int = 0, stream=None):
+    """NCHW fp32 activation / gradient -> quantized channel-batch-first tensor (same result as
+    mq_relayout_cbf then mq_quantize, without the fp32 copy)."""
+    q = dst.struct()
+    _check(_lib.mq_quantize_nchw(_ptr(src_nchw), ctypes.byref(q), rnd, seed & (2 ** 64 - 1),
+                                 _ptr(amax_ws), _nbytes(amax_ws), flags, _stream(stream)),
+           "mq_quantize_nchw")
 
 
 def mq_quantize_weight(w_oihw: torch.Tensor, dst: QTensor, rnd: int, seed: int,

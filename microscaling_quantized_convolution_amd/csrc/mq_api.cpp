@@ -138,6 +138,24 @@ mq_status mq_quantize(const float *src, const mq_qtensor *dst, int32_t rnd, uint
                                              (flags & MQ_QUANTIZE_AMAX_READY) != 0, stream));
 }
 
+mq_status mq_quantize_nchw(const float *src, const mq_qtensor *dst, int32_t rnd, uint64_t seed,
+                           uint32_t *amax_ws, size_t amax_ws_bytes, uint32_t flags,
+                           hipStream_t stream)
+{
+    if (!src || !qtensor_ok(dst) || (rnd != MQ_RNE && rnd != MQ_SR)) return MQ_ERR_ARG;
+    if (flags & ~(uint32_t)MQ_QUANTIZE_AMAX_READY) return MQ_ERR_ARG;
+    if (dst->role == MQ_ROLE_WEIGHT) return MQ_ERR_SHAPE;
+    if (!amax_ws || amax_ws_bytes < MQ_QUANTIZE_WS_BYTES) return MQ_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(amax_ws) & 3u) != 0) return MQ_ERR_ARG;
+    // zero-padded source (4*ceil(N/4) x 4*ceil(C/4) planes) below 2^31 bytes
+    const int64_t pad = 16 * (int64_t)((dst->s + 3) / 4) * ((dst->r + 3) / 4) * dst->o0 * dst->o1 * 4;
+    if (pad >= ((int64_t)1 << 31)) return MQ_ERR_UNSUPPORTED;
+    return launch_status(mq::launch_quantize_nchw(src, dst->s, dst->r, dst->o0, dst->o1, dst->fmt,
+                                                  rnd, seed, dst->codes, dst->scales, dst->tscale,
+                                                  amax_ws, (flags & MQ_QUANTIZE_AMAX_READY) != 0,
+                                                  stream));
+}
+
 mq_status mq_quantize_weight(const float *w, const mq_qtensor *dst, int32_t rnd, uint64_t seed,
                              uint32_t *amax_ws, size_t amax_ws_bytes, hipStream_t stream)
 {

@@ -18,6 +18,13 @@ hipError_t launch_relayout_weight(const float *src, float *dst, int Cout, int Ci
 hipError_t launch_quantize(const float *src, int64_t planes, int R, int S, int fmt, int rnd,
                            uint64_t seed, uint8_t *codes, uint8_t *scales, float *tscale,
                            uint32_t *amax_ws, bool amax_ready, hipStream_t st);
+// NCHW fp32 -> quantized channel-batch-first squares [H][W][C4][N4]: the same codes, scales and
+// T as launch_relayout_cbf followed by launch_quantize, without the fp32 copy (the amax pass,
+// unless amax_ready, then one launch). hipErrorInvalidValue when the zero-padded tensor
+// reaches 2^31 bytes.
+hipError_t launch_quantize_nchw(const float *src, int N, int C, int H, int W, int fmt, int rnd,
+                                uint64_t seed, uint8_t *codes, uint8_t *scales, float *tscale,
+                                uint32_t *amax_ws, bool amax_ready, hipStream_t st);
 // OIHW fp32 weight [Cout][Cin][Kh][Kw] -> quantized tap-major squares [Kh][Kw][Cout][Cin], the
 // same codes, scales and T as launch_relayout_weight followed by launch_quantize, without the
 // fp32 copy (one launch for a weight of at most 65536 elements, every workgroup reducing the

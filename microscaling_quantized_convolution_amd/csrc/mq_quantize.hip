@@ -13,6 +13,7 @@
 // (this amax kernel, or a relayout that already moved the tensor, which then saves a full read).
 #include "mq_device.hpp"
 #include "mq_kernels.hpp"
+#include "mq_stage.hpp"
 
 namespace mq {
 
@@ -356,6 +357,128 @@ static hipError_t launch_quant(const QuantArgs &a, bool full, hipStream_t st)
     return hipGetLastError();
 }
 
+// ---- NCHW fp32 straight to quantized channel-batch-first squares ----
+//
+// The same codes, scales and T as the NCHW -> [H][W][C][N] relayout followed by quantize_kernel,
+// without the fp32 channel-batch-first copy: square t = ((p*C4 + c4)*N4 + n4) of pixel p holds
+// x[4*n4 + j][4*c4 + i][p] at element 4i + j. A lane owns one pixel and NQ consecutive batch
+// squares of one channel square; a wave covers 64 consecutive pixels, so each load instruction
+// reads 256 contiguous bytes of one (n, c) plane, and the lane's NQ squares (NQ*8 or NQ*12 code
+// bytes, NQ scale bytes) are contiguous in the output. Waves are ordered batch group fastest,
+// then channel square, so the four waves of a workgroup complete whole output lines.
+struct QuantNchwArgs {
+    const float *src;        // [N][C][HW]
+    uint8_t *codes, *scales;
+    float *tscale;
+    const uint32_t *amax_ws; // partial maxima of this tensor
+    int N, C, HW, C4, N4, NG; // NG = N4 / NQ batch-square groups
+    int items;                // waves of work: ceil(HW/64) * C4 * NG
+    uint32_t bytes;           // N*C*HW*4 (below 2^31)
+    uint32_t seed_lo, seed_hi;
+};
+
+template <int FMT, int NQ>
+__device__ __forceinline__ void store_group(const QuantNchwArgs &a, int t0, const uint32_t (&w)[NQ][3],
+                                            const uint32_t (&bc)[NQ])
+{
+    if constexpr (NQ == 4) {
+        // t0 is a multiple of 4: 32 (NVFP4) or 48 (NVFP6) aligned code bytes, one scale word
+        uint4 *dst = reinterpret_cast<uint4 *>(a.codes + (FMT == kFP4 ? 8 : 12) * (int64_t)t0);
+        if (FMT == kFP4) {
+            dst[0] = make_uint4(w[0][0], w[0][1], w[1][0], w[1][1]);
+            dst[1] = make_uint4(w[2][0], w[2][1], w[3][0], w[3][1]);
+        } else {
+            dst[0] = make_uint4(w[0][0], w[0][1], w[0][2], w[1][0]);
+            dst[1] = make_uint4(w[1][1], w[1][2], w[2][0], w[2][1]);
+            dst[2] = make_uint4(w[2][2], w[3][0], w[3][1], w[3][2]);
+        }
+        *reinterpret_cast<uint32_t *>(a.scales + t0) = bc[0] | (bc[1] << 8) | (bc[2] << 16) | (bc[3] << 24);
+    } else {
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+            store_square_codes<FMT>(a.codes, t0 + k, w[k]);
+            a.scales[t0 + k] = (uint8_t)bc[k];
+        }
+    }
+}
+
+template <int FMT, bool SR, int NQ>
+__global__ void __launch_bounds__(256) quantize_nchw_kernel(QuantNchwArgs a)
+{
+    using F = Fmt<FMT>;
+    __shared__ uint32_t red[4];
+    const uint32_t np = min(a.amax_ws[0], (uint32_t)kAmaxParts);
+    uint32_t pm = 0u;
+#pragma unroll
+    for (int k = 0; k < kAmaxParts / 256; ++k) {
+        const uint32_t i = threadIdx.x + 256u * k;
+        pm = max(pm, i < np ? a.amax_ws[1 + i] : 0u);
+    }
+    const uint32_t abits = block_max_u32<256>(pm, red);
+    const bool nonfinite = abits >= 0x7F800000u;
+    const float T = __uint_as_float(abits) / (448.0f * F::kEmax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.tscale = nonfinite ? __uint_as_float(0x7FC00000u) : T;
+
+    const int item = wave_uniform((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
+    if (item >= a.items) return;
+    const int lane = threadIdx.x & 63;
+    const int ng = item % a.NG, c4 = (item / a.NG) % a.C4, pb = item / a.NG / a.C4;
+    const int p = pb * 64 + lane;
+    const bool pin = p < a.HW;
+    // lane offset of element (n, c) = (4*ng*NQ, 4*c4); the others add a wave-uniform offset.
+    // Rows n >= N lie past the end of the tensor and read as zero through the range check;
+    // channels c >= C and pixels past HW are masked to an out-of-range offset.
+    const rsrc_t src = make_rsrc(a.src, a.bytes);
+    const uint32_t CHW4 = (uint32_t)a.C * (uint32_t)a.HW * 4u, HW4 = (uint32_t)a.HW * 4u;
+    const uint32_t lane_off = (uint32_t)(4 * ng * NQ) * CHW4 + (uint32_t)(4 * c4) * HW4 + 4u * (uint32_t)p;
+    float x[NQ][16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool cin = 4 * c4 + i < a.C;
+        const uint32_t voff = (pin && cin) ? lane_off : kBad;
+#pragma unroll
+        for (int k = 0; k < NQ; ++k)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                x[k][4 * i + j] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(
+                               src, (int)voff, (int)((uint32_t)(4 * k + j) * CHW4 + (uint32_t)i * HW4), 0));
+    }
+    if (!pin) return;
+    const int t0 = (p * a.C4 + c4) * a.N4 + ng * NQ; // square indices fit in 31 bits
+    uint32_t w[NQ][3], bc[NQ];
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+        Philox4 r0 = {}, r1 = {};
+        if (SR) {
+            const uint64_t jj = 2u * (uint64_t)(t0 + k);
+            r0 = philox4x32_10((uint32_t)jj, (uint32_t)(jj >> 32), 0u, 0u, a.seed_lo, a.seed_hi);
+            r1 = philox4x32_10((uint32_t)(jj + 1), (uint32_t)((jj + 1) >> 32), 0u, 0u, a.seed_lo,
+                               a.seed_hi);
+        }
+        bc[k] = quantize_square<FMT, SR>(x[k], T, nonfinite, r0, r1, w[k]);
+    }
+    store_group<FMT, NQ>(a, t0, w, bc);
+}
+
+template <int FMT, bool SR>
+static hipError_t launch_quant_nchw(const QuantNchwArgs &a0, hipStream_t st)
+{
+    QuantNchwArgs a = a0;
+    const int pbs = (a.HW + 63) / 64;
+    const dim3 block(256);
+    if (a.N4 % 4 == 0) {
+        a.NG = a.N4 / 4;
+        a.items = pbs * a.C4 * a.NG;
+        hipLaunchKernelGGL((quantize_nchw_kernel<FMT, SR, 4>), dim3((a.items + 3) / 4), block, 0, st, a);
+    } else {
+        a.NG = a.N4;
+        a.items = pbs * a.C4 * a.NG;
+        hipLaunchKernelGGL((quantize_nchw_kernel<FMT, SR, 1>), dim3((a.items + 3) / 4), block, 0, st, a);
+    }
+    return hipGetLastError();
+}
+
 // A small weight (at most kSmallWeight floats), from OIHW fp32 to quantized tap-major squares in
 // one launch: every workgroup reduces the whole tensor's amax itself (1024 lanes, a few 16-byte
 // loads each; no step across workgroups, no workspace), then its first kSmallSquares lanes
@@ -487,6 +610,34 @@ hipError_t launch_quantize(const float *src, int64_t planes, int R, int S, int f
     if (fmt == kFP4)
         return rnd ? launch_quant<kFP4, true>(a, full, st) : launch_quant<kFP4, false>(a, full, st);
     return rnd ? launch_quant<kFP6, true>(a, full, st) : launch_quant<kFP6, false>(a, full, st);
+}
+
+hipError_t launch_quantize_nchw(const float *src, int N, int C, int H, int W, int fmt, int rnd,
+                                uint64_t seed, uint8_t *codes, uint8_t *scales, float *tscale,
+                                uint32_t *amax_ws, bool amax_ready, hipStream_t st)
+{
+    const int64_t n = (int64_t)N * C * H * W;
+    const int64_t HW = (int64_t)H * W;
+    const int64_t C4 = (C + 3) / 4, N4 = (N + 3) / 4;
+    // 32-bit byte offsets below 2^31 even for the zero-padded rows and channels (4*N4 x 4*C4
+    // planes); 31-bit square and work-item indices
+    if (16 * N4 * C4 * HW * 4 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    if (!amax_ready) {
+        const int64_t want = (n / 4 + 8 * kAmaxThreads - 1) / (8 * kAmaxThreads);
+        const int parts = (int)(want < 1 ? 1 : (want > kAmaxParts ? kAmaxParts : want));
+        hipLaunchKernelGGL(amax_kernel, dim3(parts), dim3(kAmaxThreads), 0, st, src, n, amax_ws);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    QuantNchwArgs a;
+    a.src = src; a.codes = codes; a.scales = scales; a.tscale = tscale; a.amax_ws = amax_ws;
+    a.N = N; a.C = C; a.HW = (int)HW; a.C4 = (int)C4; a.N4 = (int)N4;
+    a.NG = 0; a.items = 0;
+    a.bytes = (uint32_t)(n * 4);
+    a.seed_lo = (uint32_t)seed; a.seed_hi = (uint32_t)(seed >> 32);
+    if (fmt == kFP4)
+        return rnd ? launch_quant_nchw<kFP4, true>(a, st) : launch_quant_nchw<kFP4, false>(a, st);
+    return rnd ? launch_quant_nchw<kFP6, true>(a, st) : launch_quant_nchw<kFP6, false>(a, st);
 }
 
 } // namespace mq

@@ -4,10 +4,10 @@
 through the library, following the onedev.kr MicroQonv digest (sections "How it works" and "How it
 differs"):
 
-  forward   X (NCHW) -> channel-batch-first copy (+ amax partials) -> quantize once (RNE)
-            W (OIHW) -> quantized tap-major squares in one call       (quantize once, RNE)
+  forward   X (NCHW) -> quantized channel-batch-first squares, one call  (quantize once, RNE)
+            W (OIHW) -> quantized tap-major squares, one call           (quantize once, RNE)
             Y = conv_fwd(Xq, Wq), back to NCHW
-  backward  G_Y (NCHW) -> channel-batch-first copy (+ amax partials) -> quantize once (SR)
+  backward  G_Y (NCHW) -> quantized channel-batch-first squares, one call (quantize once, SR)
             G_W = conv_wgrad(G_Yq, Xq) (the forward's Xq is kept, not re-quantized)
             G_X = conv_dgrad(Wq, G_Yq)   (the forward's Wq is kept)
 
@@ -32,10 +32,10 @@ from typing import List, Optional, Tuple
 import torch
 from torch import nn
 
-from . import (MQ_NVFP4, MQ_QUANTIZE_AMAX_READY, MQ_QUANTIZE_WS_BYTES, MQ_ROLE_ACT, MQ_ROLE_GRAD,
-               MQ_ROLE_WEIGHT, MQ_RNE, MQ_SR, QTensor, mq_conv_dgrad, mq_conv_fwd,
-               mq_conv_wgrad, mq_quantize, mq_quantize_weight, mq_relayout_cbf,
-               mq_relayout_weight, mq_wgrad_workspace_bytes, out_hw)
+from . import (MQ_NVFP4, MQ_QUANTIZE_WS_BYTES, MQ_ROLE_ACT, MQ_ROLE_GRAD, MQ_ROLE_WEIGHT,
+               MQ_RNE, MQ_SR, QTensor, mq_conv_dgrad, mq_conv_fwd, mq_conv_wgrad,
+               mq_quantize_nchw, mq_quantize_weight, mq_relayout_cbf, mq_relayout_weight,
+               mq_wgrad_workspace_bytes, out_hw)
 
 
 def _check_input(t: torch.Tensor, what: str, ndim: int = 4):
@@ -54,13 +54,11 @@ def quantize_weight(weight: torch.Tensor, fmt: int, ws: torch.Tensor) -> QTensor
 
 def quantize_activation(x: torch.Tensor, fmt: int, rnd: int, seed: int, role: int,
                         ws: torch.Tensor) -> QTensor:
-    """NCHW fp32 tensor -> quantized channel-batch-first tensor (relayout with amax, then
-    quantize with the given rounding)."""
+    """NCHW fp32 tensor -> quantized channel-batch-first tensor with the given rounding (one
+    library call: amax pass, then a pass that reads NCHW and writes squares)."""
     N, C, H, W = x.shape
-    xc = torch.empty(H * W * C * N, dtype=torch.float32, device=x.device)
-    mq_relayout_cbf(x, xc, N, C, H, W, 0, amax_ws=ws)
     q = QTensor(H, W, C, N, fmt, role, x.device)
-    mq_quantize(xc, q, rnd, seed, ws, MQ_QUANTIZE_AMAX_READY)
+    mq_quantize_nchw(x, q, rnd, seed, ws)
     return q
 
 

@@ -3,13 +3,14 @@
 Device buffers for one layer (fp32 inputs, their channel-batch-first copies, the three quantized
 tensors, the outputs and the weight-gradient workspace) and the calls of one pass, in order:
 
-  relayout_x   X NCHW -> CBF (+ amax partials)   quantize_x  X (round to nearest)
+  quantize_x   X NCHW -> quantized channel-batch-first squares (round to nearest)
   quantize_w   W OIHW -> quantized tap-major squares (round to nearest), one call
   quantize_g   G_Y (stochastic, seed per pass)   conv_fwd / conv_wgrad / conv_dgrad
 
-The relayout of X writes its tensor-amax partials, so X's quantization skips the amax pass
-(MQ_QUANTIZE_AMAX_READY). W goes from OIHW to its quantized tap-major layout in one call
-(mq_quantize_weight: no fp32 tap-major copy). G_Y's quantization runs its own amax pass.
+X goes from NCHW to its quantized channel-batch-first layout in one call (mq_quantize_nchw: an
+amax pass, then a pass that reads NCHW and writes squares; no fp32 channel-batch-first copy).
+W goes from OIHW to its quantized tap-major layout in one call (mq_quantize_weight). G_Y's
+quantization runs its own amax pass.
 
 G_Y is taken as already channel-batch-first (it is the next layer's input-gradient output).
 Every call goes through the C ABI on the current stream; nothing here computes.
@@ -21,10 +22,10 @@ from typing import Callable, Dict
 
 import torch
 
-from . import (MQ_QUANTIZE_AMAX_READY, MQ_QUANTIZE_WS_BYTES, MQ_ROLE_ACT, MQ_ROLE_GRAD,
+from . import (MQ_QUANTIZE_WS_BYTES, MQ_ROLE_ACT, MQ_ROLE_GRAD,
                MQ_ROLE_WEIGHT, MQ_RNE, MQ_SR, QTensor, conv_struct,
-               mq_conv_dgrad, mq_conv_fwd, mq_conv_wgrad, mq_quantize, mq_quantize_weight,
-               mq_relayout_cbf, mq_wgrad_workspace_bytes, out_hw)
+               mq_conv_dgrad, mq_conv_fwd, mq_conv_wgrad, mq_quantize, mq_quantize_nchw,
+               mq_quantize_weight, mq_wgrad_workspace_bytes, out_hw)
 
 
 class LayerStep:
@@ -40,7 +41,6 @@ class LayerStep:
         self.fmt, self.sr_seed_base = int(fmt), int(sr_seed_base)
         self.x, self.w, self.gc = x, w, g_cbf
         f32 = dict(dtype=torch.float32, device=dev)
-        self.xc = torch.empty(c.H * c.W * c.Cin * c.N, **f32)
         nws = MQ_QUANTIZE_WS_BYTES
         self.amax = torch.empty(3 * nws, dtype=torch.uint8, device=dev)
         self.qx = QTensor(c.H, c.W, c.Cin, c.N, fmt, MQ_ROLE_ACT, dev)
@@ -54,10 +54,7 @@ class LayerStep:
         a0, a1, a2 = (self.amax[i * nws:(i + 1) * nws] for i in range(3))
         p = self.p
         self.ops: Dict[str, Callable[[int], None]] = OrderedDict([
-            ("relayout_x", lambda s: mq_relayout_cbf(self.x, self.xc, c.N, c.Cin, c.H, c.W, 0,
-                                                     amax_ws=a0)),
-            ("quantize_x", lambda s: mq_quantize(self.xc, self.qx, MQ_RNE, 0, a0,
-                                                 MQ_QUANTIZE_AMAX_READY)),
+            ("quantize_x", lambda s: mq_quantize_nchw(self.x, self.qx, MQ_RNE, 0, a0)),
             ("quantize_w", lambda s: mq_quantize_weight(self.w, self.qw, MQ_RNE, 0, a1)),
             ("quantize_g", lambda s: mq_quantize(self.gc, self.qg, MQ_SR,
                                                  self.sr_seed_base + s, a2)),
@@ -93,10 +90,7 @@ class LayerStep:
                 raise MQError(st, name)
 
         fixed = {
-            "relayout_x": (L.mq_relayout_cbf, (P(self.x), P(self.xc), c.N, c.Cin, c.H, c.W, 0,
-                                               a[0], wsb, hs)),
-            "quantize_x": (L.mq_quantize, (P(self.xc), bx, MQ_RNE, 0, a[0], wsb,
-                                           MQ_QUANTIZE_AMAX_READY, hs)),
+            "quantize_x": (L.mq_quantize_nchw, (P(self.x), bx, MQ_RNE, 0, a[0], wsb, 0, hs)),
             "quantize_w": (L.mq_quantize_weight, (P(self.w), bw, MQ_RNE, 0, a[1], wsb, hs)),
             "conv_fwd": (L.mq_conv_fwd, (conv, bx, bw, P(self.y), hs)),
             "conv_wgrad": (L.mq_conv_wgrad, (conv, bg, bx, P(self.gw), P(self.ws), nws, hs)),

@@ -82,6 +82,17 @@ def test_validation_errors_without_gpu():
     assert L.mq_quantize_weight(y, ctypes.byref(w), 0, 0, None, ws, s0) == mq.MQ_ERR_WORKSPACE
     assert L.mq_quantize_weight(y, ctypes.byref(w), 0, 0, y, ws - 1, s0) == mq.MQ_ERR_WORKSPACE
     assert L.mq_quantize_weight(y, ctypes.byref(w), 0, 0, ctypes.c_void_p(0x2002), ws, s0) == mq.MQ_ERR_ARG
+    # NCHW activations / gradients straight to the quantized layout
+    assert L.mq_quantize_nchw(None, ctypes.byref(x), 0, 0, y, ws, 0, s0) == mq.MQ_ERR_ARG
+    assert L.mq_quantize_nchw(y, ctypes.byref(x), 2, 0, y, ws, 0, s0) == mq.MQ_ERR_ARG
+    assert L.mq_quantize_nchw(y, ctypes.byref(x), 0, 0, y, ws, 4, s0) == mq.MQ_ERR_ARG  # flag
+    assert L.mq_quantize_nchw(y, ctypes.byref(w), 0, 0, y, ws, 0, s0) == mq.MQ_ERR_SHAPE  # role
+    assert L.mq_quantize_nchw(y, ctypes.byref(g), 1, 0, None, ws, 0, s0) == mq.MQ_ERR_WORKSPACE
+    assert L.mq_quantize_nchw(y, ctypes.byref(g), 1, 0, y, ws - 4, 0, s0) == mq.MQ_ERR_WORKSPACE
+    assert L.mq_quantize_nchw(y, ctypes.byref(g), 1, 0, ctypes.c_void_p(0x2002), ws, 0, s0) == mq.MQ_ERR_ARG
+    assert L.mq_quantize_nchw(y, ctypes.byref(bad), 0, 0, y, ws, 0, s0) == mq.MQ_ERR_ARG
+    big = _fake_q((1024, 1024, 32, 16))  # 2^31 source bytes once padded
+    assert L.mq_quantize_nchw(y, ctypes.byref(big), 0, 0, y, ws, 0, s0) == mq.MQ_ERR_UNSUPPORTED
     # misaligned codes (16 B) or scales (4 B) -> MQ_ERR_ARG
     mis = mq.mq_qtensor(8, 8, 16, 2, mq.MQ_NVFP4, mq.MQ_ROLE_ACT, 0x1008, 0x1000, 0x1000)
     assert L.mq_quantize(y, ctypes.byref(mis), 0, 0, y, ws, 0, s0) == mq.MQ_ERR_ARG

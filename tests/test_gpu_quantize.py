@@ -195,6 +195,83 @@ def test_relayout_amax_then_quantize(case, shape, fmt):
                        f"weight {case}")
 
 
+# ---- activations and gradients straight from NCHW (mq_quantize_nchw) ----------------------
+
+NCHW_SHAPES = [  # (N, C, H, W): batch and channel counts off and on multiples of 4 and 16,
+    # pixel counts below, at and past whole 64-pixel waves
+    (1, 1, 1, 1), (2, 3, 5, 7), (4, 4, 8, 8), (5, 9, 3, 11), (16, 8, 8, 8), (32, 64, 14, 14),
+    (7, 20, 9, 13), (12, 6, 16, 9), (8, 16, 1, 64), (3, 130, 2, 33),
+]
+
+
+@pytest.mark.parametrize("fmt", [4, 6])
+@pytest.mark.parametrize("rnd", [0, 1])
+@pytest.mark.parametrize("shape", NCHW_SHAPES)
+def test_quantize_nchw_matches_relayout_then_quantize(shape, fmt, rnd):
+    """Codes, scales and T bit-exact against the oracle's quantization of the channel-batch-first
+    tensor, with the amax pass inside the call and with partials from a relayout."""
+    N, C, H, W = shape
+    log("quantize_nchw", shape, fmt, rnd)
+    x = workloads.random_array(shape, seed=N * 31 + C + H, dist="relu" if rnd == 0 else "normal")
+    seed = 4242 + rnd
+    ref = oracle.quantize(oracle.nchw_to_cbf(x), fmt, rnd, seed)
+    t = to_dev(x)
+    role = mq.MQ_ROLE_GRAD if rnd else mq.MQ_ROLE_ACT
+    ws = mq.quantize_workspace()
+    q = mq.QTensor(H, W, C, N, fmt, role)
+    mq.mq_quantize_nchw(t, q, rnd, seed, ws)
+    torch.cuda.synchronize()
+    assert_quant_equal(q, ref, fmt, f"nchw {shape} {fmt} {rnd}")
+    # amax partials written by a relayout of the same values
+    xc = torch.empty(x.size, dtype=torch.float32, device="cuda")
+    ws2 = mq.quantize_workspace()
+    mq.mq_relayout_cbf(t, xc, N, C, H, W, 0, amax_ws=ws2)
+    q2 = mq.QTensor(H, W, C, N, fmt, role)
+    mq.mq_quantize_nchw(t, q2, rnd, seed, ws2, mq.MQ_QUANTIZE_AMAX_READY)
+    torch.cuda.synchronize()
+    assert_quant_equal(q2, ref, fmt, f"nchw amax-ready {shape} {fmt} {rnd}")
+
+
+@pytest.mark.parametrize("fmt", [4, 6])
+@pytest.mark.parametrize("case", ["zeros", "neg_zeros", "nan", "inf", "tiny", "denormal", "huge",
+                                  "sparse_zero_squares", "ties"])
+def test_quantize_nchw_special_values(case, fmt):
+    shape = (2, 3, 9, 10)
+    x = SPECIAL[case](shape)
+    for rnd in (0, 1):
+        q = mq.QTensor(9, 10, 3, 2, fmt, mq.MQ_ROLE_ACT)
+        mq.mq_quantize_nchw(to_dev(x), q, rnd, 99, mq.quantize_workspace())
+        torch.cuda.synchronize()
+        assert_quant_equal(q, oracle.quantize(oracle.nchw_to_cbf(x), fmt, rnd, 99), fmt,
+                           f"nchw {case} {rnd}")
+
+
+@pytest.mark.parametrize("cfg", ["c2", "c3", "c5"])
+def test_quantize_nchw_full_size_layers(cfg):
+    """The layer inputs (RNE) and output gradients (SR) of the workloads at full size."""
+    layers = workloads.CONFIGS[cfg]()
+    if cfg == "c5":
+        layers = [layers[0], layers[5]]  # the largest input and a stride-2 output gradient
+    for layer in layers:
+        log("full-size quantize_nchw", layer.name)
+        x, _, g = workloads.make_tensors(layer)
+        for name, a, role, rnd, seed in (("x", x, mq.MQ_ROLE_ACT, 0, 0),
+                                         ("g", g, mq.MQ_ROLE_GRAD, 1, layer.sr_seed)):
+            n_, c_, h_, w_ = a.shape
+            q = mq.QTensor(h_, w_, c_, n_, layer.fmt, role)
+            mq.mq_quantize_nchw(to_dev(a), q, rnd, seed, mq.quantize_workspace())
+            torch.cuda.synchronize()
+            assert_quant_equal(q, oracle.quantize(oracle.nchw_to_cbf(a), layer.fmt, rnd, seed),
+                               layer.fmt, f"{layer.name}.{name}")
+
+
+def test_quantize_nchw_rejects_weight_role():
+    q = mq.QTensor(3, 3, 8, 8, 4, mq.MQ_ROLE_WEIGHT, "cuda")
+    with pytest.raises(mq.MQError):
+        mq.mq_quantize_nchw(torch.zeros(8, 8, 3, 3, device="cuda"), q, 0, 0,
+                            mq.quantize_workspace("cuda"))
+
+
 # ---- weights straight from OIHW (mq_quantize_weight) -------------------------------------
 
 WEIGHT_SHAPES = [  # (Cout, Cin, Kh, Kw): small (one launch) and large (amax pass + gather)
