@@ -45,18 +45,33 @@ struct WgradArgs {
 // pixel and channel square is then 32 contiguous bytes, so neighbouring lanes stay contiguous).
 // Output pixels per stage: 16 / KS for stride 1, 8 / KS for stride 2 (twice as wide an X
 // segment), so that two stage buffers fit in LDS.
-template <int SI, int KS> struct StagePixels { static constexpr int kPW = (SI == 1 ? 16 : 8) / KS; };
+// GL (stride 1, and the batch has a multiple of 16 elements, so every item is four real squares
+// or none): the stage width is chosen so that the stage has exactly 512 items, one per producer
+// lane (7 pixels for KS = 2, 15 for KS = 1), so that each SIMD decodes two items per stage
+// instead of three on one of them. A wave may then hold G_Y and X items at once, so items are
+// loaded through per-lane global addresses instead of buffer descriptors.
+template <int SI, int KS, bool GL> struct StagePixels {
+    static constexpr int kPW = GL ? (SI == 1 ? (KS == 2 ? 7 : 15) : (KS == 2 ? 5 : 10))
+                                  : (SI == 1 ? 16 : 8) / KS;
+};
+inline int stage_pixels(int si, int ks, bool gl)
+{
+    return gl ? (si == 1 ? (ks == 2 ? 7 : 15) : (ks == 2 ? 5 : 10)) : (si == 1 ? 16 : 8) / ks;
+}
 // Producer threads: two waves per SIMD, so that one wave's decode overlaps the other's LDS
 // writes and load issue (one producer wave per SIMD left each stage producer-bound).
 constexpr int kNP = 512;
 constexpr int kWgradThreads = 256 + kNP;
 inline int stage_ks(int N4) { return N4 >= 8 ? 2 : 1; }
+// (stride 2 keeps the descriptor path: its global-load variant made the compiler wait for the
+// stage just loaded inside the loop)
+inline bool stage_gl(int N4, int si) { return N4 % 4 == 0 && si == 1; }
 
 // KF: the kernel width Kw when fixed at compile time (1 or 3), 0 = read at run time.
-template <int FMT, int SI, int KF, int kKS>
+template <int FMT, int SI, int KF, int kKS, bool GL>
 __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
 {
-    constexpr int kPWg = StagePixels<SI, kKS>::kPW;
+    constexpr int kPWg = StagePixels<SI, kKS, GL>::kPW;
     constexpr int KWM = KF ? KF : 3;
     constexpr int HCM = (kPWg - 1) * SI + KWM;
     constexpr int GBYTES = kPWg * kKS * 64 * kRowBytes, XBYTES = HCM * kKS * 64 * kRowBytes;
@@ -88,8 +103,8 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
         // Producer items: it < nG -> G_Y strip (pixel, co4, batch half); else X segment (column,
         // ci4, batch half). With KS = 2 bit 0 picks the half of the stage's eight batch squares,
         // four squares (consecutive in memory) per item, so neighbouring lanes read neighbouring
-        // 32-byte pieces of one pixel's [channel square][batch square] block. nG is a whole
-        // number of waves, so no wave mixes the two kinds.
+        // 32-byte pieces of one pixel's [channel square][batch square] block. Without GL, nG is a
+        // whole number of waves, so no wave mixes the two kinds.
         // Two register stages: stage c + 3 is loaded into the slot stage c + 1 was just decoded
         // from (two stage times ahead of its use). The loop is unrolled by two so that slots are
         // never copied, which keeps the compiler's waits down to the stage being decoded.
@@ -99,6 +114,59 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
         int l_nc = st0 % a.nch, l_ob = (st0 / a.nch) % a.owb, l_oh = st0 / a.nch / a.owb;
         auto load = [&](int st, RawItem<FMT>(&dst)[ITEMS]) {
             const int nc = l_nc, ob = l_ob, oh = l_oh;
+            if constexpr (GL) {
+                {
+                    const bool c1 = l_nc + 1 >= a.nch;
+                    l_nc = c1 ? 0 : l_nc + 1;
+                    const bool c2 = c1 && l_ob + 1 >= a.owb;
+                    l_ob = c1 ? (c2 ? 0 : l_ob + 1) : l_ob;
+                    l_oh += c2 ? 1 : 0;
+                }
+                const int ow0 = ob * kPWg;
+                const int ih = oh * SI - a.ph + kh;
+                const int iw0 = ow0 * SI - a.pw;
+                constexpr int SH = kKS == 2 ? 1 : 0;
+#pragma unroll
+                for (int q = 0; q < ITEMS; ++q) {
+                    const int it = ptid + q * kNP;
+                    const bool isG = it < nG;
+                    const int nh = it & (kKS - 1); // nG is even, so X items keep the same bit
+                    // every item is four real squares or none (N4 % 4 == 0); an empty item
+                    // reads the array's first squares and decodes them as zeros (mask 0)
+                    const bool nok = st < st1 && a.N4 - 4 * (kKS * nc + nh) > 0;
+                    const int ow = ow0 + (it >> (4 + SH)), co4 = co4_0 + ((it >> SH) & 15);
+                    const uint32_t sqg =
+                        (((uint32_t)oh * a.Wo + ow) * a.Cout4 + co4) * a.N4 + 4 * (kKS * nc + nh);
+                    const bool gok = ow < a.Wo && co4 < a.Cout4;
+                    const int j = it - nG;
+                    const int iw = iw0 + (j >> (4 + SH)), ci4 = ci4_0 + ((j >> SH) & 15);
+                    const uint32_t sqx =
+                        (((uint32_t)ih * a.W + iw) * a.Cin4 + ci4) * a.N4 + 4 * (kKS * nc + nh);
+                    const bool xok = it < nGX && ih >= 0 && ih < a.H && iw >= 0 && iw < a.W &&
+                                     ci4 < a.Cin4;
+                    const bool ok = nok && (isG ? gok : xok);
+                    const uint32_t sq = ok ? (isG ? sqg : sqx) : 0u;
+                    const uint8_t *cp = (isG ? a.g_codes : a.x_codes) + (size_t)sq * CB;
+                    const uint8_t *sp = (isG ? a.g_scales : a.x_scales) + sq;
+                    RawItem<FMT> &r = dst[q];
+                    const u32x4_t v0 = *reinterpret_cast<const u32x4_t *>(cp);
+                    const u32x4_t v1 = *reinterpret_cast<const u32x4_t *>(cp + 16);
+                    if constexpr (FMT == kFP4) {
+                        r.w[0][0] = v0[0]; r.w[0][1] = v0[1]; r.w[1][0] = v0[2]; r.w[1][1] = v0[3];
+                        r.w[2][0] = v1[0]; r.w[2][1] = v1[1]; r.w[3][0] = v1[2]; r.w[3][1] = v1[3];
+                    } else {
+                        const u32x4_t v2 = *reinterpret_cast<const u32x4_t *>(cp + 32);
+                        r.w[0][0] = v0[0]; r.w[0][1] = v0[1]; r.w[0][2] = v0[2];
+                        r.w[1][0] = v0[3]; r.w[1][1] = v1[0]; r.w[1][2] = v1[1];
+                        r.w[2][0] = v1[2]; r.w[2][1] = v1[3]; r.w[2][2] = v2[0];
+                        r.w[3][0] = v2[1]; r.w[3][1] = v2[2]; r.w[3][2] = v2[3];
+                    }
+                    r.sc = *reinterpret_cast<const uint32_t *>(sp); // sq % 4 == 0: one word
+                    r.sh = 0u;
+                    r.m = ok ? 0xFu : 0u;
+                }
+                return;
+            }
             {
                 const bool c1 = l_nc + 1 >= a.nch;
                 l_nc = c1 ? 0 : l_nc + 1;
@@ -135,6 +203,21 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
             }
         };
         auto store = [&](int buf, const RawItem<FMT>(&src)[ITEMS]) {
+            if constexpr (GL) {
+                constexpr int SH = kKS == 2 ? 1 : 0;
+#pragma unroll
+                for (int q = 0; q < ITEMS; ++q) {
+                    const int it = ptid + q * kNP;
+                    if (it >= nGX) continue;
+                    // LDS rows: [pixel or column][reduction step][64 channels]
+                    const bool isG = it < nG;
+                    const int i2 = isG ? it : it - nG;
+                    store_item<FMT, false>(src[q], lds[buf] + (isG ? 0 : GBYTES),
+                                           ((i2 >> (4 + SH)) * kKS + (i2 & (kKS - 1))) * 64 +
+                                               4 * ((i2 >> SH) & 15));
+                }
+                return;
+            }
     #pragma unroll
             for (int q = 0; q < ITEMS; ++q) {
                 const int it = ptid + q * kNP;
@@ -286,7 +369,7 @@ Plan plan(const ConvGeom &g)
 {
     Plan p;
     const int ks = stage_ks(g.N4);
-    const int kPWg = (g.sh == 1 ? 16 : 8) / ks;
+    const int kPWg = stage_pixels(g.sh, ks, stage_gl(g.N4, g.sh));
     p.owb = (g.Wo + kPWg - 1) / kPWg;
     p.nch = (g.N4 + 4 * ks - 1) / (4 * ks);
     p.stages = g.Ho * p.owb * p.nch;
@@ -337,21 +420,28 @@ bool wgrad_fast_supported(const ConvGeom &g)
 
 size_t wgrad_fast_workspace_bytes(const ConvGeom &g) { return plan(g).bytes; }
 
-template <int FMT, int SI, int KS>
+template <int FMT, int SI, int KS, bool GL>
 static void launch_wgrad_ks(const ConvGeom &g, dim3 grid, const WgradArgs &a, hipStream_t st)
 {
     if (g.Kw == 3)
-        hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 3, KS>), grid, dim3(kWgradThreads), 0, st, a);
+        hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 3, KS, GL>), grid, dim3(kWgradThreads), 0, st, a);
     else if (g.Kw == 1)
-        hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 1, KS>), grid, dim3(kWgradThreads), 0, st, a);
-    else hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 0, KS>), grid, dim3(kWgradThreads), 0, st, a);
+        hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 1, KS, GL>), grid, dim3(kWgradThreads), 0, st, a);
+    else hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 0, KS, GL>), grid, dim3(kWgradThreads), 0, st, a);
 }
 
 template <int FMT, int SI>
 static void launch_wgrad_si(const ConvGeom &g, dim3 grid, const WgradArgs &a, hipStream_t st)
 {
-    if (stage_ks(g.N4) == 2) launch_wgrad_ks<FMT, SI, 2>(g, grid, a, st);
-    else launch_wgrad_ks<FMT, SI, 1>(g, grid, a, st);
+    constexpr bool kGL = SI == 1;
+    const bool gl = stage_gl(g.N4, SI);
+    if (stage_ks(g.N4) == 2) {
+        if (gl) launch_wgrad_ks<FMT, SI, 2, kGL>(g, grid, a, st);
+        else launch_wgrad_ks<FMT, SI, 2, false>(g, grid, a, st);
+    } else {
+        if (gl) launch_wgrad_ks<FMT, SI, 1, kGL>(g, grid, a, st);
+        else launch_wgrad_ks<FMT, SI, 1, false>(g, grid, a, st);
+    }
 }
 
 template <int FMT>

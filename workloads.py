@@ -194,4 +194,15 @@ def parity_layers() -> List[ConvLayer]:
                   x_dist="relu", seed=109, sr_seed=15),
         ConvLayer("p.many.s2", N=4, Cin=8, H=100, W=100, Cout=8, Kh=3, Kw=3, stride=2, pad=1,
                   x_dist="normal", seed=110, sr_seed=16),
+        # batches of whole 16-element groups, stride 1: the weight gradient's stages then hold
+        # exactly one staging item per producer lane (15-pixel stages for 16 batch elements,
+        # 7-pixel stages for 32 and more), with ragged pixel blocks and channel tiles
+        ConvLayer("p.b16.s1", N=16, Cin=20, H=17, W=19, Cout=24, Kh=3, Kw=3, stride=1, pad=1,
+                  x_dist="relu", seed=111, sr_seed=17),
+        ConvLayer("p.b32.s1", N=32, Cin=12, H=9, W=23, Cout=40, Kh=3, Kw=3, stride=1, pad=1,
+                  x_dist="normal", seed=112, sr_seed=18),
+        ConvLayer("p.b48.1x1", N=48, Cin=36, H=6, W=11, Cout=20, Kh=1, Kw=1, stride=1, pad=0,
+                  x_dist="silu", seed=113, sr_seed=19),
+        ConvLayer("p.b16.k2", N=16, Cin=8, H=7, W=9, Cout=8, Kh=2, Kw=2, stride=1, pad=0,
+                  x_dist="t3", seed=114, sr_seed=20),
     ]
