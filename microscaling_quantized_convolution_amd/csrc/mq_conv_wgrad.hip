@@ -45,11 +45,11 @@ struct WgradArgs {
 // pixel and channel square is then 32 contiguous bytes, so neighbouring lanes stay contiguous).
 // Output pixels per stage: 16 / KS for stride 1, 8 / KS for stride 2 (twice as wide an X
 // segment), so that two stage buffers fit in LDS.
-// GL (stride 1, and the batch has a multiple of 16 elements, so every item is four real squares
-// or none): the stage width is chosen so that the stage has exactly 512 items, one per producer
-// lane (7 pixels for KS = 2, 15 for KS = 1), so that each SIMD decodes two items per stage
-// instead of three on one of them. A wave may then hold G_Y and X items at once, so items are
-// loaded through per-lane global addresses instead of buffer descriptors.
+// GL (the batch has a multiple of 16 elements, so every item is four real squares or none): the
+// stage width is chosen so that the stage has at most 512 items, one per producer lane (stride
+// 1: 7 pixels for KS = 2, 15 for KS = 1; stride 2: 5 and 10), so that no SIMD decodes more than
+// two items per stage. A wave may then hold G_Y and X items at once, so items are loaded through
+// per-lane global addresses instead of buffer descriptors.
 template <int SI, int KS, bool GL> struct StagePixels {
     static constexpr int kPW = GL ? (SI == 1 ? (KS == 2 ? 7 : 15) : (KS == 2 ? 5 : 10))
                                   : (SI == 1 ? 16 : 8) / KS;
@@ -63,9 +63,7 @@ inline int stage_pixels(int si, int ks, bool gl)
 constexpr int kNP = 512;
 constexpr int kWgradThreads = 256 + kNP;
 inline int stage_ks(int N4) { return N4 >= 8 ? 2 : 1; }
-// (stride 2 keeps the descriptor path: its global-load variant made the compiler wait for the
-// stage just loaded inside the loop)
-inline bool stage_gl(int N4, int si) { return N4 % 4 == 0 && si == 1; }
+inline bool stage_gl(int N4, int si) { return N4 % 4 == 0 && (si == 1 || si == 2); }
 
 // KF: the kernel width Kw when fixed at compile time (1 or 3), 0 = read at run time.
 template <int FMT, int SI, int KF, int kKS, bool GL>
@@ -112,6 +110,20 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
         // (batch chunk, pixel block, output row) of the next load's stage: loads go through the
         // stages in order, so the position is stepped with carries instead of divided out
         int l_nc = st0 % a.nch, l_ob = (st0 / a.nch) % a.owb, l_oh = st0 / a.nch / a.owb;
+        // GL: one item per lane (ITEMS == 1), the same (pixel or column, channel square, batch
+        // half) at every stage; its square offset within the stage, its validity along the
+        // channels and its arrays are fixed
+        static_assert(!GL || ITEMS == 1, "one staging item per producer lane");
+        constexpr int SHg = kKS == 2 ? 1 : 0;
+        const bool gl_isG = ptid < nG;
+        const int gl_i2 = gl_isG ? ptid : ptid - nG;
+        const int gl_pix = gl_i2 >> (4 + SHg), gl_c4 = (gl_i2 >> SHg) & 15, gl_nh = gl_i2 & (kKS - 1);
+        const bool gl_inv = ptid < nGX && (gl_isG ? co4_0 + gl_c4 < a.Cout4 : ci4_0 + gl_c4 < a.Cin4);
+        const int gl_lsq = (gl_pix * (gl_isG ? a.Cout4 : a.Cin4) + (gl_isG ? co4_0 : ci4_0) + gl_c4) * a.N4 +
+                           4 * gl_nh;
+        const uint8_t *gl_cb = gl_isG ? a.g_codes : a.x_codes;
+        const uint8_t *gl_sb = gl_isG ? a.g_scales : a.x_scales;
+        const int gl_row = (gl_pix * kKS + gl_nh) * 64 + 4 * gl_c4;
         auto load = [&](int st, RawItem<FMT>(&dst)[ITEMS]) {
             const int nc = l_nc, ob = l_ob, oh = l_oh;
             if constexpr (GL) {
@@ -122,49 +134,37 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
                     l_ob = c1 ? (c2 ? 0 : l_ob + 1) : l_ob;
                     l_oh += c2 ? 1 : 0;
                 }
+                // the stage moves a wave-uniform base; the lane's part is fixed (gl_*)
                 const int ow0 = ob * kPWg;
                 const int ih = oh * SI - a.ph + kh;
                 const int iw0 = ow0 * SI - a.pw;
-                constexpr int SH = kKS == 2 ? 1 : 0;
-#pragma unroll
-                for (int q = 0; q < ITEMS; ++q) {
-                    const int it = ptid + q * kNP;
-                    const bool isG = it < nG;
-                    const int nh = it & (kKS - 1); // nG is even, so X items keep the same bit
-                    // every item is four real squares or none (N4 % 4 == 0); an empty item
-                    // reads the array's first squares and decodes them as zeros (mask 0)
-                    const bool nok = st < st1 && a.N4 - 4 * (kKS * nc + nh) > 0;
-                    const int ow = ow0 + (it >> (4 + SH)), co4 = co4_0 + ((it >> SH) & 15);
-                    const uint32_t sqg =
-                        (((uint32_t)oh * a.Wo + ow) * a.Cout4 + co4) * a.N4 + 4 * (kKS * nc + nh);
-                    const bool gok = ow < a.Wo && co4 < a.Cout4;
-                    const int j = it - nG;
-                    const int iw = iw0 + (j >> (4 + SH)), ci4 = ci4_0 + ((j >> SH) & 15);
-                    const uint32_t sqx =
-                        (((uint32_t)ih * a.W + iw) * a.Cin4 + ci4) * a.N4 + 4 * (kKS * nc + nh);
-                    const bool xok = it < nGX && ih >= 0 && ih < a.H && iw >= 0 && iw < a.W &&
-                                     ci4 < a.Cin4;
-                    const bool ok = nok && (isG ? gok : xok);
-                    const uint32_t sq = ok ? (isG ? sqg : sqx) : 0u;
-                    const uint8_t *cp = (isG ? a.g_codes : a.x_codes) + (size_t)sq * CB;
-                    const uint8_t *sp = (isG ? a.g_scales : a.x_scales) + sq;
-                    RawItem<FMT> &r = dst[q];
-                    const u32x4_t v0 = *reinterpret_cast<const u32x4_t *>(cp);
-                    const u32x4_t v1 = *reinterpret_cast<const u32x4_t *>(cp + 16);
-                    if constexpr (FMT == kFP4) {
-                        r.w[0][0] = v0[0]; r.w[0][1] = v0[1]; r.w[1][0] = v0[2]; r.w[1][1] = v0[3];
-                        r.w[2][0] = v1[0]; r.w[2][1] = v1[1]; r.w[3][0] = v1[2]; r.w[3][1] = v1[3];
-                    } else {
-                        const u32x4_t v2 = *reinterpret_cast<const u32x4_t *>(cp + 32);
-                        r.w[0][0] = v0[0]; r.w[0][1] = v0[1]; r.w[0][2] = v0[2];
-                        r.w[1][0] = v0[3]; r.w[1][1] = v1[0]; r.w[1][2] = v1[1];
-                        r.w[2][0] = v1[2]; r.w[2][1] = v1[3]; r.w[2][2] = v2[0];
-                        r.w[3][0] = v2[1]; r.w[3][1] = v2[2]; r.w[3][2] = v2[3];
-                    }
-                    r.sc = *reinterpret_cast<const uint32_t *>(sp); // sq % 4 == 0: one word
-                    r.sh = 0u;
-                    r.m = ok ? 0xFu : 0u;
+                const int bg = ((oh * a.Wo + ow0) * a.Cout4) * a.N4 + 4 * kKS * nc;
+                const int bx = ((ih * a.W + iw0) * a.Cin4) * a.N4 + 4 * kKS * nc;
+                // every item is four real squares or none (N4 % 4 == 0); an empty item reads
+                // the array's first squares and decodes them as zeros (mask 0)
+                const bool nok = st < st1 && 4 * gl_nh < a.N4 - 4 * kKS * nc;
+                const bool pok = gl_isG ? gl_pix < a.Wo - ow0
+                                        : (ih >= 0 && ih < a.H && gl_pix >= -iw0 && gl_pix < a.W - iw0);
+                const bool ok = gl_inv && nok && pok;
+                const uint32_t sq = ok ? (uint32_t)((gl_isG ? bg : bx) + gl_lsq) : 0u;
+                const uint8_t *cp = gl_cb + (size_t)sq * CB;
+                const uint8_t *sp = gl_sb + sq;
+                RawItem<FMT> &r = dst[0];
+                const u32x4_t v0 = *reinterpret_cast<const u32x4_t *>(cp);
+                const u32x4_t v1 = *reinterpret_cast<const u32x4_t *>(cp + 16);
+                if constexpr (FMT == kFP4) {
+                    r.w[0][0] = v0[0]; r.w[0][1] = v0[1]; r.w[1][0] = v0[2]; r.w[1][1] = v0[3];
+                    r.w[2][0] = v1[0]; r.w[2][1] = v1[1]; r.w[3][0] = v1[2]; r.w[3][1] = v1[3];
+                } else {
+                    const u32x4_t v2 = *reinterpret_cast<const u32x4_t *>(cp + 32);
+                    r.w[0][0] = v0[0]; r.w[0][1] = v0[1]; r.w[0][2] = v0[2];
+                    r.w[1][0] = v0[3]; r.w[1][1] = v1[0]; r.w[1][2] = v1[1];
+                    r.w[2][0] = v1[2]; r.w[2][1] = v1[3]; r.w[2][2] = v2[0];
+                    r.w[3][0] = v2[1]; r.w[3][1] = v2[2]; r.w[3][2] = v2[3];
                 }
+                r.sc = *reinterpret_cast<const uint32_t *>(sp); // sq % 4 == 0: one word
+                r.sh = 0u;
+                r.m = ok ? 0xFu : 0u;
                 return;
             }
             {
@@ -204,18 +204,9 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
         };
         auto store = [&](int buf, const RawItem<FMT>(&src)[ITEMS]) {
             if constexpr (GL) {
-                constexpr int SH = kKS == 2 ? 1 : 0;
-#pragma unroll
-                for (int q = 0; q < ITEMS; ++q) {
-                    const int it = ptid + q * kNP;
-                    if (it >= nGX) continue;
-                    // LDS rows: [pixel or column][reduction step][64 channels]
-                    const bool isG = it < nG;
-                    const int i2 = isG ? it : it - nG;
-                    store_item<FMT, false>(src[q], lds[buf] + (isG ? 0 : GBYTES),
-                                           ((i2 >> (4 + SH)) * kKS + (i2 & (kKS - 1))) * 64 +
-                                               4 * ((i2 >> SH) & 15));
-                }
+                // LDS rows: [pixel or column][reduction step][64 channels]
+                if (ptid < nGX)
+                    store_item<FMT, false>(src[0], lds[buf] + (gl_isG ? 0 : GBYTES), gl_row);
                 return;
             }
     #pragma unroll
@@ -433,7 +424,7 @@ static void launch_wgrad_ks(const ConvGeom &g, dim3 grid, const WgradArgs &a, hi
 template <int FMT, int SI>
 static void launch_wgrad_si(const ConvGeom &g, dim3 grid, const WgradArgs &a, hipStream_t st)
 {
-    constexpr bool kGL = SI == 1;
+    constexpr bool kGL = true;
     const bool gl = stage_gl(g.N4, SI);
     if (stage_ks(g.N4) == 2) {
         if (gl) launch_wgrad_ks<FMT, SI, 2, kGL>(g, grid, a, st);

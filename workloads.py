@@ -201,8 +201,15 @@ def parity_layers() -> List[ConvLayer]:
                   x_dist="relu", seed=111, sr_seed=17),
         ConvLayer("p.b32.s1", N=32, Cin=12, H=9, W=23, Cout=40, Kh=3, Kw=3, stride=1, pad=1,
                   x_dist="normal", seed=112, sr_seed=18),
-        ConvLayer("p.b48.1x1", N=48, Cin=36, H=6, W=11, Cout=20, Kh=1, Kw=1, stride=1, pad=0,
-                  x_dist="silu", seed=113, sr_seed=19),
+        ConvLayer("p.b48.1x1.fp6", N=48, Cin=36, H=6, W=11, Cout=20, Kh=1, Kw=1, stride=1,
+                  pad=0, fmt=FP6, x_dist="silu", seed=113, sr_seed=19),
         ConvLayer("p.b16.k2", N=16, Cin=8, H=7, W=9, Cout=8, Kh=2, Kw=2, stride=1, pad=0,
                   x_dist="t3", seed=114, sr_seed=20),
+        # the same at stride 2 (10-pixel stages for 16 batch elements, 5 for 32 and more)
+        ConvLayer("p.b16.s2", N=16, Cin=20, H=15, W=17, Cout=24, Kh=3, Kw=3, stride=2, pad=1,
+                  x_dist="relu", seed=115, sr_seed=21),
+        ConvLayer("p.b32.s2.fp6", N=32, Cin=12, H=11, W=13, Cout=20, Kh=3, Kw=3, stride=2,
+                  pad=1, fmt=FP6, x_dist="normal", seed=116, sr_seed=22),
+        ConvLayer("p.b32.1x1s2", N=32, Cin=24, H=9, W=10, Cout=36, Kh=1, Kw=1, stride=2, pad=0,
+                  x_dist="silu", seed=117, sr_seed=23),
     ]
