@@ -90,19 +90,21 @@ __device__ __forceinline__ uint32_t grid_rne(float a)
 }
 
 // Stochastic grid rounding of a = |q|: from the lower neighbour up iff u16 < frac * 65536,
-// frac = (a - lo) / step (exact; lo is the grid value at or below a, step a power of two).
+// frac = (a - lo) / step (lo is the grid value at or below a, step a power of two).
+// With x = a / step (exact) that is ceil(x - u16 / 65536): for x < 2^8 the difference is exact
+// or keeps its sign and integer part (for x below 1 with a draw far above it), so its ceiling
+// is floor(x) + 1 exactly when the fractional part exceeds the draw. Codes past the largest
+// element saturate (the min).
 template <int FMT>
 __device__ __forceinline__ uint32_t grid_sr(float a, uint32_t u16)
 {
     using F = Fmt<FMT>;
-    float sc = a < 2.0f ? F::kScale0 : (a < 4.0f ? 0.5f * F::kScale0 : 0.25f * F::kScale0);
-    float ad = a < 2.0f ? 0.0f : (a < 4.0f ? F::kAdd1 : F::kAdd2);
+    const float sc = a < 2.0f ? F::kScale0 : (a < 4.0f ? 0.5f * F::kScale0 : 0.25f * F::kScale0);
+    const uint32_t ad = a < 2.0f ? 0u : (a < 4.0f ? (uint32_t)F::kAdd1 : (uint32_t)F::kAdd2);
     const float x = a * sc;                   // exact: sc is a power of two
-    const float fl = __builtin_floorf(x);
-    const float frac = x - fl;                // exact (Sterbenz for x >= 1; fl = 0 below)
-    uint32_t up = ((float)u16 < frac * 65536.0f) ? 1u : 0u;
-    const uint32_t c = (uint32_t)(fl + ad) + up;
-    return a >= F::kEmax ? F::kMaxMag : c;   // at or above the largest element: saturate
+    const float y = __builtin_fmaf(-(float)u16, 0x1p-16f, x);
+    const uint32_t c = (uint32_t)__builtin_ceilf(y) + ad;
+    return c < F::kMaxMag ? c : F::kMaxMag;
 }
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): multipliers 0xD2511F53 / 0xCD9E8D57,

@@ -381,18 +381,24 @@ template <int FMT, int NQ>
 __device__ __forceinline__ void store_group(const QuantNchwArgs &a, int t0, const uint32_t (&w)[NQ][3],
                                             const uint32_t (&bc)[NQ])
 {
-    if constexpr (NQ == 4) {
-        // t0 is a multiple of 4: 32 (NVFP4) or 48 (NVFP6) aligned code bytes, one scale word
-        uint4 *dst = reinterpret_cast<uint4 *>(a.codes + (FMT == kFP4 ? 8 : 12) * (int64_t)t0);
-        if (FMT == kFP4) {
-            dst[0] = make_uint4(w[0][0], w[0][1], w[1][0], w[1][1]);
-            dst[1] = make_uint4(w[2][0], w[2][1], w[3][0], w[3][1]);
-        } else {
-            dst[0] = make_uint4(w[0][0], w[0][1], w[0][2], w[1][0]);
-            dst[1] = make_uint4(w[1][1], w[1][2], w[2][0], w[2][1]);
-            dst[2] = make_uint4(w[2][2], w[3][0], w[3][1], w[3][2]);
+    if constexpr (NQ % 4 == 0) {
+        // t0 is a multiple of 4: per four squares 32 (NVFP4) or 48 (NVFP6) aligned code bytes
+        // and one scale word
+#pragma unroll
+        for (int g = 0; g < NQ / 4; ++g) {
+            const int b = 4 * g;
+            uint4 *dst = reinterpret_cast<uint4 *>(a.codes + (FMT == kFP4 ? 8 : 12) * (int64_t)(t0 + b));
+            if (FMT == kFP4) {
+                dst[0] = make_uint4(w[b][0], w[b][1], w[b + 1][0], w[b + 1][1]);
+                dst[1] = make_uint4(w[b + 2][0], w[b + 2][1], w[b + 3][0], w[b + 3][1]);
+            } else {
+                dst[0] = make_uint4(w[b][0], w[b][1], w[b][2], w[b + 1][0]);
+                dst[1] = make_uint4(w[b + 1][1], w[b + 1][2], w[b + 2][0], w[b + 2][1]);
+                dst[2] = make_uint4(w[b + 2][2], w[b + 3][0], w[b + 3][1], w[b + 3][2]);
+            }
+            *reinterpret_cast<uint32_t *>(a.scales + t0 + b) =
+                bc[b] | (bc[b + 1] << 8) | (bc[b + 2] << 16) | (bc[b + 3] << 24);
         }
-        *reinterpret_cast<uint32_t *>(a.scales + t0) = bc[0] | (bc[1] << 8) | (bc[2] << 16) | (bc[3] << 24);
     } else {
 #pragma unroll
         for (int k = 0; k < NQ; ++k) {
@@ -402,7 +408,33 @@ __device__ __forceinline__ void store_group(const QuantNchwArgs &a, int t0, cons
     }
 }
 
-template <int FMT, bool SR, int NQ>
+template <int PX> struct PixelLoad;
+template <> struct PixelLoad<1> {
+    static __device__ __forceinline__ void get(rsrc_t r, uint32_t v, uint32_t s, float (&o)[1])
+    {
+        o[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)v, (int)s, 0));
+    }
+};
+template <> struct PixelLoad<2> {
+    static __device__ __forceinline__ void get(rsrc_t r, uint32_t v, uint32_t s, float (&o)[2])
+    {
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t t = __builtin_amdgcn_raw_buffer_load_b64(r, (int)v, (int)s, 0);
+        o[0] = __uint_as_float(t[0]); o[1] = __uint_as_float(t[1]);
+    }
+};
+template <> struct PixelLoad<4> {
+    static __device__ __forceinline__ void get(rsrc_t r, uint32_t v, uint32_t s, float (&o)[4])
+    {
+        const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(r, (int)v, (int)s, 0);
+        o[0] = __uint_as_float(t[0]); o[1] = __uint_as_float(t[1]);
+        o[2] = __uint_as_float(t[2]); o[3] = __uint_as_float(t[3]);
+    }
+};
+
+// PX: consecutive pixels per lane, read as one PX-float load per (n, c) plane (H*W a multiple
+// of PX and the source PX*4-byte aligned, so a lane's pixels are all inside or all past H*W).
+template <int FMT, bool SR, int NQ, int PX>
 __global__ void __launch_bounds__(256) quantize_nchw_kernel(QuantNchwArgs a)
 {
     using F = Fmt<FMT>;
@@ -423,7 +455,7 @@ __global__ void __launch_bounds__(256) quantize_nchw_kernel(QuantNchwArgs a)
     if (item >= a.items) return;
     const int lane = threadIdx.x & 63;
     const int ng = item % a.NG, c4 = (item / a.NG) % a.C4, pb = item / a.NG / a.C4;
-    const int p = pb * 64 + lane;
+    const int p = (pb * 64 + lane) * PX;
     const bool pin = p < a.HW;
     // lane offset of element (n, c) = (4*ng*NQ, 4*c4); the others add a wave-uniform offset.
     // Rows n >= N lie past the end of the tensor and read as zero through the range check;
@@ -431,7 +463,7 @@ __global__ void __launch_bounds__(256) quantize_nchw_kernel(QuantNchwArgs a)
     const rsrc_t src = make_rsrc(a.src, a.bytes);
     const uint32_t CHW4 = (uint32_t)a.C * (uint32_t)a.HW * 4u, HW4 = (uint32_t)a.HW * 4u;
     const uint32_t lane_off = (uint32_t)(4 * ng * NQ) * CHW4 + (uint32_t)(4 * c4) * HW4 + 4u * (uint32_t)p;
-    float x[NQ][16];
+    float x[PX][NQ][16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const bool cin = 4 * c4 + i < a.C;
@@ -439,43 +471,50 @@ __global__ void __launch_bounds__(256) quantize_nchw_kernel(QuantNchwArgs a)
 #pragma unroll
         for (int k = 0; k < NQ; ++k)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                x[k][4 * i + j] = __builtin_bit_cast(
-                    float, __builtin_amdgcn_raw_buffer_load_b32(
-                               src, (int)voff, (int)((uint32_t)(4 * k + j) * CHW4 + (uint32_t)i * HW4), 0));
+            for (int j = 0; j < 4; ++j) {
+                float v[PX];
+                PixelLoad<PX>::get(src, voff, (uint32_t)(4 * k + j) * CHW4 + (uint32_t)i * HW4, v);
+#pragma unroll
+                for (int q = 0; q < PX; ++q) x[q][k][4 * i + j] = v[q];
+            }
     }
     if (!pin) return;
-    const int t0 = (p * a.C4 + c4) * a.N4 + ng * NQ; // square indices fit in 31 bits
-    uint32_t w[NQ][3], bc[NQ];
 #pragma unroll
-    for (int k = 0; k < NQ; ++k) {
-        Philox4 r0 = {}, r1 = {};
-        if (SR) {
-            const uint64_t jj = 2u * (uint64_t)(t0 + k);
-            r0 = philox4x32_10((uint32_t)jj, (uint32_t)(jj >> 32), 0u, 0u, a.seed_lo, a.seed_hi);
-            r1 = philox4x32_10((uint32_t)(jj + 1), (uint32_t)((jj + 1) >> 32), 0u, 0u, a.seed_lo,
-                               a.seed_hi);
+    for (int q = 0; q < PX; ++q) {
+        const int t0 = ((p + q) * a.C4 + c4) * a.N4 + ng * NQ; // square indices fit in 31 bits
+        uint32_t w[NQ][3], bc[NQ];
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+            Philox4 r0 = {}, r1 = {};
+            if (SR) {
+                const uint64_t jj = 2u * (uint64_t)(t0 + k);
+                r0 = philox4x32_10((uint32_t)jj, (uint32_t)(jj >> 32), 0u, 0u, a.seed_lo, a.seed_hi);
+                r1 = philox4x32_10((uint32_t)(jj + 1), (uint32_t)((jj + 1) >> 32), 0u, 0u,
+                                   a.seed_lo, a.seed_hi);
+            }
+            bc[k] = quantize_square<FMT, SR>(x[q][k], T, nonfinite, r0, r1, w[k]);
         }
-        bc[k] = quantize_square<FMT, SR>(x[k], T, nonfinite, r0, r1, w[k]);
+        store_group<FMT, NQ>(a, t0, w, bc);
     }
-    store_group<FMT, NQ>(a, t0, w, bc);
+}
+
+template <int FMT, bool SR, int NQ, int PX>
+static void launch_nchw_shape(QuantNchwArgs a, hipStream_t st)
+{
+    const int pbs = (a.HW + 64 * PX - 1) / (64 * PX);
+    a.NG = a.N4 / NQ;
+    a.items = pbs * a.C4 * a.NG;
+    hipLaunchKernelGGL((quantize_nchw_kernel<FMT, SR, NQ, PX>), dim3((a.items + 3) / 4), dim3(256),
+                       0, st, a);
 }
 
 template <int FMT, bool SR>
-static hipError_t launch_quant_nchw(const QuantNchwArgs &a0, hipStream_t st)
+static hipError_t launch_quant_nchw(const QuantNchwArgs &a, hipStream_t st)
 {
-    QuantNchwArgs a = a0;
-    const int pbs = (a.HW + 63) / 64;
-    const dim3 block(256);
-    if (a.N4 % 4 == 0) {
-        a.NG = a.N4 / 4;
-        a.items = pbs * a.C4 * a.NG;
-        hipLaunchKernelGGL((quantize_nchw_kernel<FMT, SR, 4>), dim3((a.items + 3) / 4), block, 0, st, a);
-    } else {
-        a.NG = a.N4;
-        a.items = pbs * a.C4 * a.NG;
-        hipLaunchKernelGGL((quantize_nchw_kernel<FMT, SR, 1>), dim3((a.items + 3) / 4), block, 0, st, a);
-    }
+    const bool al16 = (reinterpret_cast<uintptr_t>(a.src) & 15u) == 0;
+    if (a.N4 % 4 == 0) launch_nchw_shape<FMT, SR, 4, 1>(a, st);
+    else if (al16 && a.HW % 4 == 0) launch_nchw_shape<FMT, SR, 1, 4>(a, st);
+    else launch_nchw_shape<FMT, SR, 1, 1>(a, st);
     return hipGetLastError();
 }
 
@@ -493,41 +532,47 @@ __global__ void __launch_bounds__(kSmallThreads) quantize_weight_small_kernel(Qu
     using F = Fmt<FMT>;
     __shared__ uint32_t red[kSmallThreads / 64];
     const int n = (int)(a.planes * a.R * a.S);
-    uint32_t m = 0u;
-    int tail = 0;
-    if ((reinterpret_cast<uintptr_t>(a.src) & 15u) == 0) {
-        const int n4 = n >> 2;
-        const u32x4_t *x4 = reinterpret_cast<const u32x4_t *>(a.src);
-        int j = threadIdx.x;
-        for (; j + 7 * kSmallThreads < n4; j += 8 * kSmallThreads) {
-            u32x4_t v[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) v[k] = x4[j + k * kSmallThreads];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) m = max(m, absmax4(v[k]));
-        }
-        for (; j < n4; j += kSmallThreads) m = max(m, absmax4(x4[j]));
-        tail = n4 << 2;
-    }
-    for (int j = tail + threadIdx.x; j < n; j += kSmallThreads)
-        m = max(m, __float_as_uint(a.src[j]) & 0x7FFFFFFFu);
-    const uint32_t abits = block_max_u32<kSmallThreads>(m, red);
-    const bool nonfinite = abits >= 0x7F800000u;
-    const float T = __uint_as_float(abits) / (448.0f * F::kEmax);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *a.tscale = nonfinite ? __uint_as_float(0x7FC00000u) : T;
+    // The square's own 16 values and the whole-tensor amax reads do not depend on each other:
+    // all of them are issued before any is used, so the launch costs one memory round trip.
     const int t = (int)blockIdx.x * kSmallSquares + (int)threadIdx.x;
-    if (threadIdx.x >= kSmallSquares || t >= (int)a.nsq) return;
+    const bool mine = threadIdx.x < kSmallSquares && t < (int)a.nsq;
+    const int tt = mine ? t : 0;
     const int planes = (int)a.planes;
-    const int s4 = t % a.S4, r4 = (t / a.S4) % a.R4, plane = t / a.S4 / a.R4;
+    const int s4 = tt % a.S4, r4 = (tt / a.S4) % a.R4, plane = tt / a.S4 / a.R4;
     float x[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 4 * r4 + i, c = 4 * s4 + j;
-            const bool in = r < a.R && c < a.S;
+            const bool in = mine && r < a.R && c < a.S;
             x[4 * i + j] = in ? a.src[(r * a.S + c) * planes + plane] : 0.0f;
         }
+    uint32_t m = 0u;
+    if ((reinterpret_cast<uintptr_t>(a.src) & 15u) == 0) {
+        // n <= kSmallWeight: at most kSmallWeight / 4 / kSmallThreads 16-byte loads per lane
+        constexpr int kV = kSmallWeight / 4 / kSmallThreads;
+        const int n4 = n >> 2;
+        const u32x4_t *x4 = reinterpret_cast<const u32x4_t *>(a.src);
+        u32x4_t v[kV];
+#pragma unroll
+        for (int k = 0; k < kV; ++k) {
+            const int j = (int)threadIdx.x + k * kSmallThreads;
+            v[k] = j < n4 ? x4[j] : u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int k = 0; k < kV; ++k) m = max(m, absmax4(v[k]));
+        const int tail = (n4 << 2) + (int)threadIdx.x; // n % 4 trailing floats
+        if (tail < n) m = max(m, __float_as_uint(a.src[tail]) & 0x7FFFFFFFu);
+    } else {
+        for (int j = threadIdx.x; j < n; j += kSmallThreads)
+            m = max(m, __float_as_uint(a.src[j]) & 0x7FFFFFFFu);
+    }
+    const uint32_t abits = block_max_u32<kSmallThreads>(m, red);
+    const bool nonfinite = abits >= 0x7F800000u;
+    const float T = __uint_as_float(abits) / (448.0f * F::kEmax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.tscale = nonfinite ? __uint_as_float(0x7FC00000u) : T;
+    if (!mine) return;
     Philox4 r0 = {}, r1 = {};
     if (SR) {
         const uint64_t jj = 2u * (uint64_t)t;
