@@ -2,10 +2,10 @@
 """Benchmark of the quantize-once convolution hot path on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input, for the ResNet-style
-3x3 layer (N=32, Cin=Cout=64, 56x56, stride 1, pad 1, NVFP4): quantize X from NCHW into its
-channel-batch-first squares (round-to-nearest; amax pass + one quantizing pass), quantize W from
-OIHW into its tap-major squares (round-to-nearest, one call), quantize G_Y (stochastic, a new seed
-every step), then the forward, weight-gradient and input-gradient GEMMs. Inputs are resident
+3x3 layer (N=32, Cin=Cout=64, 56x56, stride 1, pad 1, NVFP4): quantize X from NCHW and W from
+OIHW into their squares together, as the forward pass does (round-to-nearest; one batched call:
+an amax launch and a quantizing launch over both), quantize G_Y (stochastic, a new seed every
+step), then the forward, weight-gradient and input-gradient GEMMs. Inputs are resident
 in HBM before the timed region starts.
 
 The timed steps call the C ABI back to back on one stream (arguments marshalled once, so the
@@ -41,6 +41,7 @@ CALIB_ELEMS = 1 << 26        # plain copy for counter calibration: 256 MiB read 
 
 # which kernels make up each op (rocprofv3 kernel names start with these)
 OP_KERNELS = {
+    "quantize_xw": ["mq::amax_batch_kernel", "void mq::quantize_batch_kernel"],
     "quantize_x": ["mq::amax_kernel", "void mq::quantize_nchw_kernel"],
     "quantize_w": ["void mq::quantize_weight_small_kernel", "mq::amax_kernel",
                    "void mq::quantize_kernel"],
@@ -154,10 +155,9 @@ def main():
     qbytes = lambda shape: sq(*shape) * (8 if fmt == 4 else 12) + sq(*shape)  # codes + scales
     nx, nw, ng = x.size, w.size, g.size
     qx_b, qw_b, qg_b = qbytes((H, W, Ci, N)), qbytes((Kh, Kw, Co, Ci)), qbytes((Ho, Wo, Co, N))
-    # algorithmic bytes: quantize of X and G_Y = amax read + quantize read + codes/scales;
-    # quantize of W = one read + codes/scales
+    # algorithmic bytes: every quantization = amax read + quantize read + codes/scales
     alg = {
-        "quantize_x": ("hbm", 8 * nx + qx_b), "quantize_w": ("hbm", 4 * nw + qw_b),
+        "quantize_xw": ("hbm", 8 * nx + qx_b + 8 * nw + qw_b),
         "quantize_g": ("hbm", 8 * ng + qg_b),
         "conv_fwd": ("gemm", flops), "conv_wgrad": ("gemm", flops), "conv_dgrad": ("gemm", flops),
     }
@@ -301,7 +301,8 @@ def main():
         "dtype": "fp16",
         "data": "synthetic (seeded numpy PCG64; X=ReLU(N(0,1)), W Kaiming-normal, G_Y~N(0,1e-3))",
         "config": {"workload": "resnet-3x3-s1p1 N=32 Cin=Cout=64 56x56 NVFP4: quantize X "
-                               "(from NCHW), W, G_Y (RNE, RNE, SR), conv fwd/wgrad/dgrad",
+                               "(from NCHW) and W (from OIHW) in one batched call (RNE), G_Y "
+                               "(SR), conv fwd/wgrad/dgrad",
                    "N": N, "Cin": Ci, "Cout": Co, "H": H, "W": W, "K": Kh, "stride": 1, "pad": 1,
                    "format": "NVFP4 (E2M1 codes, E4M3 4x4-square scales, fp32 tensor scale)",
                    "mfma": "fp16 operands decoded exactly, fp32 accumulate"},
@@ -382,12 +383,11 @@ def run_config(args):
                 f(s_)
         torch.cuda.synchronize()
         if args.inference:  # W stays quantized from the warm-up: activations only
-            calls = collections.OrderedDict((k, calls[k]) for k in
-                                            ("quantize_x", "conv_fwd"))
+            calls = st.inference_calls(stream)
         eb = 0.5625 if l.fmt == 4 else 0.8125
         nx, nw, ng = l.N * l.Cin * l.H * l.W, l.Cout * l.Cin * l.Kh * l.Kw, l.N * l.Cout * l.Ho * l.Wo
         fl = l.gemm_flops()
-        byt = {"quantize_x": 8 * nx + eb * nx,
+        byt = {"quantize_x": 8 * nx + eb * nx, "quantize_xw": 8 * (nx + nw) + eb * (nx + nw),
                "quantize_w": 4 * nw + eb * nw, "quantize_g": 8 * ng + eb * ng,
                "conv_fwd": eb * (nx + nw) + 4 * ng, "conv_wgrad": eb * (nx + ng) + 4 * nw,
                "conv_dgrad": eb * (nw + ng) + 4 * nx}
@@ -429,8 +429,8 @@ def run_config(args):
         "config": {"workload": (f"{args.config} inference: {len(layers)} layers, quantize X "
                                 f"(from NCHW), conv fwd each (weights quantized once)")
                    if args.inference else
-                   (f"{args.config}: {len(layers)} layers, quantize X (from NCHW), W, G_Y, "
-                    f"conv fwd/wgrad/dgrad each")},
+                   (f"{args.config}: {len(layers)} layers, quantize X and W (one batched call), "
+                    f"G_Y, conv fwd/wgrad/dgrad each")},
         "per_layer": per_layer,
     }
     print(json.dumps(result), flush=True)

@@ -187,6 +187,45 @@ mq_status mq_quantize_nchw(const float *src_dev, const mq_qtensor *dst, int32_t 
                            uint32_t *amax_ws_dev, size_t amax_ws_bytes, uint32_t flags,
                            hipStream_t stream);
 
+/* Source order of a batched quantization job (mq_quant_job.layout). */
+typedef enum {
+    MQ_SRC_DENSE = 0, /* [o0][o1][r][s] as stored by the quantized layout (mq_quantize) */
+    MQ_SRC_NCHW = 1,  /* NCHW activation or gradient, dst (o0, o1, r, s) = (H, W, C, N) */
+    MQ_SRC_OIHW = 2   /* OIHW weight, dst (o0, o1, r, s) = (Kh, Kw, Cout, Cin) */
+} mq_source_layout;
+
+#define MQ_QUANTIZE_BATCH_MAX 4
+
+/* One tensor of mq_quantize_batch: what mq_quantize (MQ_SRC_DENSE), mq_quantize_nchw
+ * (MQ_SRC_NCHW) or mq_quantize_weight (MQ_SRC_OIHW) would take, with its own workspace. */
+typedef struct {
+    const float *src;     /* device fp32 source in the order `layout` names */
+    int32_t layout;       /* mq_source_layout */
+    int32_t rnd;          /* mq_round */
+    uint64_t seed;        /* SR seed (ignored for MQ_RNE) */
+    uint32_t flags;       /* 0 or MQ_QUANTIZE_AMAX_READY */
+    mq_qtensor dst;       /* destination (device buffers) */
+    uint32_t *amax_ws;    /* this tensor's amax workspace, device, 4-byte aligned */
+    size_t amax_ws_bytes; /* >= MQ_QUANTIZE_WS_BYTES */
+} mq_quant_job;
+
+/*
+ * mq_quantize_batch: quantize up to MQ_QUANTIZE_BATCH_MAX tensors of one format with one amax
+ * launch and one quantizing launch, each exactly as the single-tensor call for its layout would
+ * (same recipe of the onedev.kr digest, section "How it differs"; same codes, scales, T and
+ * stochastic draws). Batching lets a small tensor share the launches of a large one: the
+ * forward pass of a layer quantizes X (NCHW) and W (OIHW) together.
+ * jobs: host array of njobs (1..MQ_QUANTIZE_BATCH_MAX) job descriptions; every job needs its own
+ *       amax workspace (the same pointer twice is MQ_ERR_ARG).
+ * Errors: MQ_ERR_ARG (null pointer, bad enum or flag, misaligned pointer, non-positive dims,
+ *         shared workspace), MQ_ERR_SHAPE (formats differ between jobs; an NCHW job with a
+ *         weight destination or an OIHW job with another role), MQ_ERR_WORKSPACE (a workspace
+ *         missing or below MQ_QUANTIZE_WS_BYTES), MQ_ERR_UNSUPPORTED (more than
+ *         MQ_QUANTIZE_BATCH_MAX jobs, 2^31 squares or more, or an NCHW source that reaches 2^31
+ *         bytes once zero-padded to whole squares).
+ */
+mq_status mq_quantize_batch(const mq_quant_job *jobs, int32_t njobs, hipStream_t stream);
+
 /*
  * mq_quantize_weight: quantize an OIHW fp32 weight straight into the tap-major quantized layout
  * [Kh][Kw][Cout][Cin] of the 2-D weight matrix (onedev.kr digest, section "How it differs"),

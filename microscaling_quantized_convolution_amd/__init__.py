@@ -22,10 +22,13 @@ MQ_ROLE_ACT, MQ_ROLE_WEIGHT, MQ_ROLE_GRAD = 0, 1, 2
 MQ_RNE, MQ_SR = 0, 1
 MQ_QUANTIZE_WS_BYTES = 8192  # tensor-amax workspace (mq_quantize, relayouts)
 MQ_QUANTIZE_AMAX_READY = 1   # mq_quantize flag: the workspace already holds this tensor's amax
+MQ_SRC_DENSE, MQ_SRC_NCHW, MQ_SRC_OIHW = 0, 1, 2  # mq_quant_job.layout
+MQ_QUANTIZE_BATCH_MAX = 4
 
 EXPORTS = (
     "mq_status_str", "mq_codes_bytes", "mq_scales_bytes", "mq_relayout_cbf",
-    "mq_relayout_weight", "mq_quantize", "mq_quantize_nchw", "mq_quantize_weight", "mq_conv_fwd",
+    "mq_relayout_weight", "mq_quantize", "mq_quantize_nchw", "mq_quantize_batch",
+    "mq_quantize_weight", "mq_conv_fwd",
     "mq_wgrad_workspace_bytes",
     "mq_conv_wgrad", "mq_conv_dgrad",
 )
@@ -42,6 +45,12 @@ class mq_qtensor(ctypes.Structure):
                 ("s", ctypes.c_int32), ("fmt", ctypes.c_int32), ("role", ctypes.c_int32),
                 ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("tscale", ctypes.c_void_p)]
+
+
+class mq_quant_job(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p), ("layout", ctypes.c_int32), ("rnd", ctypes.c_int32),
+                ("seed", ctypes.c_uint64), ("flags", ctypes.c_uint32), ("dst", mq_qtensor),
+                ("amax_ws", ctypes.c_void_p), ("amax_ws_bytes", ctypes.c_size_t)]
 
 
 class mq_conv(ctypes.Structure):
@@ -67,6 +76,7 @@ def _load() -> ctypes.CDLL:
     L.mq_quantize_nchw.argtypes = [P, ctypes.POINTER(mq_qtensor), i32, u64, P, sz,
                                    ctypes.c_uint32, P]
     L.mq_quantize_weight.argtypes = [P, ctypes.POINTER(mq_qtensor), i32, u64, P, sz, P]
+    L.mq_quantize_batch.argtypes = [ctypes.POINTER(mq_quant_job), i32, P]
     L.mq_conv_fwd.argtypes = [ctypes.POINTER(mq_conv), ctypes.POINTER(mq_qtensor),
                               ctypes.POINTER(mq_qtensor), P, P]
     L.mq_wgrad_workspace_bytes.restype = sz
@@ -179,6 +189,19 @@ def mq_quantize_nchw(src_nchw: torch.Tensor, dst: QTensor, rnd: int, seed: int,
     _check(_lib.mq_quantize_nchw(_ptr(src_nchw), ctypes.byref(q), rnd, seed & (2 ** 64 - 1),
                                  _ptr(amax_ws), _nbytes(amax_ws), flags, _stream(stream)),
            "mq_quantize_nchw")
+
+
+def quant_job(src: torch.Tensor, layout: int, dst: QTensor, rnd: int, seed: int,
+              amax_ws: torch.Tensor, flags: int = 0) -> mq_quant_job:
+    """One mq_quant_job (the caller keeps src, dst and amax_ws alive until the call is done)."""
+    return mq_quant_job(ctypes.c_void_p(src.data_ptr()), layout, rnd, seed & (2 ** 64 - 1), flags,
+                        dst.struct(), ctypes.c_void_p(amax_ws.data_ptr()), _nbytes(amax_ws))
+
+
+def mq_quantize_batch(jobs: Sequence[mq_quant_job], stream=None):
+    """Several tensors in one amax launch and one quantizing launch (see quant_job)."""
+    arr = (mq_quant_job * len(jobs))(*jobs)
+    _check(_lib.mq_quantize_batch(arr, len(jobs), _stream(stream)), "mq_quantize_batch")
 
 
 def mq_quantize_weight(w_oihw: torch.Tensor, dst: QTensor, rnd: int, seed: int,

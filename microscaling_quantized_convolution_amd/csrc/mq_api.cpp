@@ -156,6 +156,42 @@ mq_status mq_quantize_nchw(const float *src, const mq_qtensor *dst, int32_t rnd,
                                                   stream));
 }
 
+mq_status mq_quantize_batch(const mq_quant_job *jobs, int32_t njobs, hipStream_t stream)
+{
+    if (!jobs || njobs < 1) return MQ_ERR_ARG;
+    if (njobs > MQ_QUANTIZE_BATCH_MAX) return MQ_ERR_UNSUPPORTED;
+    mq::QuantJobDesc d[MQ_QUANTIZE_BATCH_MAX];
+    for (int i = 0; i < njobs; ++i) {
+        const mq_quant_job &j = jobs[i];
+        const mq_qtensor *q = &j.dst;
+        if (!j.src || !qtensor_ok(q) || (j.rnd != MQ_RNE && j.rnd != MQ_SR)) return MQ_ERR_ARG;
+        if (j.layout != MQ_SRC_DENSE && j.layout != MQ_SRC_NCHW && j.layout != MQ_SRC_OIHW)
+            return MQ_ERR_ARG;
+        if (j.flags & ~(uint32_t)MQ_QUANTIZE_AMAX_READY) return MQ_ERR_ARG;
+        if (!j.amax_ws || j.amax_ws_bytes < MQ_QUANTIZE_WS_BYTES) return MQ_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(j.amax_ws) & 3u) != 0) return MQ_ERR_ARG;
+        for (int k = 0; k < i; ++k)
+            if (jobs[k].amax_ws == j.amax_ws) return MQ_ERR_ARG; // one workspace per tensor
+        if (q->fmt != jobs[0].dst.fmt) return MQ_ERR_SHAPE;
+        if ((j.layout == MQ_SRC_NCHW && q->role == MQ_ROLE_WEIGHT) ||
+            (j.layout == MQ_SRC_OIHW && q->role != MQ_ROLE_WEIGHT))
+            return MQ_ERR_SHAPE;
+        if (squares(q->o0, q->o1, q->r, q->s) >= ((int64_t)1 << 31)) return MQ_ERR_UNSUPPORTED;
+        if (j.layout == MQ_SRC_NCHW) {
+            const int64_t pad = 16 * (int64_t)((q->s + 3) / 4) * ((q->r + 3) / 4) * q->o0 * q->o1 * 4;
+            if (pad >= ((int64_t)1 << 31)) return MQ_ERR_UNSUPPORTED;
+        }
+        d[i].src = j.src;
+        d[i].layout = j.layout == MQ_SRC_NCHW ? 1 : (j.layout == MQ_SRC_OIHW ? 2 : 0);
+        d[i].o0 = q->o0; d[i].o1 = q->o1; d[i].r = q->r; d[i].s = q->s;
+        d[i].rnd = j.rnd; d[i].seed = j.seed;
+        d[i].codes = q->codes; d[i].scales = q->scales; d[i].tscale = q->tscale;
+        d[i].amax_ws = j.amax_ws;
+        d[i].amax_ready = (j.flags & MQ_QUANTIZE_AMAX_READY) != 0;
+    }
+    return launch_status(mq::launch_quantize_batch(d, njobs, jobs[0].dst.fmt, stream));
+}
+
 mq_status mq_quantize_weight(const float *w, const mq_qtensor *dst, int32_t rnd, uint64_t seed,
                              uint32_t *amax_ws, size_t amax_ws_bytes, hipStream_t stream)
 {

@@ -25,6 +25,23 @@ hipError_t launch_quantize(const float *src, int64_t planes, int R, int S, int f
 hipError_t launch_quantize_nchw(const float *src, int N, int C, int H, int W, int fmt, int rnd,
                                 uint64_t seed, uint8_t *codes, uint8_t *scales, float *tscale,
                                 uint32_t *amax_ws, bool amax_ready, hipStream_t st);
+// One tensor of a batched quantization. layout: 0 = dense [o0][o1][r][s] (channel-batch-first
+// activations and gradients, tap-major weights), 1 = NCHW with (o0, o1, r, s) = (H, W, C, N),
+// 2 = OIHW weight with (o0, o1, r, s) = (Kh, Kw, Cout, Cin). Dimensions, pointers and workspace
+// are validated by the caller; rnd 0 = RNE, 1 = SR.
+struct QuantJobDesc {
+    const float *src;
+    int layout, o0, o1, r, s, rnd;
+    uint64_t seed;
+    uint8_t *codes, *scales;
+    float *tscale;
+    uint32_t *amax_ws;
+    bool amax_ready;
+};
+// Up to four tensors of one format: one amax launch (jobs without their amax ready) and one
+// quantizing launch. hipErrorInvalidValue for more than four jobs, 2^31 squares or more, or an
+// NCHW source whose zero-padded size reaches 2^31 bytes.
+hipError_t launch_quantize_batch(const QuantJobDesc *jobs, int njobs, int fmt, hipStream_t st);
 // OIHW fp32 weight [Cout][Cin][Kh][Kw] -> quantized tap-major squares [Kh][Kw][Cout][Cin], the
 // same codes, scales and T as launch_relayout_weight followed by launch_quantize, without the
 // fp32 copy (one launch for a weight of at most 65536 elements, every workgroup reducing the

@@ -54,37 +54,53 @@ constexpr int kAmaxThreads = 1024;
 constexpr int kAmaxVec = 8;
 constexpr int64_t kQuantBlocks = 1024;
 
-// Partial maxima: workgroup b writes max |x| over its grid-stride share to ws[1 + b]; ws[0] is the
-// number of workgroups. Eight independent 16-byte loads per lane are in flight at a time, enough
-// to cover HBM latency.
-__global__ void __launch_bounds__(kAmaxThreads) amax_kernel(const float *__restrict__ x, int64_t n,
-                                                            uint32_t *__restrict__ ws)
+// Partial maxima: workgroup b of P writes max |x| over its grid-stride share to ws[1 + b]; ws[0]
+// is P. Eight independent 16-byte loads per lane are in flight at a time, enough to cover HBM
+// latency.
+__device__ __forceinline__ void amax_body(const float *__restrict__ x, int64_t n,
+                                          uint32_t *__restrict__ ws, int b, int P, uint32_t *red)
 {
     uint32_t m = 0u;
-    const int64_t nt = (int64_t)gridDim.x * kAmaxThreads;
-    const int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+    const int64_t nt = (int64_t)P * kAmaxThreads;
+    const int64_t i = (int64_t)b * kAmaxThreads + threadIdx.x;
     int64_t tail = 0;
     if ((reinterpret_cast<uintptr_t>(x) & 15u) == 0) {
         const int64_t n4 = n >> 2;
         const u32x4_t *x4 = reinterpret_cast<const u32x4_t *>(x);
-        int64_t j = i;
-        for (; j + (kAmaxVec - 1) * nt < n4; j += kAmaxVec * nt) {
+        // groups of kAmaxVec loads, the last one predicated, so that every load of a group is
+        // in flight at once (a lane with fewer loads than a group still pays one round trip)
+        for (int64_t j = i; j < n4; j += kAmaxVec * nt) {
             u32x4_t v[kAmaxVec];
 #pragma unroll
-            for (int k = 0; k < kAmaxVec; ++k) v[k] = x4[j + k * nt]; // cached: quantize reads x next
+            for (int k = 0; k < kAmaxVec; ++k) {
+                const int64_t jk = j + k * nt;
+                v[k] = jk < n4 ? x4[jk] : u32x4_t{0u, 0u, 0u, 0u}; // cached: quantize reads x next
+            }
 #pragma unroll
             for (int k = 0; k < kAmaxVec; ++k) m = max(m, absmax4(v[k]));
         }
-        for (; j < n4; j += nt) m = max(m, absmax4(x4[j]));
         tail = n4 << 2;
     }
     for (int64_t j = tail + i; j < n; j += nt) m = max(m, __float_as_uint(x[j]) & 0x7FFFFFFFu);
-    __shared__ uint32_t red[kAmaxThreads / 64];
     m = block_max_u32<kAmaxThreads>(m, red);
     if (threadIdx.x == 0) {
-        ws[1 + blockIdx.x] = m;
-        if (blockIdx.x == 0) ws[0] = gridDim.x;
+        ws[1 + b] = m;
+        if (b == 0) ws[0] = (uint32_t)P;
     }
+}
+
+__global__ void __launch_bounds__(kAmaxThreads) amax_kernel(const float *__restrict__ x, int64_t n,
+                                                            uint32_t *__restrict__ ws)
+{
+    __shared__ uint32_t red[kAmaxThreads / 64];
+    amax_body(x, n, ws, (int)blockIdx.x, (int)gridDim.x, red);
+}
+
+// Workgroups of a pass: at least one, at most kAmaxParts, about kAmaxVec 16-byte loads per lane.
+inline int amax_parts(int64_t n)
+{
+    const int64_t want = (n / 4 + kAmaxVec * kAmaxThreads - 1) / (kAmaxVec * kAmaxThreads);
+    return (int)(want < 1 ? 1 : (want > kAmaxParts ? kAmaxParts : want));
 }
 
 struct QuantArgs {
@@ -251,28 +267,44 @@ __device__ __forceinline__ void store_square_codes(uint8_t *codes, int64_t t, co
 // the four rows are aligned float4 loads. OIHW: the source is a weight in OIHW order (plane =
 // kh*Kw + kw, R = Cout, S = Cin): element (plane, r, s) is read from src[(r*S + s)*planes +
 // plane], so the tap-major fp32 copy is never written.
-template <int FMT, bool SR, bool FULL, bool OIHW = false>
-__global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a)
+// Tensor scale T from the partial maxima in ws (every lane of a 256-lane workgroup takes part).
+template <int FMT>
+__device__ __forceinline__ float tensor_scale(const uint32_t *ws, uint32_t *red, bool &nonfinite)
 {
-    using F = Fmt<FMT>;
-    // Tensor scale: reduce the partial maxima (every lane of the workgroup).
-    __shared__ uint32_t red[4];
-    const uint32_t np = min(a.amax_ws[0], (uint32_t)kAmaxParts);
+    const uint32_t np = min(ws[0], (uint32_t)kAmaxParts);
     uint32_t pm = 0u;
 #pragma unroll
     for (int k = 0; k < kAmaxParts / 256; ++k) {
         const uint32_t i = threadIdx.x + 256u * k;
-        pm = max(pm, i < np ? a.amax_ws[1 + i] : 0u);
+        pm = max(pm, i < np ? ws[1 + i] : 0u);
     }
     const uint32_t abits = block_max_u32<256>(pm, red);
-    const bool nonfinite = abits >= 0x7F800000u;
-    const float T = __uint_as_float(abits) / (448.0f * F::kEmax);
-    // square indices fit in 31 bits (checked at launch)
-    const int t0 = (int)(blockIdx.x * blockDim.x + threadIdx.x);
-    if (t0 == 0) *a.tscale = nonfinite ? __uint_as_float(0x7FC00000u) : T;
+    nonfinite = abits >= 0x7F800000u;
+    return __uint_as_float(abits) / (448.0f * Fmt<FMT>::kEmax);
+}
+
+__device__ __forceinline__ void store_tscale(float *tscale, float T, bool nonfinite)
+{
+    *tscale = nonfinite ? __uint_as_float(0x7FC00000u) : T;
+}
+
+template <bool OIHW> constexpr int kCbfLanes = OIHW ? 64 : 256;
+
+// Squares of one tensor, grid-stride over the P workgroups of the pass (this is workgroup b).
+// The lane's first square is loaded before the tensor scale is reduced (the two do not depend
+// on each other), so their memory round trips overlap; workgroup 0 stores T.
+template <int FMT, bool SR, bool FULL, bool OIHW>
+__device__ __forceinline__ void cbf_body(const QuantArgs &a, uint32_t *red, int b, int P)
+{
+    // square indices fit in 31 bits (checked at launch). A gathering (OIHW) pass uses 64 lanes
+    // per workgroup: its loads are scattered, which the per-CU memory pipeline serves a few
+    // lanes at a time, so its squares are spread over four times as many workgroups.
+    constexpr int LANES = kCbfLanes<OIHW>;
     const int nsq = (int)a.nsq;
-    if (t0 >= nsq) return;
-    const int stride = (int)(gridDim.x * blockDim.x);
+    const int t0 = b * LANES + (int)threadIdx.x;
+    const bool active = (int)threadIdx.x < LANES && t0 < nsq;
+    const int tl = active ? t0 : 0; // an idle lane loads square 0 and never uses it
+    const int stride = P * LANES;
 
     // Square t = (plane * R4 + r4) * S4 + s4, stepped by `stride` with carries instead of
     // divisions: the step is (dp, dr, ds) in the same mixed radix.
@@ -321,9 +353,35 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a)
 
     // Grid-stride over squares with the next square's loads in flight while this one is
     // quantized (the last step reloads its own square, so every step issues the same loads).
-    Pos pos = {t0 / a.S4 / a.R4, (t0 / a.S4) % a.R4, t0 % a.S4};
+    Pos pos = {tl / a.S4 / a.R4, (tl / a.S4) % a.R4, tl % a.S4};
     float xn[16];
     load(pos, xn);
+    bool nonfinite;
+    const float T = tensor_scale<FMT>(a.amax_ws, red, nonfinite);
+    if (b == 0 && threadIdx.x == 0) store_tscale(a.tscale, T, nonfinite);
+    if (!active) return;
+    if constexpr (OIHW) {
+        // one or a few squares per lane: no prefetch (a reload of the last square would double
+        // the scattered loads)
+        for (int t = t0;;) {
+            Philox4 r0 = {}, r1 = {};
+            if (SR) {
+                const uint64_t j = 2u * (uint64_t)t;
+                r0 = philox4x32_10((uint32_t)j, (uint32_t)(j >> 32), 0u, 0u, a.seed_lo, a.seed_hi);
+                r1 = philox4x32_10((uint32_t)(j + 1), (uint32_t)((j + 1) >> 32), 0u, 0u,
+                                   a.seed_lo, a.seed_hi);
+            }
+            uint32_t w[3];
+            const uint32_t bcode = quantize_square<FMT, SR>(xn, T, nonfinite, r0, r1, w);
+            a.scales[t] = (uint8_t)bcode;
+            store_square_codes<FMT>(a.codes, t, w);
+            t += stride;
+            if (t >= nsq) break;
+            pos = advance(pos);
+            load(pos, xn);
+        }
+        return;
+    }
     for (int t = t0; t < nsq; t += stride) {
         float x[16];
 #pragma unroll
@@ -345,6 +403,13 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a)
         a.scales[t] = (uint8_t)bcode;
         store_square_codes<FMT>(a.codes, t, w);
     }
+}
+
+template <int FMT, bool SR, bool FULL, bool OIHW = false>
+__global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a)
+{
+    __shared__ uint32_t red[4];
+    cbf_body<FMT, SR, FULL, OIHW>(a, red, (int)blockIdx.x, (int)gridDim.x);
 }
 
 template <int FMT, bool SR>
@@ -437,25 +502,14 @@ template <> struct PixelLoad<4> {
 
 // PX: consecutive pixels per lane, read as one PX-float load per (n, c) plane (H*W a multiple
 // of PX and the source PX*4-byte aligned, so a lane's pixels are all inside or all past H*W).
+// The lane's loads are issued before the tensor scale is reduced (their round trips overlap);
+// workgroup 0 stores T.
 template <int FMT, bool SR, int NQ, int PX>
-__global__ void __launch_bounds__(256) quantize_nchw_kernel(QuantNchwArgs a)
+__device__ __forceinline__ void nchw_body(const QuantNchwArgs &a, uint32_t *red, int b)
 {
-    using F = Fmt<FMT>;
-    __shared__ uint32_t red[4];
-    const uint32_t np = min(a.amax_ws[0], (uint32_t)kAmaxParts);
-    uint32_t pm = 0u;
-#pragma unroll
-    for (int k = 0; k < kAmaxParts / 256; ++k) {
-        const uint32_t i = threadIdx.x + 256u * k;
-        pm = max(pm, i < np ? a.amax_ws[1 + i] : 0u);
-    }
-    const uint32_t abits = block_max_u32<256>(pm, red);
-    const bool nonfinite = abits >= 0x7F800000u;
-    const float T = __uint_as_float(abits) / (448.0f * F::kEmax);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *a.tscale = nonfinite ? __uint_as_float(0x7FC00000u) : T;
-
-    const int item = wave_uniform((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
-    if (item >= a.items) return;
+    const int witem = wave_uniform(b * 4 + (int)(threadIdx.x >> 6));
+    const bool act = witem < a.items; // an idle wave loads nothing (out-of-range offsets)
+    const int item = act ? witem : 0;
     const int lane = threadIdx.x & 63;
     const int ng = item % a.NG, c4 = (item / a.NG) % a.C4, pb = item / a.NG / a.C4;
     const int p = (pb * 64 + lane) * PX;
@@ -470,7 +524,7 @@ __global__ void __launch_bounds__(256) quantize_nchw_kernel(QuantNchwArgs a)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const bool cin = 4 * c4 + i < a.C;
-        const uint32_t voff = (pin && cin) ? lane_off : kBad;
+        const uint32_t voff = (act && pin && cin) ? lane_off : kBad;
 #pragma unroll
         for (int k = 0; k < NQ; ++k)
 #pragma unroll
@@ -481,7 +535,10 @@ __global__ void __launch_bounds__(256) quantize_nchw_kernel(QuantNchwArgs a)
                 for (int q = 0; q < PX; ++q) x[q][k][4 * i + j] = v[q];
             }
     }
-    if (!pin) return;
+    bool nonfinite;
+    const float T = tensor_scale<FMT>(a.amax_ws, red, nonfinite);
+    if (b == 0 && threadIdx.x == 0) store_tscale(a.tscale, T, nonfinite);
+    if (!act || !pin) return;
 #pragma unroll
     for (int q = 0; q < PX; ++q) {
         const int t0 = ((p + q) * a.C4 + c4) * a.N4 + ng * NQ; // square indices fit in 31 bits
@@ -502,6 +559,13 @@ __global__ void __launch_bounds__(256) quantize_nchw_kernel(QuantNchwArgs a)
 }
 
 template <int FMT, bool SR, int NQ, int PX>
+__global__ void __launch_bounds__(256) quantize_nchw_kernel(QuantNchwArgs a)
+{
+    __shared__ uint32_t red[4];
+    nchw_body<FMT, SR, NQ, PX>(a, red, (int)blockIdx.x);
+}
+
+template <int FMT, bool SR, int NQ, int PX>
 static void launch_nchw_shape(QuantNchwArgs a, hipStream_t st)
 {
     const int pbs = (a.HW + 64 * PX - 1) / (64 * PX);
@@ -519,6 +583,80 @@ static hipError_t launch_quant_nchw(const QuantNchwArgs &a, hipStream_t st)
     else if (al16 && a.HW % 4 == 0) launch_nchw_shape<FMT, SR, 1, 4>(a, st);
     else launch_nchw_shape<FMT, SR, 1, 1>(a, st);
     return hipGetLastError();
+}
+
+// ---- several tensors in one amax launch and one quantizing launch ----
+//
+// Each job is one tensor with its own source order (channel-batch-first or any [o0][o1][r][s]
+// array, NCHW, or an OIHW weight), rounding, seed, amax workspace and destination; the codes,
+// scales and T are those of the single-tensor calls. The amax pass runs every job's workgroups
+// in one grid (contiguous ranges, jobs with the amax ready take none), and so does the
+// quantizing pass, so small tensors ride along with a large one instead of paying a launch and
+// a memory round trip of their own.
+enum { kJobCbf = 0, kJobNchw = 1, kJobOihw = 2 };
+constexpr int kMaxJobs = 4;
+
+struct QuantJob {
+    int kind, sr, full, nq;
+    int a_b0, a_P; // amax pass workgroups (a_P = 0: partial maxima already in the workspace)
+    int q_b0, q_P; // quantizing pass workgroups
+    int64_t an;    // elements (amax pass; the source and workspace are the kind's own)
+    union {
+        QuantArgs cbf;      // kJobCbf, kJobOihw
+        QuantNchwArgs nchw; // kJobNchw
+    };
+};
+
+// NJ job slots: the kernel arguments are read by every workgroup, so a batch of one or two
+// tensors takes the two-slot variant (measured 0.4 us faster per launch pair than four slots).
+template <int NJ> struct QuantBatchArgs {
+    QuantJob job[NJ];
+    int njobs;
+};
+
+template <int NJ>
+__global__ void __launch_bounds__(kAmaxThreads) amax_batch_kernel(QuantBatchArgs<NJ> a)
+{
+    __shared__ uint32_t red[kAmaxThreads / 64];
+    const int b = (int)blockIdx.x;
+    int j = 0;
+#pragma unroll
+    for (int k = 1; k < NJ; ++k) j = (k < a.njobs && b >= a.job[k].a_b0 && a.job[k].a_P > 0) ? k : j;
+    const QuantJob &jb = a.job[j];
+    const bool nchw = jb.kind == kJobNchw;
+    amax_body(nchw ? jb.nchw.src : jb.cbf.src, jb.an,
+              const_cast<uint32_t *>(nchw ? jb.nchw.amax_ws : jb.cbf.amax_ws), b - jb.a_b0,
+              jb.a_P, red);
+}
+
+template <int FMT, int NJ>
+__global__ void __launch_bounds__(256) quantize_batch_kernel(QuantBatchArgs<NJ> a)
+{
+    __shared__ uint32_t red[4];
+    const int b = (int)blockIdx.x;
+    int j = 0;
+#pragma unroll
+    for (int k = 1; k < NJ; ++k) j = (k < a.njobs && b >= a.job[k].q_b0) ? k : j;
+    const QuantJob &jb = a.job[j];
+    const int lb = b - jb.q_b0;
+    if (jb.kind == kJobNchw) {
+        if (jb.nq == 4) {
+            if (jb.sr) nchw_body<FMT, true, 4, 1>(jb.nchw, red, lb);
+            else nchw_body<FMT, false, 4, 1>(jb.nchw, red, lb);
+        } else {
+            if (jb.sr) nchw_body<FMT, true, 1, 1>(jb.nchw, red, lb);
+            else nchw_body<FMT, false, 1, 1>(jb.nchw, red, lb);
+        }
+    } else if (jb.kind == kJobOihw) {
+        if (jb.sr) cbf_body<FMT, true, false, true>(jb.cbf, red, lb, jb.q_P);
+        else cbf_body<FMT, false, false, true>(jb.cbf, red, lb, jb.q_P);
+    } else if (jb.full) {
+        if (jb.sr) cbf_body<FMT, true, true, false>(jb.cbf, red, lb, jb.q_P);
+        else cbf_body<FMT, false, true, false>(jb.cbf, red, lb, jb.q_P);
+    } else {
+        if (jb.sr) cbf_body<FMT, true, false, false>(jb.cbf, red, lb, jb.q_P);
+        else cbf_body<FMT, false, false, false>(jb.cbf, red, lb, jb.q_P);
+    }
 }
 
 // A small weight (at most kSmallWeight floats), from OIHW fp32 to quantized tap-major squares in
@@ -600,14 +738,13 @@ static hipError_t launch_quant_weight(const QuantArgs &a, uint32_t *amax_ws, hip
         return hipGetLastError();
     }
     // larger: the amax pass over the OIHW array (same values), then the gathering quantizer
-    const int64_t want = (n / 4 + kAmaxVec * kAmaxThreads - 1) / (kAmaxVec * kAmaxThreads);
-    const int parts = (int)(want < 1 ? 1 : (want > kAmaxParts ? kAmaxParts : want));
+    const int parts = amax_parts(n);
     hipLaunchKernelGGL(amax_kernel, dim3(parts), dim3(kAmaxThreads), 0, st, a.src, n, amax_ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     QuantArgs b = a;
     b.amax_ws = amax_ws;
-    const int64_t wantq = (a.nsq + 255) / 256;
+    const int64_t wantq = (a.nsq + kCbfLanes<true> - 1) / kCbfLanes<true>;
     const unsigned blocks = (unsigned)(wantq < kQuantBlocks ? wantq : kQuantBlocks);
     hipLaunchKernelGGL((quantize_kernel<FMT, SR, false, true>), dim3(blocks), dim3(256), 0, st, b);
     return hipGetLastError();
@@ -639,8 +776,7 @@ hipError_t launch_quantize(const float *src, int64_t planes, int R, int S, int f
         return hipErrorInvalidValue; // square indices are 31-bit
     const int64_t n = planes * (int64_t)R * S;
     // at least 8 float4 per lane where the tensor allows, at most kAmaxParts workgroups
-    const int64_t want = (n / 4 + kAmaxVec * kAmaxThreads - 1) / (kAmaxVec * kAmaxThreads);
-    const int parts = (int)(want < 1 ? 1 : (want > kAmaxParts ? kAmaxParts : want));
+    const int parts = amax_parts(n);
     if (!amax_ready) {
         hipLaunchKernelGGL(amax_kernel, dim3(parts), dim3(kAmaxThreads), 0, st, src, n, amax_ws);
         hipError_t e = hipGetLastError();
@@ -671,8 +807,7 @@ hipError_t launch_quantize_nchw(const float *src, int N, int C, int H, int W, in
     // planes); 31-bit square and work-item indices
     if (16 * N4 * C4 * HW * 4 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     if (!amax_ready) {
-        const int64_t want = (n / 4 + kAmaxVec * kAmaxThreads - 1) / (kAmaxVec * kAmaxThreads);
-        const int parts = (int)(want < 1 ? 1 : (want > kAmaxParts ? kAmaxParts : want));
+        const int parts = amax_parts(n);
         hipLaunchKernelGGL(amax_kernel, dim3(parts), dim3(kAmaxThreads), 0, st, src, n, amax_ws);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -686,6 +821,89 @@ hipError_t launch_quantize_nchw(const float *src, int N, int C, int H, int W, in
     if (fmt == kFP4)
         return rnd ? launch_quant_nchw<kFP4, true>(a, st) : launch_quant_nchw<kFP4, false>(a, st);
     return rnd ? launch_quant_nchw<kFP6, true>(a, st) : launch_quant_nchw<kFP6, false>(a, st);
+}
+
+template <int NJ>
+static hipError_t launch_batch_nj(const QuantJobDesc *jobs, int njobs, int fmt, hipStream_t st)
+{
+    QuantBatchArgs<NJ> a = {};
+    a.njobs = njobs;
+    int64_t atot = 0, qtot = 0;
+    for (int i = 0; i < njobs; ++i) {
+        const QuantJobDesc &d = jobs[i];
+        QuantJob &jb = a.job[i];
+        jb.sr = d.rnd != 0;
+        const int64_t n = (int64_t)d.o0 * d.o1 * d.r * d.s;
+        const int64_t R4 = (d.r + 3) / 4, S4 = (d.s + 3) / 4;
+        const int64_t nsq = (int64_t)d.o0 * d.o1 * R4 * S4;
+        if (nsq >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+        jb.an = n;
+        jb.a_P = d.amax_ready ? 0 : amax_parts(n);
+        if (d.layout == kJobNchw) {
+            // dims (o0, o1, r, s) = (H, W, C, N)
+            const int64_t HW = (int64_t)d.o0 * d.o1;
+            if (16 * S4 * R4 * HW * 4 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+            jb.kind = kJobNchw;
+            QuantNchwArgs &q = jb.nchw;
+            q.src = d.src; q.codes = d.codes; q.scales = d.scales; q.tscale = d.tscale;
+            q.amax_ws = d.amax_ws;
+            q.N = d.s; q.C = d.r; q.HW = (int)HW; q.C4 = (int)R4; q.N4 = (int)S4;
+            jb.nq = q.N4 % 4 == 0 ? 4 : 1;
+            q.NG = q.N4 / jb.nq;
+            q.items = (int)((HW + 63) / 64) * q.C4 * q.NG;
+            q.bytes = (uint32_t)(n * 4);
+            q.seed_lo = (uint32_t)d.seed; q.seed_hi = (uint32_t)(d.seed >> 32);
+            jb.q_P = (q.items + 3) / 4;
+        } else {
+            // kJobCbf: [o0*o1][r][s]; kJobOihw: weight [r=Cout][s=Cin][o0*o1 taps]
+            jb.kind = d.layout;
+            QuantArgs &q = jb.cbf;
+            q.src = d.src; q.codes = d.codes; q.scales = d.scales; q.tscale = d.tscale;
+            q.amax_ws = d.amax_ws;
+            q.planes = (int64_t)d.o0 * d.o1; q.R = d.r; q.S = d.s; q.R4 = (int)R4; q.S4 = (int)S4;
+            q.nsq = nsq;
+            q.seed_lo = (uint32_t)d.seed; q.seed_hi = (uint32_t)(d.seed >> 32);
+            jb.full = d.layout == kJobCbf && d.r % 4 == 0 && d.s % 4 == 0 &&
+                      (reinterpret_cast<uintptr_t>(d.src) & 15u) == 0;
+            const int lanes = d.layout == kJobOihw ? 64 : 256;
+            const int64_t want = (nsq + lanes - 1) / lanes;
+            jb.q_P = (int)(want < kQuantBlocks ? want : kQuantBlocks);
+        }
+    }
+    // Quantizing-pass ranges smallest job first: the hardware dispatches workgroups in index
+    // order, so a small job's few workgroups start at once instead of trailing the large one.
+    // (Job order is free: each job carries its own pointers; the amax ranges follow it.)
+    for (int i = 1; i < njobs; ++i)
+        for (int k = i; k > 0 && a.job[k].q_P < a.job[k - 1].q_P; --k) {
+            const QuantJob t = a.job[k];
+            a.job[k] = a.job[k - 1];
+            a.job[k - 1] = t;
+        }
+    atot = 0;
+    for (int i = 0; i < njobs; ++i) {
+        QuantJob &jb = a.job[i];
+        jb.a_b0 = (int)atot;
+        atot += jb.a_P;
+        jb.q_b0 = (int)qtot;
+        qtot += jb.q_P;
+    }
+    if (atot > 0) {
+        hipLaunchKernelGGL((amax_batch_kernel<NJ>), dim3((unsigned)atot), dim3(kAmaxThreads), 0, st, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (fmt == kFP4)
+        hipLaunchKernelGGL((quantize_batch_kernel<kFP4, NJ>), dim3((unsigned)qtot), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((quantize_batch_kernel<kFP6, NJ>), dim3((unsigned)qtot), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_batch(const QuantJobDesc *jobs, int njobs, int fmt, hipStream_t st)
+{
+    if (njobs < 1 || njobs > kMaxJobs) return hipErrorInvalidValue;
+    return njobs <= 2 ? launch_batch_nj<2>(jobs, njobs, fmt, st)
+                      : launch_batch_nj<kMaxJobs>(jobs, njobs, fmt, st);
 }
 
 } // namespace mq

@@ -4,8 +4,8 @@
 through the library, following the onedev.kr MicroQonv digest (sections "How it works" and "How it
 differs"):
 
-  forward   X (NCHW) -> quantized channel-batch-first squares, one call  (quantize once, RNE)
-            W (OIHW) -> quantized tap-major squares, one call           (quantize once, RNE)
+  forward   X (NCHW) -> quantized channel-batch-first squares  } one batched call
+            W (OIHW) -> quantized tap-major squares             } (quantize once, RNE)
             Y = conv_fwd(Xq, Wq), back to NCHW
   backward  G_Y (NCHW) -> quantized channel-batch-first squares, one call (quantize once, SR)
             G_W = conv_wgrad(G_Yq, Xq) (the forward's Xq is kept, not re-quantized)
@@ -33,9 +33,10 @@ import torch
 from torch import nn
 
 from . import (MQ_NVFP4, MQ_QUANTIZE_WS_BYTES, MQ_ROLE_ACT, MQ_ROLE_GRAD, MQ_ROLE_WEIGHT,
-               MQ_RNE, MQ_SR, QTensor, mq_conv_dgrad, mq_conv_fwd, mq_conv_wgrad,
-               mq_quantize_nchw, mq_quantize_weight, mq_relayout_cbf, mq_relayout_weight,
-               mq_wgrad_workspace_bytes, out_hw)
+               MQ_RNE, MQ_SR, MQ_SRC_NCHW, MQ_SRC_OIHW, QTensor, mq_conv_dgrad, mq_conv_fwd,
+               mq_conv_wgrad, mq_quantize_batch, mq_quantize_nchw, mq_quantize_weight,
+               mq_relayout_cbf, mq_relayout_weight, mq_wgrad_workspace_bytes, out_hw,
+               quant_job)
 
 
 def _check_input(t: torch.Tensor, what: str, ndim: int = 4):
@@ -80,9 +81,15 @@ class MQConv2dFunction(torch.autograd.Function):
         Ho, Wo = out_hw(conv)
         dev = x.device
         ws = torch.empty(2 * MQ_QUANTIZE_WS_BYTES, dtype=torch.uint8, device=dev)
-        qx = quantize_activation(x, fmt, MQ_RNE, 0, MQ_ROLE_ACT, ws[:MQ_QUANTIZE_WS_BYTES])
-        qw = qw_cached if qw_cached is not None else \
-            quantize_weight(weight, fmt, ws[MQ_QUANTIZE_WS_BYTES:])
+        if qw_cached is not None:
+            qx = quantize_activation(x, fmt, MQ_RNE, 0, MQ_ROLE_ACT, ws[:MQ_QUANTIZE_WS_BYTES])
+            qw = qw_cached
+        else:  # X and W together: one amax launch and one quantizing launch
+            qx = QTensor(H, W, Cin, N, fmt, MQ_ROLE_ACT, dev)
+            qw = QTensor(Kh, Kw, Cout, Cin, fmt, MQ_ROLE_WEIGHT, dev)
+            mq_quantize_batch([
+                quant_job(x, MQ_SRC_NCHW, qx, MQ_RNE, 0, ws[:MQ_QUANTIZE_WS_BYTES]),
+                quant_job(weight, MQ_SRC_OIHW, qw, MQ_RNE, 0, ws[MQ_QUANTIZE_WS_BYTES:])])
         yc = torch.empty(Ho * Wo * Cout * N, dtype=torch.float32, device=dev)
         mq_conv_fwd(conv, qx, qw, yc)
         y = torch.empty((N, Cout, Ho, Wo), dtype=torch.float32, device=dev)

@@ -3,14 +3,14 @@
 Device buffers for one layer (fp32 inputs, their channel-batch-first copies, the three quantized
 tensors, the outputs and the weight-gradient workspace) and the calls of one pass, in order:
 
-  quantize_x   X NCHW -> quantized channel-batch-first squares (round to nearest)
-  quantize_w   W OIHW -> quantized tap-major squares (round to nearest), one call
+  quantize_xw  X NCHW -> quantized channel-batch-first squares and W OIHW -> quantized
+               tap-major squares (both round to nearest), one batched call
   quantize_g   G_Y (stochastic, seed per pass)   conv_fwd / conv_wgrad / conv_dgrad
 
-X goes from NCHW to its quantized channel-batch-first layout in one call (mq_quantize_nchw: an
-amax pass, then a pass that reads NCHW and writes squares; no fp32 channel-batch-first copy).
-W goes from OIHW to its quantized tap-major layout in one call (mq_quantize_weight). G_Y's
-quantization runs its own amax pass.
+X and W are quantized together, as a layer's forward pass does (mq_quantize_batch: one amax
+launch over both, then one launch that reads X in NCHW and W in OIHW order and writes their
+squares; no fp32 channel-batch-first or tap-major copy). G_Y, which only exists in the backward
+pass, is quantized on its own, with its own amax pass.
 
 G_Y is taken as already channel-batch-first (it is the next layer's input-gradient output).
 Every call goes through the C ABI on the current stream; nothing here computes.
@@ -22,10 +22,10 @@ from typing import Callable, Dict
 
 import torch
 
-from . import (MQ_QUANTIZE_WS_BYTES, MQ_ROLE_ACT, MQ_ROLE_GRAD,
-               MQ_ROLE_WEIGHT, MQ_RNE, MQ_SR, QTensor, conv_struct,
-               mq_conv_dgrad, mq_conv_fwd, mq_conv_wgrad, mq_quantize, mq_quantize_nchw,
-               mq_quantize_weight, mq_wgrad_workspace_bytes, out_hw)
+from . import (MQ_QUANTIZE_WS_BYTES, MQ_ROLE_ACT, MQ_ROLE_GRAD, MQ_ROLE_WEIGHT, MQ_RNE, MQ_SR,
+               MQ_SRC_NCHW, MQ_SRC_OIHW, QTensor, conv_struct, mq_conv_dgrad, mq_conv_fwd,
+               mq_conv_wgrad, mq_quant_job, mq_quantize, mq_quantize_batch,
+               mq_wgrad_workspace_bytes, out_hw, quant_job)
 
 
 class LayerStep:
@@ -52,10 +52,12 @@ class LayerStep:
         self.ws = torch.empty(max(1, mq_wgrad_workspace_bytes(self.p)), dtype=torch.uint8,
                               device=dev)
         a0, a1, a2 = (self.amax[i * nws:(i + 1) * nws] for i in range(3))
+        self._a0 = a0
         p = self.p
+        self.xw_jobs = [quant_job(self.x, MQ_SRC_NCHW, self.qx, MQ_RNE, 0, a0),
+                        quant_job(self.w, MQ_SRC_OIHW, self.qw, MQ_RNE, 0, a1)]
         self.ops: Dict[str, Callable[[int], None]] = OrderedDict([
-            ("quantize_x", lambda s: mq_quantize_nchw(self.x, self.qx, MQ_RNE, 0, a0)),
-            ("quantize_w", lambda s: mq_quantize_weight(self.w, self.qw, MQ_RNE, 0, a1)),
+            ("quantize_xw", lambda s: mq_quantize_batch(self.xw_jobs)),
             ("quantize_g", lambda s: mq_quantize(self.gc, self.qg, MQ_SR,
                                                  self.sr_seed_base + s, a2)),
             ("conv_fwd", lambda s: mq_conv_fwd(p, self.qx, self.qw, self.y)),
@@ -89,9 +91,10 @@ class LayerStep:
             if st != MQ_OK:
                 raise MQError(st, name)
 
+        jobs = (mq_quant_job * 2)(*self.xw_jobs)
+        self._keep = self._keep + (jobs,)
         fixed = {
-            "quantize_x": (L.mq_quantize_nchw, (P(self.x), bx, MQ_RNE, 0, a[0], wsb, 0, hs)),
-            "quantize_w": (L.mq_quantize_weight, (P(self.w), bw, MQ_RNE, 0, a[1], wsb, hs)),
+            "quantize_xw": (L.mq_quantize_batch, (jobs, 2, hs)),
             "conv_fwd": (L.mq_conv_fwd, (conv, bx, bw, P(self.y), hs)),
             "conv_wgrad": (L.mq_conv_wgrad, (conv, bg, bx, P(self.gw), P(self.ws), nws, hs)),
             "conv_dgrad": (L.mq_conv_dgrad, (conv, bw, bg, P(self.gx), hs)),
@@ -106,6 +109,32 @@ class LayerStep:
             else:
                 f, args = fixed[name]
                 out[name] = lambda s, f=f, args=args, n=name: chk(f(*args), n)
+        return out
+
+    def inference_calls(self, stream) -> Dict[str, Callable[[int], None]]:
+        """The forward pass with the weight already quantized: X alone (mq_quantize_nchw), then
+        the forward GEMM, as direct foreign-function calls on a fixed stream."""
+        import ctypes
+        from . import MQ_OK, MQError, _lib, _stream
+        hs = _stream(stream)
+        qx, qw = self.qx.struct(), self.qw.struct()
+        conv = ctypes.byref(self.p)
+        self._keep_inf = (qx, qw, conv)
+        a0 = ctypes.c_void_p(self._a0.data_ptr())
+        calls = {
+            "quantize_x": (_lib.mq_quantize_nchw, (ctypes.c_void_p(self.x.data_ptr()),
+                                                   ctypes.byref(qx), MQ_RNE, 0, a0,
+                                                   MQ_QUANTIZE_WS_BYTES, 0, hs)),
+            "conv_fwd": (_lib.mq_conv_fwd, (conv, ctypes.byref(qx), ctypes.byref(qw),
+                                            ctypes.c_void_p(self.y.data_ptr()), hs)),
+        }
+        out: Dict[str, Callable[[int], None]] = OrderedDict()
+        for name, (f, args) in calls.items():
+            def call(s, f=f, args=args, n=name):
+                st = f(*args)
+                if st != MQ_OK:
+                    raise MQError(st, n)
+            out[name] = call
         return out
 
     def outputs(self):

@@ -93,6 +93,30 @@ def test_validation_errors_without_gpu():
     assert L.mq_quantize_nchw(y, ctypes.byref(bad), 0, 0, y, ws, 0, s0) == mq.MQ_ERR_ARG
     big = _fake_q((1024, 1024, 32, 16))  # 2^31 source bytes once padded
     assert L.mq_quantize_nchw(y, ctypes.byref(big), 0, 0, y, ws, 0, s0) == mq.MQ_ERR_UNSUPPORTED
+    # batched quantization
+    x6 = _fake_q((8, 8, 16, 2), fmt=mq.MQ_NVFP6)
+
+    def job(src=y, layout=mq.MQ_SRC_NCHW, dst=x, rnd=0, flags=0, ws_ptr=0x3000, nbytes=ws):
+        return mq.mq_quant_job(src, layout, rnd, 0, flags, dst, ws_ptr, nbytes)
+
+    def batch(*js):
+        arr = (mq.mq_quant_job * max(1, len(js)))(*js)
+        return L.mq_quantize_batch(arr, len(js), s0)
+    assert L.mq_quantize_batch(None, 1, s0) == mq.MQ_ERR_ARG
+    assert batch() == mq.MQ_ERR_ARG  # no jobs
+    assert batch(*[job(ws_ptr=0x3000 + 0x4000 * i) for i in range(5)]) == mq.MQ_ERR_UNSUPPORTED
+    assert batch(job(src=None)) == mq.MQ_ERR_ARG
+    assert batch(job(layout=3)) == mq.MQ_ERR_ARG
+    assert batch(job(rnd=2)) == mq.MQ_ERR_ARG
+    assert batch(job(flags=2)) == mq.MQ_ERR_ARG
+    assert batch(job(nbytes=ws - 4)) == mq.MQ_ERR_WORKSPACE
+    assert batch(job(ws_ptr=0)) == mq.MQ_ERR_WORKSPACE
+    assert batch(job(ws_ptr=0x3002)) == mq.MQ_ERR_ARG
+    assert batch(job(), job(dst=g, rnd=1)) == mq.MQ_ERR_ARG  # shared workspace
+    assert batch(job(), job(dst=x6, ws_ptr=0x8000)) == mq.MQ_ERR_SHAPE  # formats differ
+    assert batch(job(dst=w)) == mq.MQ_ERR_SHAPE  # NCHW source, weight role
+    assert batch(job(layout=mq.MQ_SRC_OIHW, dst=x)) == mq.MQ_ERR_SHAPE  # OIHW, not a weight
+    assert batch(job(dst=_fake_q((1024, 1024, 32, 16)))) == mq.MQ_ERR_UNSUPPORTED
     # misaligned codes (16 B) or scales (4 B) -> MQ_ERR_ARG
     mis = mq.mq_qtensor(8, 8, 16, 2, mq.MQ_NVFP4, mq.MQ_ROLE_ACT, 0x1008, 0x1000, 0x1000)
     assert L.mq_quantize(y, ctypes.byref(mis), 0, 0, y, ws, 0, s0) == mq.MQ_ERR_ARG

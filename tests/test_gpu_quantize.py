@@ -272,6 +272,87 @@ def test_quantize_nchw_rejects_weight_role():
                             mq.quantize_workspace("cuda"))
 
 
+# ---- several tensors in one launch pair (mq_quantize_batch) ---------------------------------
+
+def _oracle_for(layout, a, fmt, rnd, seed):
+    if layout == mq.MQ_SRC_NCHW:
+        return oracle.quantize(oracle.nchw_to_cbf(a), fmt, rnd, seed)
+    if layout == mq.MQ_SRC_OIHW:
+        return oracle.quantize(oracle.oihw_to_tap_major(a), fmt, rnd, seed)
+    return oracle.quantize(a, fmt, rnd, seed)
+
+
+BATCHES = {
+    # a layer's forward pass: X from NCHW and W from OIHW together
+    "x_w": [(mq.MQ_SRC_NCHW, (32, 64, 14, 14), mq.MQ_ROLE_ACT, 0),
+            (mq.MQ_SRC_OIHW, (64, 64, 3, 3), mq.MQ_ROLE_WEIGHT, 0)],
+    # every source order and both roundings, ragged shapes
+    "mixed": [(mq.MQ_SRC_NCHW, (5, 9, 7, 11), mq.MQ_ROLE_ACT, 0),
+              (mq.MQ_SRC_OIHW, (17, 13, 3, 3), mq.MQ_ROLE_WEIGHT, 0),
+              (mq.MQ_SRC_DENSE, (6, 7, 20, 12), mq.MQ_ROLE_GRAD, 1),
+              (mq.MQ_SRC_NCHW, (16, 8, 9, 9), mq.MQ_ROLE_GRAD, 1)],
+    "one": [(mq.MQ_SRC_DENSE, (3, 5, 13, 18), mq.MQ_ROLE_ACT, 1)],
+}
+
+
+def _batch_tensors(name, fmt):
+    out = []
+    for i, (layout, shape, role, rnd) in enumerate(BATCHES[name]):
+        a = workloads.random_array(shape, seed=300 + 7 * i, dist="relu" if rnd == 0 else "normal")
+        if layout == mq.MQ_SRC_NCHW:
+            n, c, h, w_ = shape
+            qshape = (h, w_, c, n)
+        elif layout == mq.MQ_SRC_OIHW:
+            co, ci, kh, kw = shape
+            qshape = (kh, kw, co, ci)
+        else:
+            qshape = shape
+        out.append((layout, a, qshape, role, rnd, 1000 + i))
+    return out
+
+
+@pytest.mark.parametrize("fmt", [4, 6])
+@pytest.mark.parametrize("name", sorted(BATCHES))
+def test_quantize_batch_matches_single_calls(name, fmt):
+    log("quantize_batch", name, fmt)
+    items = _batch_tensors(name, fmt)
+    keep, jobs = [], []
+    for layout, a, qshape, role, rnd, seed in items:
+        t = to_dev(a)
+        q = mq.QTensor(*qshape, fmt, role)
+        ws = mq.quantize_workspace()
+        keep.append((t, q, ws))
+        jobs.append(mq.quant_job(t, layout, q, rnd, seed, ws))
+    mq.mq_quantize_batch(jobs)
+    torch.cuda.synchronize()
+    for (layout, a, qshape, role, rnd, seed), (_, q, _) in zip(items, keep):
+        assert_quant_equal(q, _oracle_for(layout, a, fmt, rnd, seed), fmt,
+                           f"batch {name} layout {layout} {qshape}")
+
+
+def test_quantize_batch_amax_ready_and_special_values():
+    """A job whose partial maxima come from a relayout, next to jobs holding NaN and zeros."""
+    shape = (8, 12, 9, 10)
+    x = workloads.random_array(shape, seed=5)
+    nan = SPECIAL["nan"](shape)
+    zeros = np.zeros((16, 4, 3, 3), np.float32)
+    tx, tn, tz = to_dev(x), to_dev(nan), to_dev(zeros)
+    ws = [mq.quantize_workspace() for _ in range(3)]
+    xc = torch.empty(x.size, dtype=torch.float32, device="cuda")
+    mq.mq_relayout_cbf(tx, xc, 8, 12, 9, 10, 0, amax_ws=ws[0])
+    qx = mq.QTensor(9, 10, 12, 8, 4, mq.MQ_ROLE_ACT)
+    qn = mq.QTensor(9, 10, 12, 8, 4, mq.MQ_ROLE_GRAD)
+    qz = mq.QTensor(3, 3, 16, 4, 4, mq.MQ_ROLE_WEIGHT)
+    mq.mq_quantize_batch([
+        mq.quant_job(tx, mq.MQ_SRC_NCHW, qx, 0, 0, ws[0], mq.MQ_QUANTIZE_AMAX_READY),
+        mq.quant_job(tn, mq.MQ_SRC_NCHW, qn, 1, 3, ws[1]),
+        mq.quant_job(tz, mq.MQ_SRC_OIHW, qz, 0, 0, ws[2])])
+    torch.cuda.synchronize()
+    assert_quant_equal(qx, oracle.quantize(oracle.nchw_to_cbf(x), 4, 0, 0), 4, "amax ready")
+    assert_quant_equal(qn, oracle.quantize(oracle.nchw_to_cbf(nan), 4, 1, 3), 4, "nan")
+    assert_quant_equal(qz, oracle.quantize(oracle.oihw_to_tap_major(zeros), 4, 0, 0), 4, "zeros")
+
+
 # ---- weights straight from OIHW (mq_quantize_weight) -------------------------------------
 
 WEIGHT_SHAPES = [  # (Cout, Cin, Kh, Kw): small (one launch) and large (amax pass + gather)
