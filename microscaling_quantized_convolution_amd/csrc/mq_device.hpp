@@ -94,16 +94,20 @@ __device__ __forceinline__ uint32_t grid_rne(float a)
 // With x = a / step (exact) that is ceil(x - u16 / 65536): for x < 2^8 the difference is exact
 // or keeps its sign and integer part (for x below 1 with a draw far above it), so its ceiling
 // is floor(x) + 1 exactly when the fractional part exceeds the draw. Codes past the largest
-// element saturate (the min).
+// element saturate (the min). Checked on the device against the threshold form for every fp32
+// magnitude below 12, with the draws at and next to each threshold.
 template <int FMT>
 __device__ __forceinline__ uint32_t grid_sr(float a, uint32_t u16)
 {
     using F = Fmt<FMT>;
-    const float sc = a < 2.0f ? F::kScale0 : (a < 4.0f ? 0.5f * F::kScale0 : 0.25f * F::kScale0);
-    const uint32_t ad = a < 2.0f ? 0u : (a < 4.0f ? (uint32_t)F::kAdd1 : (uint32_t)F::kAdd2);
-    const float x = a * sc;                   // exact: sc is a power of two
+    // binade of the grid step: m = 1 below 2 (one step size down to zero), 2 on [2,4), 3 from 4
+    // up (frexp's exponent of a, clamped); x = a / step and the code offset follow from m
+    constexpr int kL = FMT == kFP4 ? 1 : 3; // log2(kScale0) = log2(kAdd1)
+    const int e = __builtin_amdgcn_frexp_expf(a);
+    const int m = min(max(e, 1), 3);
+    const float x = __builtin_amdgcn_ldexpf(a, kL + 1 - m); // exact: a power-of-two scaling
     const float y = __builtin_fmaf(-(float)u16, 0x1p-16f, x);
-    const uint32_t c = (uint32_t)__builtin_ceilf(y) + ad;
+    const uint32_t c = (uint32_t)__builtin_ceilf(y) + ((uint32_t)(m - 1) << kL);
     return c < F::kMaxMag ? c : F::kMaxMag;
 }
 

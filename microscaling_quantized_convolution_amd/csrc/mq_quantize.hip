@@ -216,11 +216,12 @@ __device__ __forceinline__ uint32_t quantize_square(const float (&x)[16], float 
             const float Dlo = D * 0x1p-20f;
             bool slow = !(D >= 0x1p-64f && D <= 0x1p64f);
             if (SR) {
+                // some 0 < |x| < Dlo: on the bit patterns shifted left once (sign dropped), 2|x|-2
+                // wraps for |x| = 0, so its minimum over the square is below 2Dlo-2 exactly then
+                uint32_t mn = 0xFFFFFFFFu;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float ax = fabsf(x[e]);
-                    slow |= (ax < Dlo) && (ax != 0.0f);
-                }
+                for (int e = 0; e < 16; ++e) mn = min(mn, (__float_as_uint(x[e]) << 1) - 2u);
+                slow |= mn < (__float_as_uint(Dlo) << 1) - 2u;
             }
             if (slow) {
 #pragma unroll
