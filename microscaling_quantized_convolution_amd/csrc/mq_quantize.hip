@@ -591,7 +591,7 @@ static hipError_t launch_quant_nchw(const QuantNchwArgs &a, hipStream_t st)
 // Each job is one tensor with its own source order (channel-batch-first or any [o0][o1][r][s]
 // array, NCHW, or an OIHW weight), rounding, seed, amax workspace and destination; the codes,
 // scales and T are those of the single-tensor calls. The amax pass runs every job's workgroups
-// in one grid (contiguous ranges, jobs with the amax ready take none), and so does the
+// in one grid (one grid row per job; jobs with the amax ready take none), and so does the
 // quantizing pass, so small tensors ride along with a large one instead of paying a launch and
 // a memory round trip of their own.
 enum { kJobCbf = 0, kJobNchw = 1, kJobOihw = 2 };
@@ -599,8 +599,8 @@ constexpr int kMaxJobs = 4;
 
 struct QuantJob {
     int kind, sr, full, nq;
-    int a_b0, a_P; // amax pass workgroups (a_P = 0: partial maxima already in the workspace)
-    int q_b0, q_P; // quantizing pass workgroups
+    int a_P;       // amax pass workgroups (0: partial maxima already in the workspace)
+    int q_P;       // quantizing pass workgroups
     int64_t an;    // elements (amax pass; the source and workspace are the kind's own)
     union {
         QuantArgs cbf;      // kJobCbf, kJobOihw
@@ -615,31 +615,29 @@ template <int NJ> struct QuantBatchArgs {
     int njobs;
 };
 
+// Grid (workgroups of the largest job, jobs): workgroup (b, j) is block b of job j, and blocks
+// past a job's own count leave at once. The job comes from the grid, not from a search over the
+// arguments, which would put a chain of dependent argument loads before every workgroup's
+// first memory access (measured 0.5 us per launch pair).
 template <int NJ>
 __global__ void __launch_bounds__(kAmaxThreads) amax_batch_kernel(QuantBatchArgs<NJ> a)
 {
     __shared__ uint32_t red[kAmaxThreads / 64];
+    const QuantJob &jb = a.job[blockIdx.y];
     const int b = (int)blockIdx.x;
-    int j = 0;
-#pragma unroll
-    for (int k = 1; k < NJ; ++k) j = (k < a.njobs && b >= a.job[k].a_b0 && a.job[k].a_P > 0) ? k : j;
-    const QuantJob &jb = a.job[j];
+    if (b >= jb.a_P) return;
     const bool nchw = jb.kind == kJobNchw;
     amax_body(nchw ? jb.nchw.src : jb.cbf.src, jb.an,
-              const_cast<uint32_t *>(nchw ? jb.nchw.amax_ws : jb.cbf.amax_ws), b - jb.a_b0,
-              jb.a_P, red);
+              const_cast<uint32_t *>(nchw ? jb.nchw.amax_ws : jb.cbf.amax_ws), b, jb.a_P, red);
 }
 
 template <int FMT, int NJ>
 __global__ void __launch_bounds__(256) quantize_batch_kernel(QuantBatchArgs<NJ> a)
 {
     __shared__ uint32_t red[4];
-    const int b = (int)blockIdx.x;
-    int j = 0;
-#pragma unroll
-    for (int k = 1; k < NJ; ++k) j = (k < a.njobs && b >= a.job[k].q_b0) ? k : j;
-    const QuantJob &jb = a.job[j];
-    const int lb = b - jb.q_b0;
+    const QuantJob &jb = a.job[blockIdx.y];
+    const int lb = (int)blockIdx.x;
+    if (lb >= jb.q_P) return; // (a whole workgroup: before any barrier)
     if (jb.kind == kJobNchw) {
         if (jb.nq == 4) {
             if (jb.sr) nchw_body<FMT, true, 4, 1>(jb.nchw, red, lb);
@@ -829,7 +827,6 @@ static hipError_t launch_batch_nj(const QuantJobDesc *jobs, int njobs, int fmt, 
 {
     QuantBatchArgs<NJ> a = {};
     a.njobs = njobs;
-    int64_t atot = 0, qtot = 0;
     for (int i = 0; i < njobs; ++i) {
         const QuantJobDesc &d = jobs[i];
         QuantJob &jb = a.job[i];
@@ -871,32 +868,32 @@ static hipError_t launch_batch_nj(const QuantJobDesc *jobs, int njobs, int fmt, 
             jb.q_P = (int)(want < kQuantBlocks ? want : kQuantBlocks);
         }
     }
-    // Quantizing-pass ranges smallest job first: the hardware dispatches workgroups in index
-    // order, so a small job's few workgroups start at once instead of trailing the large one.
-    // (Job order is free: each job carries its own pointers; the amax ranges follow it.)
+    // largest job in grid row 0: the hardware dispatches row by row, so the small jobs' empty
+    // columns come after the large job's workgroups instead of before them (job order is free:
+    // each job carries its own pointers)
     for (int i = 1; i < njobs; ++i)
-        for (int k = i; k > 0 && a.job[k].q_P < a.job[k - 1].q_P; --k) {
+        for (int k = i; k > 0 && a.job[k].q_P > a.job[k - 1].q_P; --k) {
             const QuantJob t = a.job[k];
             a.job[k] = a.job[k - 1];
             a.job[k - 1] = t;
         }
-    atot = 0;
+    int amax_max = 0, q_max = 0;
     for (int i = 0; i < njobs; ++i) {
-        QuantJob &jb = a.job[i];
-        jb.a_b0 = (int)atot;
-        atot += jb.a_P;
-        jb.q_b0 = (int)qtot;
-        qtot += jb.q_P;
+        amax_max = a.job[i].a_P > amax_max ? a.job[i].a_P : amax_max;
+        q_max = a.job[i].q_P > q_max ? a.job[i].q_P : q_max;
     }
-    if (atot > 0) {
-        hipLaunchKernelGGL((amax_batch_kernel<NJ>), dim3((unsigned)atot), dim3(kAmaxThreads), 0, st, a);
+    if (amax_max > 0) {
+        hipLaunchKernelGGL((amax_batch_kernel<NJ>), dim3((unsigned)amax_max, (unsigned)njobs),
+                           dim3(kAmaxThreads), 0, st, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (fmt == kFP4)
-        hipLaunchKernelGGL((quantize_batch_kernel<kFP4, NJ>), dim3((unsigned)qtot), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((quantize_batch_kernel<kFP4, NJ>), dim3((unsigned)q_max, (unsigned)njobs),
+                           dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL((quantize_batch_kernel<kFP6, NJ>), dim3((unsigned)qtot), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((quantize_batch_kernel<kFP6, NJ>), dim3((unsigned)q_max, (unsigned)njobs),
+                           dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
