@@ -31,7 +31,7 @@ struct SpatialClass {
     int r0, c0;       // input offset of sub-kernel tap (0,0)
     int Ah, Bh, Aw, Bw; // weight tap row = Ah + Bh*kh', column = Aw + Bw*kw'
     int tiles_w, tiles;  // pixel tiles along the sub-grid width, total pixel tiles
-    int P, b0;           // workgroups of this class and the first one's index in the grid
+    int P;               // workgroups of this class (grid row = class)
 };
 
 struct SpatialArgs {
@@ -48,7 +48,6 @@ struct SpatialArgs {
     int OWf, M, N;        // output [..][OWf][M][N]
     int M4, nblk;         // row squares, batch blocks of 32
     int sO;
-    int nclass;
     SpatialClass cls[4];
 };
 
@@ -80,12 +79,12 @@ conv_spatial_kernel(SpatialArgs a)
     constexpr int ITEMS = ((KHM * KWM * 16 + 63) / 64 * 64 + HRM * HCM * 8 + NP - 1) / NP;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][ABYTES + BBYTES];
 
-    // The grid holds the workgroups of every class back to back (class k from cls[k].b0 on).
-    const int bx = (int)blockIdx.x;
-    int z = 0;
-#pragma unroll
-    for (int k = 1; k < 4; ++k) z = (k < a.nclass && bx >= a.cls[k].b0) ? k : z;
-    const SpatialClass &cl = a.cls[z];
+    // Grid (workgroups of the largest class, classes): workgroup (b, z) is number b of class z,
+    // and numbers past the class's own count leave at once (a whole workgroup, before any
+    // barrier). The class comes from the grid rather than a search of the classes' ranges in
+    // the arguments, which put dependent argument loads before the first memory access.
+    const SpatialClass &cl = a.cls[blockIdx.y];
+    if ((int)blockIdx.x >= cl.P) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
     // Work items of this class: (M block of 64 rows, pixel tile, batch block), batch block
     // fastest. Workgroup b of the class's P takes items b, b + P, ...; its chunks form one
@@ -94,7 +93,7 @@ conv_spatial_kernel(SpatialArgs a)
     const int nmb = (a.M4 + 15) / 16;
     const int tiles_h = cl.tiles / (cl.tiles_w > 0 ? cl.tiles_w : 1);
     const int T = cl.tiles * a.nblk * nmb;
-    const int P = cl.P, b = bx - cl.b0;
+    const int P = cl.P, b = (int)blockIdx.x;
     // PERSIST: each workgroup loops over several items; otherwise one item per workgroup
     const int nmine = b < T ? (PERSIST ? (T - 1 - b) / P + 1 : 1) : 0;
     // Item w = ((mb * tiles_h + ti) * tiles_w + tj) * nblk + nb, stepped by P in that mixed radix
@@ -452,12 +451,10 @@ static hipError_t launch_spatial_tiles(SpatialArgs &a, int nclass, hipStream_t s
             P = P < 1 ? 1 : (P > items[c] ? items[c] : P);
         }
         a.cls[c].P = P;
-        a.cls[c].b0 = nwg;
-        nwg += P;
+        nwg = P > nwg ? P : nwg;
     }
-    a.nclass = nclass;
     if (nwg == 0) return hipSuccess;
-    dim3 grid((unsigned)nwg, 1, 1);
+    dim3 grid((unsigned)nwg, (unsigned)nclass, 1);
     const bool full3 = nclass == 1 && a.cls[0].kh == 3 && a.cls[0].kw == 3;
 #define MQ_SPATIAL_LAUNCH(KFV, PV)                                                              \
     hipLaunchKernelGGL((conv_spatial_kernel<FMT, A_KR, SI, PH, PW, MW, KFV, PV>), grid,          \
