@@ -5,12 +5,12 @@ One step = one pass of the whole hot path over one batch of synthetic input, for
 3x3 layer (N=32, Cin=Cout=64, 56x56, stride 1, pad 1, NVFP4): quantize X from NCHW and W from
 OIHW into their squares together, as the forward pass does (round-to-nearest; one batched call:
 an amax launch and a quantizing launch over both), quantize G_Y (stochastic, a new seed every
-step), then the forward, weight-gradient and input-gradient GEMMs. Inputs are resident
-in HBM before the timed region starts.
+step), then the forward GEMM and the two gradient GEMMs (weight and input gradient in one call,
+mq_conv_backward). Inputs are resident in HBM before the timed region starts.
 
 The timed steps call the C ABI back to back on one stream (arguments marshalled once, so the
-GPU, not the host, sets the pace), with HIP events on that stream around every launch of the op
-that takes the longest (`roofline`). `--graph` replays one HIP graph per step instead (split
+GPU, not the host, sets the pace), with HIP events on that stream around the op that takes the
+longest (`roofline`) in every `--event-every`-th step. `--graph` replays one HIP graph per step instead (split
 around that op so the events stay outside the graphs). `per_op` times each op alone as a graph
 of back-to-back launches. `cpu_baseline` times the CPU oracle on a bounded sample (rank 0, N=1).
 
@@ -47,6 +47,8 @@ OP_KERNELS = {
                    "void mq::quantize_kernel"],
     "quantize_g": ["mq::amax_kernel", "void mq::quantize_kernel"],
     "conv_fwd": ["void mq::conv_spatial_kernel<4, false"],
+    "conv_backward": ["void mq::conv_wgrad_kernel", "void mq::conv_spatial_kernel<4, true",
+                      "mq::wgrad_sum_kernel"],
     "conv_wgrad": ["void mq::conv_wgrad_kernel", "mq::wgrad_sum_kernel"],
     "conv_dgrad": ["void mq::conv_spatial_kernel<4, true"],
 }
@@ -162,11 +164,13 @@ def main():
         "quantize_xw": ("hbm", 8 * nx + qx_b + 8 * nw + qw_b),
         "quantize_g": ("hbm", 8 * ng + qg_b),
         "conv_fwd": ("gemm", flops), "conv_wgrad": ("gemm", flops), "conv_dgrad": ("gemm", flops),
+        "conv_backward": ("gemm", 2 * flops),
     }
     # conv: quantized operands read once + fp32 result written once
     conv_bytes = {"conv_fwd": qx_b + qw_b + 4 * Ho * Wo * Co * N,
                   "conv_wgrad": qg_b + qx_b + 4 * Kh * Kw * Co * Ci,
                   "conv_dgrad": qw_b + qg_b + 4 * H * W * Ci * N}
+    conv_bytes["conv_backward"] = conv_bytes["conv_wgrad"] + conv_bytes["conv_dgrad"]
     ridge = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 
     def capture(fns):
@@ -185,9 +189,10 @@ def main():
             st.run(s)
     torch.cuda.synchronize()
 
-    # ---- per-op breakdown: each op alone, `op_reps` launches back to back ----
+    # ---- per-op breakdown: each op alone, `op_reps` launches back to back (the step's ops, and
+    # the two gradients as calls of their own, for comparison) ----
     per_op = {}
-    for name, f in ops.items():
+    for name, f in list(ops.items()) + list(st.parts.items()):
         with torch.cuda.stream(stream):
             gr = capture([lambda r=r: f(r) for r in range(args.op_reps)])
             gr.replay()
@@ -210,7 +215,9 @@ def main():
                             "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                             "alg_flops": amount, "alg_bytes": conv_bytes[name],
                             "bound": "mfma" if amount / conv_bytes[name] >= ridge else "hbm"}
-    dominant = args.roofline_op or max(per_op, key=lambda k: per_op[k]["ms"])
+    dominant = args.roofline_op or max(ops, key=lambda k: per_op[k]["ms"])
+    if dominant not in ops:
+        sys.exit(f"--roofline-op {dominant}: not an op of the step ({', '.join(ops)})")
     names = list(ops)
     di = names.index(dominant)
 
@@ -310,7 +317,7 @@ def main():
         "data": "synthetic (seeded numpy PCG64; X=ReLU(N(0,1)), W Kaiming-normal, G_Y~N(0,1e-3))",
         "config": {"workload": "resnet-3x3-s1p1 N=32 Cin=Cout=64 56x56 NVFP4: quantize X "
                                "(from NCHW) and W (from OIHW) in one batched call (RNE), G_Y "
-                               "(SR), conv fwd/wgrad/dgrad",
+                               "(SR), conv fwd, conv backward (wgrad + dgrad in one call)",
                    "N": N, "Cin": Ci, "Cout": Co, "H": H, "W": W, "K": Kh, "stride": 1, "pad": 1,
                    "format": "NVFP4 (E2M1 codes, E4M3 4x4-square scales, fp32 tensor scale)",
                    "mfma": "fp16 operands decoded exactly, fp32 accumulate"},
@@ -399,13 +406,15 @@ def run_config(args):
                "quantize_w": 4 * nw + eb * nw, "quantize_g": 8 * ng + eb * ng,
                "conv_fwd": eb * (nx + nw) + 4 * ng, "conv_wgrad": eb * (nx + ng) + 4 * nw,
                "conv_dgrad": eb * (nw + ng) + 4 * nx}
+        byt["conv_backward"] = byt["conv_wgrad"] + byt["conv_dgrad"]
         ops = {}
         for name, f in calls.items():
             ms = _time_graph([f], args.op_reps, stream)
             gbs = byt[name] / (ms * 1e-3) / 1e9
             if name.startswith("conv"):
-                tf = fl / (ms * 1e-3) / 1e12
-                mfma = fl / byt[name] >= ridge
+                fo = 2 * fl if name == "conv_backward" else fl
+                tf = fo / (ms * 1e-3) / 1e12
+                mfma = fo / byt[name] >= ridge
                 ops[name] = {"ms": round(ms, 5), "TFLOP_s": round(tf, 1), "GB_s": round(gbs, 1),
                              "bound": "mfma" if mfma else "hbm",
                              "frac": round(tf / MFMA_PEAK_TFLOPS if mfma else
@@ -438,7 +447,7 @@ def run_config(args):
                                 f"(from NCHW), conv fwd each (weights quantized once)")
                    if args.inference else
                    (f"{args.config}: {len(layers)} layers, quantize X and W (one batched call), "
-                    f"G_Y, conv fwd/wgrad/dgrad each")},
+                    f"G_Y, conv fwd and backward (wgrad + dgrad in one call) each")},
         "per_layer": per_layer,
     }
     print(json.dumps(result), flush=True)
@@ -588,7 +597,7 @@ def summarize_pmc(fetch_db: str, write_db: str):
         print(f"| {k[:90]} | {fetch[k][1]} | {fk:.1f} | {wk:.1f} | {b:.0f} |")
     # per op (quantize_x/w/g share kernel names with different sizes, so only
     # the convolutions, whose kernels are distinct, get a per-op figure)
-    for op in ("conv_fwd", "conv_wgrad", "conv_dgrad"):
+    for op in ("conv_fwd", "conv_backward", "conv_wgrad", "conv_dgrad"):
         tot = sum(b for k, b in per_kernel.items()
                   if any(k.replace("(anonymous namespace)::", "").startswith(p)
                          for p in OP_KERNELS[op]))

@@ -290,6 +290,22 @@ mq_status mq_conv_wgrad(const mq_conv *p, const mq_qtensor *gy, const mq_qtensor
 mq_status mq_conv_dgrad(const mq_conv *p, const mq_qtensor *w, const mq_qtensor *gy,
                         float *gx_dev, hipStream_t stream);
 
+/*
+ * mq_conv_backward: both gradients of one convolution, G_W as mq_conv_wgrad and G_X as
+ * mq_conv_dgrad compute them (same values, bit for bit), for the backward pass that needs both.
+ * For the tuned shapes the weight gradient's split sum runs inside the input-gradient launch, on
+ * workgroups of its own (when the CUs that launch leaves idle finish it in a few passes), instead
+ * of as a launch between the two GEMMs. gw_dev, gx_dev and ws_dev must not overlap.
+ * w: MQ_ROLE_WEIGHT (Kh, Kw, Cout, Cin); gy: MQ_ROLE_GRAD (Hout, Wout, Cout, N);
+ * x: MQ_ROLE_ACT (H, W, Cin, N); one format.
+ * gw_dev: fp32 [Kh][Kw][Cout][Cin]; gx_dev: fp32 [H][W][Cin][N]; both fully overwritten.
+ * ws_dev / ws_bytes: as for mq_conv_wgrad (mq_wgrad_workspace_bytes(p)).
+ * Errors: MQ_ERR_ARG, MQ_ERR_SHAPE, MQ_ERR_WORKSPACE, MQ_ERR_UNSUPPORTED.
+ */
+mq_status mq_conv_backward(const mq_conv *p, const mq_qtensor *w, const mq_qtensor *gy,
+                           const mq_qtensor *x, float *gw_dev, float *gx_dev, void *ws_dev,
+                           size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

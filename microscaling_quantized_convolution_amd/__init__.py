@@ -30,7 +30,7 @@ EXPORTS = (
     "mq_relayout_weight", "mq_quantize", "mq_quantize_nchw", "mq_quantize_batch",
     "mq_quantize_weight", "mq_conv_fwd",
     "mq_wgrad_workspace_bytes",
-    "mq_conv_wgrad", "mq_conv_dgrad",
+    "mq_conv_wgrad", "mq_conv_dgrad", "mq_conv_backward",
 )
 
 
@@ -85,6 +85,9 @@ def _load() -> ctypes.CDLL:
                                 ctypes.POINTER(mq_qtensor), P, P, sz, P]
     L.mq_conv_dgrad.argtypes = [ctypes.POINTER(mq_conv), ctypes.POINTER(mq_qtensor),
                                 ctypes.POINTER(mq_qtensor), P, P]
+    L.mq_conv_backward.argtypes = [ctypes.POINTER(mq_conv), ctypes.POINTER(mq_qtensor),
+                                   ctypes.POINTER(mq_qtensor), ctypes.POINTER(mq_qtensor), P, P,
+                                   P, sz, P]
     for name in EXPORTS:
         getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int
     return L
@@ -237,6 +240,15 @@ def mq_conv_dgrad(p: ConvLike, w: QTensor, gy: QTensor, gx: torch.Tensor, stream
     c, qw, qg = conv_struct(p), w.struct(), gy.struct()
     _check(_lib.mq_conv_dgrad(ctypes.byref(c), ctypes.byref(qw), ctypes.byref(qg), _ptr(gx),
                               _stream(stream)), "mq_conv_dgrad")
+
+
+def mq_conv_backward(p: ConvLike, w: QTensor, gy: QTensor, x: QTensor, gw: torch.Tensor,
+                     gx: torch.Tensor, ws: torch.Tensor, stream=None):
+    """Both gradients (G_W as mq_conv_wgrad, G_X as mq_conv_dgrad) in one call."""
+    c, qw, qg, qx = conv_struct(p), w.struct(), gy.struct(), x.struct()
+    _check(_lib.mq_conv_backward(ctypes.byref(c), ctypes.byref(qw), ctypes.byref(qg),
+                                 ctypes.byref(qx), _ptr(gw), _ptr(gx), _ptr(ws), _nbytes(ws),
+                                 _stream(stream)), "mq_conv_backward")
 
 
 def out_hw(p: ConvLike) -> Tuple[int, int]:

@@ -4,6 +4,7 @@
 // Nothing here allocates, synchronizes or reads device memory.
 #include "../../include/mq.h"
 #include "mq_kernels.hpp"
+#include "mq_wgrad_sum.hpp"
 
 #include <stdint.h>
 #include <stdlib.h>
@@ -260,6 +261,33 @@ mq_status mq_conv_dgrad(const mq_conv *p, const mq_qtensor *w, const mq_qtensor 
         return launch_status(
             mq::launch_conv_dgrad_spatial(g, w->fmt, operand(w), operand(gy), gx, stream));
     return launch_status(mq::launch_conv_dgrad(g, w->fmt, operand(w), operand(gy), gx, stream));
+}
+
+mq_status mq_conv_backward(const mq_conv *p, const mq_qtensor *w, const mq_qtensor *gy,
+                           const mq_qtensor *x, float *gw, float *gx, void *ws, size_t ws_bytes,
+                           hipStream_t stream)
+{
+    mq::ConvGeom g;
+    if (!conv_geom(p, &g) || !qtensor_ok(w) || !qtensor_ok(gy) || !qtensor_ok(x) || !gw || !gx)
+        return MQ_ERR_ARG;
+    if (!dims_are(w, p->Kh, p->Kw, p->Cout, p->Cin, MQ_ROLE_WEIGHT) ||
+        !dims_are(gy, g.Ho, g.Wo, p->Cout, p->N, MQ_ROLE_GRAD) ||
+        !dims_are(x, p->H, p->W, p->Cin, p->N, MQ_ROLE_ACT) || w->fmt != gy->fmt ||
+        x->fmt != gy->fmt)
+        return MQ_ERR_SHAPE;
+    if (!conv_supported(g)) return MQ_ERR_UNSUPPORTED;
+    if (mq::wgrad_fast_supported(g) && mq::spatial_supported(g)) {
+        if (!ws || ws_bytes < mq::wgrad_fast_workspace_bytes(g)) return MQ_ERR_WORKSPACE;
+        mq::WgradSum sum;
+        const hipError_t e = mq::launch_conv_wgrad_partials(g, x->fmt, operand(gy), operand(x),
+                                                            gw, ws, ws_bytes, stream, &sum);
+        if (e != hipSuccess) return launch_status(e);
+        return launch_status(mq::launch_conv_dgrad_spatial(g, w->fmt, operand(w), operand(gy),
+                                                           gx, stream, &sum));
+    }
+    const mq_status st = mq_conv_wgrad(p, gy, x, gw, ws, ws_bytes, stream);
+    if (st != MQ_OK) return st;
+    return mq_conv_dgrad(p, w, gy, gx, stream);
 }
 
 } // extern "C"

@@ -21,6 +21,7 @@
 // every pixel. The im2col matrix never exists outside registers.
 #include "mq_kernels.hpp"
 #include "mq_stage.hpp"
+#include "mq_wgrad_sum.hpp"
 
 namespace mq {
 
@@ -48,6 +49,9 @@ struct SpatialArgs {
     int OWf, M, N;        // output [..][OWf][M][N]
     int M4, nblk;         // row squares, batch blocks of 32
     int sO;
+    int nclass;           // grid rows 0 .. nclass-1: convolution classes
+    int sum_P;            // grid row nclass (if sum_P > 0): workgroups of the weight-gradient sum
+    WgradSum sum;
     SpatialClass cls[4];
 };
 
@@ -68,6 +72,7 @@ template <int FMT, bool A_KR, int SI, int PH, int PW, int MW, int KF, bool PERSI
 __global__ void __launch_bounds__(32 * PH * PW * (2 / MW))
 conv_spatial_kernel(SpatialArgs a)
 {
+    constexpr int THREADS_OF = 32 * PH * PW * (2 / MW);
     constexpr int NCW = PH * PW / 4 * (2 / MW); // consumer waves (4 pixels x 32*MW rows each)
     constexpr int NP = 64 * NCW;                // producer threads
     constexpr int KHM = 3, KWM = 3;
@@ -83,6 +88,21 @@ conv_spatial_kernel(SpatialArgs a)
     // and numbers past the class's own count leave at once (a whole workgroup, before any
     // barrier). The class comes from the grid rather than a search of the classes' ranges in
     // the arguments, which put dependent argument loads before the first memory access.
+    if ((int)blockIdx.y >= a.nclass) {
+        // the weight gradient's split sum, riding along: two 64-output blocks per pass (one per
+        // 256 lanes), workgroup b taking passes b, b + sum_P, ... (the loop count is the same for
+        // every lane: each call below holds a barrier)
+        static_assert(THREADS_OF == 512, "the sum role takes two 256-lane groups");
+        if ((int)blockIdx.x >= a.sum_P) return;
+        float4(*red)[17] = reinterpret_cast<float4(*)[17]>(lds[0]);
+        const int64_t nb = (a.sum.total + 63) / 64;
+        const int half = (int)threadIdx.x >> 8;
+        for (int64_t base = 2 * (int64_t)blockIdx.x; base < nb; base += 2 * (int64_t)a.sum_P) {
+            wgrad_sum_block(a.sum, base + half, (int)threadIdx.x & 255, red + 16 * half);
+            __syncthreads(); // the next pass reuses red
+        }
+        return;
+    }
     const SpatialClass &cl = a.cls[blockIdx.y];
     if ((int)blockIdx.x >= cl.P) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
@@ -443,7 +463,7 @@ static hipError_t launch_spatial_tiles(SpatialArgs &a, int nclass, hipStream_t s
     // classes, measured slower than the hardware's own dispatch of one workgroup per item,
     // which is used then.
     const bool persist = total >= (nclass == 1 ? 640 : 1024);
-    int nwg = 0;
+    int nwg = 0, conv_wgs = 0;
     for (int c = 0; c < nclass; ++c) {
         int P = items[c];
         if (persist) {
@@ -452,9 +472,29 @@ static hipError_t launch_spatial_tiles(SpatialArgs &a, int nclass, hipStream_t s
         }
         a.cls[c].P = P;
         nwg = P > nwg ? P : nwg;
+        conv_wgs += P;
     }
+    a.nclass = nclass;
+    if (a.sum_P < 0) {
+        // The weight-gradient sum: on the CUs this launch leaves idle (one workgroup per CU:
+        // the LDS), or, when it fills them, on 256 workgroups after its own. A workgroup sums
+        // two 64-output blocks per pass, a chain of dependent loads and a barrier (about 1.5 us),
+        // so the sum rides along only when its passes hide behind the convolution or cost less
+        // than a kernel of their own; otherwise it runs as its own kernel, ahead.
+        const int64_t pairs = ((a.sum.total + 63) / 64 + 1) / 2;
+        const int spare = 256 - conv_wgs;
+        const int64_t P = spare >= 32 ? spare : 256;
+        if ((pairs + P - 1) / P <= (spare >= 32 ? 8 : 2)) {
+            a.sum_P = (int)(pairs < 1 ? 1 : (pairs < P ? pairs : P));
+        } else {
+            a.sum_P = 0;
+            const hipError_t e = launch_wgrad_sum(a.sum, st);
+            if (e != hipSuccess) return e;
+        }
+    }
+    nwg = a.sum_P > nwg ? a.sum_P : nwg;
     if (nwg == 0) return hipSuccess;
-    dim3 grid((unsigned)nwg, (unsigned)nclass, 1);
+    dim3 grid((unsigned)nwg, (unsigned)(nclass + (a.sum_P > 0 ? 1 : 0)), 1);
     const bool full3 = nclass == 1 && a.cls[0].kh == 3 && a.cls[0].kw == 3;
 #define MQ_SPATIAL_LAUNCH(KFV, PV)                                                              \
     hipLaunchKernelGGL((conv_spatial_kernel<FMT, A_KR, SI, PH, PW, MW, KFV, PV>), grid,          \
@@ -533,9 +573,13 @@ static void dgrad_class_dim(int a, int pad, int K, int s, int &cnt, int &r0, int
 }
 
 hipError_t launch_conv_dgrad_spatial(const ConvGeom &g, int fmt, QOperand w, QOperand gy,
-                                     float *gx, hipStream_t st)
+                                     float *gx, hipStream_t st, const WgradSum *sum)
 {
     SpatialArgs a = {};
+    if (sum) {
+        a.sum = *sum;
+        a.sum_P = -1; // sized by the launch
+    }
     a.in_codes = gy.codes; a.in_scales = gy.scales; a.in_T = gy.tscale;
     a.IH = g.Ho; a.IW = g.Wo; a.K4 = g.Cout4; a.N4 = g.N4;
     a.w_codes = w.codes; a.w_scales = w.scales; a.w_T = w.tscale;

@@ -18,6 +18,7 @@
 // splits in a fixed order (deterministic) and applies the tensor scales.
 #include "mq_kernels.hpp"
 #include "mq_stage.hpp"
+#include "mq_wgrad_sum.hpp"
 
 namespace mq {
 
@@ -297,57 +298,11 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
     }
 }
 
-// out[i] = T_G * T_X * sum_{s = 0..S-1} part[s][i], summed in split order. A workgroup holds 64
-// consecutive i (as 16 float4) x 16 split groups; group g sums splits g, g+16, ... in order and
-// the 16 group sums are added in group order.
-__global__ void __launch_bounds__(256) wgrad_sum_kernel(const float *__restrict__ part, int S,
-                                                        int64_t stride, int64_t total,
-                                                        const float *tg, const float *tx,
-                                                        float *__restrict__ out)
+// The split sum as a kernel of its own: one 64-output block per 256-lane workgroup.
+__global__ void __launch_bounds__(256) wgrad_sum_kernel(WgradSum w)
 {
     __shared__ float4 red[16][17];
-    const int v = threadIdx.x & 15, g = threadIdx.x >> 4;
-    const int64_t i4 = (int64_t)blockIdx.x * 16 + v; // float4 index
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    const bool vec = (total % 4 == 0) && (stride % 4 == 0);
-    if (vec && i4 * 4 < total) {
-        // eight loads in flight per batch, added in split order afterwards
-        for (int z0 = g; z0 < S; z0 += 16 * 8) {
-            float4 p[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int z = z0 + 16 * k;
-                p[k] = z < S ? *reinterpret_cast<const float4 *>(part + z * stride + i4 * 4)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (z0 + 16 * k < S) { s.x += p[k].x; s.y += p[k].y; s.z += p[k].z; s.w += p[k].w; }
-        }
-    } else if (!vec) {
-        float e[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int q = 0; q < 4; ++q) {
-            const int64_t i = i4 * 4 + q;
-            if (i < total)
-                for (int z = g; z < S; z += 16) e[q] += part[z * stride + i];
-        }
-        s = make_float4(e[0], e[1], e[2], e[3]);
-    }
-    red[g][v] = s;
-    __syncthreads();
-    if (g == 0) {
-        float4 t = red[0][v];
-        for (int q = 1; q < 16; ++q) {
-            const float4 p = red[q][v];
-            t.x += p.x; t.y += p.y; t.z += p.z; t.w += p.w;
-        }
-        const double sc = (double)*tg * (double)*tx;
-        const float r[4] = {t.x, t.y, t.z, t.w};
-        for (int q = 0; q < 4; ++q) {
-            const int64_t i = i4 * 4 + q;
-            if (i < total) out[i] = (float)((double)r[q] * sc);
-        }
-    }
+    wgrad_sum_block(w, blockIdx.x, (int)threadIdx.x, red);
 }
 
 struct Plan {
@@ -442,8 +397,9 @@ static void launch_wgrad_fmt(const ConvGeom &g, dim3 grid, const WgradArgs &a, h
     else launch_wgrad_si<FMT, 2>(g, grid, a, st);
 }
 
-hipError_t launch_conv_wgrad_fast(const ConvGeom &g, int fmt, QOperand gy, QOperand x, float *gw,
-                                  void *ws, size_t ws_bytes, hipStream_t st)
+hipError_t launch_conv_wgrad_partials(const ConvGeom &g, int fmt, QOperand gy, QOperand x,
+                                      float *gw, void *ws, size_t ws_bytes, hipStream_t st,
+                                      WgradSum *sum)
 {
     const Plan p = plan(g);
     if (ws_bytes < p.bytes) return hipErrorInvalidValue;
@@ -459,13 +415,29 @@ hipError_t launch_conv_wgrad_fast(const ConvGeom &g, int fmt, QOperand gy, QOper
     dim3 grid((unsigned)p.splits, (unsigned)p.tiles, 1);
     if (fmt == kFP4) launch_wgrad_fmt<kFP4>(g, grid, a, st);
     else launch_wgrad_fmt<kFP6>(g, grid, a, st);
-    hipError_t e = hipGetLastError();
+    sum->part = reinterpret_cast<const float *>(ws);
+    sum->S = p.splits;
+    sum->stride = p.split_stride;
+    sum->total = p.split_stride;
+    sum->tg = gy.tscale;
+    sum->tx = x.tscale;
+    sum->out = gw;
+    return hipGetLastError();
+}
+
+hipError_t launch_conv_wgrad_fast(const ConvGeom &g, int fmt, QOperand gy, QOperand x, float *gw,
+                                  void *ws, size_t ws_bytes, hipStream_t st)
+{
+    WgradSum w;
+    const hipError_t e = launch_conv_wgrad_partials(g, fmt, gy, x, gw, ws, ws_bytes, st, &w);
     if (e != hipSuccess) return e;
-    const int64_t total = p.split_stride;
-    const unsigned blocks = (unsigned)((total + 63) / 64);
-    hipLaunchKernelGGL(wgrad_sum_kernel, dim3(blocks), dim3(256), 0, st,
-                       reinterpret_cast<const float *>(ws), p.splits, p.split_stride, total,
-                       gy.tscale, x.tscale, gw);
+    return launch_wgrad_sum(w, st);
+}
+
+hipError_t launch_wgrad_sum(const WgradSum &w, hipStream_t st)
+{
+    if (w.total <= 0) return hipSuccess;
+    hipLaunchKernelGGL(wgrad_sum_kernel, dim3((unsigned)((w.total + 63) / 64)), dim3(256), 0, st, w);
     return hipGetLastError();
 }
 

@@ -70,12 +70,16 @@ hipError_t launch_conv_wgrad(const ConvGeom &g, int fmt, QOperand gy, QOperand x
 hipError_t launch_conv_dgrad(const ConvGeom &g, int fmt, QOperand w, QOperand gy, float *gx,
                              hipStream_t st);
 
+struct WgradSum;
+
 // Halo-tiled forward / input-gradient kernels (Kh, Kw <= 3, equal strides 1 or 2).
+// launch_conv_dgrad_spatial with a sum: the weight gradient's split sum runs in the same launch,
+// on workgroups of its own (a grid row after the input-gradient classes).
 bool spatial_supported(const ConvGeom &g);
 hipError_t launch_conv_fwd_spatial(const ConvGeom &g, int fmt, QOperand x, QOperand w, float *y,
                                    hipStream_t st);
 hipError_t launch_conv_dgrad_spatial(const ConvGeom &g, int fmt, QOperand w, QOperand gy,
-                                     float *gx, hipStream_t st);
+                                     float *gx, hipStream_t st, const struct WgradSum *sum = nullptr);
 
 // Split-K weight gradient with all kw taps of one kernel row per workgroup (Kw <= 3,
 // equal strides 1 or 2) and a deterministic split sum.
@@ -83,5 +87,12 @@ bool wgrad_fast_supported(const ConvGeom &g);
 size_t wgrad_fast_workspace_bytes(const ConvGeom &g);
 hipError_t launch_conv_wgrad_fast(const ConvGeom &g, int fmt, QOperand gy, QOperand x, float *gw,
                                   void *ws, size_t ws_bytes, hipStream_t st);
+// The split-K kernel alone: the partial sums go to ws and *sum describes their sum into gw, to be
+// run by launch_wgrad_sum or by workgroups riding along in the input-gradient launch.
+hipError_t launch_conv_wgrad_partials(const ConvGeom &g, int fmt, QOperand gy, QOperand x,
+                                      float *gw, void *ws, size_t ws_bytes, hipStream_t st,
+                                      struct WgradSum *sum);
+// The sum of those partials as a kernel of its own (nothing when there is nothing to sum).
+hipError_t launch_wgrad_sum(const struct WgradSum &sum, hipStream_t st);
 
 } // namespace mq

@@ -33,8 +33,8 @@ import torch
 from torch import nn
 
 from . import (MQ_NVFP4, MQ_QUANTIZE_WS_BYTES, MQ_ROLE_ACT, MQ_ROLE_GRAD, MQ_ROLE_WEIGHT,
-               MQ_RNE, MQ_SR, MQ_SRC_NCHW, MQ_SRC_OIHW, QTensor, mq_conv_dgrad, mq_conv_fwd,
-               mq_conv_wgrad, mq_quantize_batch, mq_quantize_nchw, mq_quantize_weight,
+               MQ_RNE, MQ_SR, MQ_SRC_NCHW, MQ_SRC_OIHW, QTensor, mq_conv_backward,
+               mq_conv_dgrad, mq_conv_fwd, mq_conv_wgrad, mq_quantize_batch, mq_quantize_nchw, mq_quantize_weight,
                mq_relayout_cbf, mq_relayout_weight, mq_wgrad_workspace_bytes, out_hw,
                quant_job)
 
@@ -108,16 +108,23 @@ class MQConv2dFunction(torch.autograd.Function):
         ws = torch.empty(MQ_QUANTIZE_WS_BYTES, dtype=torch.uint8, device=dev)
         qg = quantize_activation(gy, fmt, MQ_SR, ctx.sr_seed, MQ_ROLE_GRAD, ws)
         gx = gw = None
-        if ctx.needs_input_grad[1]:
+        need_x, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        if need_w:
             gwk = torch.empty(Kh * Kw * Cout * Cin, dtype=torch.float32, device=dev)
             wsb = torch.empty(max(1, mq_wgrad_workspace_bytes(conv)), dtype=torch.uint8,
                               device=dev)
+        if need_x:
+            gxc = torch.empty(H * W * Cin * N, dtype=torch.float32, device=dev)
+        if need_w and need_x:  # both gradients in one call (their launches overlap)
+            mq_conv_backward(conv, ctx.qw, qg, ctx.qx, gwk, gxc, wsb)
+        elif need_w:
             mq_conv_wgrad(conv, qg, ctx.qx, gwk, wsb)
+        elif need_x:
+            mq_conv_dgrad(conv, ctx.qw, qg, gxc)
+        if need_w:
             gw = torch.empty((Cout, Cin, Kh, Kw), dtype=torch.float32, device=dev)
             mq_relayout_weight(gwk, gw, Cout, Cin, Kh, Kw, 1)
-        if ctx.needs_input_grad[0]:
-            gxc = torch.empty(H * W * Cin * N, dtype=torch.float32, device=dev)
-            mq_conv_dgrad(conv, ctx.qw, qg, gxc)
+        if need_x:
             gx = torch.empty((N, Cin, H, W), dtype=torch.float32, device=dev)
             mq_relayout_cbf(gxc, gx, N, Cin, H, W, 1)
         ctx.qx = ctx.qw = None

@@ -5,7 +5,13 @@ tensors, the outputs and the weight-gradient workspace) and the calls of one pas
 
   quantize_xw  X NCHW -> quantized channel-batch-first squares and W OIHW -> quantized
                tap-major squares (both round to nearest), one batched call
-  quantize_g   G_Y (stochastic, seed per pass)   conv_fwd / conv_wgrad / conv_dgrad
+  quantize_g   G_Y (stochastic, seed per pass)
+  conv_fwd     Y = W.X'
+  conv_backward  G_W = G_Y.X'^T and G_X = W^T.G_Y in one call (mq_conv_backward: the weight
+               gradient's split sum rides in the input-gradient launch)
+
+conv_wgrad and conv_dgrad, the two gradients as calls of their own, stay available in
+`parts` (same results, bit for bit).
 
 X and W are quantized together, as a layer's forward pass does (mq_quantize_batch: one amax
 launch over both, then one launch that reads X in NCHW and W in OIHW order and writes their
@@ -23,8 +29,8 @@ from typing import Callable, Dict
 import torch
 
 from . import (MQ_QUANTIZE_WS_BYTES, MQ_ROLE_ACT, MQ_ROLE_GRAD, MQ_ROLE_WEIGHT, MQ_RNE, MQ_SR,
-               MQ_SRC_NCHW, MQ_SRC_OIHW, QTensor, conv_struct, mq_conv_dgrad, mq_conv_fwd,
-               mq_conv_wgrad, mq_quant_job, mq_quantize, mq_quantize_batch,
+               MQ_SRC_NCHW, MQ_SRC_OIHW, QTensor, conv_struct, mq_conv_backward, mq_conv_dgrad,
+               mq_conv_fwd, mq_conv_wgrad, mq_quant_job, mq_quantize, mq_quantize_batch,
                mq_wgrad_workspace_bytes, out_hw, quant_job)
 
 
@@ -61,6 +67,10 @@ class LayerStep:
             ("quantize_g", lambda s: mq_quantize(self.gc, self.qg, MQ_SR,
                                                  self.sr_seed_base + s, a2)),
             ("conv_fwd", lambda s: mq_conv_fwd(p, self.qx, self.qw, self.y)),
+            ("conv_backward", lambda s: mq_conv_backward(p, self.qw, self.qg, self.qx, self.gw,
+                                                         self.gx, self.ws)),
+        ])
+        self.parts: Dict[str, Callable[[int], None]] = OrderedDict([
             ("conv_wgrad", lambda s: mq_conv_wgrad(p, self.qg, self.qx, self.gw, self.ws)),
             ("conv_dgrad", lambda s: mq_conv_dgrad(p, self.qw, self.qg, self.gx)),
         ])
@@ -96,6 +106,8 @@ class LayerStep:
         fixed = {
             "quantize_xw": (L.mq_quantize_batch, (jobs, 2, hs)),
             "conv_fwd": (L.mq_conv_fwd, (conv, bx, bw, P(self.y), hs)),
+            "conv_backward": (L.mq_conv_backward, (conv, bw, bg, bx, P(self.gw), P(self.gx),
+                                                   P(self.ws), nws, hs)),
             "conv_wgrad": (L.mq_conv_wgrad, (conv, bg, bx, P(self.gw), P(self.ws), nws, hs)),
             "conv_dgrad": (L.mq_conv_dgrad, (conv, bw, bg, P(self.gx), hs)),
         }

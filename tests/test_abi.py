@@ -136,6 +136,15 @@ def test_validation_errors_without_gpu():
     assert L.mq_conv_wgrad(ctypes.byref(conv), ctypes.byref(g), ctypes.byref(x), y, None, 0, s0) == mq.MQ_ERR_WORKSPACE
     need = L.mq_wgrad_workspace_bytes(ctypes.byref(conv))
     assert L.mq_conv_wgrad(ctypes.byref(conv), ctypes.byref(g), ctypes.byref(x), y, y, need - 1, s0) == mq.MQ_ERR_WORKSPACE
+    # both gradients in one call
+    bw = lambda *a: L.mq_conv_backward(ctypes.byref(conv), *a, s0)
+    assert bw(ctypes.byref(w), ctypes.byref(g), ctypes.byref(x), y, None, y, need, ) == mq.MQ_ERR_ARG
+    assert bw(ctypes.byref(w), ctypes.byref(g), ctypes.byref(x), None, y, y, need) == mq.MQ_ERR_ARG
+    assert bw(ctypes.byref(x), ctypes.byref(g), ctypes.byref(x), y, y, y, need) == mq.MQ_ERR_SHAPE
+    assert bw(ctypes.byref(w), ctypes.byref(g7), ctypes.byref(x), y, y, y, need) == mq.MQ_ERR_SHAPE
+    assert bw(ctypes.byref(w), ctypes.byref(g), ctypes.byref(x6), y, y, y, need) == mq.MQ_ERR_SHAPE
+    assert bw(ctypes.byref(w), ctypes.byref(g), ctypes.byref(x), y, y, None, 0) == mq.MQ_ERR_WORKSPACE
+    assert bw(ctypes.byref(w), ctypes.byref(g), ctypes.byref(x), y, y, y, need - 1) == mq.MQ_ERR_WORKSPACE
     # an impossible convolution -> MQ_ERR_ARG
     badc = mq.conv_struct((2, 16, 2, 2, 16, 3, 3, 1, 1, 0, 0))
     assert L.mq_conv_fwd(ctypes.byref(badc), ctypes.byref(x), ctypes.byref(w), y, s0) == mq.MQ_ERR_ARG

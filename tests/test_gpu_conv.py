@@ -136,3 +136,20 @@ def test_conv_one_hot_weight_reads_im2col_column():
                                            atol=0)
         others = [c for c in range(layer.Cout) if c != co]
         assert (y[:, :, others, :] == 0).all()
+
+
+@pytest.mark.parametrize("layer", SMALL + [workloads.config2()[0], workloads.config3()[0]],
+                         ids=lambda l: l.name)
+def test_conv_backward_equals_separate_calls(layer):
+    """mq_conv_backward (the weight gradient's split sum riding in the input-gradient launch)
+    gives G_W and G_X bit for bit equal to mq_conv_wgrad and mq_conv_dgrad."""
+    log("conv backward", layer.name)
+    gl = run_gpu_layer(layer)
+    p = layer.conv_tuple()
+    gw = torch.full_like(gl.gw, float("nan"))
+    gx = torch.full_like(gl.gx, float("nan"))
+    ws = torch.empty(mq.mq_wgrad_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    mq.mq_conv_backward(p, gl.qw, gl.qg, gl.qx, gw, gx, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(gw, gl.gw), f"{layer.name}: G_W differs"
+    assert torch.equal(gx, gl.gx), f"{layer.name}: G_X differs"
