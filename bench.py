@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--roofline-op", default=None,
                     help="op the roofline covers (default: the one with the longest per-op time)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--parts", action="store_true",
+                    help="also time conv_wgrad and conv_dgrad as calls of their own in per_op "
+                         "(not part of the step)")
     ap.add_argument("--cpu-sample-n", type=int, default=32,
                     help="batch elements of the layer the CPU oracle runs on")
     ap.add_argument("--calib-copy", action="store_true",
@@ -189,10 +192,10 @@ def main():
             st.run(s)
     torch.cuda.synchronize()
 
-    # ---- per-op breakdown: each op alone, `op_reps` launches back to back (the step's ops, and
-    # the two gradients as calls of their own, for comparison) ----
+    # ---- per-op breakdown: each op alone, `op_reps` launches back to back (the step's ops; with
+    # --parts also the two gradients as calls of their own, for comparison) ----
     per_op = {}
-    for name, f in list(ops.items()) + list(st.parts.items()):
+    for name, f in list(ops.items()) + (list(st.parts.items()) if args.parts else []):
         with torch.cuda.stream(stream):
             gr = capture([lambda r=r: f(r) for r in range(args.op_reps)])
             gr.replay()
