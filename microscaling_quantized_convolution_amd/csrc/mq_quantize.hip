@@ -268,16 +268,35 @@ __device__ __forceinline__ void store_square_codes(uint8_t *codes, int64_t t, co
 // the four rows are aligned float4 loads. OIHW: the source is a weight in OIHW order (plane =
 // kh*Kw + kw, R = Cout, S = Cin): element (plane, r, s) is read from src[(r*S + s)*planes +
 // plane], so the tap-major fp32 copy is never written.
-// Tensor scale T from the partial maxima in ws (every lane of a 256-lane workgroup takes part).
-template <int FMT>
-__device__ __forceinline__ float tensor_scale(const uint32_t *ws, uint32_t *red, bool &nonfinite)
+// Tensor scale T from the partial maxima in ws (every lane of a 256-lane workgroup takes part),
+// in two halves: the loads, issued before a lane loads its squares, and the reduction. Vector
+// loads complete in issue order, so partial maxima loaded after the squares would hold the
+// reduction (and every square's arithmetic) until the lane's last square load had landed. Every
+// one of the kAmaxParts words is loaded (the workspace always holds them) and the count masks
+// the unused ones afterwards, so no load waits for another.
+struct TScaleIn {
+    uint32_t np;
+    uint32_t v[kAmaxParts / 256];
+};
+
+__device__ __forceinline__ TScaleIn load_tscale_in(const uint32_t *ws)
 {
-    const uint32_t np = min(ws[0], (uint32_t)kAmaxParts);
+    TScaleIn in;
+    in.np = ws[0];
+#pragma unroll
+    for (int k = 0; k < kAmaxParts / 256; ++k) in.v[k] = ws[1 + threadIdx.x + 256u * k];
+    return in;
+}
+
+template <int FMT>
+__device__ __forceinline__ float tensor_scale(const TScaleIn &in, uint32_t *red, bool &nonfinite)
+{
+    const uint32_t np = min(in.np, (uint32_t)kAmaxParts);
     uint32_t pm = 0u;
 #pragma unroll
     for (int k = 0; k < kAmaxParts / 256; ++k) {
         const uint32_t i = threadIdx.x + 256u * k;
-        pm = max(pm, i < np ? ws[1 + i] : 0u);
+        pm = max(pm, i < np ? in.v[k] : 0u);
     }
     const uint32_t abits = block_max_u32<256>(pm, red);
     nonfinite = abits >= 0x7F800000u;
@@ -355,10 +374,11 @@ __device__ __forceinline__ void cbf_body(const QuantArgs &a, uint32_t *red, int 
     // Grid-stride over squares with the next square's loads in flight while this one is
     // quantized (the last step reloads its own square, so every step issues the same loads).
     Pos pos = {tl / a.S4 / a.R4, (tl / a.S4) % a.R4, tl % a.S4};
+    const TScaleIn tin = load_tscale_in(a.amax_ws);
     float xn[16];
     load(pos, xn);
     bool nonfinite;
-    const float T = tensor_scale<FMT>(a.amax_ws, red, nonfinite);
+    const float T = tensor_scale<FMT>(tin, red, nonfinite);
     if (b == 0 && threadIdx.x == 0) store_tscale(a.tscale, T, nonfinite);
     if (!active) return;
     if constexpr (OIHW) {
@@ -521,13 +541,16 @@ __device__ __forceinline__ void nchw_body(const QuantNchwArgs &a, uint32_t *red,
     const rsrc_t src = make_rsrc(a.src, a.bytes);
     const uint32_t CHW4 = (uint32_t)a.C * (uint32_t)a.HW * 4u, HW4 = (uint32_t)a.HW * 4u;
     const uint32_t lane_off = (uint32_t)(4 * ng * NQ) * CHW4 + (uint32_t)(4 * c4) * HW4 + 4u * (uint32_t)p;
+    const TScaleIn tin = load_tscale_in(a.amax_ws);
+    // square by square, so that the first square's arithmetic can start while the later
+    // squares' loads are still in flight
     float x[PX][NQ][16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const bool cin = 4 * c4 + i < a.C;
-        const uint32_t voff = (act && pin && cin) ? lane_off : kBad;
+    for (int k = 0; k < NQ; ++k) {
 #pragma unroll
-        for (int k = 0; k < NQ; ++k)
+        for (int i = 0; i < 4; ++i) {
+            const bool cin = 4 * c4 + i < a.C;
+            const uint32_t voff = (act && pin && cin) ? lane_off : kBad;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 float v[PX];
@@ -535,9 +558,11 @@ __device__ __forceinline__ void nchw_body(const QuantNchwArgs &a, uint32_t *red,
 #pragma unroll
                 for (int q = 0; q < PX; ++q) x[q][k][4 * i + j] = v[q];
             }
+        }
+        __builtin_amdgcn_sched_barrier(0); // keep the squares' loads in this order
     }
     bool nonfinite;
-    const float T = tensor_scale<FMT>(a.amax_ws, red, nonfinite);
+    const float T = tensor_scale<FMT>(tin, red, nonfinite);
     if (b == 0 && threadIdx.x == 0) store_tscale(a.tscale, T, nonfinite);
     if (!act || !pin) return;
 #pragma unroll
