@@ -33,7 +33,20 @@ struct SpatialClass {
     int Ah, Bh, Aw, Bw; // weight tap row = Ah + Bh*kh', column = Aw + Bw*kw'
     int tiles_w, tiles;  // pixel tiles along the sub-grid width, total pixel tiles
     int P;               // workgroups of this class (grid row = class)
+    // Set by the launch, so that a workgroup's first item and its step through the items take
+    // no division on the device: tiles_h pixel tiles along the height, T items, the step P in
+    // the items' mixed radix, and multipliers m with n / d = mulhi(n, m) for the divisors nblk,
+    // tiles_w, tiles_h and P (exact for n * d < 2^32; m = 0 stands for d = 1).
+    int tiles_h, T;
+    int step_nb, step_tj, step_ti, step_mb;
+    uint32_t m_nblk, m_tw, m_th, m_P;
 };
+
+// n / d for the multiplier m of d (see SpatialClass).
+__device__ __forceinline__ int div_by(int n, uint32_t m)
+{
+    return m ? (int)__umulhi((uint32_t)n, m) : n;
+}
 
 struct SpatialArgs {
     const uint8_t *in_codes;
@@ -72,6 +85,7 @@ template <int FMT, bool A_KR, int SI, int PH, int PW, int MW, int KF, bool PERSI
 __global__ void __launch_bounds__(32 * PH * PW * (2 / MW))
 conv_spatial_kernel(SpatialArgs a)
 {
+    warm_kernel_args<SpatialArgs>();
     constexpr int THREADS_OF = 32 * PH * PW * (2 / MW);
     constexpr int NCW = PH * PW / 4 * (2 / MW); // consumer waves (4 pixels x 32*MW rows each)
     constexpr int NP = 64 * NCW;                // producer threads
@@ -110,31 +124,31 @@ conv_spatial_kernel(SpatialArgs a)
     // fastest. Workgroup b of the class's P takes items b, b + P, ...; its chunks form one
     // stream (item-major), so the producer runs into the next item while the consumers write
     // the current one's output.
-    const int nmb = (a.M4 + 15) / 16;
-    const int tiles_h = cl.tiles / (cl.tiles_w > 0 ? cl.tiles_w : 1);
-    const int T = cl.tiles * a.nblk * nmb;
-    const int P = cl.P, b = (int)blockIdx.x;
+    const int tiles_h = cl.tiles_h;
+    const int T = cl.T;
+    const int b = (int)blockIdx.x;
     // PERSIST: each workgroup loops over several items; otherwise one item per workgroup
-    const int nmine = b < T ? (PERSIST ? (T - 1 - b) / P + 1 : 1) : 0;
+    const int nmine = b < T ? (PERSIST ? div_by(T - 1 - b, cl.m_P) + 1 : 1) : 0;
     // Item w = ((mb * tiles_h + ti) * tiles_w + tj) * nblk + nb, stepped by P in that mixed radix
     // with carries (no division per item).
     struct ItemPos { int nb, tj, ti, mb; };
-    ItemPos step_p;
-    {
-        int r = P;
-        step_p.nb = r % a.nblk; r /= a.nblk;
-        step_p.tj = r % cl.tiles_w; r /= cl.tiles_w;
-        step_p.ti = r % tiles_h; r /= tiles_h;
-        step_p.mb = r;
-    }
+    const ItemPos step_p = {cl.step_nb, cl.step_tj, cl.step_ti, cl.step_mb};
     ItemPos first;
     {
-        int r = b;
-        first.nb = r % a.nblk; r /= a.nblk;
-        first.tj = r % cl.tiles_w; r /= cl.tiles_w;
-        first.ti = r % tiles_h; r /= tiles_h;
-        first.mb = r;
+        const int q0 = div_by(b, cl.m_nblk), q1 = div_by(q0, cl.m_tw), q2 = div_by(q1, cl.m_th);
+        first.nb = b - q0 * a.nblk;
+        first.tj = q0 - q1 * cl.tiles_w;
+        first.ti = q1 - q2 * tiles_h;
+        first.mb = q2;
     }
+    // The arguments the producer needs before its first load, read here, together: left to
+    // the compiler, each was loaded next to its first use, and the chain of dependent
+    // argument reads delayed the first load by about a microsecond.
+    asm volatile("" ::"s"(step_p.nb), "s"(step_p.tj), "s"(step_p.ti), "s"(step_p.mb),
+                 "s"(first.nb), "s"(first.tj), "s"(first.ti), "s"(first.mb), "s"(nmine));
+    asm volatile("" ::"s"(cl.r0), "s"(cl.c0), "s"(cl.Ah), "s"(cl.Bh), "s"(cl.Aw), "s"(cl.Bw),
+                 "s"(a.IH), "s"(a.IW), "s"(a.K4), "s"(a.N4), "s"(a.Kw), "s"(a.Cout4), "s"(a.Cin4),
+                 "s"(a.M4));
     auto advance = [&](ItemPos p) {
         p.nb += step_p.nb;
         int c = p.nb >= a.nblk;
@@ -295,11 +309,12 @@ conv_spatial_kernel(SpatialArgs a)
                 }
             }
         };
-        // step g: decode chunk g + 1 from slot (g + 1) & 1 into LDS buffer (g + 1) & 1, then
-        // load chunk g + 3 into that slot
+        // chunk 0 alone first (issued together with chunk 1, it landed about 0.4 us later);
+        // then step g: decode chunk g + 1 from slot (g + 1) & 1 into LDS buffer (g + 1) & 1,
+        // then load chunk g + 3 into that slot
         load(0, raw[0]);
-        load(1, raw[1]);
         store(0, raw[0]);
+        load(1, raw[1]);
         load(2, raw[0]);
         __syncthreads();
         int gs = 0;
@@ -422,7 +437,30 @@ template <> struct TileShape<2> { static constexpr int PH = 1, PW = 8, MW = 1; }
 static void set_tiles(SpatialClass &c, int PH, int PW)
 {
     c.tiles_w = (c.OWs + PW - 1) / PW;
-    c.tiles = c.tiles_w * ((c.OHs + PH - 1) / PH);
+    c.tiles_h = (c.OHs + PH - 1) / PH;
+    c.tiles = c.tiles_w * c.tiles_h;
+}
+
+// Multiplier m of divisor d >= 1: n / d = mulhi(n, m) for n * d < 2^32 (the error of
+// m = floor(2^32 / d) + 1 is below n / 2^32 < 1 / d); 0 for d = 1.
+static uint32_t div_multiplier(int d)
+{
+    return d <= 1 ? 0u : (uint32_t)((1ull << 32) / (uint64_t)d + 1ull);
+}
+
+// The item bookkeeping of a class with its workgroup count P set.
+static void set_items(SpatialClass &c, int nblk, int nmb)
+{
+    c.T = c.tiles * nblk * nmb;
+    int r = c.P;
+    c.step_nb = r % nblk; r /= nblk;
+    c.step_tj = r % (c.tiles_w > 0 ? c.tiles_w : 1); r /= (c.tiles_w > 0 ? c.tiles_w : 1);
+    c.step_ti = r % (c.tiles_h > 0 ? c.tiles_h : 1); r /= (c.tiles_h > 0 ? c.tiles_h : 1);
+    c.step_mb = r;
+    c.m_nblk = div_multiplier(nblk);
+    c.m_tw = div_multiplier(c.tiles_w);
+    c.m_th = div_multiplier(c.tiles_h);
+    c.m_P = div_multiplier(c.P);
 }
 
 bool spatial_supported(const ConvGeom &g)
@@ -437,7 +475,17 @@ bool spatial_supported(const ConvGeom &g)
                    ws = (uint64_t)g.Kh * g.Kw * g.Cout4 * g.Cin4 * 12,
                    ys = (uint64_t)g.Ho * g.Wo * g.Cout * g.N * 4,
                    xo = (uint64_t)g.H * g.W * g.Cin * g.N * 4;
-    return xs < lim && gs < lim && ws < lim && ys < lim && xo < lim;
+    if (!(xs < lim && gs < lim && ws < lim && ys < lim && xo < lim)) return false;
+    // the item bookkeeping's divisions by multiplier: items * divisor < 2^32 (tiles of at least
+    // 1 x 8 pixels; divisors nblk, tiles along a dimension, and at most 256 workgroups)
+    const uint64_t Hm = g.H > g.Ho ? g.H : g.Ho, Wm = g.W > g.Wo ? g.W : g.Wo;
+    const uint64_t tw = (Wm + 7) / 8, nblk = (g.N4 + 7) / 8;
+    const uint64_t nmb = ((g.Cin4 > g.Cout4 ? g.Cin4 : g.Cout4) + 15) / 16;
+    uint64_t dmax = 256;
+    dmax = nblk > dmax ? nblk : dmax;
+    dmax = tw > dmax ? tw : dmax;
+    dmax = Hm > dmax ? Hm : dmax;
+    return Hm * tw * nblk * nmb * dmax < (1ull << 32);
 }
 
 template <int FMT, bool A_KR, int SI, int PH, int PW, int MW>
@@ -471,6 +519,7 @@ static hipError_t launch_spatial_tiles(SpatialArgs &a, int nclass, hipStream_t s
             P = P < 1 ? 1 : (P > items[c] ? items[c] : P);
         }
         a.cls[c].P = P;
+        set_items(a.cls[c], a.nblk, (a.M4 + 15) / 16);
         nwg = P > nwg ? P : nwg;
         conv_wgs += P;
     }

@@ -70,6 +70,7 @@ inline bool stage_gl(int N4, int si) { return N4 % 4 == 0 && (si == 1 || si == 2
 template <int FMT, int SI, int KF, int kKS, bool GL>
 __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
 {
+    warm_kernel_args<WgradArgs>();
     constexpr int kPWg = StagePixels<SI, kKS, GL>::kPW;
     constexpr int KWM = KF ? KF : 3;
     constexpr int HCM = (kPWg - 1) * SI + KWM;

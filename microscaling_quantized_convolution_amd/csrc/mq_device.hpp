@@ -141,4 +141,39 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
 // bf16 bit pattern of an fp32 value that is exactly representable in bf16.
 __device__ __forceinline__ uint32_t bf16_bits_exact(float v) { return __float_as_uint(v) >> 16; }
 
+// Bring a kernel's argument block into the scalar cache in one round trip: one load per 64-byte
+// line, all in flight together, and one wait. Left to the compiler, each argument is loaded next
+// to its first use, and the lines of a large argument block (per-job or per-class tables
+// indexed by the grid) then arrive one dependent miss after another before the first memory
+// access of the kernel. The loads wait inside the asm block, so no load is in flight once it
+// ends.
+template <typename Args>
+__device__ __forceinline__ void warm_kernel_args()
+{
+    static_assert(sizeof(Args) >= 4 && sizeof(Args) <= 640, "argument block of 1 to 10 lines");
+    constexpr uint32_t kLast = ((uint32_t)sizeof(Args) - 4u) & ~3u; // last dword of the block
+#define MQ_LINE(k) ((64u * (k)) < kLast ? 64u * (k) : kLast)
+    const uint64_t kp = (uint64_t)__builtin_amdgcn_kernarg_segment_ptr();
+    uint32_t d0, d1, d2, d3, d4, d5, d6, d7, d8, d9;
+    asm volatile("s_load_dword %0, %10, 0\n\t"
+                 "s_load_dword %1, %10, %11\n\t"
+                 "s_load_dword %2, %10, %12\n\t"
+                 "s_load_dword %3, %10, %13\n\t"
+                 "s_load_dword %4, %10, %14\n\t"
+                 "s_load_dword %5, %10, %15\n\t"
+                 "s_load_dword %6, %10, %16\n\t"
+                 "s_load_dword %7, %10, %17\n\t"
+                 "s_load_dword %8, %10, %18\n\t"
+                 "s_load_dword %9, %10, %19\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&s"(d0), "=&s"(d1), "=&s"(d2), "=&s"(d3), "=&s"(d4), "=&s"(d5), "=&s"(d6),
+                   "=&s"(d7), "=&s"(d8), "=&s"(d9)
+                 : "s"(kp), "i"(MQ_LINE(1)), "i"(MQ_LINE(2)), "i"(MQ_LINE(3)), "i"(MQ_LINE(4)),
+                   "i"(MQ_LINE(5)), "i"(MQ_LINE(6)), "i"(MQ_LINE(7)), "i"(MQ_LINE(8)),
+                   "i"(MQ_LINE(9)));
+#undef MQ_LINE
+    asm volatile("" ::"s"(d0), "s"(d1), "s"(d2), "s"(d3), "s"(d4), "s"(d5), "s"(d6), "s"(d7),
+                 "s"(d8), "s"(d9));
+}
+
 } // namespace mq

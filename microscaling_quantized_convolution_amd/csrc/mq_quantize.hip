@@ -429,6 +429,7 @@ __device__ __forceinline__ void cbf_body(const QuantArgs &a, uint32_t *red, int 
 template <int FMT, bool SR, bool FULL, bool OIHW = false>
 __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a)
 {
+    warm_kernel_args<QuantArgs>();
     __shared__ uint32_t red[4];
     cbf_body<FMT, SR, FULL, OIHW>(a, red, (int)blockIdx.x, (int)gridDim.x);
 }
@@ -587,6 +588,7 @@ __device__ __forceinline__ void nchw_body(const QuantNchwArgs &a, uint32_t *red,
 template <int FMT, bool SR, int NQ, int PX>
 __global__ void __launch_bounds__(256) quantize_nchw_kernel(QuantNchwArgs a)
 {
+    warm_kernel_args<QuantNchwArgs>();
     __shared__ uint32_t red[4];
     nchw_body<FMT, SR, NQ, PX>(a, red, (int)blockIdx.x);
 }
@@ -647,6 +649,7 @@ template <int NJ> struct QuantBatchArgs {
 template <int NJ>
 __global__ void __launch_bounds__(kAmaxThreads) amax_batch_kernel(QuantBatchArgs<NJ> a)
 {
+    warm_kernel_args<QuantBatchArgs<NJ>>();
     __shared__ uint32_t red[kAmaxThreads / 64];
     const QuantJob &jb = a.job[blockIdx.y];
     const int b = (int)blockIdx.x;
@@ -659,6 +662,7 @@ __global__ void __launch_bounds__(kAmaxThreads) amax_batch_kernel(QuantBatchArgs
 template <int FMT, int NJ>
 __global__ void __launch_bounds__(256) quantize_batch_kernel(QuantBatchArgs<NJ> a)
 {
+    warm_kernel_args<QuantBatchArgs<NJ>>();
     __shared__ uint32_t red[4];
     const QuantJob &jb = a.job[blockIdx.y];
     const int lb = (int)blockIdx.x;
