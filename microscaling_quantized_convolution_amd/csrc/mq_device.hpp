@@ -120,12 +120,14 @@ struct Philox4 {
 __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
                                                  uint32_t c3, uint32_t k0, uint32_t k1)
 {
-    // each 32 x 32 -> 64-bit product is one v_mad_u64_u32 (high and low halves together)
+    // each 32 x 32 -> 64-bit product is one v_mad_u64_u32 (high and low halves together), and
+    // each three-way exclusive or one v_bitop3_b32 (truth table 0x96)
 #pragma unroll
     for (int i = 0; i < 10; ++i) {
         const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
         const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+        const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
         c0 = n0;
         c1 = (uint32_t)p1;
         c2 = n2;
