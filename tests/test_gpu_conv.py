@@ -138,8 +138,14 @@ def test_conv_one_hot_weight_reads_im2col_column():
         assert (y[:, :, others, :] == 0).all()
 
 
-@pytest.mark.parametrize("layer", SMALL + [workloads.config2()[0], workloads.config3()[0]],
-                         ids=lambda l: l.name)
+# full-size layers: the split sum on the CUs the input gradient leaves idle (c2), as its own
+# kernel ahead of the input gradient (c3: too many passes), after a persistent input gradient
+# that fills the chip (c5 layer 1), and NVFP6 at stride 2 with four parity classes (c4 layer 2)
+BACKWARD_FULL = [workloads.config2()[0], workloads.config3()[0], workloads.config5()[0],
+                 workloads.config4()[1]]
+
+
+@pytest.mark.parametrize("layer", SMALL + BACKWARD_FULL, ids=lambda l: l.name)
 def test_conv_backward_equals_separate_calls(layer):
     """mq_conv_backward (the weight gradient's split sum riding in the input-gradient launch)
     gives G_W and G_X bit for bit equal to mq_conv_wgrad and mq_conv_dgrad."""
