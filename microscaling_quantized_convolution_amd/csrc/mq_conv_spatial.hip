@@ -143,7 +143,7 @@ conv_spatial_kernel(SpatialArgs a)
     }
     // The arguments the producer needs before its first load, read here, together: left to
     // the compiler, each was loaded next to its first use, and the chain of dependent
-    // argument reads delayed the first load by about a microsecond.
+    // argument reads delayed the first load by about 0.2 us more.
     asm volatile("" ::"s"(step_p.nb), "s"(step_p.tj), "s"(step_p.ti), "s"(step_p.mb),
                  "s"(first.nb), "s"(first.tj), "s"(first.ti), "s"(first.mb), "s"(nmine));
     asm volatile("" ::"s"(cl.r0), "s"(cl.c0), "s"(cl.Ah), "s"(cl.Bh), "s"(cl.Aw), "s"(cl.Bw),
