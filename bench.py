@@ -68,9 +68,10 @@ def parse():
     ap.add_argument("--roofline-op", default=None,
                     help="op the roofline covers (default: the one with the longest per-op time)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--parts", action="store_true",
-                    help="also time conv_wgrad and conv_dgrad as calls of their own in per_op "
-                         "(not part of the step)")
+    ap.add_argument("--no-parts", action="store_true",
+                    help="leave out of per_op the timing of conv_wgrad and conv_dgrad as calls of "
+                         "their own (they are not part of the step; profiling runs leave them out "
+                         "so that every kernel in the trace belongs to one op)")
     ap.add_argument("--cpu-sample-n", type=int, default=32,
                     help="batch elements of the layer the CPU oracle runs on")
     ap.add_argument("--calib-copy", action="store_true",
@@ -192,10 +193,10 @@ def main():
             st.run(s)
     torch.cuda.synchronize()
 
-    # ---- per-op breakdown: each op alone, `op_reps` launches back to back (the step's ops; with
-    # --parts also the two gradients as calls of their own, for comparison) ----
+    # ---- per-op breakdown: each op alone, `op_reps` launches back to back (the step's ops, and
+    # unless --no-parts the two gradients as calls of their own: the per-GEMM rates) ----
     per_op = {}
-    for name, f in list(ops.items()) + (list(st.parts.items()) if args.parts else []):
+    for name, f in list(ops.items()) + ([] if args.no_parts else list(st.parts.items())):
         with torch.cuda.stream(stream):
             gr = capture([lambda r=r: f(r) for r in range(args.op_reps)])
             gr.replay()
