@@ -57,10 +57,10 @@ OP_KERNELS = {
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--op-reps", type=int, default=20, help="launches per op for the breakdown")
-    ap.add_argument("--event-every", type=int, default=4,
+    ap.add_argument("--event-every", type=int, default=8,
                     help="bracket the dominant op with HIP events in every n-th timed step")
     ap.add_argument("--eager", action="store_true",
                     help="time plain launches (the default; kept for the profiling commands)")
