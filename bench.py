@@ -1,23 +1,33 @@
 #!/usr/bin/env python3
 """Benchmark of the quantize-once convolution hot path on one MI355X.
 
-One step = one pass of the whole hot path over one batch of synthetic input, for the ResNet-style
-3x3 layer (N=32, Cin=Cout=64, 56x56, stride 1, pad 1, NVFP4): quantize X from NCHW and W from
-OIHW into their squares together, as the forward pass does (round-to-nearest; one batched call:
-an amax launch and a quantizing launch over both), quantize G_Y (stochastic, a new seed every
-step), then the forward GEMM and the two gradient GEMMs (weight and input gradient in one call,
-mq_conv_backward). Inputs are resident in HBM before the timed region starts.
+One step = one pass of the whole hot path over one batch of synthetic input for every layer of a
+workload. The default workload is the ResNet-18 convolution body (19 convolutions, N = 128,
+224x224 input, NVFP4; the stem convolution and the classifier stay fp32 and are not part of the
+path). For every layer, in order:
+  quantize_xw    X from NCHW and W from OIHW into their squares together (round to nearest; one
+                 batched call: an amax launch and a quantizing launch over both)
+  quantize_g     G_Y (stochastic rounding; seed 1 + layers*step + layer index)
+  conv_fwd       Y = W.X'
+  conv_backward  G_W = G_Y.X'^T and G_X = W^T.G_Y in one call
+Every layer has its own buffers and all inputs are resident in HBM before the timed region
+starts. G_Y arrives channel-batch-first (it is the next layer's input-gradient output).
 
 The timed steps call the C ABI back to back on one stream (arguments marshalled once, so the
-GPU, not the host, sets the pace), with HIP events on that stream around the op that takes the
-longest (`roofline`) in every `--event-every`-th step. `--graph` replays one HIP graph per step instead (split
-around that op so the events stay outside the graphs). `per_op` times each op alone as a graph
-of back-to-back launches. `cpu_baseline` times the CPU oracle on a bounded sample (rank 0, N=1).
+GPU, not the host, sets the pace). HIP events on that stream bracket every launch of the step's
+dominant op (the op and layer shape with the most time per step) in every `--event-every`-th
+step: `roofline` is that op's algorithmic work per launch over its mean bracketed duration.
+`per_layer` times each op of each distinct layer shape alone (a HIP graph of back-to-back
+launches), also the two gradients as calls of their own. `quantize_cold` times the largest
+layer's quantizations with the MALL flushed before each launch. `cpu_baseline` times the CPU
+oracle on a bounded sample of the first layer.
 
-`roofline.traffic` is the HBM traffic of that op per launch from rocprofv3 FETCH_SIZE and
-WRITE_SIZE counters (profiles/c2_pmc_traffic.txt), scaled by what the same counters read for a
-plain copy of known size; it is null when the kernel sources differ from the ones counted.
-`--summarize-pmc FETCH_DB WRITE_DB` writes that file's body from two rocprofv3 --pmc databases.
+`roofline.traffic` is the HBM traffic of the dominant op per launch from rocprofv3 FETCH_SIZE and
+WRITE_SIZE counters (profiles/<workload>_<layer>_pmc_traffic.txt), scaled by what the same
+counters read for a plain copy of known size; null when the kernel sources differ from the ones
+counted. `--summarize-pmc FETCH_DB WRITE_DB` writes that file's body from two rocprofv3 --pmc
+databases; `--summarize-trace DB` and `--summarize-mfma DB` turn a kernel-trace database and an
+MFMA-counter database into the summaries kept under profiles/.
 
 Prints one JSON line.
 """
@@ -36,59 +46,74 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = 2516.6    # MI355X dense fp16/bf16 MFMA, TFLOP/s (256 CU x 2.4 GHz x 4096)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "c2_pmc_traffic.txt")
 CALIB_ELEMS = 1 << 26        # plain copy for counter calibration: 256 MiB read + 256 MiB written
+FLUSH_BYTES = 512 << 20      # written before each cold launch (the MALL holds 256 MB)
+METRIC = "quant GB/s (% HBM peak) + conv fwd/wgrad/dgrad TFLOP/s (% bf16 MFMA) per layer"
 
 # which kernels make up each op (rocprofv3 kernel names start with these)
 OP_KERNELS = {
     "quantize_xw": ["mq::amax_batch_kernel", "void mq::quantize_batch_kernel"],
     "quantize_x": ["mq::amax_kernel", "void mq::quantize_nchw_kernel"],
-    "quantize_w": ["void mq::quantize_weight_small_kernel", "mq::amax_kernel",
-                   "void mq::quantize_kernel"],
     "quantize_g": ["mq::amax_kernel", "void mq::quantize_kernel"],
-    "conv_fwd": ["void mq::conv_spatial_kernel<4, false"],
+    "conv_fwd": ["void mq::conv_spatial_kernel<4, false", "void mq::conv_spatial_kernel<6, false",
+                 "void mq::conv_gemm_kernel"],
     "conv_backward": ["void mq::conv_wgrad_kernel", "void mq::conv_spatial_kernel<4, true",
-                      "mq::wgrad_sum_kernel"],
-    "conv_wgrad": ["void mq::conv_wgrad_kernel", "mq::wgrad_sum_kernel"],
-    "conv_dgrad": ["void mq::conv_spatial_kernel<4, true"],
+                      "void mq::conv_spatial_kernel<6, true", "mq::wgrad_sum_kernel",
+                      "void mq::conv_gemm_kernel", "mq::wgrad_reduce_kernel"],
+    "conv_wgrad": ["void mq::conv_wgrad_kernel", "mq::wgrad_sum_kernel",
+                   "void mq::conv_gemm_kernel", "mq::wgrad_reduce_kernel"],
+    "conv_dgrad": ["void mq::conv_spatial_kernel<4, true", "void mq::conv_spatial_kernel<6, true",
+                   "void mq::conv_gemm_kernel"],
 }
+STEP_OPS = ["quantize_xw", "quantize_g", "conv_fwd", "conv_backward"]
+INFERENCE_OPS = ["quantize_x", "conv_fwd"]
+PARTS = ["conv_wgrad", "conv_dgrad"]
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--op-reps", type=int, default=20, help="launches per op for the breakdown")
-    ap.add_argument("--event-every", type=int, default=8,
-                    help="bracket the dominant op with HIP events in every n-th timed step")
-    ap.add_argument("--eager", action="store_true",
-                    help="time plain launches (the default; kept for the profiling commands)")
-    ap.add_argument("--graph", action="store_true", help="time HIP graph replays of the steps")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5"],
+                    help="c5: ResNet-18 body at N=128 (default); c2: ResNet 3x3 layer at N=32; "
+                         "c3: strided 3x3 at N=64; c4: YOLO-like NVFP6 stack at N=16; c1: tiny")
+    ap.add_argument("--layers", default=None,
+                    help="comma-separated layer names: time only these layers of the workload "
+                         "(per-shape profiles)")
+    ap.add_argument("--op-reps", type=int, default=10, help="launches per op for the breakdown")
+    ap.add_argument("--event-every", type=int, default=2,
+                    help="bracket the dominant op's launches with HIP events in every n-th step")
     ap.add_argument("--roofline-op", default=None,
-                    help="op the roofline covers (default: the one with the longest per-op time)")
+                    help="op the roofline covers (default: the op with the most time per step)")
+    ap.add_argument("--no-per-op", action="store_true",
+                    help="skip the per-op breakdown (profiled runs: every kernel in the trace "
+                         "then belongs to a step)")
+    ap.add_argument("--cold-reps", type=int, default=5,
+                    help="cold-MALL launches of each quantization of the largest layer (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-parts", action="store_true",
-                    help="leave out of per_op the timing of conv_wgrad and conv_dgrad as calls of "
-                         "their own (they are not part of the step; profiling runs leave them out "
-                         "so that every kernel in the trace belongs to one op)")
-    ap.add_argument("--cpu-sample-n", type=int, default=32,
-                    help="batch elements of the layer the CPU oracle runs on")
+    ap.add_argument("--cpu-sample-n", type=int, default=0,
+                    help="batch elements of the first layer the CPU oracle runs on (0: the "
+                         "workload's default sample)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
-                    help="print the traffic summary from two rocprofv3 --pmc databases")
-    ap.add_argument("--config", default=None, choices=["c1", "c2", "c3", "c4", "c5"],
-                    help="time the hot path of every layer of a workload (one step = every "
-                         "layer once) instead of the single 3x3 layer")
+    ap.add_argument("--inference", action="store_true",
+                    help="the inference path only: quantize X from NCHW and conv fwd per layer "
+                         "(weights quantized once before timing)")
     ap.add_argument("--network", default=None, choices=["resnet18"],
                     help="time a full training step of ResNet-18 (19 body convolutions on the "
                          "library, the rest in PyTorch fp32)")
     ap.add_argument("--batch", type=int, default=128, help="batch size of --network")
-    ap.add_argument("--inference", action="store_true",
-                    help="with --config: the inference path only (quantize X from NCHW, "
-                         "conv fwd; the weights are quantized once before timing)")
-    return ap.parse_args()
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="print the traffic summary from two rocprofv3 --pmc databases")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DB",
+                    help="print a kernel-trace summary (per kernel and launch shape) from a "
+                         "rocprofv3 --kernel-trace database")
+    ap.add_argument("--summarize-mfma", metavar="DB",
+                    help="print MFMA busy and MFMA op counts per kernel from a rocprofv3 --pmc "
+                         "database of SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_F16, "
+                         "SQ_BUSY_CU_CYCLES, GRBM_GUI_ACTIVE")
+    return ap.parse_args(argv)
 
 
 def kernel_source_hash() -> str:
@@ -102,13 +127,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(op: str):
-    """HBM bytes per launch of `op` from the committed counter summary, or None if there is none
+def traffic_file(workload: str, layer: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{workload}_{layer.replace('.', '_')}_pmc_traffic.txt")
+
+
+def read_traffic(path: str, op: str):
+    """HBM bytes per launch of `op` from a committed counter summary, or None if there is none
     or it was taken on other kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
     kv = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith((" ", "#", "|")):
                 k, v = line.split(":", 1)
@@ -119,233 +148,47 @@ def read_traffic(op: str):
     return None if v is None else int(float(v))
 
 
-def main():
-    args = parse()
-    if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc)
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the hot path here is single-device; "
-              "run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-    if args.network:
-        run_network(args)
-        return
-    if args.config:
-        run_config(args)
-        return
+# ---- the work of one layer's ops (algorithmic, as the method defines it) -----------------------
 
-    import torch
+def _squares(o0, o1, r, s):
+    return o0 * o1 * ((r + 3) // 4) * ((s + 3) // 4)
 
-    import microscaling_quantized_convolution_amd as mq
-    from microscaling_quantized_convolution_amd.step import LayerStep
-    import workloads
 
-    layer = workloads.config2()[0]
-    N, Ci, H, W, Co, Kh, Kw = (layer.N, layer.Cin, layer.H, layer.W, layer.Cout, layer.Kh,
-                               layer.Kw)
-    Ho, Wo = layer.Ho, layer.Wo
-    fmt = layer.fmt
-    dev = "cuda:0"
-    torch.cuda.set_device(0)
-
-    x, w, g = workloads.make_tensors(layer)
-    gc = torch.empty(g.size, dtype=torch.float32, device=dev)
-    # G_Y arrives channel-batch-first (it is the next layer's input-gradient output)
-    mq.mq_relayout_cbf(torch.from_numpy(g).to(dev), gc, N, Co, Ho, Wo, 0)
-    st = LayerStep(layer.conv_tuple(), fmt, torch.from_numpy(x).to(dev),
-                   torch.from_numpy(w).to(dev), gc, sr_seed_base=layer.sr_seed)
-    ops = st.ops
-    stream = torch.cuda.Stream()
-
-    flops = layer.gemm_flops()
-    sq = lambda o0, o1, r, s_: o0 * o1 * ((r + 3) // 4) * ((s_ + 3) // 4)
-    qbytes = lambda shape: sq(*shape) * (8 if fmt == 4 else 12) + sq(*shape)  # codes + scales
-    nx, nw, ng = x.size, w.size, g.size
-    qx_b, qw_b, qg_b = qbytes((H, W, Ci, N)), qbytes((Kh, Kw, Co, Ci)), qbytes((Ho, Wo, Co, N))
-    # algorithmic bytes: every quantization = amax read + quantize read + codes/scales
-    alg = {
-        "quantize_xw": ("hbm", 8 * nx + qx_b + 8 * nw + qw_b),
-        "quantize_g": ("hbm", 8 * ng + qg_b),
-        "conv_fwd": ("gemm", flops), "conv_wgrad": ("gemm", flops), "conv_dgrad": ("gemm", flops),
-        "conv_backward": ("gemm", 2 * flops),
+def layer_work(l):
+    """Per op of one layer: (kind, algorithmic amount, algorithmic bytes). kind 'hbm' amounts
+    are bytes; 'gemm' amounts are flops. Quantization reads its fp32 tensor twice (the amax pass
+    and the quantizing pass) and writes codes and scales; a GEMM reads both quantized operands
+    once and writes its fp32 result once."""
+    cb = 8 if l.fmt == 4 else 12
+    q = lambda *shape: _squares(*shape) * (cb + 1)
+    nx, nw, ng = l.N * l.Cin * l.H * l.W, l.Cout * l.Cin * l.Kh * l.Kw, l.N * l.Cout * l.Ho * l.Wo
+    qx, qw, qg = q(l.H, l.W, l.Cin, l.N), q(l.Kh, l.Kw, l.Cout, l.Cin), q(l.Ho, l.Wo, l.Cout, l.N)
+    F = l.gemm_flops()
+    fwd_b, wg_b, dg_b = qx + qw + 4 * ng, qg + qx + 4 * nw, qw + qg + 4 * nx
+    return {
+        "quantize_xw": ("hbm", 8 * (nx + nw) + qx + qw, 8 * (nx + nw) + qx + qw),
+        "quantize_x": ("hbm", 8 * nx + qx, 8 * nx + qx),
+        "quantize_g": ("hbm", 8 * ng + qg, 8 * ng + qg),
+        "conv_fwd": ("gemm", F, fwd_b),
+        "conv_wgrad": ("gemm", F, wg_b),
+        "conv_dgrad": ("gemm", F, dg_b),
+        "conv_backward": ("gemm", 2 * F, wg_b + dg_b),
     }
-    # conv: quantized operands read once + fp32 result written once
-    conv_bytes = {"conv_fwd": qx_b + qw_b + 4 * Ho * Wo * Co * N,
-                  "conv_wgrad": qg_b + qx_b + 4 * Kh * Kw * Co * Ci,
-                  "conv_dgrad": qw_b + qg_b + 4 * H * W * Ci * N}
-    conv_bytes["conv_backward"] = conv_bytes["conv_wgrad"] + conv_bytes["conv_dgrad"]
+
+
+def rate(kind, amount, nbytes, ms):
+    """Rates and roofline fraction of one op launch taking `ms`."""
     ridge = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-
-    def capture(fns):
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr, stream=stream):
-            for f in fns:
-                f()
-        return gr
-
-    def ev():
-        return torch.cuda.Event(enable_timing=True)
-
-    # ---- warm-up (eager) ----
-    with torch.cuda.stream(stream):
-        for s in range(max(args.warmup, 1)):
-            st.run(s)
-    torch.cuda.synchronize()
-
-    # ---- per-op breakdown: each op alone, `op_reps` launches back to back (the step's ops, and
-    # unless --no-parts the two gradients as calls of their own: the per-GEMM rates) ----
-    per_op = {}
-    for name, f in list(ops.items()) + ([] if args.no_parts else list(st.parts.items())):
-        with torch.cuda.stream(stream):
-            gr = capture([lambda r=r: f(r) for r in range(args.op_reps)])
-            gr.replay()
-            e0, e1 = ev(), ev()
-            e0.record(stream)
-            gr.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / args.op_reps
-        kind, amount = alg[name]
-        if kind == "hbm":
-            gbs = amount / (ms * 1e-3) / 1e9
-            per_op[name] = {"ms": round(ms, 5), "GB_s": round(gbs, 1),
-                            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "alg_bytes": amount}
-        else:
-            tf = amount / (ms * 1e-3) / 1e12
-            gbs = conv_bytes[name] / (ms * 1e-3) / 1e9
-            per_op[name] = {"ms": round(ms, 5), "TFLOP_s": round(tf, 1),
-                            "frac_mfma": round(tf / MFMA_PEAK_TFLOPS, 4),
-                            "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                            "alg_flops": amount, "alg_bytes": conv_bytes[name],
-                            "bound": "mfma" if amount / conv_bytes[name] >= ridge else "hbm"}
-    dominant = args.roofline_op or max(ops, key=lambda k: per_op[k]["ms"])
-    if dominant not in ops:
-        sys.exit(f"--roofline-op {dominant}: not an op of the step ({', '.join(ops)})")
-    names = list(ops)
-    di = names.index(dominant)
-
-    # ---- timed steps: pre-ops, the dominant op between two events, post-ops ----
-    total = args.warmup + args.steps
-    calls = st.direct_calls(stream)
-    if not args.graph:
-        plan = None
-    else:
-        plan = []
-        for s in range(total):
-            fs = [lambda f=ops[n], s=s: f(s) for n in names]
-            plan.append((capture(fs[:di]) if di > 0 else None, capture([fs[di]]),
-                         capture(fs[di + 1:]) if di + 1 < len(fs) else None))
-        torch.cuda.synchronize()
-
-    def run_step(s, e_in=None, e_out=None):
-        if plan is None:
-            for n in names[:di]:
-                calls[n](s)
-            if e_in is not None:
-                e_in.record(stream)
-            calls[dominant](s)
-            if e_out is not None:
-                e_out.record(stream)
-            for n in names[di + 1:]:
-                calls[n](s)
-        else:
-            pre, dom, post = plan[s]
-            if pre is not None:
-                pre.replay()
-            if e_in is not None:
-                e_in.record(stream)
-            dom.replay()
-            if e_out is not None:
-                e_out.record(stream)
-            if post is not None:
-                post.replay()
-
-    with torch.cuda.stream(stream):
-        for s in range(args.warmup):
-            run_step(s)
-    torch.cuda.synchronize()
-    # events around the dominant op in every args.event_every-th timed step: each pair of event
-    # records adds about 5 us to the step it sits in (measured), so they sample the op's launches
-    # instead of instrumenting all of them
-    dom_ev = [(ev(), ev()) if s_ % args.event_every == 0 else (None, None)
-              for s_ in range(args.steps)]
-    t0, t1 = ev(), ev()
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        t0.record(stream)
-        for s in range(args.steps):
-            run_step(args.warmup + s, *dom_ev[s])
-        t1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = t0.elapsed_time(t1) / args.steps
-    sampled = [(a, b) for a, b in dom_ev if a is not None]
-    dom_ms = sum(a.elapsed_time(b) for a, b in sampled) / len(sampled)
-
-    kind, amount = alg[dominant]
+    gbs = nbytes / (ms * 1e-3) / 1e9
     if kind == "hbm":
-        ach = amount / (dom_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    elif amount / conv_bytes[dominant] >= ridge:
-        ach = amount / (dom_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s"}
-    else:
-        ach = conv_bytes[dominant] / (dom_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = read_traffic(dominant)
-    roof["op"] = dominant
-    roof["kernels"] = OP_KERNELS[dominant]
-    roof["ms_per_launch"] = round(dom_ms, 5)
-    roof["launches_timed"] = len(sampled)
-    roof["alg_per_launch"] = amount if roof["bound"] != "hbm" or kind == "hbm" \
-        else conv_bytes[dominant]
-
-    result = {
-        "metric": "quant GB/s (% HBM peak) + conv fwd/wgrad/dgrad TFLOP/s (% bf16 MFMA) per layer",
-        "value": round(3 * flops / (ms_step * 1e-3) / 1e12, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "wall_s_timed": round(wall, 4),
-        "timing": "HIP graph replay per step" if args.graph else "back-to-back launches",
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp16",
-        "data": "synthetic (seeded numpy PCG64; X=ReLU(N(0,1)), W Kaiming-normal, G_Y~N(0,1e-3))",
-        "config": {"workload": "resnet-3x3-s1p1 N=32 Cin=Cout=64 56x56 NVFP4: quantize X "
-                               "(from NCHW) and W (from OIHW) in one batched call (RNE), G_Y "
-                               "(SR), conv fwd, conv backward (wgrad + dgrad in one call)",
-                   "N": N, "Cin": Ci, "Cout": Co, "H": H, "W": W, "K": Kh, "stride": 1, "pad": 1,
-                   "format": "NVFP4 (E2M1 codes, E4M3 4x4-square scales, fp32 tensor scale)",
-                   "mfma": "fp16 operands decoded exactly, fp32 accumulate"},
-        "per_op": per_op,
-        "roofline": roof,
-    }
-
-    if args.calib_copy:
-        import torch as _t
-        src = _t.full((CALIB_ELEMS,), 1.0, dtype=_t.float32, device=dev)
-        dst = _t.empty_like(src)
-        _t.cuda.synchronize()
-        e0, e1 = ev(), ev()
-        e0.record()
-        _t.neg(src, out=dst)
-        e1.record()
-        _t.cuda.synchronize()
-        result["calib_copy"] = {"bytes_read": CALIB_ELEMS * 4, "bytes_written": CALIB_ELEMS * 4,
-                                "ms": round(e0.elapsed_time(e1), 4)}
-
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(layer, args.cpu_sample_n)
-
-    print(json.dumps(result), flush=True)
+        return {"ms": round(ms, 5), "GB_s": round(gbs, 1), "bound": "hbm",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "alg_bytes": int(nbytes)}
+    tf = amount / (ms * 1e-3) / 1e12
+    mfma = amount / nbytes >= ridge
+    return {"ms": round(ms, 5), "TFLOP_s": round(tf, 1), "GB_s": round(gbs, 1),
+            "bound": "mfma" if mfma else "hbm",
+            "frac": round(tf / MFMA_PEAK_TFLOPS if mfma else gbs / HBM_PEAK_GBS, 4),
+            "alg_flops": int(amount), "alg_bytes": int(nbytes)}
 
 
 def _time_graph(fns, reps: int, stream) -> float:
@@ -366,95 +209,259 @@ def _time_graph(fns, reps: int, stream) -> float:
     return e0.elapsed_time(e1) / reps
 
 
-def run_config(args):
-    """Every layer of a workload through the hot path: one step = each layer's three
-    quantizations and three GEMMs once (layers that repeat a shape are timed once and counted
-    with their multiplicity). Per layer and op: time, rate and fraction of the bound."""
+def host_cpu():
+    """(model name, threads the oracle's OpenMP runs with)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    avail = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    threads = min(avail, int(omp)) if omp and omp.isdigit() and int(omp) > 0 else avail
+    return model, threads
+
+
+def main(argv=None):
+    args = parse(argv)
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the hot path here is single-device; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.network:
+        run_network(args)
+        return
+    run_workload(args)
+
+
+def run_workload(args):
     import collections
 
-    import numpy as np
     import torch
 
+    import microscaling_quantized_convolution_amd as mq
     from microscaling_quantized_convolution_amd.step import LayerStep
     import workloads
 
     torch.cuda.set_device(0)
     dev = "cuda:0"
-    layers = workloads.CONFIGS[args.config]()
-    groups = collections.OrderedDict()
-    for l in layers:
-        groups.setdefault(l.conv_tuple() + (l.fmt,), []).append(l)
+    all_layers = workloads.CONFIGS[args.workload]()
+    layers = all_layers
+    if args.layers:
+        want = args.layers.split(",")
+        layers = [l for l in all_layers if l.name in want]
+        if len(layers) != len(want):
+            sys.exit(f"--layers: unknown names in {want} (have {[l.name for l in all_layers]})")
+    nl = len(all_layers)
     stream = torch.cuda.Stream()
-    ridge = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    per_layer, step_ms, flops_total = [], 0.0, 0
-    for key, ls in groups.items():
-        l = ls[0]
+    ops = INFERENCE_OPS if args.inference else STEP_OPS
+
+    # ---- every layer's inputs resident on the device, its own buffers ----
+    steps, calls = [], []
+    for l in layers:
         x, w, g = workloads.make_tensors(l)
         gc = torch.empty(g.size, dtype=torch.float32, device=dev)
-        import microscaling_quantized_convolution_amd as mq
         mq.mq_relayout_cbf(torch.from_numpy(g).to(dev), gc, l.N, l.Cout, l.Ho, l.Wo, 0)
         st = LayerStep(l.conv_tuple(), l.fmt, torch.from_numpy(x).to(dev),
-                       torch.from_numpy(w).to(dev), gc, sr_seed_base=l.sr_seed)
+                       torch.from_numpy(w).to(dev), gc, sr_seed_base=l.sr_seed, seed_stride=nl)
         del x, w, g
-        calls = st.direct_calls(stream)
-        for s_ in range(max(args.warmup, 1)):
-            for f in calls.values():
-                f(s_)
-        torch.cuda.synchronize()
-        if args.inference:  # W stays quantized from the warm-up: activations only
-            calls = st.inference_calls(stream)
-        eb = 0.5625 if l.fmt == 4 else 0.8125
-        nx, nw, ng = l.N * l.Cin * l.H * l.W, l.Cout * l.Cin * l.Kh * l.Kw, l.N * l.Cout * l.Ho * l.Wo
-        fl = l.gemm_flops()
-        byt = {"quantize_x": 8 * nx + eb * nx, "quantize_xw": 8 * (nx + nw) + eb * (nx + nw),
-               "quantize_w": 4 * nw + eb * nw, "quantize_g": 8 * ng + eb * ng,
-               "conv_fwd": eb * (nx + nw) + 4 * ng, "conv_wgrad": eb * (nx + ng) + 4 * nw,
-               "conv_dgrad": eb * (nw + ng) + 4 * nx}
-        byt["conv_backward"] = byt["conv_wgrad"] + byt["conv_dgrad"]
-        ops = {}
-        for name, f in calls.items():
-            ms = _time_graph([f], args.op_reps, stream)
-            gbs = byt[name] / (ms * 1e-3) / 1e9
-            if name.startswith("conv"):
-                fo = 2 * fl if name == "conv_backward" else fl
-                tf = fo / (ms * 1e-3) / 1e12
-                mfma = fo / byt[name] >= ridge
-                ops[name] = {"ms": round(ms, 5), "TFLOP_s": round(tf, 1), "GB_s": round(gbs, 1),
-                             "bound": "mfma" if mfma else "hbm",
-                             "frac": round(tf / MFMA_PEAK_TFLOPS if mfma else
-                                           gbs / HBM_PEAK_GBS, 4)}
-            else:
-                ops[name] = {"ms": round(ms, 5), "GB_s": round(gbs, 1),
-                             "frac": round(gbs / HBM_PEAK_GBS, 4)}
-        fns = list(calls.values())
-        ms_layer = _time_graph(fns, max(2, args.op_reps // 4), stream)
-        step_ms += ms_layer * len(ls)
-        flops_total += (1 if args.inference else 3) * fl * len(ls)
-        per_layer.append({"layers": [x_.name for x_ in ls], "shape": {
-            "N": l.N, "Cin": l.Cin, "Cout": l.Cout, "H": l.H, "W": l.W, "K": l.Kh,
-            "stride": l.stride, "pad": l.pad, "format": f"NVFP{l.fmt}"},
-            "ms_layer_step": round(ms_layer, 5), "per_op": ops})
-        del st, calls, gc
-        torch.cuda.empty_cache()
+        steps.append(st)
+        c = st.direct_calls(stream)
+        if args.inference:
+            for s_ in range(2):  # W quantized once, before timing
+                c["quantize_xw"](s_)
+            c.update(st.inference_calls(stream))
+        calls.append(c)
+    torch.cuda.synchronize()
+
+    groups = collections.OrderedDict()  # distinct shape -> indices into layers
+    for i, l in enumerate(layers):
+        groups.setdefault(l.conv_tuple() + (l.fmt,), []).append(i)
+
+    def run_step(s, brackets=None):
+        for i in range(len(layers)):
+            for op in ops:
+                if brackets is not None and (i, op) in brackets:
+                    e0, e1 = brackets[i, op]
+                    e0.record(stream)
+                    calls[i][op](s)
+                    e1.record(stream)
+                else:
+                    calls[i][op](s)
+
+    with torch.cuda.stream(stream):
+        for s in range(max(args.warmup, 1)):
+            run_step(s)
+    torch.cuda.synchronize()
+
+    # ---- per distinct layer shape: each op alone, `op_reps` launches back to back ----
+    per_layer, op_ms = [], {}
+    if not args.no_per_op:
+        for key, idx in groups.items():
+            l, c = layers[idx[0]], calls[idx[0]]
+            work = layer_work(l)
+            entry = {}
+            for op in ops + ([] if args.inference else PARTS):
+                ms = _time_graph([c[op]], args.op_reps, stream)
+                kind, amount, nbytes = work[op]
+                entry[op] = rate(kind, amount, nbytes, ms)
+                op_ms[idx[0], op] = ms
+            layer_ms = _time_graph([c[op] for op in ops], max(2, args.op_reps // 2), stream)
+            per_layer.append({
+                "layers": [layers[i].name for i in idx],
+                "shape": {"N": l.N, "Cin": l.Cin, "Cout": l.Cout, "H": l.H, "W": l.W,
+                          "K": [l.Kh, l.Kw], "stride": [l.stride, l.sw], "pad": [l.pad, l.pw],
+                          "format": f"NVFP{l.fmt}"},
+                "ms_layer": round(layer_ms, 5), "per_op": entry})
+
+    # ---- the dominant op: the (shape, op) with the most time per step ----
+    if args.roofline_op and args.roofline_op not in ops:
+        sys.exit(f"--roofline-op {args.roofline_op}: not an op of the step ({', '.join(ops)})")
+    if op_ms:
+        cand = [(op_ms[idx[0], op] * len(idx), key, op) for key, idx in groups.items()
+                for op in ops if args.roofline_op in (None, op)]
+        _, dom_key, dom_op = max(cand)
+    else:
+        dom_key = next(iter(groups))
+        dom_op = args.roofline_op or ("conv_fwd" if args.inference else "conv_backward")
+    dom_idx = groups[dom_key]
+
+    # ---- timed steps ----
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    brackets = [({(i, dom_op): (ev(), ev()) for i in dom_idx}
+                 if s_ % args.event_every == 0 else None) for s_ in range(args.steps)]
+    t0, t1 = ev(), ev()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        t0.record(stream)
+        for s in range(args.steps):
+            run_step(args.warmup + s, brackets[s])
+        t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / args.steps
+    sampled = [p for b in brackets if b is not None for p in b.values()]
+    dom_ms = sum(a.elapsed_time(b) for a, b in sampled) / len(sampled)
+
+    dl = layers[dom_idx[0]]
+    kind, amount, nbytes = layer_work(dl)[dom_op]
+    roof = rate(kind, amount, nbytes, dom_ms)
+    if roof["bound"] == "hbm":
+        roof = {"bound": "hbm", "achieved": roof["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        alg = nbytes
+    else:
+        roof = {"bound": "mfma", "achieved": roof["TFLOP_s"], "peak": MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+        alg = amount
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = read_traffic(traffic_file(args.workload, dl.name), dom_op)
+    roof.update({"op": dom_op, "layers": [layers[i].name for i in dom_idx],
+                 "kernels": OP_KERNELS[dom_op], "ms_per_launch": round(dom_ms, 5),
+                 "launches_timed": len(sampled), "alg_per_launch": int(alg)})
+
+    flops = sum(l.gemm_flops() for l in layers) * (1 if args.inference else 3)
     result = {
-        "metric": "quant GB/s (% HBM peak) + conv fwd/wgrad/dgrad TFLOP/s (% bf16 MFMA) per layer",
-        "value": round(flops_total / (step_ms * 1e-3) / 1e12, 2),
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "ms_per_step": round(step_ms, 5),
-        "timing": "per layer: one HIP graph of back-to-back layer steps; the step is the sum "
-                  "over the workload's layers with their multiplicity",
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "wall_s_timed": round(wall, 4),
+        "timing": "back-to-back launches on one stream",
         "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
         "dtype": "fp16",
-        "data": "synthetic (seeded numpy PCG64, the workload's value distributions)",
-        "config": {"workload": (f"{args.config} inference: {len(layers)} layers, quantize X "
-                                f"(from NCHW), conv fwd each (weights quantized once)")
-                   if args.inference else
-                   (f"{args.config}: {len(layers)} layers, quantize X and W (one batched call), "
-                    f"G_Y, conv fwd and backward (wgrad + dgrad in one call) each")},
+        "data": "synthetic (seeded numpy PCG64: X=ReLU(N(0,1)) / SiLU / 0.5*t3, W Kaiming-normal, "
+                "G_Y~N(0,1e-3))",
+        "config": {"workload": workload_name(args, layers),
+                   "layers": len(layers), "gemm_flops_per_step": int(flops),
+                   "format": "NVFP4 (E2M1 codes, E4M3 4x4-square scales, fp32 tensor scale)"
+                   if layers[0].fmt == 4 else "NVFP6 (E2M3 codes, E4M3 4x4-square scales, fp32 "
+                                               "tensor scale)",
+                   "mfma": "fp16 operands decoded exactly, fp32 accumulate"},
+        "roofline": roof,
         "per_layer": per_layer,
     }
+
+    if args.cold_reps > 0 and not args.inference:
+        result["quantize_cold"] = quantize_cold(layers, calls, args.cold_reps, stream)
+
+    if args.calib_copy:
+        src = torch.full((CALIB_ELEMS,), 1.0, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        torch.neg(src, out=dst)
+        e1.record()
+        torch.cuda.synchronize()
+        result["calib_copy"] = {"bytes_read": CALIB_ELEMS * 4, "bytes_written": CALIB_ELEMS * 4,
+                                "ms": round(e0.elapsed_time(e1), 4)}
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(layers[0], args.cpu_sample_n)
+
     print(json.dumps(result), flush=True)
+
+
+def workload_name(args, layers):
+    names = {"c1": "tiny 3x3 conv N=2 16->16 8x8 (NVFP4)",
+             "c2": "ResNet 3x3 s1p1 conv N=32 64->64 56x56 (NVFP4)",
+             "c3": "strided 3x3 s2p1 conv N=64 128->256 28->14 (NVFP4)",
+             "c4": "YOLOv8n-like stack of 8 convs N=16, 160->20, 3 of 8 1x1 (NVFP6)",
+             "c5": "ResNet-18 conv body (19 convs) N=128 at 224x224 (NVFP4)"}
+    what = ("inference: quantize X (from NCHW), conv fwd per layer (W quantized once)"
+            if args.inference else "per layer: quantize X (NCHW) + W (OIHW) in one batched call "
+            "(RNE), G_Y (SR), conv fwd, conv backward (wgrad + dgrad in one call)")
+    sel = "" if not args.layers else f" [layers {','.join(l.name for l in layers)}]"
+    return f"{args.workload}: {names[args.workload]}{sel}; {what}"
+
+
+def quantize_cold(layers, calls, reps, stream):
+    """The largest layer's quantizations, each launch after writing FLUSH_BYTES of scratch (the
+    MALL and L2 then hold none of its inputs), against the same launches back to back (warm)."""
+    import torch
+    i = max(range(len(layers)), key=lambda k: layers[k].N * layers[k].Cin * layers[k].H * layers[k].W)
+    l = layers[i]
+    work = layer_work(l)
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    out = {"layer": l.name}
+    for op in ("quantize_xw", "quantize_g"):
+        cold = []
+        with torch.cuda.stream(stream):
+            for r in range(reps + 1):
+                scratch.fill_(float(r))
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                calls[i][op](r)
+                e1.record(stream)
+                cold.append((e0, e1))
+        torch.cuda.synchronize()
+        ms_cold = sum(a.elapsed_time(b) for a, b in cold[1:]) / reps
+        ms_warm = _time_graph([calls[i][op]], 10, stream)
+        kind, amount, nbytes = work[op]
+        out[op] = {"cold": rate(kind, amount, nbytes, ms_cold),
+                   "warm": rate(kind, amount, nbytes, ms_warm)}
+    return out
 
 
 def run_network(args):
@@ -514,20 +521,22 @@ def run_network(args):
 
 
 def cpu_baseline(layer, nsample: int):
-    """The CPU oracle, as it stands, on the first `nsample` batch elements of the same layer:
-    relayout, three quantizations, dequantization and the three explicit-im2col GEMMs in double.
-    Reported in the same unit as `value` (conv TFLOP/s of the sample's three GEMMs)."""
+    """The CPU oracle, as it stands, on the first `nsample` batch elements of a layer: relayout,
+    three quantizations, dequantization and the three explicit-im2col GEMMs in double, repeated
+    to about 10 s. Reported in the same unit as `value` (TFLOP/s of the sample's three GEMMs)."""
     import dataclasses
 
     import oracle
     import workloads
 
+    if nsample <= 0:
+        nsample = min(layer.N, 8)
+    nsample = min(nsample, layer.N)
     sub = dataclasses.replace(layer, N=nsample)
     x, w, g = workloads.make_tensors(layer)
     x, g = x[:nsample].copy(), g[:nsample].copy()
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    model, threads = host_cpu()
     p = sub.conv_tuple()
-    # repeat the pass until about 10 s of CPU work (at most 8 passes), report the mean
     secs = []
     while (not secs or sum(secs) < 10.0) and len(secs) < 8:
         t = time.perf_counter()
@@ -541,13 +550,16 @@ def cpu_baseline(layer, nsample: int):
         secs.append(time.perf_counter() - t)
     sec = sum(secs) / len(secs)
     tf = 3 * sub.gemm_flops() / sec / 1e12
-    return {"value": round(tf, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "seconds_per_pass": round(sec, 3), "passes": len(secs),
-            "sample": f"same layer with N={nsample} of {layer.N} batch elements: relayout, "
-                      f"3 quantizations, dequantization, explicit-im2col fwd/wgrad/dgrad in "
-                      f"double, repeated to about 10 s; flops of the sample's three GEMMs / "
-                      f"mean wall time per pass"}
+    return {"value": round(tf, 6), "unit": "TFLOP/s", "cores": threads, "cpu": model,
+            "kind": "oracle", "seconds_per_pass": round(sec, 3), "passes": len(secs),
+            "sample": f"layer {layer.name} ({layer.Cin}->{layer.Cout}, {layer.H}x{layer.W}, "
+                      f"{layer.Kh}x{layer.Kw}) with N={nsample} of {layer.N} batch elements: "
+                      f"relayout, 3 quantizations, dequantization, explicit-im2col "
+                      f"fwd/wgrad/dgrad in double, repeated to about 10 s; flops of the "
+                      f"sample's three GEMMs / mean wall time per pass"}
 
+
+# ---- profile summaries --------------------------------------------------------------------------
 
 def _short(name: str) -> str:
     """Kernel name without its parameter list."""
@@ -560,26 +572,31 @@ def _short(name: str) -> str:
     return name
 
 
-def _pmc_per_kernel(db: str, counter: str):
-    """Mean per dispatch of `counter` (summed over its instances) per kernel name."""
+def _pmc_per_kernel(db: str, counters):
+    """Mean per dispatch of each counter (summed over its instances) per kernel name."""
     import collections
     import sqlite3
     con = sqlite3.connect(db)
     cols = [r[1] for r in con.execute("pragma table_info(counters_collection)")]
     ki, ci, vi, di = (cols.index(c) for c in ("kernel_name", "counter_name", "value",
                                               "dispatch_id"))
-    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    per = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(float)))
     for row in con.execute("select * from counters_collection"):
-        if row[ci] == counter:
-            per[_short(row[ki])][row[di]] += row[vi]
-    return {k: (sum(d.values()) / len(d), len(d)) for k, d in per.items()}
+        if row[ci] in counters:
+            d = per[row[ci]][_short(row[ki])]
+            if row[ci] == "GRBM_GUI_ACTIVE":  # one chip-wide clock: the largest instance
+                d[row[di]] = max(d[row[di]], row[vi])
+            else:
+                d[row[di]] += row[vi]
+    return {c: {k: (sum(d.values()) / len(d), len(d)) for k, d in per[c].items()}
+            for c in counters}
 
 
 def summarize_pmc(fetch_db: str, write_db: str):
     """Traffic summary (key: value lines) from a FETCH_SIZE run and a WRITE_SIZE run of
-    `bench.py --eager --calib-copy`; the counters are KiB per dispatch."""
-    fetch = _pmc_per_kernel(fetch_db, "FETCH_SIZE")
-    write = _pmc_per_kernel(write_db, "WRITE_SIZE")
+    `bench.py --calib-copy` on one layer; the counters are KiB per dispatch."""
+    fetch = _pmc_per_kernel(fetch_db, ["FETCH_SIZE"])["FETCH_SIZE"]
+    write = _pmc_per_kernel(write_db, ["WRITE_SIZE"])["WRITE_SIZE"]
     copy = [k for k in fetch if "neg_kernel" in k]
     if not copy:
         raise SystemExit("no calibration copy kernel in the FETCH_SIZE database")
@@ -599,13 +616,63 @@ def summarize_pmc(fetch_db: str, write_db: str):
         b = fk * 1024 / f_cal + wk * 1024 / w_cal
         per_kernel[k] = b
         print(f"| {k[:90]} | {fetch[k][1]} | {fk:.1f} | {wk:.1f} | {b:.0f} |")
-    # per op (quantize_x/w/g share kernel names with different sizes, so only
-    # the convolutions, whose kernels are distinct, get a per-op figure)
+    # per op of the layer (the quantize ops share kernel names, so only the convolutions, whose
+    # kernels are distinct, get a per-op figure)
     for op in ("conv_fwd", "conv_backward", "conv_wgrad", "conv_dgrad"):
         tot = sum(b for k, b in per_kernel.items()
                   if any(k.replace("(anonymous namespace)::", "").startswith(p)
                          for p in OP_KERNELS[op]))
         print(f"traffic_bytes_per_launch.{op}: {tot:.0f}")
+
+
+def summarize_trace(db: str):
+    """Markdown table from a rocprofv3 --kernel-trace database: per kernel and launch shape (grid
+    and workgroup size, so the layer shapes of one kernel template stay apart), the dispatches,
+    mean / min / max duration, total time and share, registers and LDS."""
+    import collections
+    import sqlite3
+    con = sqlite3.connect(db)
+    groups = collections.defaultdict(list)
+    info = {}
+    for name, dur, gx, gy, gz, wx, vg, ag, lds in con.execute(
+            "select name, duration, grid_x, grid_y, grid_z, workgroup_x, vgpr_count, "
+            "accum_vgpr_count, lds_size from kernels"):
+        key = (_short(name).replace("(anonymous namespace)::", ""), gx // max(wx, 1), gy, gz, wx)
+        groups[key].append(dur)
+        info[key] = (vg, ag, lds)
+    tot = sum(sum(v) for v in groups.values())
+    print(f"kernel_sources_sha256: {kernel_source_hash()}")
+    print()
+    print("| kernel | workgroups (x, y, z) x lanes | dispatches | mean us | min us | max us | "
+          "total us | share | VGPR / AGPR | LDS B |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for key, d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        name, bx, gy, gz, wx = key
+        vg, ag, lds = info[key]
+        print(f"| `{name[:100]}` | ({bx}, {gy}, {gz}) x {wx} | {len(d)} | "
+              f"{sum(d) / len(d) / 1e3:.2f} | {min(d) / 1e3:.2f} | {max(d) / 1e3:.2f} | "
+              f"{sum(d) / 1e3:.1f} | {sum(d) / tot:.3f} | {vg} / {ag} | {lds} |")
+
+
+def summarize_mfma(db: str):
+    """MFMA utilisation per kernel: SQ_VALU_MFMA_BUSY_CYCLES over (GRBM_GUI_ACTIVE x 4 SIMDs x
+    256 CUs), and the fp16 MFMA flops counted by SQ_INSTS_VALU_MFMA_MOPS_F16 (512 flop each)."""
+    cs = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_BUSY_CU_CYCLES",
+          "GRBM_GUI_ACTIVE"]
+    per = _pmc_per_kernel(db, cs)
+    print(f"kernel_sources_sha256: {kernel_source_hash()}")
+    print()
+    print("| kernel | dispatches | MFMA busy cycles | GRBM_GUI_ACTIVE | MFMA util | "
+          "fp16 MFMA GFLOP / dispatch |")
+    print("|---|---|---|---|---|---|")
+    names = sorted(set().union(*[set(per[c]) for c in cs]))
+    for k in names:
+        busy = per["SQ_VALU_MFMA_BUSY_CYCLES"].get(k, (0.0, 0))
+        act = per["GRBM_GUI_ACTIVE"].get(k, (0.0, 0))[0]
+        mops = per["SQ_INSTS_VALU_MFMA_MOPS_F16"].get(k, (0.0, 0))[0]
+        util = busy[0] / (act * 4 * 256) if act else 0.0
+        print(f"| `{k.replace('(anonymous namespace)::', '')[:100]}` | {busy[1]} | {busy[0]:.3e} | "
+              f"{act:.3e} | {util:.3f} | {mops * 512 / 1e9:.3f} |")
 
 
 if __name__ == "__main__":

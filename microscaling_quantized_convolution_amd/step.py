@@ -39,12 +39,14 @@ class LayerStep:
     [Ho][Wo][Cout][N] order (all fp32 device tensors, any shape with the right element count)."""
 
     def __init__(self, conv, fmt: int, x: torch.Tensor, w: torch.Tensor, g_cbf: torch.Tensor,
-                 sr_seed_base: int = 1):
+                 sr_seed_base: int = 1, seed_stride: int = 1):
         self.p = conv_struct(conv)
         c = self.p
         dev = x.device
         Ho, Wo = out_hw(c)
-        self.fmt, self.sr_seed_base = int(fmt), int(sr_seed_base)
+        # G_Y's stochastic-rounding seed in pass s: sr_seed_base + seed_stride * s (a network of
+        # L layers with bases 1..L and stride L gives every (layer, pass) its own seed)
+        self.fmt, self.sr_seed_base, self.seed_stride = int(fmt), int(sr_seed_base), int(seed_stride)
         self.x, self.w, self.gc = x, w, g_cbf
         f32 = dict(dtype=torch.float32, device=dev)
         nws = MQ_QUANTIZE_WS_BYTES
@@ -64,8 +66,7 @@ class LayerStep:
                         quant_job(self.w, MQ_SRC_OIHW, self.qw, MQ_RNE, 0, a1)]
         self.ops: Dict[str, Callable[[int], None]] = OrderedDict([
             ("quantize_xw", lambda s: mq_quantize_batch(self.xw_jobs)),
-            ("quantize_g", lambda s: mq_quantize(self.gc, self.qg, MQ_SR,
-                                                 self.sr_seed_base + s, a2)),
+            ("quantize_g", lambda s: mq_quantize(self.gc, self.qg, MQ_SR, self.seed(s), a2)),
             ("conv_fwd", lambda s: mq_conv_fwd(p, self.qx, self.qw, self.y)),
             ("conv_backward", lambda s: mq_conv_backward(p, self.qw, self.qg, self.qx, self.gw,
                                                          self.gx, self.ws)),
@@ -75,6 +76,10 @@ class LayerStep:
             ("conv_dgrad", lambda s: mq_conv_dgrad(p, self.qw, self.qg, self.gx)),
         ])
 
+    def seed(self, s: int) -> int:
+        """G_Y's stochastic-rounding seed in pass s."""
+        return (self.sr_seed_base + self.seed_stride * s) & (2 ** 64 - 1)
+
     def run(self, s: int = 0):
         for f in self.ops.values():
             f(s)
@@ -82,7 +87,8 @@ class LayerStep:
     def direct_calls(self, stream) -> Dict[str, Callable[[int], None]]:
         """The same calls with their C arguments marshalled once, for a fixed stream: each call
         is then one foreign-function call (the per-call cost that matters when launches are
-        timed back to back). Each returns nothing and raises MQError on a failed status."""
+        timed back to back): the ops of a pass, then the two gradients as calls of their own.
+        Each returns nothing and raises MQError on a failed status."""
         import ctypes
         from . import MQ_OK, MQError, _lib, _stream
         c = self.p
@@ -112,11 +118,11 @@ class LayerStep:
             "conv_dgrad": (L.mq_conv_dgrad, (conv, bw, bg, P(self.gx), hs)),
         }
         out: Dict[str, Callable[[int], None]] = OrderedDict()
-        for name in self.ops:
+        for name in list(self.ops) + list(self.parts):
             if name == "quantize_g":
                 gsrc = P(self.gc)
                 out[name] = lambda s, f=L.mq_quantize, g=gsrc: chk(
-                    f(g, bg, MQ_SR, (self.sr_seed_base + s) & (2 ** 64 - 1), a[2], wsb, 0, hs),
+                    f(g, bg, MQ_SR, self.seed(s), a[2], wsb, 0, hs),
                     "mq_quantize")
             else:
                 f, args = fixed[name]

@@ -73,6 +73,24 @@ def run_gpu_layer(layer: workloads.ConvLayer, dev="cuda", tensors=None) -> GpuLa
     return GpuLayer(layer, qx, qw, qg, y, gw, gx)
 
 
+def run_layer_step(layer: workloads.ConvLayer, dev="cuda", step=0) -> GpuLayer:
+    """One pass of the path the benchmark times (LayerStep): X from NCHW and W from OIHW in one
+    batched quantization, G_Y (already channel-batch-first, as the next layer's input gradient
+    leaves it) with stochastic rounding and seed sr_seed + step, the forward GEMM and both
+    gradients in one call. The outputs are filled with NaN first."""
+    from microscaling_quantized_convolution_amd.step import LayerStep
+    x, w, g = workloads.make_tensors(layer)
+    gc = torch.empty(g.size, dtype=torch.float32, device=dev)
+    mq.mq_relayout_cbf(to_dev(g, dev), gc, layer.N, layer.Cout, layer.Ho, layer.Wo, 0)
+    st = LayerStep(layer.conv_tuple(), layer.fmt, to_dev(x, dev), to_dev(w, dev), gc,
+                   sr_seed_base=layer.sr_seed)
+    for t in (st.y, st.gw, st.gx):
+        t.fill_(float("nan"))
+    st.run(step)
+    torch.cuda.synchronize()
+    return GpuLayer(layer, st.qx, st.qw, st.qg, st.y, st.gw, st.gx)
+
+
 @dataclasses.dataclass
 class OracleLayer:
     q: dict          # name -> (codes, scales, T)
@@ -103,6 +121,22 @@ def assert_quant_equal(qt: mq.QTensor, ref, fmt, what=""):
                             f"{got_scales[bad_s[:5]]} vs {scales[bad_s[:5]]}"
     bad_c = np.nonzero(got_codes != exp_codes)[0]
     assert bad_c.size == 0, f"{what}: {bad_c.size} code bytes differ, first at byte {bad_c[:5]}"
+
+
+def check_layer(gl: GpuLayer, ol: OracleLayer, layer: workloads.ConvLayer):
+    """Quantized tensors bit-exact, and every element of Y, G_W and G_X within the bound."""
+    assert_quant_equal(gl.qx, ol.q["x"], layer.fmt, f"{layer.name} x")
+    assert_quant_equal(gl.qw, ol.q["w"], layer.fmt, f"{layer.name} w")
+    assert_quant_equal(gl.qg, ol.q["g"], layer.fmt, f"{layer.name} g")
+    p = layer.conv_tuple()
+    y, ya = oracle.conv_fwd(p, ol.deq["x"], ol.deq["w"])
+    assert_conv_close(gl.y.cpu().numpy(), y, ya, f"{layer.name} fwd")
+    del y, ya
+    gw, gwa = oracle.conv_wgrad(p, ol.deq["g"], ol.deq["x"])
+    assert_conv_close(gl.gw.cpu().numpy(), gw, gwa, f"{layer.name} wgrad")
+    del gw, gwa
+    gx, gxa = oracle.conv_dgrad(p, ol.deq["w"], ol.deq["g"])
+    assert_conv_close(gl.gx.cpu().numpy(), gx, gxa, f"{layer.name} dgrad")
 
 
 def assert_conv_close(got: np.ndarray, ref: np.ndarray, refabs: np.ndarray, what=""):

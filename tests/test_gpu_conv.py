@@ -5,8 +5,8 @@ fused), on channel-batch-first square-quantized tensors (onedev.kr MicroQonv dig
 "How it works" and "How it differs"). Per element |gpu - oracle| <= 2^-10 * sum|w*x| (the
 GPU sums exact bf16 products in fp32), and exactly 0 where every term is 0.
 
-Small and mid-sized layers are compared element by element; the full-size workload layers are
-compared on random samples of outputs that the oracle evaluates one at a time.
+Every layer is compared element by element: the small and ragged parity layers through the
+single-tensor calls, and every full-size workload layer through the calls the benchmark times.
 """
 import numpy as np
 import pytest
@@ -15,8 +15,7 @@ import torch
 import microscaling_quantized_convolution_amd as mq
 import oracle
 import workloads
-from gpu_parity import (assert_conv_close, assert_quant_equal, log, oracle_layer,
-                        run_gpu_layer)
+from gpu_parity import (check_layer, log, oracle_layer, run_gpu_layer, run_layer_step)
 
 pytestmark = pytest.mark.gpu
 
@@ -26,65 +25,33 @@ SMALL = workloads.config1() + workloads.parity_layers()
 @pytest.mark.parametrize("layer", SMALL, ids=lambda l: l.name)
 def test_conv_parity_full_tensor(layer):
     log("conv parity", layer.name)
-    gl = run_gpu_layer(layer)
-    ol = oracle_layer(layer)
-    assert_quant_equal(gl.qx, ol.q["x"], layer.fmt, "x")
-    assert_quant_equal(gl.qw, ol.q["w"], layer.fmt, "w")
-    assert_quant_equal(gl.qg, ol.q["g"], layer.fmt, "g")
-    p = layer.conv_tuple()
-    y, ya = oracle.conv_fwd(p, ol.deq["x"], ol.deq["w"])
-    gw, gwa = oracle.conv_wgrad(p, ol.deq["g"], ol.deq["x"])
-    gx, gxa = oracle.conv_dgrad(p, ol.deq["w"], ol.deq["g"])
-    assert_conv_close(gl.y.cpu().numpy(), y, ya, f"{layer.name} fwd")
-    assert_conv_close(gl.gw.cpu().numpy(), gw, gwa, f"{layer.name} wgrad")
-    assert_conv_close(gl.gx.cpu().numpy(), gx, gxa, f"{layer.name} dgrad")
+    check_layer(run_gpu_layer(layer), oracle_layer(layer), layer)
 
 
-def _sample_idx(rng, shape, n):
-    return np.stack([rng.integers(0, d, n) for d in shape], 1).astype(np.int32)
+def _distinct(layers):
+    seen, out = set(), []
+    for l in layers:
+        key = l.conv_tuple() + (l.fmt,)
+        if key not in seen:
+            seen.add(key)
+            out.append(l)
+    return out
 
 
-def _check_sampled(layer, nsamp=1500):
-    log("sampled conv parity", layer.name)
-    gl = run_gpu_layer(layer)
-    ol = oracle_layer(layer)
-    assert_quant_equal(gl.qx, ol.q["x"], layer.fmt, "x")
-    assert_quant_equal(gl.qw, ol.q["w"], layer.fmt, "w")
-    assert_quant_equal(gl.qg, ol.q["g"], layer.fmt, "g")
-    p = layer.conv_tuple()
-    rng = np.random.default_rng(hash(layer.name) % 2 ** 32)
-    Ho, Wo = layer.Ho, layer.Wo
-    yshape = (Ho, Wo, layer.Cout, layer.N)
-    wshape = (layer.Kh, layer.Kw, layer.Cout, layer.Cin)
-    xshape = (layer.H, layer.W, layer.Cin, layer.N)
-    for name, shape, fn, a, b, got in (
-            ("fwd", yshape, oracle.conv_fwd_at, ol.deq["x"], ol.deq["w"], gl.y),
-            ("wgrad", wshape, oracle.conv_wgrad_at, ol.deq["g"], ol.deq["x"], gl.gw),
-            ("dgrad", xshape, oracle.conv_dgrad_at, ol.deq["w"], ol.deq["g"], gl.gx)):
-        n = nsamp if name != "wgrad" else min(nsamp, 200)
-        idx = _sample_idx(rng, shape, n)
-        ref, refa = fn(p, a, b, idx)
-        g = got.cpu().numpy().reshape(shape)[tuple(idx.T)]
-        assert_conv_close(g, ref, refa, f"{layer.name} {name}")
-        assert np.isfinite(got.cpu().numpy()).all(), f"{layer.name} {name}: non-finite output"
+# Every full-size workload layer (each distinct shape of the ResNet-18 body once), through the
+# calls the benchmark times: the batched NCHW/OIHW quantization, the stochastic G_Y quantization,
+# the forward GEMM and the one-call backward. Every output element is compared.
+FULL_SIZE = (workloads.config2() + workloads.config3() + workloads.config4() +
+             _distinct(workloads.config5()))
 
 
-@pytest.mark.parametrize("cfg", ["c2", "c3"])
-def test_conv_parity_full_size_sampled(cfg):
-    for layer in workloads.CONFIGS[cfg]():
-        _check_sampled(layer)
-
-
-def test_conv_parity_yolo_stack_sampled():
-    for layer in workloads.config4():
-        _check_sampled(layer, nsamp=800)
-
-
-@pytest.mark.parametrize("which", [[0, 4], [5, 6, 9], [10, 11, 14], [15, 16, 18]])
-def test_conv_parity_resnet18_body_sampled(which):
-    layers = workloads.config5()
-    for i in which:
-        _check_sampled(layers[i], nsamp=600)
+@pytest.mark.parametrize("layer", FULL_SIZE, ids=lambda l: l.name)
+def test_layer_step_parity_full_size(layer):
+    log("layer step parity (full tensors)", layer.name, layer.conv_tuple())
+    gl = run_layer_step(layer)
+    check_layer(gl, oracle_layer(layer), layer)
+    for t, what in ((gl.y, "fwd"), (gl.gw, "wgrad"), (gl.gx, "dgrad")):
+        assert torch.isfinite(t).all(), f"{layer.name} {what}: non-finite output"
 
 
 def test_conv_deterministic():

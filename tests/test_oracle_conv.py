@@ -44,7 +44,7 @@ LAYERS = workloads.config1() + workloads.parity_layers()
 @pytest.mark.parametrize("layer", LAYERS, ids=lambda l: l.name)
 def test_gemms_match_torch_float64(layer):
     p = layer.conv_tuple()
-    s, pad = layer.stride, layer.pad
+    s, pad = (layer.stride, layer.sw), (layer.pad, layer.pw)
     xh, wh, gh = _deq(layer)
     y, ya = oracle.conv_fwd(p, xh, wh)
     gw, gwa = oracle.conv_wgrad(p, gh, xh)
@@ -71,7 +71,7 @@ def _exact_direct(layer, xh, wh, gh):
     """Textbook direct convolution and its two gradients in exact rationals (NCHW/OIHW)."""
     N, Ci, H, W, Co, Kh, Kw = (layer.N, layer.Cin, layer.H, layer.W, layer.Cout, layer.Kh,
                                layer.Kw)
-    s, p, Ho, Wo = layer.stride, layer.pad, layer.Ho, layer.Wo
+    sh, sw, ph, pw, Ho, Wo = layer.stride, layer.sw, layer.pad, layer.pw, layer.Ho, layer.Wo
     X = [[[[Fraction(float(xh[h, w, c, n])) for w in range(W)] for h in range(H)]
           for c in range(Ci)] for n in range(N)]
     Wf = [[[[Fraction(float(wh[kh, kw, o, c])) for kw in range(Kw)] for kh in range(Kh)]
@@ -87,14 +87,14 @@ def _exact_direct(layer, xh, wh, gh):
         for o in range(Co):
             for ho in range(Ho):
                 for wo in range(Wo):
-                    y[n, o, ho, wo] = sum(Wf[o][c][kh][kw] * xin(n, c, ho * s - p + kh, wo * s - p + kw)
+                    y[n, o, ho, wo] = sum(Wf[o][c][kh][kw] * xin(n, c, ho * sh - ph + kh, wo * sw - pw + kw)
                                           for c in range(Ci) for kh in range(Kh) for kw in range(Kw))
     gw = {}
     for o in range(Co):
         for c in range(Ci):
             for kh in range(Kh):
                 for kw in range(Kw):
-                    gw[o, c, kh, kw] = sum(G[n][o][ho][wo] * xin(n, c, ho * s - p + kh, wo * s - p + kw)
+                    gw[o, c, kh, kw] = sum(G[n][o][ho][wo] * xin(n, c, ho * sh - ph + kh, wo * sw - pw + kw)
                                            for n in range(N) for ho in range(Ho) for wo in range(Wo))
     gx = {(n, c, h, w): Fraction(0) for n in range(N) for c in range(Ci) for h in range(H)
           for w in range(W)}
@@ -105,24 +105,27 @@ def _exact_direct(layer, xh, wh, gh):
                     for c in range(Ci):
                         for kh in range(Kh):
                             for kw in range(Kw):
-                                h, w = ho * s - p + kh, wo * s - p + kw
+                                h, w = ho * sh - ph + kh, wo * sw - pw + kw
                                 if 0 <= h < H and 0 <= w < W:
                                     gx[n, c, h, w] += Wf[o][c][kh][kw] * G[n][o][ho][wo]
     return y, gw, gx
 
 
-@pytest.mark.parametrize("stride,pad,k", [(2, 1, 3), (1, 0, 3), (1, 1, 1), (2, 0, 1)])
-def test_gemms_match_exact_direct_convolution(stride, pad, k):
-    layer = workloads.ConvLayer("tiny", N=2, Cin=3, H=5, W=6, Cout=2, Kh=k, Kw=k, stride=stride,
-                                pad=pad, x_dist="normal", w_dist="normal", g_dist="normal",
-                                seed=7, sr_seed=3)
+@pytest.mark.parametrize("sh,sw,ph,pw,kh,kw", [(2, 2, 1, 1, 3, 3), (1, 1, 0, 0, 3, 3),
+                                               (1, 1, 1, 1, 1, 1), (2, 2, 0, 0, 1, 1),
+                                               (1, 2, 0, 1, 1, 3), (3, 3, 1, 1, 3, 3),
+                                               (2, 1, 1, 0, 3, 2)])
+def test_gemms_match_exact_direct_convolution(sh, sw, ph, pw, kh, kw):
+    layer = workloads.ConvLayer("tiny", N=2, Cin=3, H=5, W=6, Cout=2, Kh=kh, Kw=kw, stride=sh,
+                                pad=ph, stride_w=sw, pad_w=pw, x_dist="normal", w_dist="normal",
+                                g_dist="normal", seed=7, sr_seed=3)
     p = layer.conv_tuple()
     xh, wh, gh = _deq(layer)
     y, ya = oracle.conv_fwd(p, xh, wh)
     gw, gwa = oracle.conv_wgrad(p, gh, xh)
     gx, gxa = oracle.conv_dgrad(p, wh, gh)
     ey, egw, egx = _exact_direct(layer, xh, wh, gh)
-    K = layer.Cin * k * k
+    K = layer.Cin * kh * kw
     rel = 2.0 ** -52 * max(K, layer.N * layer.Ho * layer.Wo)
     for (n, o, ho, wo), v in ey.items():
         assert abs(Fraction(y[ho, wo, o, n]) - v) <= rel * Fraction(ya[ho, wo, o, n])

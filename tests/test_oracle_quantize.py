@@ -6,6 +6,7 @@ per 4x4 square, element rounding; RNE for weights/activations, stochastic roundi
 gradients), and statistics of the stochastic rounding.
 """
 import os
+import zlib
 
 import numpy as np
 import pytest
@@ -78,7 +79,8 @@ CASES = [
 
 @pytest.mark.parametrize("shape,dist,fmt", CASES)
 def test_rne_invariants(shape, dist, fmt):
-    x = workloads.random_array(shape, seed=hash((shape, dist)) % 1000, dist=dist)
+    x = workloads.random_array(shape, seed=zlib.crc32(repr((shape, dist)).encode()) % 1000,
+                               dist=dist)
     codes, scales, T = oracle.quantize(x, fmt, oracle.RNE)
     grid = _grid(fmt)
     emax = grid[-1]

@@ -39,14 +39,24 @@ class ConvLayer:
     Cout: int
     Kh: int
     Kw: int
-    stride: int = 1
-    pad: int = 0
+    stride: int = 1             # stride along the height (and the width unless stride_w is set)
+    pad: int = 0                # zero padding along the height (and the width unless pad_w is set)
     fmt: int = FP4
     x_dist: str = "normal"      # normal | relu | silu | t3
     w_dist: str = "kaiming"     # normal | kaiming
     g_dist: str = "normal1e-3"  # normal | normal1e-3
     seed: int = 0
     sr_seed: int = 1
+    stride_w: int = -1          # stride along the width; -1: the same as `stride`
+    pad_w: int = -1             # padding along the width; -1: the same as `pad`
+
+    @property
+    def sw(self) -> int:
+        return self.stride if self.stride_w < 0 else self.stride_w
+
+    @property
+    def pw(self) -> int:
+        return self.pad if self.pad_w < 0 else self.pad_w
 
     @property
     def Ho(self) -> int:
@@ -54,7 +64,7 @@ class ConvLayer:
 
     @property
     def Wo(self) -> int:
-        return (self.W + 2 * self.pad - self.Kw) // self.stride + 1
+        return (self.W + 2 * self.pw - self.Kw) // self.sw + 1
 
     def gemm_flops(self) -> int:
         """2*Cout*Cin*Kh*Kw*N*Ho*Wo: the algorithmic flop count of one of the three GEMMs."""
@@ -63,7 +73,7 @@ class ConvLayer:
     def conv_tuple(self) -> Tuple[int, ...]:
         """(N, Cin, H, W, Cout, Kh, Kw, stride_h, stride_w, pad_h, pad_w)."""
         return (self.N, self.Cin, self.H, self.W, self.Cout, self.Kh, self.Kw,
-                self.stride, self.stride, self.pad, self.pad)
+                self.stride, self.sw, self.pad, self.pw)
 
 
 def _draw(rng: np.random.Generator, shape, dist: str, fan_in: int) -> np.ndarray:
@@ -212,4 +222,18 @@ def parity_layers() -> List[ConvLayer]:
                   pad=1, fmt=FP6, x_dist="normal", seed=116, sr_seed=22),
         ConvLayer("p.b32.1x1s2", N=32, Cin=24, H=9, W=10, Cout=36, Kh=1, Kw=1, stride=2, pad=0,
                   x_dist="silu", seed=117, sr_seed=23),
+        # kernels, strides and paddings that differ between height and width, stride 3, and a
+        # padding as large as the kernel
+        ConvLayer("p.1x3.p01", N=6, Cin=12, H=9, W=11, Cout=20, Kh=1, Kw=3, stride=1, pad=0,
+                  pad_w=1, x_dist="relu", seed=118, sr_seed=24),
+        ConvLayer("p.3x1.p10.fp6", N=8, Cin=16, H=10, W=7, Cout=12, Kh=3, Kw=1, stride=1, pad=1,
+                  pad_w=0, fmt=FP6, x_dist="silu", seed=119, sr_seed=25),
+        ConvLayer("p.3x3.s12", N=5, Cin=10, H=9, W=12, Cout=14, Kh=3, Kw=3, stride=1, pad=1,
+                  stride_w=2, x_dist="normal", seed=120, sr_seed=26),
+        ConvLayer("p.3x3.p01", N=16, Cin=20, H=8, W=9, Cout=24, Kh=3, Kw=3, stride=1, pad=0,
+                  pad_w=1, x_dist="t3", seed=121, sr_seed=27),
+        ConvLayer("p.3x3.s3", N=4, Cin=8, H=13, W=14, Cout=12, Kh=3, Kw=3, stride=3, pad=1,
+                  x_dist="relu", seed=122, sr_seed=28),
+        ConvLayer("p.1x1.p1", N=8, Cin=12, H=6, W=7, Cout=16, Kh=1, Kw=1, stride=1, pad=1,
+                  x_dist="normal", seed=123, sr_seed=29),
     ]
