@@ -73,6 +73,26 @@ mq_status amax_ws_check(const uint32_t *ws, size_t bytes)
 
 } // namespace
 
+namespace mq {
+
+// Host-side validation of mq_conv_backward's arguments (everything but the workspace).
+mq_status backward_check(const mq_conv *p, const mq_qtensor *w, const mq_qtensor *gy,
+                         const mq_qtensor *x, const float *gw, const float *gx)
+{
+    ConvGeom g;
+    if (!conv_geom(p, &g) || !qtensor_ok(w) || !qtensor_ok(gy) || !qtensor_ok(x) || !gw || !gx)
+        return MQ_ERR_ARG;
+    if (!dims_are(w, p->Kh, p->Kw, p->Cout, p->Cin, MQ_ROLE_WEIGHT) ||
+        !dims_are(gy, g.Ho, g.Wo, p->Cout, p->N, MQ_ROLE_GRAD) ||
+        !dims_are(x, p->H, p->W, p->Cin, p->N, MQ_ROLE_ACT) || w->fmt != gy->fmt ||
+        x->fmt != gy->fmt)
+        return MQ_ERR_SHAPE;
+    if (!conv_supported(g)) return MQ_ERR_UNSUPPORTED;
+    return MQ_OK;
+}
+
+} // namespace mq
+
 extern "C" {
 
 const char *mq_status_str(mq_status st)
@@ -267,15 +287,10 @@ mq_status mq_conv_backward(const mq_conv *p, const mq_qtensor *w, const mq_qtens
                            const mq_qtensor *x, float *gw, float *gx, void *ws, size_t ws_bytes,
                            hipStream_t stream)
 {
+    const mq_status chk = mq::backward_check(p, w, gy, x, gw, gx);
+    if (chk != MQ_OK) return chk;
     mq::ConvGeom g;
-    if (!conv_geom(p, &g) || !qtensor_ok(w) || !qtensor_ok(gy) || !qtensor_ok(x) || !gw || !gx)
-        return MQ_ERR_ARG;
-    if (!dims_are(w, p->Kh, p->Kw, p->Cout, p->Cin, MQ_ROLE_WEIGHT) ||
-        !dims_are(gy, g.Ho, g.Wo, p->Cout, p->N, MQ_ROLE_GRAD) ||
-        !dims_are(x, p->H, p->W, p->Cin, p->N, MQ_ROLE_ACT) || w->fmt != gy->fmt ||
-        x->fmt != gy->fmt)
-        return MQ_ERR_SHAPE;
-    if (!conv_supported(g)) return MQ_ERR_UNSUPPORTED;
+    conv_geom(p, &g);
     if (mq::wgrad_fast_supported(g) && mq::spatial_supported(g)) {
         if (!ws || ws_bytes < mq::wgrad_fast_workspace_bytes(g)) return MQ_ERR_WORKSPACE;
         mq::WgradSum sum;

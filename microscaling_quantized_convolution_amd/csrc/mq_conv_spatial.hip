@@ -72,23 +72,26 @@ struct SpatialArgs {
 // otherwise its second (Cin) is (forward). The input operand's squares always have the
 // reduction (channels) along their first dimension.
 //
-// Waves [0, NCW) consume: MFMAs on one LDS buffer. Waves [NCW, 2*NCW) produce: they load the
-// squares of the stage after next into registers and decode the next stage into the other LDS
-// buffer. Both sides meet at one barrier per stage, so a SIMD runs one MFMA wave and one decode
-// wave side by side.
+// Waves [0, NCW) consume: MFMAs on one LDS buffer. Waves [NCW, (1+PF)*NCW) produce: they load
+// the squares of the stage after next into registers and decode the next stage into the other LDS
+// buffer. Both sides meet at one barrier per stage, so a SIMD runs one MFMA wave and PF decode
+// waves side by side (MFMA and VALU work of different waves on one SIMD execute together).
+// PF = 2 where the consumer's accumulators leave room for three waves per SIMD (32-row consumer
+// waves): the decode of a 1 x 8 tile's halo and weights then keeps up with its MFMAs.
 // KF = 3: every workgroup's class has the full 3 x 3 taps (compile-time tap loops, so the
 // consumer's LDS reads for later taps can be issued ahead of earlier taps' MFMAs); KF = 0: the
 // class's sub-kernel extent is read at run time.
 // MW: 32-row blocks per consumer wave (2: a wave owns all 64 rows of 4 pixels; 1: two waves
 // share 4 pixels, 32 rows each, so that small pixel tiles still give four MFMA waves).
-template <int FMT, bool A_KR, int SI, int PH, int PW, int MW, int KF, bool PERSIST>
-__global__ void __launch_bounds__(32 * PH * PW * (2 / MW))
+template <int FMT, bool A_KR, int SI, int PH, int PW, int MW, int PF, int KF, bool PERSIST>
+__global__ void __launch_bounds__(32 * PH * PW * (2 / MW) * (1 + PF) / 2)
 conv_spatial_kernel(SpatialArgs a)
 {
     warm_kernel_args<SpatialArgs>();
-    constexpr int THREADS_OF = 32 * PH * PW * (2 / MW);
     constexpr int NCW = PH * PW / 4 * (2 / MW); // consumer waves (4 pixels x 32*MW rows each)
-    constexpr int NP = 64 * NCW;                // producer threads
+    constexpr int NCT = 64 * NCW;               // consumer threads
+    constexpr int NP = NCT * PF;                // producer threads
+    constexpr int THREADS_OF = NCT + NP;
     constexpr int KHM = 3, KWM = 3;
     constexpr int HRM = (PH - 1) * SI + KHM, HCM = (PW - 1) * SI + KWM;
     constexpr int WCOLS = 3 * SI + KWM; // halo columns one wave touches (4 pixels)
@@ -103,16 +106,17 @@ conv_spatial_kernel(SpatialArgs a)
     // barrier). The class comes from the grid rather than a search of the classes' ranges in
     // the arguments, which put dependent argument loads before the first memory access.
     if ((int)blockIdx.y >= a.nclass) {
-        // the weight gradient's split sum, riding along: two 64-output blocks per pass (one per
-        // 256 lanes), workgroup b taking passes b, b + sum_P, ... (the loop count is the same for
+        // the weight gradient's split sum, riding along: one 64-output block per 256 lanes and
+        // pass, workgroup b taking passes b, b + sum_P, ... (the loop count is the same for
         // every lane: each call below holds a barrier)
-        static_assert(THREADS_OF == 512, "the sum role takes two 256-lane groups");
+        constexpr int SG = THREADS_OF / 256;
+        static_assert(THREADS_OF % 256 == 0, "the sum role takes whole 256-lane groups");
         if ((int)blockIdx.x >= a.sum_P) return;
         float4(*red)[17] = reinterpret_cast<float4(*)[17]>(lds[0]);
         const int64_t nb = (a.sum.total + 63) / 64;
-        const int half = (int)threadIdx.x >> 8;
-        for (int64_t base = 2 * (int64_t)blockIdx.x; base < nb; base += 2 * (int64_t)a.sum_P) {
-            wgrad_sum_block(a.sum, base + half, (int)threadIdx.x & 255, red + 16 * half);
+        const int grp = (int)threadIdx.x >> 8;
+        for (int64_t base = SG * (int64_t)blockIdx.x; base < nb; base += SG * (int64_t)a.sum_P) {
+            wgrad_sum_block(a.sum, base + grp, (int)threadIdx.x & 255, red + 16 * grp);
             __syncthreads(); // the next pass reuses red
         }
         return;
@@ -170,7 +174,7 @@ conv_spatial_kernel(SpatialArgs a)
 
     if (wave >= NCW) {
         // ================= producer =================
-        const int ptid = tid - NP;
+        const int ptid = tid - NCT;
         const int nA = ntap * 16, nA64 = (nA + 63) & ~63, nAB = nA64 + HR * HC * 8;
         constexpr int CB = (FMT == kFP4) ? 8 : 12;
         const uint32_t in_sq = (uint32_t)a.IH * a.IW * a.K4 * a.N4;
@@ -491,7 +495,9 @@ bool spatial_supported(const ConvGeom &g)
 template <int FMT, bool A_KR, int SI, int PH, int PW, int MW>
 static hipError_t launch_spatial_tiles(SpatialArgs &a, int nclass, hipStream_t st)
 {
-    constexpr int THREADS = 32 * PH * PW * (2 / MW);
+    constexpr int PF = MW == 1 ? 2 : 1; // producer waves per consumer wave
+    constexpr int THREADS = 32 * PH * PW * (2 / MW) * (1 + PF) / 2;
+    constexpr int SG = THREADS / 256;   // 64-output sum blocks per workgroup pass
     int items[4] = {0, 0, 0, 0}, total = 0;
     double work[4] = {0, 0, 0, 0}, total_work = 0;
     for (int c = 0; c < nclass; ++c) {
@@ -527,10 +533,10 @@ static hipError_t launch_spatial_tiles(SpatialArgs &a, int nclass, hipStream_t s
     if (a.sum_P < 0) {
         // The weight-gradient sum: on the CUs this launch leaves idle (one workgroup per CU:
         // the LDS), or, when it fills them, on 256 workgroups after its own. A workgroup sums
-        // two 64-output blocks per pass, a chain of dependent loads and a barrier (about 1.5 us),
+        // SG 64-output blocks per pass, a chain of dependent loads and a barrier (about 1.5 us),
         // so the sum rides along only when its passes hide behind the convolution or cost less
         // than a kernel of their own; otherwise it runs as its own kernel, ahead.
-        const int64_t pairs = ((a.sum.total + 63) / 64 + 1) / 2;
+        const int64_t pairs = ((a.sum.total + 63) / 64 + SG - 1) / SG;
         const int spare = 256 - conv_wgs;
         const int64_t P = spare >= 32 ? spare : 256;
         if ((pairs + P - 1) / P <= (spare >= 32 ? 8 : 2)) {
@@ -546,7 +552,7 @@ static hipError_t launch_spatial_tiles(SpatialArgs &a, int nclass, hipStream_t s
     dim3 grid((unsigned)nwg, (unsigned)(nclass + (a.sum_P > 0 ? 1 : 0)), 1);
     const bool full3 = nclass == 1 && a.cls[0].kh == 3 && a.cls[0].kw == 3;
 #define MQ_SPATIAL_LAUNCH(KFV, PV)                                                              \
-    hipLaunchKernelGGL((conv_spatial_kernel<FMT, A_KR, SI, PH, PW, MW, KFV, PV>), grid,          \
+    hipLaunchKernelGGL((conv_spatial_kernel<FMT, A_KR, SI, PH, PW, MW, PF, KFV, PV>), grid,      \
                        dim3(THREADS), 0, st, a)
     if (full3 && persist) MQ_SPATIAL_LAUNCH(3, true);
     else if (full3) MQ_SPATIAL_LAUNCH(3, false);
@@ -625,7 +631,7 @@ hipError_t launch_conv_dgrad_spatial(const ConvGeom &g, int fmt, QOperand w, QOp
                                      float *gx, hipStream_t st, const WgradSum *sum)
 {
     SpatialArgs a = {};
-    if (sum) {
+    if (sum && sum->total > 0) {
         a.sum = *sum;
         a.sum_P = -1; // sized by the launch
     }

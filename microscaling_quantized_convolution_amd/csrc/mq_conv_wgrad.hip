@@ -15,7 +15,8 @@
 // Per stage it decodes the G_Y strip (PW pixels) and the X row segment it meets
 // ((PW-1)*s + Kw pixels) once into LDS as fp16; each wave runs 32x32x16 fp16 MFMAs for a
 // 32 x 32 x Kw block. The fp32 partial block goes to the workspace, and a second kernel sums the
-// splits in a fixed order (deterministic) and applies the tensor scales.
+// splits in a fixed order (deterministic) and applies the tensor scales. A reduction that is not
+// split (one split) writes G_W itself, scaled, with no partial block and no sum.
 #include "mq_kernels.hpp"
 #include "mq_stage.hpp"
 #include "mq_wgrad_sum.hpp"
@@ -30,6 +31,9 @@ struct WgradArgs {
     const uint8_t *g_codes, *g_scales; // squares [Ho][Wo][Cout4][N4]
     const uint8_t *x_codes, *x_scales; // squares [H][W][Cin4][N4]
     float *part;                       // [split][Kh*Kw][Cout][Cin] fp32 partial sums
+    float *gw;                         // G_W [Kh*Kw][Cout][Cin] (written here when direct)
+    const float *tg, *tx;              // tensor scales T_G, T_X
+    int direct;                        // one split: scale and write G_W, no partials
     int H, W, Ho, Wo, Cin, Cout, Cin4, Cout4, N4;
     int Kh, Kw, sh, sw, ph, pw;
     int owb, nch;          // pixel blocks per output row, 32-element batch chunks
@@ -284,8 +288,10 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
         __syncthreads();
     }
 
-    // ---- partial block: part[split][kh*Kw + kw][co][ci] ----
-    float *out = a.part + (int64_t)split * a.split_stride;
+    // ---- partial block part[split][kh*Kw + kw][co][ci], or (one split) G_W itself, scaled
+    // as the split sum scales a sum of one partial: (float)(acc * (double)T_G * T_X) ----
+    float *out = a.direct ? a.gw : a.part + (int64_t)split * a.split_stride;
+    const double sc = a.direct ? (double)*a.tg * (double)*a.tx : 1.0;
     const int ci = ci4_0 * 4 + wc * 32 + l32;
 #pragma unroll
     for (int t = 0; t < KWM; ++t) {
@@ -294,16 +300,22 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int co = co4_0 * 4 + wm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (co < a.Cout && ci < a.Cin) o[(int64_t)co * a.Cin + ci] = acc[t][r];
+            const float v = a.direct ? (float)((double)acc[t][r] * sc) : acc[t][r];
+            if (co < a.Cout && ci < a.Cin) o[(int64_t)co * a.Cin + ci] = v;
         }
     }
 }
 
-// The split sum as a kernel of its own: one 64-output block per 256-lane workgroup.
+// The split sum as a kernel of its own: 64-output blocks, grid-stride over the 256-lane
+// workgroups (a workgroup per block made launches of tens of thousands of tiny workgroups).
 __global__ void __launch_bounds__(256) wgrad_sum_kernel(WgradSum w)
 {
     __shared__ float4 red[16][17];
-    wgrad_sum_block(w, blockIdx.x, (int)threadIdx.x, red);
+    const int64_t nb = (w.total + 63) / 64;
+    for (int64_t blk = blockIdx.x; blk < nb; blk += gridDim.x) {
+        wgrad_sum_block(w, blk, (int)threadIdx.x, red);
+        __syncthreads(); // the next block reuses red
+    }
 }
 
 struct Plan {
@@ -340,7 +352,9 @@ Plan plan(const ConvGeom &g)
         const int64_t splits = (p.stages + per - 1) / per;
         if (splits != s) continue; // the same split as a smaller s
         const int64_t rounds = (p.tiles * splits + 255) / 256;
-        const double t = 1.9 * (double)(rounds * per) + 2.0 * (double)(splits * out_bytes) / 5e6;
+        // one split writes G_W directly: no partials to write and read back, no sum launch
+        const double t = 1.9 * (double)(rounds * per) +
+                         (splits > 1 ? 2.0 * (double)(splits * out_bytes) / 5e6 + 3.0 : 0.0);
         if (best < 0.0 || t < best) {
             best = t;
             best_per = per;
@@ -348,7 +362,8 @@ Plan plan(const ConvGeom &g)
     }
     p.per_split = (int)best_per;
     p.splits = (p.stages + p.per_split - 1) / p.per_split;
-    p.bytes = (size_t)p.splits * (size_t)p.split_stride * 4;
+    // one split needs no partials (a token workspace keeps 0 meaning "invalid convolution")
+    p.bytes = p.splits > 1 ? (size_t)p.splits * (size_t)p.split_stride * 4 : 256;
     return p;
 }
 
@@ -407,6 +422,8 @@ hipError_t launch_conv_wgrad_partials(const ConvGeom &g, int fmt, QOperand gy, Q
     WgradArgs a;
     a.g_codes = gy.codes; a.g_scales = gy.scales; a.x_codes = x.codes; a.x_scales = x.scales;
     a.part = reinterpret_cast<float *>(ws);
+    a.gw = gw; a.tg = gy.tscale; a.tx = x.tscale;
+    a.direct = p.splits == 1 ? 1 : 0;
     a.H = g.H; a.W = g.W; a.Ho = g.Ho; a.Wo = g.Wo; a.Cin = g.Cin; a.Cout = g.Cout;
     a.Cin4 = g.Cin4; a.Cout4 = g.Cout4; a.N4 = g.N4;
     a.Kh = g.Kh; a.Kw = g.Kw; a.sh = g.sh; a.sw = g.sw; a.ph = g.ph; a.pw = g.pw;
@@ -419,7 +436,7 @@ hipError_t launch_conv_wgrad_partials(const ConvGeom &g, int fmt, QOperand gy, Q
     sum->part = reinterpret_cast<const float *>(ws);
     sum->S = p.splits;
     sum->stride = p.split_stride;
-    sum->total = p.split_stride;
+    sum->total = a.direct ? 0 : p.split_stride; // nothing to sum after a direct write
     sum->tg = gy.tscale;
     sum->tx = x.tscale;
     sum->out = gw;
@@ -438,7 +455,8 @@ hipError_t launch_conv_wgrad_fast(const ConvGeom &g, int fmt, QOperand gy, QOper
 hipError_t launch_wgrad_sum(const WgradSum &w, hipStream_t st)
 {
     if (w.total <= 0) return hipSuccess;
-    hipLaunchKernelGGL(wgrad_sum_kernel, dim3((unsigned)((w.total + 63) / 64)), dim3(256), 0, st, w);
+    const int64_t nb = (w.total + 63) / 64;
+    hipLaunchKernelGGL(wgrad_sum_kernel, dim3((unsigned)(nb < 2048 ? nb : 2048)), dim3(256), 0, st, w);
     return hipGetLastError();
 }
 

@@ -5,7 +5,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/mq.h"
+
 namespace mq {
+
+// Host-side validation of mq_conv_backward's arguments other than the workspace: MQ_OK, or the
+// status mq_conv_backward returns for them (mq_api.cpp).
+mq_status backward_check(const mq_conv *p, const mq_qtensor *w, const mq_qtensor *gy,
+                         const mq_qtensor *x, const float *gw, const float *gx);
 
 // Tensor-amax workspace: word 0 = number of partial maxima P (1..kAmaxParts), words 1..P = the
 // partials (max |x| as fp32 bit patterns). Written by the amax pass or by a relayout that is
