@@ -10,7 +10,8 @@
  * Conventions shared by every call:
  *   - Every pointer argument named *_dev, and every pointer inside mq_qtensor, is device memory
  *     on the current HIP device. The caller allocates and owns all memory; the library
- *     allocates nothing and keeps no state between calls.
+ *     allocates nothing and keeps no state between calls (the one exception is the device
+ *     array of mq_conv_backward_noalloc, part of the library's code object on each GPU).
  *   - Every call is asynchronous on `stream` (0 = the null stream). The return value reports
  *     only synchronous host-side argument validation and launch errors; no call synchronizes.
  *   - Data problems are not reported through the status: a tensor containing NaN or Inf
@@ -305,6 +306,30 @@ mq_status mq_conv_dgrad(const mq_conv *p, const mq_qtensor *w, const mq_qtensor 
 mq_status mq_conv_backward(const mq_conv *p, const mq_qtensor *w, const mq_qtensor *gy,
                            const mq_qtensor *x, float *gw_dev, float *gx_dev, void *ws_dev,
                            size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Size of the device array that mq_conv_backward_noalloc keeps the weight gradient's split-K
+ * partial sums in (one array per GPU, held until the process ends).
+ */
+#define MQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * mq_conv_backward_noalloc: mq_conv_backward (same kernels, same G_W and G_X bit for bit) for
+ * callers that cannot allocate memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc. The weight gradient's split-K partial sums go to a
+ * library-owned device array of MQ_NOALLOC_SCRATCH_BYTES on the current device instead of a
+ * caller workspace; the call allocates nothing (no hipMalloc, no allocating library routine).
+ * The caller still provides every input and output as for mq_conv_backward, on the current HIP
+ * device (stream must belong to it).
+ * Every call on one GPU shares that GPU's array: calls that can overlap on one GPU (different
+ * streams, or threads without ordering between their calls) race and must not be issued;
+ * calls ordered on one stream are fine.
+ * Errors: as mq_conv_backward; MQ_ERR_UNSUPPORTED when mq_wgrad_workspace_bytes(p) exceeds
+ *         MQ_NOALLOC_SCRATCH_BYTES; MQ_ERR_LAUNCH when the device array cannot be located.
+ */
+mq_status mq_conv_backward_noalloc(const mq_conv *p, const mq_qtensor *w, const mq_qtensor *gy,
+                                   const mq_qtensor *x, float *gw_dev, float *gx_dev,
+                                   hipStream_t stream);
 
 #ifdef __cplusplus
 }

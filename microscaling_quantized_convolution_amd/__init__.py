@@ -24,13 +24,14 @@ MQ_QUANTIZE_WS_BYTES = 8192  # tensor-amax workspace (mq_quantize, relayouts)
 MQ_QUANTIZE_AMAX_READY = 1   # mq_quantize flag: the workspace already holds this tensor's amax
 MQ_SRC_DENSE, MQ_SRC_NCHW, MQ_SRC_OIHW = 0, 1, 2  # mq_quant_job.layout
 MQ_QUANTIZE_BATCH_MAX = 4
+MQ_NOALLOC_SCRATCH_BYTES = 32 << 20  # library-owned split-K scratch of mq_conv_backward_noalloc
 
 EXPORTS = (
     "mq_status_str", "mq_codes_bytes", "mq_scales_bytes", "mq_relayout_cbf",
     "mq_relayout_weight", "mq_quantize", "mq_quantize_nchw", "mq_quantize_batch",
     "mq_quantize_weight", "mq_conv_fwd",
     "mq_wgrad_workspace_bytes",
-    "mq_conv_wgrad", "mq_conv_dgrad", "mq_conv_backward",
+    "mq_conv_wgrad", "mq_conv_dgrad", "mq_conv_backward", "mq_conv_backward_noalloc",
 )
 
 
@@ -88,6 +89,9 @@ def _load() -> ctypes.CDLL:
     L.mq_conv_backward.argtypes = [ctypes.POINTER(mq_conv), ctypes.POINTER(mq_qtensor),
                                    ctypes.POINTER(mq_qtensor), ctypes.POINTER(mq_qtensor), P, P,
                                    P, sz, P]
+    L.mq_conv_backward_noalloc.argtypes = [ctypes.POINTER(mq_conv), ctypes.POINTER(mq_qtensor),
+                                           ctypes.POINTER(mq_qtensor), ctypes.POINTER(mq_qtensor),
+                                           P, P, P]
     for name in EXPORTS:
         getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int
     return L
@@ -249,6 +253,16 @@ def mq_conv_backward(p: ConvLike, w: QTensor, gy: QTensor, x: QTensor, gw: torch
     _check(_lib.mq_conv_backward(ctypes.byref(c), ctypes.byref(qw), ctypes.byref(qg),
                                  ctypes.byref(qx), _ptr(gw), _ptr(gx), _ptr(ws), _nbytes(ws),
                                  _stream(stream)), "mq_conv_backward")
+
+
+def mq_conv_backward_noalloc(p: ConvLike, w: QTensor, gy: QTensor, x: QTensor,
+                             gw: torch.Tensor, gx: torch.Tensor, stream=None):
+    """mq_conv_backward without a workspace argument: the split-K partials live in the
+    library's own device array (for callers that cannot allocate)."""
+    c, qw, qg, qx = conv_struct(p), w.struct(), gy.struct(), x.struct()
+    _check(_lib.mq_conv_backward_noalloc(ctypes.byref(c), ctypes.byref(qw), ctypes.byref(qg),
+                                         ctypes.byref(qx), _ptr(gw), _ptr(gx), _stream(stream)),
+           "mq_conv_backward_noalloc")
 
 
 def out_hw(p: ConvLike) -> Tuple[int, int]:

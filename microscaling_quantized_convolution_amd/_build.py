@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmq.so")
 SOURCES = ["mq_api.cpp", "mq_relayout.hip", "mq_quantize.hip", "mq_conv.hip",
-           "mq_conv_spatial.hip", "mq_conv_wgrad.hip"]
+           "mq_conv_spatial.hip", "mq_conv_wgrad.hip", "mq_noalloc.hip"]
 
 # -ffp-contract=off: the quantizer's fp32 scale arithmetic must round every operation as written.
 # fp32 division stays IEEE-correct (hipcc's default) and fp32 denormals are kept (no

@@ -159,3 +159,44 @@ def test_header_constants_match_binding():
     assert m and int(m.group(1)) == mq.MQ_QUANTIZE_WS_BYTES
     m = re.search(r"#define MQ_QUANTIZE_AMAX_READY (\d+)u", hdr)
     assert m and int(m.group(1)) == mq.MQ_QUANTIZE_AMAX_READY
+
+
+def test_backward_noalloc_validation_without_gpu():
+    """mq_conv_backward_noalloc checks its arguments on the host before it touches the device:
+    the statuses of mq_conv_backward, and MQ_ERR_UNSUPPORTED for a convolution whose split-K
+    partials exceed the library's own array."""
+    L = mq.lib()
+    conv = mq.conv_struct((2, 16, 8, 8, 16, 3, 3, 1, 1, 0, 0))
+    x = _fake_q((8, 8, 16, 2))
+    w = _fake_q((3, 3, 16, 16), role=mq.MQ_ROLE_WEIGHT)
+    g = _fake_q((6, 6, 16, 2), role=mq.MQ_ROLE_GRAD)
+    g7 = _fake_q((7, 6, 16, 2), role=mq.MQ_ROLE_GRAD)
+    y = ctypes.c_void_p(0x2000)
+    s0 = ctypes.c_void_p(0)
+    na = lambda c, *a: L.mq_conv_backward_noalloc(ctypes.byref(c), *a, s0)
+    assert L.mq_conv_backward_noalloc(None, ctypes.byref(w), ctypes.byref(g), ctypes.byref(x),
+                                      y, y, s0) == mq.MQ_ERR_ARG
+    assert na(conv, ctypes.byref(w), ctypes.byref(g), ctypes.byref(x), None, y) == mq.MQ_ERR_ARG
+    assert na(conv, ctypes.byref(w), ctypes.byref(g), ctypes.byref(x), y, None) == mq.MQ_ERR_ARG
+    assert na(conv, ctypes.byref(x), ctypes.byref(g), ctypes.byref(x), y, y) == mq.MQ_ERR_SHAPE
+    assert na(conv, ctypes.byref(w), ctypes.byref(g7), ctypes.byref(x), y, y) == mq.MQ_ERR_SHAPE
+    # a 5x5 512->512 convolution at N=128 on 14x14 needs more partial sums than the array holds
+    big = (128, 512, 14, 14, 512, 5, 5, 1, 1, 2, 2)
+    assert mq.mq_wgrad_workspace_bytes(big) > mq.MQ_NOALLOC_SCRATCH_BYTES
+    bc = mq.conv_struct(big)
+    bx = _fake_q((14, 14, 512, 128))
+    bw_ = _fake_q((5, 5, 512, 512), role=mq.MQ_ROLE_WEIGHT)
+    bg = _fake_q((14, 14, 512, 128), role=mq.MQ_ROLE_GRAD)
+    assert na(bc, ctypes.byref(bw_), ctypes.byref(bg), ctypes.byref(bx), y, y) == \
+        mq.MQ_ERR_UNSUPPORTED
+    # every workload layer fits
+    import workloads
+    for l in (workloads.config2() + workloads.config3() + workloads.config4() +
+              workloads.config5()):
+        assert 0 < mq.mq_wgrad_workspace_bytes(l.conv_tuple()) <= mq.MQ_NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_scratch_size_matches_binding():
+    hdr = open(os.path.join(ROOT, "include", "mq.h")).read()
+    m = re.search(r"#define MQ_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == mq.MQ_NOALLOC_SCRATCH_BYTES
