@@ -230,7 +230,11 @@ __device__ __forceinline__ uint32_t quantize_square(const float (&x)[16], float 
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const float q0 = x[e] * rD;
-                    q[e] = __builtin_fmaf(__builtin_fmaf(-q0, D, x[e]), rD, q0);
+                    // x = -0 leaves q0 = -0 and a +0 residual, whose sum is +0: the sign of x is
+                    // put back (for every other x the quotient already carries it), so that
+                    // nearest rounding keeps the code's sign bit equal to x's
+                    q[e] = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, D, x[e]), rD, q0),
+                                               x[e]);
                 }
             }
         }

@@ -46,7 +46,16 @@ SPECIAL = {
     "onehot": lambda s: _with(np.zeros(s, np.float32), (0, 0, 0, 0), 1.0),
     "sparse_zero_squares": lambda s: _zero_some(workloads.random_array(s, 7)),
     "ties": lambda s: _ties(s),
+    "neg_zero_elements": lambda s: _neg_zero_elements(s),
 }
+
+
+def _neg_zero_elements(s):
+    # -0.0 elements inside squares with a non-zero scale: their codes keep the sign bit of x
+    a = workloads.random_array(s, 8)
+    a.reshape(-1)[1::3] = -0.0
+    a.reshape(-1)[2::7] = 0.0
+    return a
 
 
 def _with(a, idx, v):
@@ -234,7 +243,7 @@ def test_quantize_nchw_matches_relayout_then_quantize(shape, fmt, rnd):
 
 @pytest.mark.parametrize("fmt", [4, 6])
 @pytest.mark.parametrize("case", ["zeros", "neg_zeros", "nan", "inf", "tiny", "denormal", "huge",
-                                  "sparse_zero_squares", "ties"])
+                                  "sparse_zero_squares", "ties", "neg_zero_elements"])
 def test_quantize_nchw_special_values(case, fmt):
     shape = (2, 3, 9, 10)
     x = SPECIAL[case](shape)
@@ -299,6 +308,7 @@ def _batch_tensors(name, fmt):
     out = []
     for i, (layout, shape, role, rnd) in enumerate(BATCHES[name]):
         a = workloads.random_array(shape, seed=300 + 7 * i, dist="relu" if rnd == 0 else "normal")
+        a.reshape(-1)[3::11] = -0.0  # negative zeros inside squares with a non-zero scale
         if layout == mq.MQ_SRC_NCHW:
             n, c, h, w_ = shape
             qshape = (h, w_, c, n)
@@ -380,8 +390,11 @@ def test_quantize_weight_from_oihw(wshape, fmt, rnd):
 @pytest.mark.parametrize("wshape", [(64, 64, 3, 3), (128, 128, 3, 3)])
 def test_quantize_weight_special_values(wshape):
     Co, Ci, Kh, Kw = wshape
+    negz = workloads.random_array(wshape, 6)
+    negz.reshape(-1)[1::3] = -0.0
     for name, w in (("zeros", np.zeros(wshape, np.float32)),
-                    ("inf", _with(workloads.random_array(wshape, 5), (1, 2, 0, 1), np.inf))):
+                    ("inf", _with(workloads.random_array(wshape, 5), (1, 2, 0, 1), np.inf)),
+                    ("neg_zero_elements", negz)):
         q = mq.QTensor(Kh, Kw, Co, Ci, 4, mq.MQ_ROLE_WEIGHT, "cuda")
         mq.mq_quantize_weight(to_dev(w), q, 0, 0, mq.quantize_workspace("cuda"))
         torch.cuda.synchronize()
