@@ -13,9 +13,14 @@ namespace {
 
 bool fmt_ok(int32_t f) { return f == MQ_NVFP4 || f == MQ_NVFP6; }
 
+// Squares of a tensor of positive dimensions, in 64-bit arithmetic (every factor is below 2^31,
+// so the product of the four fits unless the tensor has 2^62 squares or more: callers compare
+// it with limits far below that, and saturate the first two factors' product first).
 int64_t squares(int32_t o0, int32_t o1, int32_t r, int32_t s)
 {
-    return (int64_t)o0 * o1 * ((r + 3) / 4) * ((s + 3) / 4);
+    const int64_t planes = (int64_t)o0 * o1, tiles = (((int64_t)r + 3) / 4) * (((int64_t)s + 3) / 4);
+    const int64_t cap = (int64_t)1 << 62;
+    return planes > cap / tiles ? cap : planes * tiles;
 }
 
 // The kernels read codes with 16-byte loads and scales with aligned 4-byte loads (which may
@@ -35,22 +40,35 @@ bool conv_geom(const mq_conv *p, mq::ConvGeom *g)
     if (p->N < 1 || p->Cin < 1 || p->H < 1 || p->W < 1 || p->Cout < 1 || p->Kh < 1 ||
         p->Kw < 1 || p->stride_h < 1 || p->stride_w < 1 || p->pad_h < 0 || p->pad_w < 0)
         return false;
-    if (p->H + 2 * p->pad_h < p->Kh || p->W + 2 * p->pad_w < p->Kw) return false;
+    // padded extents in 64 bits (every field is below 2^31)
+    const int64_t hp = (int64_t)p->H + 2 * (int64_t)p->pad_h, wp = (int64_t)p->W + 2 * (int64_t)p->pad_w;
+    if (hp < p->Kh || wp < p->Kw) return false;
     g->N = p->N; g->Cin = p->Cin; g->H = p->H; g->W = p->W; g->Cout = p->Cout;
     g->Kh = p->Kh; g->Kw = p->Kw; g->sh = p->stride_h; g->sw = p->stride_w;
     g->ph = p->pad_h; g->pw = p->pad_w;
-    g->Ho = (p->H + 2 * p->pad_h - p->Kh) / p->stride_h + 1;
-    g->Wo = (p->W + 2 * p->pad_w - p->Kw) / p->stride_w + 1;
-    g->N4 = (p->N + 3) / 4; g->Cin4 = (p->Cin + 3) / 4; g->Cout4 = (p->Cout + 3) / 4;
+    const int64_t ho = (hp - p->Kh) / p->stride_h + 1, wo = (wp - p->Kw) / p->stride_w + 1;
+    if (ho > INT32_MAX || wo > INT32_MAX) return false;
+    g->Ho = (int)ho;
+    g->Wo = (int)wo;
+    g->N4 = (int)(((int64_t)p->N + 3) / 4);
+    g->Cin4 = (int)(((int64_t)p->Cin + 3) / 4);
+    g->Cout4 = (int)(((int64_t)p->Cout + 3) / 4);
     return true;
+}
+
+// a * b * c for non-negative factors below 2^31, saturated at 2^62 (no overflow)
+int64_t mul3_sat(int64_t a, int64_t b, int64_t c)
+{
+    const int64_t cap = (int64_t)1 << 62, ab = a * b; // below 2^62
+    return (c != 0 && ab > cap / c) ? cap : ab * c;
 }
 
 // Limits of the implemented kernels: 32-bit index arithmetic inside the GEMM kernels.
 bool conv_supported(const mq::ConvGeom &g)
 {
     const int64_t lim = (int64_t)1 << 30;
-    if ((int64_t)g.H * g.W * g.N4 >= lim / 4 || (int64_t)g.Ho * g.Wo * g.N4 >= lim / 4) return false;
-    if ((int64_t)g.Kh * g.Kw * (g.Cin4 > g.Cout4 ? g.Cin4 : g.Cout4) >= lim / 4) return false;
+    if (mul3_sat(g.H, g.W, g.N4) >= lim / 4 || mul3_sat(g.Ho, g.Wo, g.N4) >= lim / 4) return false;
+    if (mul3_sat(g.Kh, g.Kw, g.Cin4 > g.Cout4 ? g.Cin4 : g.Cout4) >= lim / 4) return false;
     return true;
 }
 
@@ -169,8 +187,8 @@ mq_status mq_quantize_nchw(const float *src, const mq_qtensor *dst, int32_t rnd,
     if (!amax_ws || amax_ws_bytes < MQ_QUANTIZE_WS_BYTES) return MQ_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(amax_ws) & 3u) != 0) return MQ_ERR_ARG;
     // zero-padded source (4*ceil(N/4) x 4*ceil(C/4) planes) below 2^31 bytes
-    const int64_t pad = 16 * (int64_t)((dst->s + 3) / 4) * ((dst->r + 3) / 4) * dst->o0 * dst->o1 * 4;
-    if (pad >= ((int64_t)1 << 31)) return MQ_ERR_UNSUPPORTED;
+    // zero-padded source: 16 floats per square
+    if (squares(dst->o0, dst->o1, dst->r, dst->s) >= ((int64_t)1 << 31) / 64) return MQ_ERR_UNSUPPORTED;
     return launch_status(mq::launch_quantize_nchw(src, dst->s, dst->r, dst->o0, dst->o1, dst->fmt,
                                                   rnd, seed, dst->codes, dst->scales, dst->tscale,
                                                   amax_ws, (flags & MQ_QUANTIZE_AMAX_READY) != 0,
@@ -199,8 +217,7 @@ mq_status mq_quantize_batch(const mq_quant_job *jobs, int32_t njobs, hipStream_t
             return MQ_ERR_SHAPE;
         if (squares(q->o0, q->o1, q->r, q->s) >= ((int64_t)1 << 31)) return MQ_ERR_UNSUPPORTED;
         if (j.layout == MQ_SRC_NCHW) {
-            const int64_t pad = 16 * (int64_t)((q->s + 3) / 4) * ((q->r + 3) / 4) * q->o0 * q->o1 * 4;
-            if (pad >= ((int64_t)1 << 31)) return MQ_ERR_UNSUPPORTED;
+            if (squares(q->o0, q->o1, q->r, q->s) >= ((int64_t)1 << 31) / 64) return MQ_ERR_UNSUPPORTED;
         }
         d[i].src = j.src;
         d[i].layout = j.layout == MQ_SRC_NCHW ? 1 : (j.layout == MQ_SRC_OIHW ? 2 : 0);
