@@ -64,10 +64,13 @@ OP_KERNELS = {
                    "void mq::conv_gemm_kernel", "mq::wgrad_reduce_kernel"],
     "conv_dgrad": ["void mq::conv_spatial_kernel<4, true", "void mq::conv_spatial_kernel<6, true",
                    "void mq::conv_gemm_kernel"],
+    "quantize_g_ready": ["void mq::quantize_kernel"],
 }
+OP_KERNELS["conv_fwd_amax"] = OP_KERNELS["conv_fwd"] + ["mq::amax_kernel"]
+OP_KERNELS["conv_backward_amax"] = OP_KERNELS["conv_backward"] + ["mq::amax_kernel"]
 STEP_OPS = ["quantize_xw", "quantize_g", "conv_fwd", "conv_backward"]
 INFERENCE_OPS = ["quantize_x", "conv_fwd"]
-PARTS = ["conv_wgrad", "conv_dgrad"]
+PARTS = ["conv_wgrad", "conv_dgrad", "conv_fwd_amax", "conv_backward_amax", "quantize_g_ready"]
 
 
 def parse(argv=None):
@@ -169,10 +172,14 @@ def layer_work(l):
         "quantize_xw": ("hbm", 8 * (nx + nw) + qx + qw, 8 * (nx + nw) + qx + qw),
         "quantize_x": ("hbm", 8 * nx + qx, 8 * nx + qx),
         "quantize_g": ("hbm", 8 * ng + qg, 8 * ng + qg),
+        # the amax comes from the producer's epilogue: one read of G_Y
+        "quantize_g_ready": ("hbm", 4 * ng + qg, 4 * ng + qg),
         "conv_fwd": ("gemm", F, fwd_b),
         "conv_wgrad": ("gemm", F, wg_b),
         "conv_dgrad": ("gemm", F, dg_b),
         "conv_backward": ("gemm", 2 * F, wg_b + dg_b),
+        "conv_fwd_amax": ("gemm", F, fwd_b),
+        "conv_backward_amax": ("gemm", 2 * F, wg_b + dg_b),
     }
 
 

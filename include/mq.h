@@ -308,6 +308,39 @@ mq_status mq_conv_backward(const mq_conv *p, const mq_qtensor *w, const mq_qtens
                            size_t ws_bytes, hipStream_t stream);
 
 /*
+ * mq_conv_fwd_amax: mq_conv_fwd (same Y, bit for bit) whose epilogue also writes the tensor-amax
+ * partial maxima of |Y| into amax_ws_dev, in the format mq_quantize reads with
+ * MQ_QUANTIZE_AMAX_READY. When Y is the next tensor to be quantized (the next layer's activation
+ * with nothing elementwise in between), mq_quantize of Y (channel-batch-first, dense source)
+ * then skips its own read of Y: the tensor amax of the NVFP4 / NVFP6 recipe (onedev.kr digest,
+ * section "How it differs": T = max|X| / (448 * Emax)) comes from the producer of the tensor.
+ * The workgroups of the tuned kernels each write one partial; other shapes run the amax pass over
+ * Y after the convolution (same partials format, same result).
+ * amax_ws_dev / amax_ws_bytes: a tensor-amax workspace (MQ_QUANTIZE_WS_BYTES, 4-byte aligned),
+ *          overwritten; pass it to mq_quantize of Y with MQ_QUANTIZE_AMAX_READY, later on the same
+ *          stream.
+ * Errors: as mq_conv_fwd; MQ_ERR_WORKSPACE (workspace null or below MQ_QUANTIZE_WS_BYTES),
+ *         MQ_ERR_ARG (misaligned workspace).
+ */
+mq_status mq_conv_fwd_amax(const mq_conv *p, const mq_qtensor *x, const mq_qtensor *w,
+                           float *y_dev, uint32_t *amax_ws_dev, size_t amax_ws_bytes,
+                           hipStream_t stream);
+
+/*
+ * mq_conv_backward_amax: mq_conv_backward (same G_W and G_X, bit for bit) whose input-gradient
+ * epilogue also writes the tensor-amax partial maxima of |G_X| into gx_amax_ws_dev (format as for
+ * mq_conv_fwd_amax). G_X is the output gradient of the layer before when nothing elementwise sits
+ * between, so its stochastic quantization (mq_quantize, MQ_QUANTIZE_AMAX_READY) skips its amax
+ * pass.
+ * gx_amax_ws_dev / gx_amax_ws_bytes: a tensor-amax workspace, overwritten.
+ * Errors: as mq_conv_backward; MQ_ERR_WORKSPACE / MQ_ERR_ARG for the amax workspace as above.
+ */
+mq_status mq_conv_backward_amax(const mq_conv *p, const mq_qtensor *w, const mq_qtensor *gy,
+                                const mq_qtensor *x, float *gw_dev, float *gx_dev, void *ws_dev,
+                                size_t ws_bytes, uint32_t *gx_amax_ws_dev, size_t gx_amax_ws_bytes,
+                                hipStream_t stream);
+
+/*
  * Size of the device array that mq_conv_backward_noalloc keeps the weight gradient's split-K
  * partial sums in (one array per GPU, held until the process ends).
  */

@@ -32,6 +32,7 @@ EXPORTS = (
     "mq_quantize_weight", "mq_conv_fwd",
     "mq_wgrad_workspace_bytes",
     "mq_conv_wgrad", "mq_conv_dgrad", "mq_conv_backward", "mq_conv_backward_noalloc",
+    "mq_conv_fwd_amax", "mq_conv_backward_amax",
 )
 
 
@@ -92,6 +93,11 @@ def _load() -> ctypes.CDLL:
     L.mq_conv_backward_noalloc.argtypes = [ctypes.POINTER(mq_conv), ctypes.POINTER(mq_qtensor),
                                            ctypes.POINTER(mq_qtensor), ctypes.POINTER(mq_qtensor),
                                            P, P, P]
+    L.mq_conv_fwd_amax.argtypes = [ctypes.POINTER(mq_conv), ctypes.POINTER(mq_qtensor),
+                                   ctypes.POINTER(mq_qtensor), P, P, sz, P]
+    L.mq_conv_backward_amax.argtypes = [ctypes.POINTER(mq_conv), ctypes.POINTER(mq_qtensor),
+                                        ctypes.POINTER(mq_qtensor), ctypes.POINTER(mq_qtensor),
+                                        P, P, P, sz, P, sz, P]
     for name in EXPORTS:
         getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int
     return L
@@ -263,6 +269,26 @@ def mq_conv_backward_noalloc(p: ConvLike, w: QTensor, gy: QTensor, x: QTensor,
     _check(_lib.mq_conv_backward_noalloc(ctypes.byref(c), ctypes.byref(qw), ctypes.byref(qg),
                                          ctypes.byref(qx), _ptr(gw), _ptr(gx), _stream(stream)),
            "mq_conv_backward_noalloc")
+
+
+def mq_conv_fwd_amax(p: ConvLike, x: QTensor, w: QTensor, y: torch.Tensor,
+                     amax_ws: torch.Tensor, stream=None):
+    """mq_conv_fwd, plus the partial maxima of |Y| in amax_ws (for MQ_QUANTIZE_AMAX_READY)."""
+    c, qx, qw = conv_struct(p), x.struct(), w.struct()
+    _check(_lib.mq_conv_fwd_amax(ctypes.byref(c), ctypes.byref(qx), ctypes.byref(qw), _ptr(y),
+                                 _ptr(amax_ws), _nbytes(amax_ws), _stream(stream)),
+           "mq_conv_fwd_amax")
+
+
+def mq_conv_backward_amax(p: ConvLike, w: QTensor, gy: QTensor, x: QTensor, gw: torch.Tensor,
+                          gx: torch.Tensor, ws: torch.Tensor, gx_amax_ws: torch.Tensor,
+                          stream=None):
+    """mq_conv_backward, plus the partial maxima of |G_X| in gx_amax_ws."""
+    c, qw, qg, qx = conv_struct(p), w.struct(), gy.struct(), x.struct()
+    _check(_lib.mq_conv_backward_amax(ctypes.byref(c), ctypes.byref(qw), ctypes.byref(qg),
+                                      ctypes.byref(qx), _ptr(gw), _ptr(gx), _ptr(ws), _nbytes(ws),
+                                      _ptr(gx_amax_ws), _nbytes(gx_amax_ws), _stream(stream)),
+           "mq_conv_backward_amax")
 
 
 def out_hw(p: ConvLike) -> Tuple[int, int]:

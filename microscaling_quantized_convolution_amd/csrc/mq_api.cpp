@@ -322,4 +322,51 @@ mq_status mq_conv_backward(const mq_conv *p, const mq_qtensor *w, const mq_qtens
     return mq_conv_dgrad(p, w, gy, gx, stream);
 }
 
+mq_status mq_conv_fwd_amax(const mq_conv *p, const mq_qtensor *x, const mq_qtensor *w, float *y,
+                           uint32_t *amax_ws, size_t amax_ws_bytes, hipStream_t stream)
+{
+    if (!amax_ws) return MQ_ERR_WORKSPACE;
+    const mq_status wst = amax_ws_check(amax_ws, amax_ws_bytes);
+    if (wst != MQ_OK) return wst;
+    mq::ConvGeom g;
+    if (!conv_geom(p, &g) || !qtensor_ok(x) || !qtensor_ok(w) || !y) return MQ_ERR_ARG;
+    if (!dims_are(x, p->H, p->W, p->Cin, p->N, MQ_ROLE_ACT) ||
+        !dims_are(w, p->Kh, p->Kw, p->Cout, p->Cin, MQ_ROLE_WEIGHT) || x->fmt != w->fmt)
+        return MQ_ERR_SHAPE;
+    if (!conv_supported(g)) return MQ_ERR_UNSUPPORTED;
+    if (mq::spatial_supported(g))
+        return launch_status(
+            mq::launch_conv_fwd_spatial(g, x->fmt, operand(x), operand(w), y, stream, amax_ws));
+    const hipError_t e = mq::launch_conv_fwd(g, x->fmt, operand(x), operand(w), y, stream);
+    if (e != hipSuccess) return launch_status(e);
+    return launch_status(
+        mq::launch_amax(y, (int64_t)g.Ho * g.Wo * g.Cout * g.N, amax_ws, stream));
+}
+
+mq_status mq_conv_backward_amax(const mq_conv *p, const mq_qtensor *w, const mq_qtensor *gy,
+                                const mq_qtensor *x, float *gw, float *gx, void *ws,
+                                size_t ws_bytes, uint32_t *gx_amax_ws, size_t gx_amax_ws_bytes,
+                                hipStream_t stream)
+{
+    if (!gx_amax_ws) return MQ_ERR_WORKSPACE;
+    const mq_status wst = amax_ws_check(gx_amax_ws, gx_amax_ws_bytes);
+    if (wst != MQ_OK) return wst;
+    const mq_status chk = mq::backward_check(p, w, gy, x, gw, gx);
+    if (chk != MQ_OK) return chk;
+    mq::ConvGeom g;
+    conv_geom(p, &g);
+    if (mq::wgrad_fast_supported(g) && mq::spatial_supported(g)) {
+        if (!ws || ws_bytes < mq::wgrad_fast_workspace_bytes(g)) return MQ_ERR_WORKSPACE;
+        mq::WgradSum sum;
+        const hipError_t e = mq::launch_conv_wgrad_partials(g, x->fmt, operand(gy), operand(x),
+                                                            gw, ws, ws_bytes, stream, &sum);
+        if (e != hipSuccess) return launch_status(e);
+        return launch_status(mq::launch_conv_dgrad_spatial(g, w->fmt, operand(w), operand(gy),
+                                                           gx, stream, &sum, gx_amax_ws));
+    }
+    const mq_status st = mq_conv_backward(p, w, gy, x, gw, gx, ws, ws_bytes, stream);
+    if (st != MQ_OK) return st;
+    return launch_status(mq::launch_amax(gx, (int64_t)g.H * g.W * g.Cin * g.N, gx_amax_ws, stream));
+}
+
 } // extern "C"

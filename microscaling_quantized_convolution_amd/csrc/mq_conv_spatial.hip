@@ -38,6 +38,7 @@ struct SpatialClass {
     // the items' mixed radix, and multipliers m with n / d = mulhi(n, m) for the divisors nblk,
     // tiles_w, tiles_h and P (exact for n * d < 2^32; m = 0 stands for d = 1).
     int tiles_h, T;
+    int amax_base;       // first output-amax partial of this class's workgroups
     int step_nb, step_tj, step_ti, step_mb;
     uint32_t m_nblk, m_tw, m_th, m_P;
 };
@@ -65,6 +66,12 @@ struct SpatialArgs {
     int nclass;           // grid rows 0 .. nclass-1: convolution classes
     int sum_P;            // grid row nclass (if sum_P > 0): workgroups of the weight-gradient sum
     WgradSum sum;
+    // Optional output amax (null = none): every convolution workgroup writes max |out| over the
+    // outputs it wrote to amax_ws[1 + cls.amax_base + b]; workgroup 0 of class 0 writes the count
+    // of partials, amax_parts, to amax_ws[0] (the tensor-amax workspace format the quantizer
+    // reads with MQ_QUANTIZE_AMAX_READY).
+    uint32_t *amax_ws;
+    int amax_parts;
     SpatialClass cls[4];
 };
 
@@ -331,6 +338,7 @@ conv_spatial_kernel(SpatialArgs a)
             __syncthreads();
         }
         if (gs < G) __syncthreads(); // last chunk: nothing left to decode
+        if (a.amax_ws) __syncthreads(); // the consumers' output-amax reduction
         return;
     }
 
@@ -349,6 +357,11 @@ conv_spatial_kernel(SpatialArgs a)
     const bool fsafe = scale_is_float_safe(sd);
     const float sf = (float)sd;
     const rsrc_t out_r = make_rsrc(a.out, a.out_bytes);
+    // max |accumulator| over this lane's outputs, as bit patterns (a NaN sorts above every
+    // number): scaled once at the end, which gives max |out| exactly (rounding the product with
+    // the non-negative scale is monotonic). Padded rows and batch columns hold exact zeros, so
+    // only whole pixels outside the output are left out.
+    uint32_t amx = 0u;
     __syncthreads();
     int gc = 0; // chunk of the stream: LDS buffer gc & 1
     ItemPos cp = first;
@@ -406,7 +419,15 @@ conv_spatial_kernel(SpatialArgs a)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int jj = j0 + wp * 4 + j;
-            const bool pix_ok = i < cl.OHs && jj < cl.OWs && n < a.N;
+            const bool pix_in = i < cl.OHs && jj < cl.OWs; // the same for the whole wave
+            const bool pix_ok = pix_in && n < a.N;
+            if (a.amax_ws && pix_in) {
+#pragma unroll
+                for (int u = 0; u < MW; ++u)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        amx = max(amx, __float_as_uint(acc[u][j][r]) & 0x7FFFFFFFu);
+            }
             const int oh = i * a.sO + cl.ah, ow = jj * a.sO + cl.aw;
 #pragma unroll
             for (int u = 0; u < MW; ++u) {
@@ -424,6 +445,24 @@ conv_spatial_kernel(SpatialArgs a)
                                                           (int)voff, dm * a.N * 4, kStoreNT);
                 }
             }
+        }
+    }
+    if (a.amax_ws) {
+        // this workgroup's partial: the waves' maxima meet in LDS (the producers pass the same
+        // barrier), scaled as the outputs were
+        __shared__ uint32_t amx_red[NCW];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) amx = max(amx, (uint32_t)__shfl_xor((int)amx, off, 64));
+        if (lane == 0) amx_red[wave] = amx;
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t m = amx_red[0];
+#pragma unroll
+            for (int w = 1; w < NCW; ++w) m = max(m, amx_red[w]);
+            const float am = __uint_as_float(m);
+            const float sc = fsafe ? am * sf : (float)((double)am * sd);
+            a.amax_ws[1 + cl.amax_base + b] = __float_as_uint(sc) & 0x7FFFFFFFu;
+            if (blockIdx.y == 0 && b == 0) a.amax_ws[0] = (uint32_t)a.amax_parts;
         }
     }
 }
@@ -530,6 +569,23 @@ static hipError_t launch_spatial_tiles(SpatialArgs &a, int nclass, hipStream_t s
         conv_wgs += P;
     }
     a.nclass = nclass;
+    // output amax: one partial per convolution workgroup, at most kAmaxParts of them (launches
+    // here run fewer than 1024 workgroups; a larger one takes the amax pass over the output)
+    bool amax_after = false;
+    uint32_t *const amax_req = a.amax_ws;
+    if (a.amax_ws) {
+        int base = 0;
+        for (int c = 0; c < nclass; ++c) {
+            a.cls[c].amax_base = base;
+            base += a.cls[c].P;
+        }
+        a.amax_parts = base;
+        if (base > kAmaxParts || base < 1) {
+            amax_after = true;
+            a.amax_ws = nullptr;
+        }
+    }
+    uint32_t *const amax_ws_after = amax_after ? amax_req : nullptr;
     if (a.sum_P < 0) {
         // The weight-gradient sum: on the CUs this launch leaves idle (one workgroup per CU:
         // the LDS), or, when it fills them, on 256 workgroups after its own. A workgroup sums
@@ -548,7 +604,8 @@ static hipError_t launch_spatial_tiles(SpatialArgs &a, int nclass, hipStream_t s
         }
     }
     nwg = a.sum_P > nwg ? a.sum_P : nwg;
-    if (nwg == 0) return hipSuccess;
+    if (nwg == 0) return amax_ws_after ? launch_amax(a.out, a.out_bytes / 4, amax_ws_after, st)
+                                       : hipSuccess;
     dim3 grid((unsigned)nwg, (unsigned)(nclass + (a.sum_P > 0 ? 1 : 0)), 1);
     const bool full3 = nclass == 1 && a.cls[0].kh == 3 && a.cls[0].kw == 3;
 #define MQ_SPATIAL_LAUNCH(KFV, PV)                                                              \
@@ -559,7 +616,9 @@ static hipError_t launch_spatial_tiles(SpatialArgs &a, int nclass, hipStream_t s
     else if (persist) MQ_SPATIAL_LAUNCH(0, true);
     else MQ_SPATIAL_LAUNCH(0, false);
 #undef MQ_SPATIAL_LAUNCH
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !amax_ws_after) return e;
+    return launch_amax(a.out, a.out_bytes / 4, amax_ws_after, st);
 }
 
 // Work items of either tile shape: the launch runs at most 256 workgroups (one per CU, their
@@ -590,9 +649,10 @@ static hipError_t launch_spatial(SpatialArgs &a, int nclass, hipStream_t st)
 }
 
 hipError_t launch_conv_fwd_spatial(const ConvGeom &g, int fmt, QOperand x, QOperand w, float *y,
-                                   hipStream_t st)
+                                   hipStream_t st, uint32_t *amax_ws)
 {
     SpatialArgs a = {};
+    a.amax_ws = amax_ws;
     a.in_codes = x.codes; a.in_scales = x.scales; a.in_T = x.tscale;
     a.IH = g.H; a.IW = g.W; a.K4 = g.Cin4; a.N4 = g.N4;
     a.w_codes = w.codes; a.w_scales = w.scales; a.w_T = w.tscale;
@@ -628,9 +688,11 @@ static void dgrad_class_dim(int a, int pad, int K, int s, int &cnt, int &r0, int
 }
 
 hipError_t launch_conv_dgrad_spatial(const ConvGeom &g, int fmt, QOperand w, QOperand gy,
-                                     float *gx, hipStream_t st, const WgradSum *sum)
+                                     float *gx, hipStream_t st, const WgradSum *sum,
+                                     uint32_t *amax_ws)
 {
     SpatialArgs a = {};
+    a.amax_ws = amax_ws;
     if (sum && sum->total > 0) {
         a.sum = *sum;
         a.sum_P = -1; // sized by the launch

@@ -82,11 +82,17 @@ struct WgradSum;
 // Halo-tiled forward / input-gradient kernels (Kh, Kw <= 3, equal strides 1 or 2).
 // launch_conv_dgrad_spatial with a sum: the weight gradient's split sum runs in the same launch,
 // on workgroups of its own (a grid row after the input-gradient classes).
+// amax_ws (null = none): a tensor-amax workspace that receives the partial maxima of |output|,
+// written by the kernel's epilogue (or by the amax pass over the output when the launch has more
+// workgroups than partials), so that quantizing the output can pass MQ_QUANTIZE_AMAX_READY.
 bool spatial_supported(const ConvGeom &g);
 hipError_t launch_conv_fwd_spatial(const ConvGeom &g, int fmt, QOperand x, QOperand w, float *y,
-                                   hipStream_t st);
+                                   hipStream_t st, uint32_t *amax_ws = nullptr);
 hipError_t launch_conv_dgrad_spatial(const ConvGeom &g, int fmt, QOperand w, QOperand gy,
-                                     float *gx, hipStream_t st, const struct WgradSum *sum = nullptr);
+                                     float *gx, hipStream_t st, const struct WgradSum *sum = nullptr,
+                                     uint32_t *amax_ws = nullptr);
+// The tensor-amax pass over n floats: partial maxima of |x| into ws (count in ws[0]).
+hipError_t launch_amax(const float *x, int64_t n, uint32_t *ws, hipStream_t st);
 
 // Split-K weight gradient with all kw taps of one kernel row per workgroup (Kw <= 3,
 // equal strides 1 or 2) and a deterministic split sum.

@@ -103,6 +103,12 @@ inline int amax_parts(int64_t n)
     return (int)(want < 1 ? 1 : (want > kAmaxParts ? kAmaxParts : want));
 }
 
+hipError_t launch_amax(const float *x, int64_t n, uint32_t *ws, hipStream_t st)
+{
+    hipLaunchKernelGGL(amax_kernel, dim3((unsigned)amax_parts(n)), dim3(kAmaxThreads), 0, st, x, n, ws);
+    return hipGetLastError();
+}
+
 struct QuantArgs {
     const float *src;
     uint8_t *codes;

@@ -11,7 +11,10 @@ tensors, the outputs and the weight-gradient workspace) and the calls of one pas
                gradient's split sum rides in the input-gradient launch)
 
 conv_wgrad and conv_dgrad, the two gradients as calls of their own, stay available in
-`parts` (same results, bit for bit).
+`parts` (same results, bit for bit), next to the variants that hand the next quantization its
+tensor amax: conv_fwd_amax and conv_backward_amax write the partial maxima of Y and G_X from
+their epilogues, and quantize_g_ready quantizes G_Y from partial maxima already in its workspace
+(as a producer's epilogue would leave them; the pass's own quantize_g writes them there).
 
 X and W are quantized together, as a layer's forward pass does (mq_quantize_batch: one amax
 launch over both, then one launch that reads X in NCHW and W in OIHW order and writes their
@@ -28,9 +31,10 @@ from typing import Callable, Dict
 
 import torch
 
-from . import (MQ_QUANTIZE_WS_BYTES, MQ_ROLE_ACT, MQ_ROLE_GRAD, MQ_ROLE_WEIGHT, MQ_RNE, MQ_SR,
-               MQ_SRC_NCHW, MQ_SRC_OIHW, QTensor, conv_struct, mq_conv_backward, mq_conv_dgrad,
-               mq_conv_fwd, mq_conv_wgrad, mq_quant_job, mq_quantize, mq_quantize_batch,
+from . import (MQ_QUANTIZE_AMAX_READY, MQ_QUANTIZE_WS_BYTES, MQ_ROLE_ACT, MQ_ROLE_GRAD,
+               MQ_ROLE_WEIGHT, MQ_RNE, MQ_SR, MQ_SRC_NCHW, MQ_SRC_OIHW, QTensor, conv_struct,
+               mq_conv_backward, mq_conv_backward_amax, mq_conv_dgrad, mq_conv_fwd,
+               mq_conv_fwd_amax, mq_conv_wgrad, mq_quant_job, mq_quantize, mq_quantize_batch,
                mq_wgrad_workspace_bytes, out_hw, quant_job)
 
 
@@ -50,7 +54,8 @@ class LayerStep:
         self.x, self.w, self.gc = x, w, g_cbf
         f32 = dict(dtype=torch.float32, device=dev)
         nws = MQ_QUANTIZE_WS_BYTES
-        self.amax = torch.empty(3 * nws, dtype=torch.uint8, device=dev)
+        # amax workspaces: X, W, G_Y, and the epilogue partials of Y and G_X
+        self.amax = torch.empty(5 * nws, dtype=torch.uint8, device=dev)
         self.qx = QTensor(c.H, c.W, c.Cin, c.N, fmt, MQ_ROLE_ACT, dev)
         self.qw = QTensor(c.Kh, c.Kw, c.Cout, c.Cin, fmt, MQ_ROLE_WEIGHT, dev)
         self.qg = QTensor(Ho, Wo, c.Cout, c.N, fmt, MQ_ROLE_GRAD, dev)
@@ -59,7 +64,7 @@ class LayerStep:
         self.gx = torch.empty(c.H * c.W * c.Cin * c.N, **f32)
         self.ws = torch.empty(max(1, mq_wgrad_workspace_bytes(self.p)), dtype=torch.uint8,
                               device=dev)
-        a0, a1, a2 = (self.amax[i * nws:(i + 1) * nws] for i in range(3))
+        a0, a1, a2, a3, a4 = (self.amax[i * nws:(i + 1) * nws] for i in range(5))
         self._a0 = a0
         p = self.p
         self.xw_jobs = [quant_job(self.x, MQ_SRC_NCHW, self.qx, MQ_RNE, 0, a0),
@@ -74,6 +79,11 @@ class LayerStep:
         self.parts: Dict[str, Callable[[int], None]] = OrderedDict([
             ("conv_wgrad", lambda s: mq_conv_wgrad(p, self.qg, self.qx, self.gw, self.ws)),
             ("conv_dgrad", lambda s: mq_conv_dgrad(p, self.qw, self.qg, self.gx)),
+            ("conv_fwd_amax", lambda s: mq_conv_fwd_amax(p, self.qx, self.qw, self.y, a3)),
+            ("conv_backward_amax", lambda s: mq_conv_backward_amax(
+                p, self.qw, self.qg, self.qx, self.gw, self.gx, self.ws, a4)),
+            ("quantize_g_ready", lambda s: mq_quantize(self.gc, self.qg, MQ_SR, self.seed(s), a2,
+                                                       MQ_QUANTIZE_AMAX_READY)),
         ])
 
     def seed(self, s: int) -> int:
@@ -98,7 +108,7 @@ class LayerStep:
         qx, qw, qg = self.qx.struct(), self.qw.struct(), self.qg.struct()
         self._keep = (qx, qw, qg, conv)
         bx, bw, bg = ctypes.byref(qx), ctypes.byref(qw), ctypes.byref(qg)
-        a = [ctypes.c_void_p(self.amax.data_ptr() + MQ_QUANTIZE_WS_BYTES * i) for i in range(3)]
+        a = [ctypes.c_void_p(self.amax.data_ptr() + MQ_QUANTIZE_WS_BYTES * i) for i in range(5)]
         wsb = MQ_QUANTIZE_WS_BYTES
         nws = self.ws.numel()
         L = _lib
@@ -116,13 +126,18 @@ class LayerStep:
                                                    P(self.ws), nws, hs)),
             "conv_wgrad": (L.mq_conv_wgrad, (conv, bg, bx, P(self.gw), P(self.ws), nws, hs)),
             "conv_dgrad": (L.mq_conv_dgrad, (conv, bw, bg, P(self.gx), hs)),
+            "conv_fwd_amax": (L.mq_conv_fwd_amax, (conv, bx, bw, P(self.y), a[3], wsb, hs)),
+            "conv_backward_amax": (L.mq_conv_backward_amax, (conv, bw, bg, bx, P(self.gw),
+                                                             P(self.gx), P(self.ws), nws, a[4],
+                                                             wsb, hs)),
         }
         out: Dict[str, Callable[[int], None]] = OrderedDict()
         for name in list(self.ops) + list(self.parts):
-            if name == "quantize_g":
+            if name in ("quantize_g", "quantize_g_ready"):
                 gsrc = P(self.gc)
-                out[name] = lambda s, f=L.mq_quantize, g=gsrc: chk(
-                    f(g, bg, MQ_SR, self.seed(s), a[2], wsb, 0, hs),
+                fl = MQ_QUANTIZE_AMAX_READY if name == "quantize_g_ready" else 0
+                out[name] = lambda s, f=L.mq_quantize, g=gsrc, fl=fl: chk(
+                    f(g, bg, MQ_SR, self.seed(s), a[2], wsb, fl, hs),
                     "mq_quantize")
             else:
                 f, args = fixed[name]

@@ -33,8 +33,9 @@ hipError_t launch_conv_fwd(const ConvGeom &, int, QOperand, QOperand, float *, h
 hipError_t launch_conv_wgrad(const ConvGeom &, int, QOperand, QOperand, float *, void *, size_t, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_conv_dgrad(const ConvGeom &, int, QOperand, QOperand, float *, hipStream_t) { ++g_launches; return hipSuccess; }
 bool spatial_supported(const ConvGeom &g) { return g.Kh <= 3 && g.Kw <= 3 && g.sh == g.sw; }
-hipError_t launch_conv_fwd_spatial(const ConvGeom &, int, QOperand, QOperand, float *, hipStream_t) { ++g_launches; return hipSuccess; }
-hipError_t launch_conv_dgrad_spatial(const ConvGeom &, int, QOperand, QOperand, float *, hipStream_t, const WgradSum *) { ++g_launches; return hipSuccess; }
+hipError_t launch_conv_fwd_spatial(const ConvGeom &, int, QOperand, QOperand, float *, hipStream_t, uint32_t *) { ++g_launches; return hipSuccess; }
+hipError_t launch_conv_dgrad_spatial(const ConvGeom &, int, QOperand, QOperand, float *, hipStream_t, const WgradSum *, uint32_t *) { ++g_launches; return hipSuccess; }
+hipError_t launch_amax(const float *, int64_t, uint32_t *, hipStream_t) { ++g_launches; return hipSuccess; }
 bool wgrad_fast_supported(const ConvGeom &g) { return g.Kw <= 3 && g.sh == g.sw; }
 size_t wgrad_fast_workspace_bytes(const ConvGeom &) { return 8192; }
 hipError_t launch_conv_wgrad_fast(const ConvGeom &, int, QOperand, QOperand, float *, void *, size_t, hipStream_t) { ++g_launches; return hipSuccess; }
@@ -146,6 +147,18 @@ int main()
     EXPECT(mq_conv_wgrad(&c, &g, &x, f, ws, need - 1, s0), MQ_ERR_WORKSPACE);
     EXPECT(mq_conv_backward(&c, &w, &g, &x, f, f, ws, need, s0), MQ_OK);
     EXPECT(mq_conv_backward(nullptr, &w, &g, &x, f, f, ws, need, s0), MQ_ERR_ARG);
+    EXPECT(mq_conv_fwd_amax(&c, &x, &w, f, ws, wsb, s0), MQ_OK);
+    EXPECT(mq_conv_fwd_amax(&c, &x, &w, f, nullptr, wsb, s0), MQ_ERR_WORKSPACE);
+    EXPECT(mq_conv_fwd_amax(&c, &x, &w, f, ws, wsb - 4, s0), MQ_ERR_WORKSPACE);
+    EXPECT(mq_conv_fwd_amax(&c, &x, &w, f, ws + 1, wsb, s0), MQ_OK); // 4-byte aligned
+    EXPECT(mq_conv_fwd_amax(&c, &x, &w, f, reinterpret_cast<uint32_t *>(0x30002), wsb, s0), MQ_ERR_ARG);
+    EXPECT(mq_conv_backward_amax(&c, &w, &g, &x, f, f, ws, need, ws, wsb, s0), MQ_OK);
+    EXPECT(mq_conv_backward_amax(&c, &w, &g, &x, f, f, ws, need, nullptr, wsb, s0), MQ_ERR_WORKSPACE);
+    EXPECT(mq_conv_backward_amax(&c, &x, &g, &x, f, f, ws, need, ws, wsb, s0), MQ_ERR_SHAPE);
+    mq_conv c5 = {2, 16, 8, 8, 16, 5, 5, 1, 1, 2, 2}; // generic kernels: the amax pass after
+    mq_qtensor w5 = qt(5, 5, 16, 16, MQ_NVFP4, MQ_ROLE_WEIGHT), g5 = qt(8, 8, 16, 2, MQ_NVFP4, MQ_ROLE_GRAD);
+    EXPECT(mq_conv_fwd_amax(&c5, &x, &w5, f, ws, wsb, s0), MQ_OK);
+    EXPECT(mq_conv_backward_amax(&c5, &w5, &g5, &x, f, f, ws, 1 << 20, ws, wsb, s0), MQ_OK);
     for (int a : big)
         for (int b : big) {
             mq_conv e = {a, b, a, 7, b, 3, a, 1, b, 0, a};
