@@ -14,11 +14,16 @@
 //                       convolution with the kernel rows kh = ah + pad - 2*(r0 + kh') (no MFMA
 //                       work is spent on the zeros a transposed convolution would insert).
 //
-// A workgroup owns 64 rows (m) x PH x PW output pixels x 32 batch elements. Per 16-channel chunk
+// A workgroup owns 64 rows (m) x PH x PW output pixels x NB batch elements. Per 16-channel chunk
 // it decodes the weight taps and the input halo ((PH-1)*SI + Kh rows x (PW-1)*SI + Kw columns)
-// once into LDS as fp16 and every wave runs 32x32x16 fp16 MFMAs for its 64 x 4-pixel tile over
-// all taps; the halo is read once per chunk and reused by every tap, and the weight tile by
-// every pixel. The im2col matrix never exists outside registers.
+// once into LDS as fp16 and every wave runs 32x32x16 fp16 MFMAs over all taps; the halo is read
+// once per chunk and reused by every tap, and the weight tile by every pixel. The im2col matrix
+// never exists outside registers. NB = 32: an MFMA's 32 columns are 32 batch elements of one
+// pixel (a wave owns 64 x 4 pixels). NB = 16, for batches of at most 16: its columns are 16 batch
+// elements of each of two neighbouring pixels (a wave owns 64 x 8 pixels), so a small batch
+// fills the matrix core instead of padding half of every MFMA and every output store. Row
+// blocks of 32 that lie wholly past the output channels (a layer with 16 or 32 of them) skip
+// their MFMAs and stores.
 #include "mq_kernels.hpp"
 #include "mq_stage.hpp"
 #include "mq_wgrad_sum.hpp"
@@ -42,6 +47,17 @@ struct SpatialClass {
     int step_nb, step_tj, step_ti, step_mb;
     uint32_t m_nblk, m_tw, m_th, m_P;
 };
+
+// A compile-time count passed to a generic lambda.
+template <int V> struct IntC { static constexpr int value = V; };
+
+// LDS offset of row P*16 + r for a halo laid out in 16-row pixel slots (NB = 16), from
+// lane_off16 = lds_row_off(r, chunk), r < 16: the swizzle of lds_row_off takes bits 2 and 3 of
+// the row from r and bits 4-6 from P.
+__device__ __forceinline__ int lds_row_off16(int P, int lane_off16)
+{
+    return (P << 9) + (lane_off16 ^ (((P << 4) & 32) | (((P ^ (P >> 2)) & 1) << 6)));
+}
 
 // n / d for the multiplier m of d (see SpatialClass).
 __device__ __forceinline__ int div_by(int n, uint32_t m)
@@ -90,22 +106,28 @@ struct SpatialArgs {
 // class's sub-kernel extent is read at run time.
 // MW: 32-row blocks per consumer wave (2: a wave owns all 64 rows of 4 pixels; 1: two waves
 // share 4 pixels, 32 rows each, so that small pixel tiles still give four MFMA waves).
-template <int FMT, bool A_KR, int SI, int PH, int PW, int MW, int PF, int KF, bool PERSIST>
-__global__ void __launch_bounds__(32 * PH * PW * (2 / MW) * (1 + PF) / 2)
+// NB: batch elements per item (32, or 16 with two pixels per MFMA; see above).
+template <int FMT, bool A_KR, int SI, int PH, int PW, int MW, int NB, int PF, int KF, bool PERSIST>
+__global__ void __launch_bounds__(64 * (PH * PW / (NB == 32 ? 4 : 8)) * (2 / MW) * (1 + PF))
 conv_spatial_kernel(SpatialArgs a)
 {
     warm_kernel_args<SpatialArgs>();
-    constexpr int NCW = PH * PW / 4 * (2 / MW); // consumer waves (4 pixels x 32*MW rows each)
+    static_assert(NB == 32 || NB == 16, "batch block of 32 or 16");
+    constexpr int PPW = NB == 32 ? 4 : 8;      // output pixels per consumer wave
+    constexpr int NCW = PH * PW / PPW * (2 / MW); // consumer waves (PPW pixels x 32*MW rows each)
     constexpr int NCT = 64 * NCW;               // consumer threads
     constexpr int NP = NCT * PF;                // producer threads
     constexpr int THREADS_OF = NCT + NP;
     constexpr int KHM = 3, KWM = 3;
     constexpr int HRM = (PH - 1) * SI + KHM, HCM = (PW - 1) * SI + KWM;
-    constexpr int WCOLS = 3 * SI + KWM; // halo columns one wave touches (4 pixels)
-    constexpr int ABYTES = KHM * KWM * 64 * 32, BBYTES = HRM * HCM * 32 * 32;
+    // halo columns whose operands one wave reads per kernel row: the MFMA over pixels (j, j + 1)
+    // of an NB = 16 wave reads column 2j*SI + tw in its lanes 0-15 and that plus SI in 16-31
+    constexpr int WCOLS = (NB == 32 ? 3 : 6) * SI + KWM;
+    constexpr int HPI = NB / 4; // halo items per pixel: 4 channel squares x NB / 16 batch groups
+    constexpr int ABYTES = KHM * KWM * 64 * 32, BBYTES = HRM * HCM * NB * 32;
     // items: weight (tap, m4) in [0, nA), halo (pixel, n4) in [nA64, nA64 + nB); nA64 rounds nA
     // up to whole waves so that no wave runs both item kinds in one slot
-    constexpr int ITEMS = ((KHM * KWM * 16 + 63) / 64 * 64 + HRM * HCM * 8 + NP - 1) / NP;
+    constexpr int ITEMS = ((KHM * KWM * 16 + 63) / 64 * 64 + HRM * HCM * HPI + NP - 1) / NP;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][ABYTES + BBYTES];
 
     // Grid (workgroups of the largest class, classes): workgroup (b, z) is number b of class z,
@@ -182,7 +204,7 @@ conv_spatial_kernel(SpatialArgs a)
     if (wave >= NCW) {
         // ================= producer =================
         const int ptid = tid - NCT;
-        const int nA = ntap * 16, nA64 = (nA + 63) & ~63, nAB = nA64 + HR * HC * 8;
+        const int nA = ntap * 16, nA64 = (nA + 63) & ~63, nAB = nA64 + HR * HC * HPI;
         constexpr int CB = (FMT == kFP4) ? 8 : 12;
         const uint32_t in_sq = (uint32_t)a.IH * a.IW * a.K4 * a.N4;
         const uint32_t w_sq = (uint32_t)a.Kh * a.Kw * a.Cout4 * a.Cin4;
@@ -222,13 +244,14 @@ conv_spatial_kernel(SpatialArgs a)
                     row[q] = t * 64 + 4 * (it & 15);
                 }
             } else if (wit < nAB) {
-                const int j = it - nA64, hp = j >> 3, g = j & 1, kcl = (j >> 1) & 3;
+                const int j = it - nA64, hp = j / HPI;
+                const int g = NB == 32 ? (j & 1) : 0, kcl = NB == 32 ? ((j >> 1) & 3) : (j & 3);
                 hrow[q] = hp / HC;
                 hcol[q] = hp - hrow[q] * HC;
                 off1[q] = 4 * g;
                 kcl_of[q] = kcl;
                 used[q] = it < nAB;
-                row[q] = hp * 32 + 16 * g;
+                row[q] = hp * NB + 16 * g;
             }
         }
         // Two register stages: chunk g + 3 of the stream is loaded into the slot chunk g + 1 was
@@ -256,7 +279,7 @@ conv_spatial_kernel(SpatialArgs a)
                     vm[q] = (used[q] && left > 0) ? (left >= 4 ? 0xFu : (1u << left) - 1u) : 0u;
                 } else {
                     const int ih = ih0 + hrow[q], iw = iw0 + hcol[q];
-                    const int n4 = nb * 8 + off1[q];
+                    const int n4 = nb * (NB / 4) + off1[q];
                     const bool inside = used[q] && ih >= 0 && ih < a.IH && iw >= 0 && iw < a.IW;
                     const int left = a.N4 - n4;
                     sqb[q] = (((uint32_t)ih * a.IW + iw) * a.K4 + kcl_of[q]) * a.N4 + n4;
@@ -344,11 +367,14 @@ conv_spatial_kernel(SpatialArgs a)
 
     // ================= consumer =================
     // (the two roles take wave-uniform branches and pass the same number of barriers)
-    constexpr int WM = 2 / MW;                        // waves per 4-pixel group
+    constexpr int WM = 2 / MW;                        // waves per pixel group
     const int wm = wave % WM, wpix = wave / WM;       // row block, pixel group
-    const int wr = wpix / (PW / 4), wp = wpix % (PW / 4); // consumer pixel row, pixel group
+    const int wr = wpix / (PW / PPW), wp = wpix % (PW / PPW); // consumer pixel row, pixel group
     const int half = lane >> 5, l32 = lane & 31;
     const int loff = lds_row_off(l32, half);
+    // NB = 16: lanes 16-31 (and 48-63) take the second pixel of each MFMA's pair
+    const int h16 = l32 >> 4;
+    const int loff16 = lds_row_off(l32 & 15, half);
     // Epilogue of every item: scale by T_in * T_w and store fp32. Buffer stores: an element
     // outside the output gets an out-of-range offset and is dropped; the row offset of each
     // accumulator register is a wave-uniform constant passed as soffset. The stores of one item
@@ -374,52 +400,73 @@ conv_spatial_kernel(SpatialArgs a)
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[u][j][r] = 0.0f;
-        for (int c = 0; c < nchunk; ++c, ++gc) {
-            const uint8_t *As = lds[gc & 1], *Bs = lds[gc & 1] + ABYTES;
+        // Row blocks of this wave that hold output channels (wave-uniform): a block wholly past
+        // M runs no MFMAs. UN = row blocks computed.
+        const int rows_left = a.M - 4 * m4_0 - 32 * wm * MW;
+        auto chunks = [&](auto un) {
+            constexpr int UN = decltype(un)::value;
+            for (int c = 0; c < nchunk; ++c, ++gc) {
+                const uint8_t *As = lds[gc & 1], *Bs = lds[gc & 1] + ABYTES;
 #pragma unroll
-            for (int th = 0; th < KHM; ++th) {
-                if (th < kh) {
-                    const int hr = wr * SI + th;
-                    // every column of the wave's window is read (columns past the sub-kernel's
-                    // extent stay inside the LDS buffer and are never used)
-                    u32x4_t bf[WCOLS];
+                for (int th = 0; th < KHM; ++th) {
+                    if (UN > 0 && th < kh) {
+                        const int hr = wr * SI + th;
+                        // every column of the wave's window is read (columns past the
+                        // sub-kernel's extent stay inside the LDS buffer and are never used)
+                        u32x4_t bf[WCOLS];
 #pragma unroll
-                    for (int cc = 0; cc < WCOLS; ++cc) {
-                        const int hc = wp * 4 * SI + cc;
-                        bf[cc] = *reinterpret_cast<const u32x4_t *>(
-                            Bs + lds_row_off32((hr * HC + hc) * 32, loff));
-                    }
+                        for (int cc = 0; cc < WCOLS; ++cc) {
+                            if constexpr (NB == 32) {
+                                const int hc = wp * 4 * SI + cc;
+                                bf[cc] = *reinterpret_cast<const u32x4_t *>(
+                                    Bs + lds_row_off32((hr * HC + hc) * 32, loff));
+                            } else if (cc % (2 * SI) < KWM) {
+                                // (stride 2: columns 4j + 3 belong to no MFMA's lanes 0-15)
+                                const int P = hr * HC + wp * 8 * SI + cc + h16 * SI;
+                                bf[cc] = *reinterpret_cast<const u32x4_t *>(
+                                    Bs + lds_row_off16(P, loff16));
+                            }
+                        }
 #pragma unroll
-                    for (int tw = 0; tw < KWM; ++tw) {
-                        if (tw < kw) {
-                            const int t = th * kw + tw;
-                            f16x8_t av[MW];
+                        for (int tw = 0; tw < KWM; ++tw) {
+                            if (tw < kw) {
+                                const int t = th * kw + tw;
+                                f16x8_t av[MW];
 #pragma unroll
-                            for (int u = 0; u < MW; ++u)
-                                av[u] = __builtin_bit_cast(
-                                    f16x8_t, *reinterpret_cast<const u32x4_t *>(
-                                                 As + lds_row_off32(t * 64 + 32 * (wm * MW + u), loff)));
+                                for (int u = 0; u < UN; ++u)
+                                    av[u] = __builtin_bit_cast(
+                                        f16x8_t, *reinterpret_cast<const u32x4_t *>(
+                                                     As + lds_row_off32(t * 64 + 32 * (wm * MW + u), loff)));
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                const f16x8_t b = __builtin_bit_cast(f16x8_t, bf[j * SI + tw]);
+                                for (int j = 0; j < 4; ++j) {
+                                    const f16x8_t b =
+                                        __builtin_bit_cast(f16x8_t, bf[j * (PPW / 4) * SI + tw]);
 #pragma unroll
-                                for (int u = 0; u < MW; ++u)
-                                    acc[u][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[u], b, acc[u][j], 0, 0, 0);
+                                    for (int u = 0; u < UN; ++u)
+                                        acc[u][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[u], b, acc[u][j], 0, 0, 0);
+                                }
                             }
                         }
                     }
                 }
+                __syncthreads();
             }
-            __syncthreads();
+        };
+        if constexpr (NB == 32) {
+            chunks(IntC<MW>{}); // batch blocks of 32 compute every row block (one loop copy)
+        } else {
+            if (rows_left > 32 * (MW - 1)) chunks(IntC<MW>{});
+            else if (rows_left > 0) chunks(IntC<1>{});
+            else chunks(IntC<0>{});
         }
 
         const int i = i0 + wr;
-        const int n = nb * 32 + l32;
+        const int n = NB == 32 ? nb * 32 + l32 : nb * 16 + (l32 & 15);
         const bool full_m = 4 * m4_0 + 64 <= a.M;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int jj = j0 + wp * 4 + j;
-            const bool pix_in = i < cl.OHs && jj < cl.OWs; // the same for the whole wave
+            const int jj = j0 + wp * PPW + (NB == 32 ? j : 2 * j + h16);
+            const bool pix_in = i < cl.OHs && jj < cl.OWs; // per half-wave pair for NB = 16
             const bool pix_ok = pix_in && n < a.N;
             if (a.amax_ws && pix_in) {
 #pragma unroll
@@ -431,11 +478,15 @@ conv_spatial_kernel(SpatialArgs a)
             const int oh = i * a.sO + cl.ah, ow = jj * a.sO + cl.aw;
 #pragma unroll
             for (int u = 0; u < MW; ++u) {
-                const int mrow = 4 * m4_0 + 32 * (wm * MW + u) + 4 * half;
+                const int mrow0 = 4 * m4_0 + 32 * (wm * MW + u); // wave-uniform
+                if (NB == 16 && mrow0 >= a.M) continue;          // a block of padding rows
+                const int mrow = mrow0 + 4 * half;
                 const uint32_t vbase =
                     pix_ok ? ((((uint32_t)oh * a.OWf + ow) * a.M + mrow) * a.N + n) * 4u : kBad;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
+                    // stores whose eight rows all lie past M are not issued (wave-uniform)
+                    if (NB == 16 && !full_m && mrow0 + 8 * (r >> 2) >= a.M) continue;
                     const int dm = 8 * (r >> 2) + (r & 3);
                     const float v = fsafe ? acc[u][j][r] * sf : (float)((double)acc[u][j][r] * sd);
                     const uint32_t voff = (full_m || mrow + dm < a.M) ? vbase : kBad;
@@ -531,11 +582,11 @@ bool spatial_supported(const ConvGeom &g)
     return Hm * tw * nblk * nmb * dmax < (1ull << 32);
 }
 
-template <int FMT, bool A_KR, int SI, int PH, int PW, int MW>
+template <int FMT, bool A_KR, int SI, int PH, int PW, int MW, int NB>
 static hipError_t launch_spatial_tiles(SpatialArgs &a, int nclass, hipStream_t st)
 {
     constexpr int PF = MW == 1 ? 2 : 1; // producer waves per consumer wave
-    constexpr int THREADS = 32 * PH * PW * (2 / MW) * (1 + PF) / 2;
+    constexpr int THREADS = 64 * (PH * PW / (NB == 32 ? 4 : 8)) * (2 / MW) * (1 + PF);
     constexpr int SG = THREADS / 256;   // 64-output sum blocks per workgroup pass
     int items[4] = {0, 0, 0, 0}, total = 0;
     double work[4] = {0, 0, 0, 0}, total_work = 0;
@@ -609,7 +660,7 @@ static hipError_t launch_spatial_tiles(SpatialArgs &a, int nclass, hipStream_t s
     dim3 grid((unsigned)nwg, (unsigned)(nclass + (a.sum_P > 0 ? 1 : 0)), 1);
     const bool full3 = nclass == 1 && a.cls[0].kh == 3 && a.cls[0].kw == 3;
 #define MQ_SPATIAL_LAUNCH(KFV, PV)                                                              \
-    hipLaunchKernelGGL((conv_spatial_kernel<FMT, A_KR, SI, PH, PW, MW, PF, KFV, PV>), grid,      \
+    hipLaunchKernelGGL((conv_spatial_kernel<FMT, A_KR, SI, PH, PW, MW, NB, PF, KFV, PV>), grid,  \
                        dim3(THREADS), 0, st, a)
     if (full3 && persist) MQ_SPATIAL_LAUNCH(3, true);
     else if (full3) MQ_SPATIAL_LAUNCH(3, false);
@@ -636,16 +687,29 @@ static int spatial_grid_wgs(const SpatialArgs &a, int nclass, int PH, int PW)
     return max_tiles * a.nblk * ((a.M4 + 15) / 16) * nclass;
 }
 
+// Batch blocks: 32 elements, or for a batch of at most 16 (four squares) one block of 16 with two
+// pixels per MFMA (tiles twice as wide: PW = 16).
 template <int FMT, bool A_KR, int SI>
 static hipError_t launch_spatial(SpatialArgs &a, int nclass, hipStream_t st)
 {
+    if (a.N4 <= 4) {
+        a.nblk = 1;
+        if constexpr (SI == 1) {
+            const int w2 = spatial_grid_wgs(a, nclass, 2, 16), w1 = spatial_grid_wgs(a, nclass, 1, 16);
+            const double t2 = 1.0 * ((w2 + 255) / 256), t1 = 0.6 * ((w1 + 255) / 256);
+            if (t1 < t2) return launch_spatial_tiles<FMT, A_KR, SI, 1, 16, 1, 16>(a, nclass, st);
+            return launch_spatial_tiles<FMT, A_KR, SI, 2, 16, 2, 16>(a, nclass, st);
+        }
+        return launch_spatial_tiles<FMT, A_KR, SI, 1, 16, 1, 16>(a, nclass, st);
+    }
+    a.nblk = (a.N4 + 7) / 8;
     constexpr int PH = TileShape<SI>::PH, PW = TileShape<SI>::PW, MW = TileShape<SI>::MW;
     if constexpr (SI == 1) {
         const int w2 = spatial_grid_wgs(a, nclass, 2, 8), w1 = spatial_grid_wgs(a, nclass, 1, 8);
         const double t2 = 1.0 * ((w2 + 255) / 256), t1 = 0.6 * ((w1 + 255) / 256);
-        if (t1 < t2) return launch_spatial_tiles<FMT, A_KR, SI, 1, 8, 1>(a, nclass, st);
+        if (t1 < t2) return launch_spatial_tiles<FMT, A_KR, SI, 1, 8, 1, 32>(a, nclass, st);
     }
-    return launch_spatial_tiles<FMT, A_KR, SI, PH, PW, MW>(a, nclass, st);
+    return launch_spatial_tiles<FMT, A_KR, SI, PH, PW, MW, 32>(a, nclass, st);
 }
 
 hipError_t launch_conv_fwd_spatial(const ConvGeom &g, int fmt, QOperand x, QOperand w, float *y,
@@ -659,7 +723,7 @@ hipError_t launch_conv_fwd_spatial(const ConvGeom &g, int fmt, QOperand x, QOper
     a.Kh = g.Kh; a.Kw = g.Kw; a.Cout4 = g.Cout4; a.Cin4 = g.Cin4;
     a.out = y; a.OWf = g.Wo; a.M = g.Cout; a.N = g.N; a.M4 = g.Cout4;
     a.out_bytes = (uint32_t)((uint64_t)g.Ho * g.Wo * g.Cout * g.N * 4);
-    a.nblk = (g.N4 + 7) / 8; a.sO = 1;
+    a.sO = 1;
     SpatialClass &c = a.cls[0];
     c.ah = c.aw = 0; c.OHs = g.Ho; c.OWs = g.Wo; c.kh = g.Kh; c.kw = g.Kw;
     c.r0 = -g.ph; c.c0 = -g.pw; c.Ah = 0; c.Bh = 1; c.Aw = 0; c.Bw = 1;
@@ -703,7 +767,6 @@ hipError_t launch_conv_dgrad_spatial(const ConvGeom &g, int fmt, QOperand w, QOp
     a.Kh = g.Kh; a.Kw = g.Kw; a.Cout4 = g.Cout4; a.Cin4 = g.Cin4;
     a.out = gx; a.OWf = g.W; a.M = g.Cin; a.N = g.N; a.M4 = g.Cin4;
     a.out_bytes = (uint32_t)((uint64_t)g.H * g.W * g.Cin * g.N * 4);
-    a.nblk = (g.N4 + 7) / 8;
     const int s = g.sh;
     a.sO = s;
     int nclass = 0;

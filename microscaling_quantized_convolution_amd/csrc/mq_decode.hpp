@@ -4,8 +4,8 @@
 // (NVFP4) or 8 (NVFP6) significant bits and lies in [2^-12, 3360], so fp16 holds it exactly and
 // fp16 MFMA products are exact in fp32. The tensor scale T stays out (applied in the epilogue).
 //
-// The E4M3 scale converts to fp16 in hardware (exact), the E2M1 codes too (two per byte), and
-// one packed fp16 multiply per element pair applies the scale.
+// The E4M3 scale converts to fp16 in hardware (exact), the E2M1 codes too (two per byte), the
+// E2M3 codes 32 at a time, and one packed fp16 multiply per element pair applies the scale.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -49,28 +49,26 @@ __device__ __forceinline__ void decode_fp4_square(uint32_t w0, uint32_t w1, _Flo
     for (int j = 0; j < 8; ++j) d[j] = __builtin_bit_cast(uint32_t, h[j] * b2);
 }
 
-// NVFP6 square (three code words, element e = bits [6e, 6e+6) of the 96-bit word) -> d as above.
-// A code s|ee|mmm placed as fp16 bits s<<15 | eemmm<<7 is E * 2^-14 (subnormal codes become
-// fp16 subnormals), so E*B = (that * 2^14) * B with both products exact.
-__device__ __forceinline__ void decode_fp6_square(uint32_t w0, uint32_t w1, uint32_t w2,
-                                                  _Float16 B, uint32_t (&d)[8])
+// Two NVFP6 squares (six code words: the first square's three, then the second's; element e of
+// a square = bits [6e, 6e+6) of its 96-bit word) with scales B0, B1 -> d0, d1 as above. One
+// v_cvt_scalef32_pk32_f16_fp6 converts the 32 E2M3 codes (code i = bits [6i, 6i+6) of the
+// 192-bit word, which is the two squares' packing) to their fp16 values exactly (scale 1: every
+// E2M3 value is an fp16 value); one packed multiply per pair applies the square's scale. A NaN
+// scale makes every element NaN, a zero scale every element +-0.
+__device__ __forceinline__ void decode_fp6_square_pair(const uint32_t (&w)[6], _Float16 B0,
+                                                       _Float16 B1, uint32_t (&d0)[8],
+                                                       uint32_t (&d1)[8])
 {
-    const f16x2_t b2 = {B, B};
-    const f16x2_t k14 = {(_Float16)16384.0f, (_Float16)16384.0f};
-    const uint64_t lo = ((uint64_t)w1 << 32) | w0;
-    const uint64_t hi = ((uint64_t)w2 << 32) | w1;
+    typedef uint32_t u32x6_t __attribute__((ext_vector_type(6)));
+    typedef _Float16 f16x32_t __attribute__((ext_vector_type(32)));
+    const u32x6_t v = {w[0], w[1], w[2], w[3], w[4], w[5]};
+    const f16x32_t h = __builtin_amdgcn_cvt_scalef32_pk32_f16_fp6(v, 1.0f);
+    const f16x2_t b0 = {B0, B0}, b1 = {B1, B1};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        uint32_t f[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int e = 2 * j + u, bit = 6 * e;
-            const uint32_t c = (bit < 58) ? (uint32_t)(lo >> bit) & 0x3Fu
-                                          : (uint32_t)(hi >> (bit - 32)) & 0x3Fu;
-            f[u] = ((c & 31u) << 7) | ((c & 32u) << 10);
-        }
-        const f16x2_t v = __builtin_bit_cast(f16x2_t, f[0] | (f[1] << 16));
-        d[j] = __builtin_bit_cast(uint32_t, (v * k14) * b2);
+        const f16x2_t e0 = {h[2 * j], h[2 * j + 1]}, e1 = {h[16 + 2 * j], h[17 + 2 * j]};
+        d0[j] = __builtin_bit_cast(uint32_t, e0 * b0);
+        d1[j] = __builtin_bit_cast(uint32_t, e1 * b1);
     }
 }
 

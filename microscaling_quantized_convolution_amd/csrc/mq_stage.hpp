@@ -114,13 +114,20 @@ __device__ __forceinline__ void item_scales(const RawItem<FMT> &r, f16x2_t (&sc)
     sc[1] = e4m3_pair_to_f16<true>(s4 & keep);
 }
 
+// Squares k0 and k0 + 1 (k0 even) of an item, decoded (d[0], d[1]).
 template <int FMT>
-__device__ __forceinline__ void decode_raw(const RawItem<FMT> &r, const f16x2_t (&sc)[2], int k,
-                                           uint32_t (&d)[8])
+__device__ __forceinline__ void decode_pair(const RawItem<FMT> &r, const f16x2_t (&sc)[2], int k0,
+                                            uint32_t (&d)[2][8])
 {
-    const _Float16 B = sc[k >> 1][k & 1];
-    if constexpr (FMT == kFP4) decode_fp4_square(r.w[k][0], r.w[k][1], B, d);
-    else decode_fp6_square(r.w[k][0], r.w[k][1], r.w[k][2], B, d);
+    const _Float16 B0 = sc[k0 >> 1][0], B1 = sc[k0 >> 1][1];
+    if constexpr (FMT == kFP4) {
+        decode_fp4_square(r.w[k0][0], r.w[k0][1], B0, d[0]);
+        decode_fp4_square(r.w[k0 + 1][0], r.w[k0 + 1][1], B1, d[1]);
+    } else {
+        const uint32_t w[6] = {r.w[k0][0],     r.w[k0][1],     r.w[k0][2],
+                               r.w[k0 + 1][0], r.w[k0 + 1][1], r.w[k0 + 1][2]};
+        decode_fp6_square_pair(w, B0, B1, d[0], d[1]);
+    }
 }
 
 // LDS operand rows: 16 fp16 (32 bytes, two 16-byte units). Bits 0-2 of the unit index
@@ -157,16 +164,20 @@ __device__ __forceinline__ void store_item(const RawItem<FMT> &r, uint8_t *lds, 
     f16x2_t sc[2];
     item_scales<FMT>(r, sc);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        uint32_t d[8];
-        decode_raw<FMT>(r, sc, k, d);
+    for (int k0 = 0; k0 < 4; k0 += 2) {
+        uint32_t dd[2][8];
+        decode_pair<FMT>(r, sc, k0, dd);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (KR) {
-                square_column(d, i, rows[i][2 * k], rows[i][2 * k + 1]);
-            } else {
-                rows[i][2 * k] = d[2 * i];
-                rows[i][2 * k + 1] = d[2 * i + 1];
+        for (int kk = 0; kk < 2; ++kk) {
+            const int k = k0 + kk;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (KR) {
+                    square_column(dd[kk], i, rows[i][2 * k], rows[i][2 * k + 1]);
+                } else {
+                    rows[i][2 * k] = dd[kk][2 * i];
+                    rows[i][2 * k + 1] = dd[kk][2 * i + 1];
+                }
             }
         }
     }
@@ -193,23 +204,27 @@ __device__ __forceinline__ void store_item_rows(const RawItem<FMT> &r, uint8_t *
     item_scales<FMT>(r, sc);
     const int Q = lds_row_off(row0, kb >> 1) + 8 * (kb & 1);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        uint32_t d[8];
-        decode_raw<FMT>(r, sc, j, d);
+    for (int j0 = 0; j0 < 4; j0 += 2) {
+        uint32_t dd[2][8];
+        decode_pair<FMT>(r, sc, j0, dd);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t p0, p1;
-            if (KR) {
-                square_column(d, i, p0, p1);
-            } else {
-                p0 = d[2 * i];
-                p1 = d[2 * i + 1];
+        for (int jj = 0; jj < 2; ++jj) {
+            const int j = j0 + jj;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t p0, p1;
+                if (KR) {
+                    square_column(dd[jj], i, p0, p1);
+                } else {
+                    p0 = dd[jj][2 * i];
+                    p1 = dd[jj][2 * i + 1];
+                }
+                // row0 is a multiple of 16: rows row0 + s differ from row0 in the swizzle only
+                // by the bits that s sets (bit 3 and bit 2 of the row move unit bits 0 and 1)
+                const int s4 = 4 * j + i;
+                const int K = (2 * s4) ^ ((s4 >> 3) & 1) ^ (((s4 >> 2) & 1) << 1);
+                *reinterpret_cast<uint2 *>(lds + (Q ^ (K << 4))) = make_uint2(p0, p1);
             }
-            // row0 is a multiple of 16: rows row0 + s differ from row0 in the swizzle only by
-            // the bits that s sets (bit 3 and bit 2 of the row move unit bits 0 and 1)
-            const int s4 = 4 * j + i;
-            const int K = (2 * s4) ^ ((s4 >> 3) & 1) ^ (((s4 >> 2) & 1) << 1);
-            *reinterpret_cast<uint2 *>(lds + (Q ^ (K << 4))) = make_uint2(p0, p1);
         }
     }
 }

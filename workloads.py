@@ -236,4 +236,10 @@ def parity_layers() -> List[ConvLayer]:
                   x_dist="relu", seed=122, sr_seed=28),
         ConvLayer("p.1x1.p1", N=8, Cin=12, H=6, W=7, Cout=16, Kh=1, Kw=1, stride=1, pad=1,
                   x_dist="normal", seed=123, sr_seed=29),
+        # batches of at most 16 (two pixels per MFMA): a ragged batch at stride 2 with a row
+        # block that is partly past the output channels, and an odd width with 72 output rows
+        ConvLayer("p.b12.s2", N=12, Cin=40, H=21, W=30, Cout=28, Kh=3, Kw=3, stride=2, pad=1,
+                  x_dist="silu", seed=124, sr_seed=30),
+        ConvLayer("p.b16.w23.fp6", N=16, Cin=36, H=13, W=23, Cout=72, Kh=3, Kw=3, stride=1,
+                  pad=1, fmt=FP6, x_dist="relu", seed=125, sr_seed=31),
     ]
