@@ -135,14 +135,14 @@ conv_spatial_kernel(SpatialArgs a)
     // barrier). The class comes from the grid rather than a search of the classes' ranges in
     // the arguments, which put dependent argument loads before the first memory access.
     if ((int)blockIdx.y >= a.nclass) {
-        // the weight gradient's split sum, riding along: one 64-output block per 256 lanes and
+        // the weight gradient's split sum, riding along: one sum block per 256 lanes and
         // pass, workgroup b taking passes b, b + sum_P, ... (the loop count is the same for
         // every lane: each call below holds a barrier)
         constexpr int SG = THREADS_OF / 256;
         static_assert(THREADS_OF % 256 == 0, "the sum role takes whole 256-lane groups");
         if ((int)blockIdx.x >= a.sum_P) return;
         float4(*red)[17] = reinterpret_cast<float4(*)[17]>(lds[0]);
-        const int64_t nb = (a.sum.total + 63) / 64;
+        const int64_t nb = wgrad_sum_blocks(a.sum);
         const int grp = (int)threadIdx.x >> 8;
         for (int64_t base = SG * (int64_t)blockIdx.x; base < nb; base += SG * (int64_t)a.sum_P) {
             wgrad_sum_block(a.sum, base + grp, (int)threadIdx.x & 255, red + 16 * grp);
@@ -587,7 +587,7 @@ static hipError_t launch_spatial_tiles(SpatialArgs &a, int nclass, hipStream_t s
 {
     constexpr int PF = MW == 1 ? 2 : 1; // producer waves per consumer wave
     constexpr int THREADS = 64 * (PH * PW / (NB == 32 ? 4 : 8)) * (2 / MW) * (1 + PF);
-    constexpr int SG = THREADS / 256;   // 64-output sum blocks per workgroup pass
+    constexpr int SG = THREADS / 256;   // sum blocks per workgroup pass
     int items[4] = {0, 0, 0, 0}, total = 0;
     double work[4] = {0, 0, 0, 0}, total_work = 0;
     for (int c = 0; c < nclass; ++c) {
@@ -640,10 +640,10 @@ static hipError_t launch_spatial_tiles(SpatialArgs &a, int nclass, hipStream_t s
     if (a.sum_P < 0) {
         // The weight-gradient sum: on the CUs this launch leaves idle (one workgroup per CU:
         // the LDS), or, when it fills them, on 256 workgroups after its own. A workgroup sums
-        // SG 64-output blocks per pass, a chain of dependent loads and a barrier (about 1.5 us),
+        // SG sum blocks per pass, a chain of dependent loads and a barrier (about 1.5 us),
         // so the sum rides along only when its passes hide behind the convolution or cost less
         // than a kernel of their own; otherwise it runs as its own kernel, ahead.
-        const int64_t pairs = ((a.sum.total + 63) / 64 + SG - 1) / SG;
+        const int64_t pairs = (wgrad_sum_blocks(a.sum) + SG - 1) / SG;
         const int spare = 256 - conv_wgs;
         const int64_t P = spare >= 32 ? spare : 256;
         if ((pairs + P - 1) / P <= (spare >= 32 ? 8 : 2)) {

@@ -306,12 +306,12 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
     }
 }
 
-// The split sum as a kernel of its own: 64-output blocks, grid-stride over the 256-lane
-// workgroups (a workgroup per block made launches of tens of thousands of tiny workgroups).
+// The split sum as a kernel of its own: blocks grid-stride over the 256-lane workgroups (a
+// workgroup per block made launches of tens of thousands of tiny workgroups).
 __global__ void __launch_bounds__(256) wgrad_sum_kernel(WgradSum w)
 {
     __shared__ float4 red[16][17];
-    const int64_t nb = (w.total + 63) / 64;
+    const int64_t nb = wgrad_sum_blocks(w);
     for (int64_t blk = blockIdx.x; blk < nb; blk += gridDim.x) {
         wgrad_sum_block(w, blk, (int)threadIdx.x, red);
         __syncthreads(); // the next block reuses red
@@ -455,7 +455,7 @@ hipError_t launch_conv_wgrad_fast(const ConvGeom &g, int fmt, QOperand gy, QOper
 hipError_t launch_wgrad_sum(const WgradSum &w, hipStream_t st)
 {
     if (w.total <= 0) return hipSuccess;
-    const int64_t nb = (w.total + 63) / 64;
+    const int64_t nb = wgrad_sum_blocks(w);
     hipLaunchKernelGGL(wgrad_sum_kernel, dim3((unsigned)(nb < 2048 ? nb : 2048)), dim3(256), 0, st, w);
     return hipGetLastError();
 }

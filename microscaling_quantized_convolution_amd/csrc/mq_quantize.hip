@@ -613,12 +613,21 @@ static void launch_nchw_shape(QuantNchwArgs a, hipStream_t st)
                        0, st, a);
 }
 
+// Batch squares per lane: four (64 loads in flight per lane, the fastest shape on large tensors)
+// when that still gives every CU a workgroup; one otherwise, so that a small tensor spreads over
+// four times as many workgroups and each lane's chain of loads is a quarter as long.
+static int nchw_nq(int N4, int HW, int C4)
+{
+    const int64_t wgs4 = ((int64_t)(HW + 63) / 64) * C4 * (N4 / 4) / 4;
+    return (N4 % 4 == 0 && wgs4 >= 256) ? 4 : 1;
+}
+
 template <int FMT, bool SR>
 static hipError_t launch_quant_nchw(const QuantNchwArgs &a, hipStream_t st)
 {
     const bool al16 = (reinterpret_cast<uintptr_t>(a.src) & 15u) == 0;
-    if (a.N4 % 4 == 0) launch_nchw_shape<FMT, SR, 4, 1>(a, st);
-    else if (al16 && a.HW % 4 == 0) launch_nchw_shape<FMT, SR, 1, 4>(a, st);
+    if (nchw_nq(a.N4, a.HW, a.C4) == 4) launch_nchw_shape<FMT, SR, 4, 1>(a, st);
+    else if (a.N4 % 4 != 0 && al16 && a.HW % 4 == 0) launch_nchw_shape<FMT, SR, 1, 4>(a, st);
     else launch_nchw_shape<FMT, SR, 1, 1>(a, st);
     return hipGetLastError();
 }
@@ -885,7 +894,7 @@ static hipError_t launch_batch_nj(const QuantJobDesc *jobs, int njobs, int fmt, 
             q.src = d.src; q.codes = d.codes; q.scales = d.scales; q.tscale = d.tscale;
             q.amax_ws = d.amax_ws;
             q.N = d.s; q.C = d.r; q.HW = (int)HW; q.C4 = (int)R4; q.N4 = (int)S4;
-            jb.nq = q.N4 % 4 == 0 ? 4 : 1;
+            jb.nq = nchw_nq(q.N4, q.HW, q.C4);
             q.NG = q.N4 / jb.nq;
             q.items = (int)((HW + 63) / 64) * q.C4 * q.NG;
             q.bytes = (uint32_t)(n * 4);
