@@ -15,8 +15,11 @@ starts. G_Y arrives channel-batch-first (it is the next layer's input-gradient o
 
 The timed steps call the C ABI back to back on one stream (arguments marshalled once, so the
 GPU, not the host, sets the pace). HIP events on that stream bracket every launch of the step's
-dominant op (the op and layer shape with the most time per step) in every `--event-every`-th
-step: `roofline` is that op's algorithmic work per launch over its mean bracketed duration.
+dominant kernel in every `--event-every`-th step: of the step's calls that launch exactly one
+kernel (the forward convolution; the quantizations launch an amax and a quantizing kernel, the
+backward call a weight-gradient and an input-gradient kernel), the layer shape with the most time
+per step. `roofline` is that kernel's algorithmic work per launch over its mean bracketed
+duration.
 `per_layer` times each op of each distinct layer shape alone (a HIP graph of back-to-back
 launches), also the two gradients as calls of their own. `quantize_cold` times the largest
 layer's quantizations with the MALL flushed before each launch. `cpu_baseline` times the CPU
@@ -70,6 +73,8 @@ OP_KERNELS["conv_fwd_amax"] = OP_KERNELS["conv_fwd"] + ["mq::amax_kernel"]
 OP_KERNELS["conv_backward_amax"] = OP_KERNELS["conv_backward"] + ["mq::amax_kernel"]
 STEP_OPS = ["quantize_xw", "quantize_g", "conv_fwd", "conv_backward"]
 INFERENCE_OPS = ["quantize_x", "conv_fwd"]
+# calls of the step that launch exactly one kernel (the spatial or generic convolution kernel)
+ONE_KERNEL_OPS = ("conv_fwd",)
 PARTS = ["conv_wgrad", "conv_dgrad", "conv_fwd_amax", "conv_backward_amax", "quantize_g_ready"]
 
 
@@ -334,16 +339,17 @@ def run_workload(args):
                           "format": f"NVFP{l.fmt}"},
                 "ms_layer": round(layer_ms, 5), "per_op": entry})
 
-    # ---- the dominant op: the (shape, op) with the most time per step ----
+    # ---- the dominant kernel: the (shape, one-kernel op) with the most time per step ----
     if args.roofline_op and args.roofline_op not in ops:
         sys.exit(f"--roofline-op {args.roofline_op}: not an op of the step ({', '.join(ops)})")
+    roof_ops = [args.roofline_op] if args.roofline_op else [op for op in ops if op in ONE_KERNEL_OPS]
     if op_ms:
         cand = [(op_ms[idx[0], op] * len(idx), key, op) for key, idx in groups.items()
-                for op in ops if args.roofline_op in (None, op)]
+                for op in roof_ops]
         _, dom_key, dom_op = max(cand)
     else:
         dom_key = next(iter(groups))
-        dom_op = args.roofline_op or ("conv_fwd" if args.inference else "conv_backward")
+        dom_op = roof_ops[0]
     dom_idx = groups[dom_key]
 
     # ---- timed steps ----
@@ -579,18 +585,24 @@ def _short(name: str) -> str:
     return name
 
 
-def _pmc_per_kernel(db: str, counters):
-    """Mean per dispatch of each counter (summed over its instances) per kernel name."""
+def _pmc_per_kernel(db: str, counters, by_grid: bool = False):
+    """Mean per dispatch of each counter (summed over its instances) per kernel name, or per kernel
+    name and grid (workgroups along x, y, z) with by_grid."""
     import collections
     import sqlite3
     con = sqlite3.connect(db)
     cols = [r[1] for r in con.execute("pragma table_info(counters_collection)")]
     ki, ci, vi, di = (cols.index(c) for c in ("kernel_name", "counter_name", "value",
                                               "dispatch_id"))
+    gi = [cols.index(c) for c in ("grid_size_x", "grid_size_y", "grid_size_z", "workgroup_size_x")]
     per = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(float)))
     for row in con.execute("select * from counters_collection"):
         if row[ci] in counters:
-            d = per[row[ci]][_short(row[ki])]
+            key = _short(row[ki])
+            if by_grid:
+                gx, gy, gz, wx = (row[i] for i in gi)
+                key = f"{key} ({gx // max(wx, 1)}, {gy}, {gz}) x {wx}"
+            d = per[row[ci]][key]
             if row[ci] == "GRBM_GUI_ACTIVE":  # one chip-wide clock: the largest instance
                 d[row[di]] = max(d[row[di]], row[vi])
             else:
@@ -662,24 +674,44 @@ def summarize_trace(db: str):
 
 
 def summarize_mfma(db: str):
-    """MFMA utilisation per kernel: SQ_VALU_MFMA_BUSY_CYCLES over (GRBM_GUI_ACTIVE x 4 SIMDs x
-    256 CUs), and the fp16 MFMA flops counted by SQ_INSTS_VALU_MFMA_MOPS_F16 (512 flop each)."""
+    """MFMA utilisation per kernel and grid from one rocprofv3 --pmc run. SQ_VALU_MFMA_BUSY_CYCLES
+    counts busy cycles summed over the 1024 SIMDs (a 32x32x16 fp16 MFMA keeps its SIMD busy 32
+    cycles); GRBM_GUI_ACTIVE reads the 8 XCDs' active cycles summed. util = busy / (GRBM_GUI_ACTIVE
+    / 8 x 1024): the matrix cores' busy fraction at the clock they ran. The fp16 MFMA flops come
+    from SQ_INSTS_VALU_MFMA_MOPS_F16 (512 flop each); TFLOP/s divides them by the dispatch's
+    duration under the counters, and frac compares that with the 2.5 PFLOP/s dense fp16 peak."""
+    import collections
+    import sqlite3
     cs = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_BUSY_CU_CYCLES",
           "GRBM_GUI_ACTIVE"]
-    per = _pmc_per_kernel(db, cs)
+    per = _pmc_per_kernel(db, cs, by_grid=True)
+    con = sqlite3.connect(db)
+    dur = collections.defaultdict(dict)
+    for name, gx, gy, gz, wx, did, d in con.execute(
+            "select kernel_name, grid_size_x, grid_size_y, grid_size_z, workgroup_size_x, "
+            "dispatch_id, duration from counters_collection"):
+        dur[f"{_short(name)} ({gx // max(wx, 1)}, {gy}, {gz}) x {wx}"][did] = d
     print(f"kernel_sources_sha256: {kernel_source_hash()}")
     print()
-    print("| kernel | dispatches | MFMA busy cycles | GRBM_GUI_ACTIVE | MFMA util | "
-          "fp16 MFMA GFLOP / dispatch |")
-    print("|---|---|---|---|---|---|")
+    print("| kernel (workgroups x lanes) | dispatches | mean us | MFMA busy SIMD-cycles | "
+          "GRBM_GUI_ACTIVE (8 XCDs) | MFMA util | fp16 MFMA GFLOP | TFLOP/s | frac of 2.5 PF |")
+    print("|---|---|---|---|---|---|---|---|---|")
     names = sorted(set().union(*[set(per[c]) for c in cs]))
+    rows = []
     for k in names:
         busy = per["SQ_VALU_MFMA_BUSY_CYCLES"].get(k, (0.0, 0))
         act = per["GRBM_GUI_ACTIVE"].get(k, (0.0, 0))[0]
         mops = per["SQ_INSTS_VALU_MFMA_MOPS_F16"].get(k, (0.0, 0))[0]
-        util = busy[0] / (act * 4 * 256) if act else 0.0
-        print(f"| `{k.replace('(anonymous namespace)::', '')[:100]}` | {busy[1]} | {busy[0]:.3e} | "
-              f"{act:.3e} | {util:.3f} | {mops * 512 / 1e9:.3f} |")
+        if mops == 0:
+            continue
+        us = sum(dur[k].values()) / max(len(dur[k]), 1) / 1e3
+        util = busy[0] / (act / 8 * 1024) if act else 0.0
+        gf = mops * 512 / 1e9
+        tf = gf / us * 1e3 if us else 0.0  # GFLOP per us = PFLOP/s
+        rows.append((-gf * busy[1], k, busy[1], us, busy[0], act, util, gf, tf))
+    for _, k, n, us, b, act, util, gf, tf in sorted(rows):
+        print(f"| `{k.replace('(anonymous namespace)::', '')[:130]}` | {n} | {us:.2f} | {b:.3e} | "
+              f"{act:.3e} | {util:.3f} | {gf:.3f} | {tf:.1f} | {tf / MFMA_PEAK_TFLOPS:.3f} |")
 
 
 if __name__ == "__main__":

@@ -159,7 +159,7 @@ conv_spatial_kernel(SpatialArgs a)
     // the current one's output.
     const int tiles_h = cl.tiles_h;
     const int T = cl.T;
-    const int b = (int)blockIdx.x;
+    const int b = xcd_number((int)blockIdx.x, cl.P);
     // PERSIST: each workgroup loops over several items; otherwise one item per workgroup
     const int nmine = b < T ? (PERSIST ? div_by(T - 1 - b, cl.m_P) + 1 : 1) : 0;
     // Item w = ((mb * tiles_h + ti) * tiles_w + tj) * nblk + nb, stepped by P in that mixed radix
