@@ -474,6 +474,25 @@ def quantize_cold(layers, calls, reps, stream):
         kind, amount, nbytes = work[op]
         out[op] = {"cold": rate(kind, amount, nbytes, ms_cold),
                    "warm": rate(kind, amount, nbytes, ms_warm)}
+    # the practical streaming ceiling for the same bytes: a plain device copy of X's size (one
+    # read, one write of fp32), cold as above
+    n = l.N * l.Cin * l.H * l.W
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    cold = []
+    with torch.cuda.stream(stream):
+        for r in range(reps + 1):
+            scratch.fill_(float(r))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dst.copy_(src)
+            e1.record(stream)
+            cold.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in cold[1:]) / reps
+    out["copy_reference"] = {"bytes": 8 * n, "ms": round(ms, 5),
+                             "GB_s": round(8 * n / (ms * 1e-3) / 1e9, 1),
+                             "frac": round(8 * n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     return out
 
 
