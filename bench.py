@@ -50,7 +50,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = 2516.6    # MI355X dense fp16/bf16 MFMA, TFLOP/s (256 CU x 2.4 GHz x 4096)
 CALIB_ELEMS = 1 << 26        # plain copy for counter calibration: 256 MiB read + 256 MiB written
-FLUSH_BYTES = 512 << 20      # written before each cold launch (the MALL holds 256 MB)
+FLUSH_BYTES = 512 << 20      # read before each cold launch (the MALL holds 256 MB)
 METRIC = "quant GB/s (% HBM peak) + conv fwd/wgrad/dgrad TFLOP/s (% bf16 MFMA) per layer"
 
 # which kernels make up each op (rocprofv3 kernel names start with these)
@@ -450,19 +450,20 @@ def workload_name(args, layers):
 
 
 def quantize_cold(layers, calls, reps, stream):
-    """The largest layer's quantizations, each launch after writing FLUSH_BYTES of scratch (the
-    MALL and L2 then hold none of its inputs), against the same launches back to back (warm)."""
+    """The largest layer's quantizations, each launch after reading FLUSH_BYTES of scratch (the
+    MALL and L2 then hold none of its inputs, and no dirty lines that the launch would have to
+    write back), against the same launches back to back (warm)."""
     import torch
     i = max(range(len(layers)), key=lambda k: layers[k].N * layers[k].Cin * layers[k].H * layers[k].W)
     l = layers[i]
     work = layer_work(l)
-    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    scratch = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     out = {"layer": l.name}
     for op in ("quantize_xw", "quantize_g"):
         cold = []
         with torch.cuda.stream(stream):
             for r in range(reps + 1):
-                scratch.fill_(float(r))
+                flush = scratch.max()  # a read of every scratch line
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
                 calls[i][op](r)
@@ -482,7 +483,7 @@ def quantize_cold(layers, calls, reps, stream):
     cold = []
     with torch.cuda.stream(stream):
         for r in range(reps + 1):
-            scratch.fill_(float(r))
+            flush = scratch.max()  # a read of every scratch line
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             dst.copy_(src)
