@@ -81,6 +81,7 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
     constexpr int GBYTES = kPWg * kKS * 64 * kRowBytes, XBYTES = HCM * kKS * 64 * kRowBytes;
     constexpr int ITEMS = (kPWg * 16 * kKS + HCM * 16 * kKS + kNP - 1) / kNP;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][GBYTES + XBYTES];
+    static_assert(3 * KWM * 16 * 64 * 4 <= GBYTES + XBYTES, "small-tile sums fit one stage buffer");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
     const int split = blockIdx.x;
@@ -94,6 +95,12 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
     const int st0 = split * a.per_split;
     const int st1 = min(a.stages, st0 + a.per_split);
     const int nst = st1 > st0 ? st1 - st0 : 0;
+    // A tile with at most 32 output and 32 input channels (a layer of 16 or 32 channels) has one
+    // 32x32 MFMA block of real outputs: all four consumer waves then compute that block, each
+    // over every fourth pixel of a stage, and their sums meet in LDS at the end (in wave order,
+    // so the result stays deterministic). Otherwise three waves would run padding only while one
+    // carried the stage's every MFMA.
+    const bool small = a.Cout - co4_0 * 4 <= 32 && a.Cin - ci4_0 * 4 <= 32;
 
     if (wave >= 4) {
         // ================= producer =================
@@ -249,6 +256,7 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
             __syncthreads();
         }
         if (c < nst) __syncthreads(); // last stage: nothing left to decode
+        if (small) __syncthreads();   // the consumers' cross-wave sum
         return;
     }
 
@@ -263,6 +271,49 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
     const int half = lane >> 5, l32 = lane & 31;
     const int loff = lds_row_off(l32, half);
     __syncthreads();
+    if (small) {
+        for (int c = 0; c < nst; ++c) {
+            const uint8_t *Gs = lds[c & 1], *Xs = lds[c & 1] + GBYTES;
+#pragma unroll
+            for (int ks = 0; ks < kKS; ++ks) {
+#pragma unroll
+                for (int i = 0; i < (kPWg + 3) / 4; ++i) {
+                    const int px = wave + 4 * i;
+                    if (px < kPWg) {
+                        const f16x8_t gf = __builtin_bit_cast(
+                            f16x8_t, *reinterpret_cast<const u32x4_t *>(
+                                         Gs + lds_row_off32((px * kKS + ks) * 64, loff)));
+#pragma unroll
+                        for (int t = 0; t < KWM; ++t)
+                            if (t < kw) {
+                                const f16x8_t xb = __builtin_bit_cast(
+                                    f16x8_t, *reinterpret_cast<const u32x4_t *>(
+                                                 Xs + lds_row_off32(((px * SI + t) * kKS + ks) * 64, loff)));
+                                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gf, xb, acc[t], 0, 0, 0);
+                            }
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        // the four waves' sums: waves 1-3 through LDS (the stage buffers are free after the last
+        // barrier), added by wave 0 in wave order
+        float *red = reinterpret_cast<float *>(&lds[0][0]);
+        if (wave > 0) {
+#pragma unroll
+            for (int t = 0; t < KWM; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) red[(((wave - 1) * KWM + t) * 16 + r) * 64 + lane] = acc[t][r];
+        }
+        __syncthreads();
+        if (wave != 0) return;
+#pragma unroll
+        for (int w = 0; w < 3; ++w)
+#pragma unroll
+            for (int t = 0; t < KWM; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[t][r] += red[((w * KWM + t) * 16 + r) * 64 + lane];
+    } else {
     for (int c = 0; c < nst; ++c) {
         const uint8_t *Gs = lds[c & 1], *Xs = lds[c & 1] + GBYTES;
 #pragma unroll
@@ -286,6 +337,7 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
             }
         }
         __syncthreads();
+    }
     }
 
     // ---- partial block part[split][kh*Kw + kw][co][ci], or (one split) G_W itself, scaled
