@@ -200,3 +200,31 @@ def test_noalloc_scratch_size_matches_binding():
     hdr = open(os.path.join(ROOT, "include", "mq.h")).read()
     m = re.search(r"#define MQ_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
     assert m and int(m.group(1)) << int(m.group(2)) == mq.MQ_NOALLOC_SCRATCH_BYTES
+
+
+def test_fused_amax_validation_without_gpu():
+    """mq_conv_fwd_amax and mq_conv_backward_amax reject a missing, short or misaligned amax
+    workspace, and the shape errors of the plain calls, on the host before any launch."""
+    L = mq.lib()
+    conv = mq.conv_struct((2, 16, 8, 8, 16, 3, 3, 1, 1, 0, 0))
+    x = _fake_q((8, 8, 16, 2))
+    w = _fake_q((3, 3, 16, 16), role=mq.MQ_ROLE_WEIGHT)
+    g = _fake_q((6, 6, 16, 2), role=mq.MQ_ROLE_GRAD)
+    y = ctypes.c_void_p(0x2000)
+    s0 = ctypes.c_void_p(0)
+    ws = mq.MQ_QUANTIZE_WS_BYTES
+    wgb = mq.mq_wgrad_workspace_bytes((2, 16, 8, 8, 16, 3, 3, 1, 1, 0, 0))
+    fa = lambda *a: L.mq_conv_fwd_amax(ctypes.byref(conv), *a, s0)
+    ba = lambda *a: L.mq_conv_backward_amax(ctypes.byref(conv), *a, s0)
+    X, W, G = ctypes.byref(x), ctypes.byref(w), ctypes.byref(g)
+    assert fa(X, W, y, None, ws) == mq.MQ_ERR_WORKSPACE
+    assert fa(X, W, y, y, ws - 4) == mq.MQ_ERR_WORKSPACE
+    assert fa(X, W, y, ctypes.c_void_p(0x3002), ws) == mq.MQ_ERR_ARG
+    assert fa(X, W, None, y, ws) == mq.MQ_ERR_ARG
+    assert fa(G, W, y, y, ws) == mq.MQ_ERR_SHAPE  # a gradient where X belongs
+    assert L.mq_conv_fwd_amax(None, X, W, y, y, ws, s0) == mq.MQ_ERR_ARG
+    assert ba(W, G, X, y, y, y, wgb, None, ws) == mq.MQ_ERR_WORKSPACE
+    assert ba(W, G, X, y, y, y, wgb, y, ws - 1) == mq.MQ_ERR_WORKSPACE
+    assert ba(W, G, X, y, y, y, wgb, ctypes.c_void_p(0x3002), ws) == mq.MQ_ERR_ARG
+    assert ba(W, G, X, y, y, None, wgb, y, ws) == mq.MQ_ERR_WORKSPACE  # split-K workspace
+    assert ba(X, G, X, y, y, y, wgb, y, ws) == mq.MQ_ERR_SHAPE
