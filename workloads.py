@@ -168,6 +168,42 @@ def config5() -> List[ConvLayer]:
     return out
 
 
+def random_layers(count: int = 40, seed: int = 2024) -> List[ConvLayer]:
+    """Seeded random layer shapes for a parity sweep: batches of 1-40 (so both the 16- and the
+    32-element batch tiles, ragged), 1-96 channels (partial row blocks and channel squares),
+    kernels 1x1 to 3x3 with unequal sides and now and then 4 or 5 (the generic kernel), strides
+    1-3 (now and then apart per axis), paddings below the kernel size and now and then equal to
+    it, NVFP4 or NVFP6, and every value
+    distribution. Each layer's GEMM stays below about 2*10^7 multiply-adds, so the CPU oracle
+    checks every output element in a fraction of a second."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out: List[ConvLayer] = []
+    dists = ["normal", "relu", "silu", "t3"]
+    while len(out) < count:
+        k = len(out)
+        N = int(rng.integers(1, 17) if rng.random() < 0.5 else rng.integers(17, 41))
+        Cin, Cout = (int(v) for v in rng.integers(1, 97, size=2))
+        if rng.random() < 0.15:
+            Kh = Kw = int(rng.integers(4, 6))
+        else:
+            Kh, Kw = (int(v) for v in rng.integers(1, 4, size=2))
+        sh, sw = (int(v) for v in rng.integers(1, 4, size=2)) if rng.random() < 0.15 else (
+            (int(rng.integers(1, 3)),) * 2)
+        ph = int(rng.integers(0, Kh + (1 if rng.random() < 0.1 else 0)))
+        pw = int(rng.integers(0, Kw + (1 if rng.random() < 0.1 else 0)))
+        H, W = (int(v) for v in rng.integers(1, 25, size=2))
+        Ho = (H + 2 * ph - Kh) // sh + 1
+        Wo = (W + 2 * pw - Kw) // sw + 1
+        if Ho < 1 or Wo < 1 or Cout * Cin * Kh * Kw * N * Ho * Wo > 20_000_000:
+            continue
+        out.append(ConvLayer(f"r{k:02d}", N=N, Cin=Cin, H=H, W=W, Cout=Cout, Kh=Kh, Kw=Kw,
+                             stride=sh, pad=ph, stride_w=sw, pad_w=pw,
+                             fmt=FP6 if rng.random() < 0.35 else FP4,
+                             x_dist=dists[int(rng.integers(0, 4))], seed=300 + k,
+                             sr_seed=int(rng.integers(1, 1 << 30))))
+    return out
+
+
 CONFIGS = {
     "c1": config1,
     "c2": config2,
