@@ -105,9 +105,18 @@ __device__ __forceinline__ uint32_t grid_sr(float a, uint32_t u16)
     constexpr int kL = FMT == kFP4 ? 1 : 3; // log2(kScale0) = log2(kAdd1)
     const int e = __builtin_amdgcn_frexp_expf(a);
     const int m = min(max(e, 1), 3);
-    const float x = __builtin_amdgcn_ldexpf(a, kL + 1 - m); // exact: a power-of-two scaling
-    const float y = __builtin_fmaf(-(float)u16, 0x1p-16f, x);
-    const uint32_t c = (uint32_t)__builtin_ceilf(y) + ((uint32_t)(m - 1) << kL);
+    const float nx = __builtin_amdgcn_ldexpf(-a, kL + 1 - m); // -x, exact
+    // z = RN(u - x) = -RN(x - u) (nearest rounding is symmetric), and ceil(x - u) = -floor(z):
+    // v_cvt_flr_i32_f32 takes the floor and the conversion in one instruction, where the
+    // compiler emits a ceiling and a conversion
+    const float z = __builtin_fmaf((float)u16, 0x1p-16f, nx);
+    int fl;
+    asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(fl) : "v"(z));
+    // the code offset of the binade in one shift-and-add (left to itself, the compiler
+    // reassociates the two subtractions into three instructions)
+    uint32_t base = ((uint32_t)m << kL) - (1u << kL);
+    asm("" : "+v"(base));
+    const uint32_t c = base - (uint32_t)fl;
     return c < F::kMaxMag ? c : F::kMaxMag;
 }
 

@@ -215,32 +215,45 @@ __device__ __forceinline__ uint32_t quantize_square(const float (&x)[16], float 
         // round-up draw). Nearest rounding sends every |q| below 2^-20 to a zero code of q's
         // sign, which the reciprocal form keeps, so there only D's range is checked.
         float q[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) q[e] = 0.0f; // zero scale: +0 codes
-        if (!zero) {
+        if (SR) {
+            // Only |q| is used (the code's sign is x's), and a zero scale's codes are cleared
+            // below whatever q holds, so the reciprocal form runs for those squares too.
             const float rD = 1.0f / D;
             const float Dlo = D * 0x1p-20f;
-            bool slow = !(D >= 0x1p-64f && D <= 0x1p64f);
-            if (SR) {
-                // some 0 < |x| < Dlo: on the bit patterns shifted left once (sign dropped), 2|x|-2
-                // wraps for |x| = 0, so its minimum over the square is below 2Dlo-2 exactly then
-                uint32_t mn = 0xFFFFFFFFu;
+            // some 0 < |x| < Dlo: on the bit patterns shifted left once (sign dropped), 2|x|-2
+            // wraps for |x| = 0, so its minimum over the square is below 2Dlo-2 exactly then
+            uint32_t mn = 0xFFFFFFFFu;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) mn = min(mn, (__float_as_uint(x[e]) << 1) - 2u);
-                slow |= mn < (__float_as_uint(Dlo) << 1) - 2u;
-            }
-            if (slow) {
+            for (int e = 0; e < 16; ++e) mn = min(mn, (__float_as_uint(x[e]) << 1) - 2u);
+            const bool slow = !(D >= 0x1p-64f && D <= 0x1p64f) || mn < (__float_as_uint(Dlo) << 1) - 2u;
+            if (slow && !zero) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) q[e] = x[e] / D; // IEEE division
             } else {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const float q0 = x[e] * rD;
-                    // x = -0 leaves q0 = -0 and a +0 residual, whose sum is +0: the sign of x is
-                    // put back (for every other x the quotient already carries it), so that
-                    // nearest rounding keeps the code's sign bit equal to x's
-                    q[e] = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, D, x[e]), rD, q0),
-                                               x[e]);
+                    q[e] = __builtin_fmaf(__builtin_fmaf(-q0, D, x[e]), rD, q0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) q[e] = 0.0f; // zero scale: +0 codes
+            if (!zero) {
+                const float rD = 1.0f / D;
+                if (!(D >= 0x1p-64f && D <= 0x1p64f)) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) q[e] = x[e] / D; // IEEE division
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const float q0 = x[e] * rD;
+                        // x = -0 leaves q0 = -0 and a +0 residual, whose sum is +0: the sign of
+                        // x is put back (for every other x the quotient already carries it), so
+                        // that nearest rounding keeps the code's sign bit equal to x's
+                        q[e] = __builtin_copysignf(
+                            __builtin_fmaf(__builtin_fmaf(-q0, D, x[e]), rD, q0), x[e]);
+                    }
                 }
             }
         }
@@ -413,13 +426,12 @@ __device__ __forceinline__ void cbf_body(const QuantArgs &a, uint32_t *red, int 
         }
         return;
     }
-    for (int t = t0; t < nsq; t += stride) {
-        float x[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = xn[e];
+    // One step: quantize square t from x while the next square's loads go into xnext. The
+    // loop is unrolled by two so that the two register sets trade roles instead of being copied.
+    auto step = [&](int t, const float (&x)[16], float (&xnext)[16]) {
         const bool more = t + stride < nsq;
         if (more) pos = advance(pos);
-        load(pos, xn); // the last step reloads its own square
+        load(pos, xnext); // the last step reloads its own square
         // The square's random bits do not depend on its values: drawn here, the Philox rounds
         // run while the square's loads are still in flight.
         Philox4 r0 = {}, r1 = {};
@@ -433,6 +445,12 @@ __device__ __forceinline__ void cbf_body(const QuantArgs &a, uint32_t *red, int 
         const uint32_t bcode = quantize_square<FMT, SR>(x, T, nonfinite, r0, r1, w);
         a.scales[t] = (uint8_t)bcode;
         store_square_codes<FMT>(a.codes, t, w);
+    };
+    float xm[16];
+    for (int t = t0; t < nsq; t += 2 * stride) {
+        step(t, xn, xm);
+        if (t + stride >= nsq) break;
+        step(t + stride, xm, xn);
     }
 }
 
