@@ -51,14 +51,6 @@ struct SpatialClass {
 // A compile-time count passed to a generic lambda.
 template <int V> struct IntC { static constexpr int value = V; };
 
-// LDS offset of row P*16 + r for a halo laid out in 16-row pixel slots (NB = 16), from
-// lane_off16 = lds_row_off(r, chunk), r < 16: the swizzle of lds_row_off takes bits 2 and 3 of
-// the row from r and bits 4-6 from P.
-__device__ __forceinline__ int lds_row_off16(int P, int lane_off16)
-{
-    return (P << 9) + (lane_off16 ^ (((P << 4) & 32) | (((P ^ (P >> 2)) & 1) << 6)));
-}
-
 // n / d for the multiplier m of d (see SpatialClass).
 __device__ __forceinline__ int div_by(int n, uint32_t m)
 {

@@ -26,6 +26,7 @@ namespace mq {
 namespace {
 
 constexpr int kRowBytes = 32; // 16 fp16 (one 16-element reduction step) per LDS row
+constexpr int kNPItems = 512;  // staging items per stage: one per producer lane
 
 struct WgradArgs {
     const uint8_t *g_codes, *g_scales; // squares [Ho][Wo][Cout4][N4]
@@ -51,35 +52,46 @@ struct WgradArgs {
 // Output pixels per stage: 16 / KS for stride 1, 8 / KS for stride 2 (twice as wide an X
 // segment), so that two stage buffers fit in LDS.
 // GL (the batch has a multiple of 16 elements, so every item is four real squares or none): the
-// stage width is chosen so that the stage has at most 512 items, one per producer lane (stride
-// 1: 7 pixels for KS = 2, 15 for KS = 1; stride 2: 5 and 10), so that no SIMD decodes more than
-// two items per stage. A wave may then hold G_Y and X items at once, so items are loaded through
-// per-lane global addresses instead of buffer descriptors.
-template <int SI, int KS, bool GL> struct StagePixels {
-    static constexpr int kPW = GL ? (SI == 1 ? (KS == 2 ? 7 : 15) : (KS == 2 ? 5 : 10))
-                                  : (SI == 1 ? 16 : 8) / KS;
-};
-inline int stage_pixels(int si, int ks, bool gl)
+// stage width is chosen so that the stage has at most 512 items, one per producer lane (with
+// 64-channel slots, stride 1: 7 pixels for KS = 2, 15 for KS = 1; stride 2: 5 and 10), so that
+// no SIMD decodes more than two items per stage. A wave may then hold G_Y and X items at once,
+// so items are loaded through per-lane global addresses instead of buffer descriptors.
+// SC: LDS rows per pixel (channel slots). 64 in general; a layer with at most 32 (16) input and
+// output channels takes 32-row (16-row) slots with GL, so that a stage carries two (four) times
+// the pixels for the same items and LDS, and each barrier, stage prologue and decode round
+// serves that much more MFMA work (with 64-row slots such a layer's stages were mostly fixed
+// costs). A 16-row slot is read as a 32-row MFMA operand whose rows 16-31 repeat rows 0-15:
+// those output rows and columns lie past the channels and are never written.
+__host__ __device__ constexpr int stage_pixels(int si, int ks, bool gl, int sc)
 {
-    return gl ? (si == 1 ? (ks == 2 ? 7 : 15) : (ks == 2 ? 5 : 10)) : (si == 1 ? 16 : 8) / ks;
+    return gl ? ((kNPItems / ((sc / 4) * ks)) - (3 - si)) / (1 + si) : (si == 1 ? 16 : 8) / ks;
 }
 // Producer threads: two waves per SIMD, so that one wave's decode overlaps the other's LDS
 // writes and load issue (one producer wave per SIMD left each stage producer-bound).
 constexpr int kNP = 512;
 constexpr int kWgradThreads = 256 + kNP;
+static_assert(kNP == kNPItems, "one staging item per producer lane");
 inline int stage_ks(int N4) { return N4 >= 8 ? 2 : 1; }
 inline bool stage_gl(int N4, int si) { return N4 % 4 == 0 && (si == 1 || si == 2); }
+inline int stage_sc(const ConvGeom &g)
+{
+    if (!stage_gl(g.N4, g.sh)) return 64;
+    const int c = g.Cout > g.Cin ? g.Cout : g.Cin;
+    return c <= 16 ? 16 : c <= 32 ? 32 : 64;
+}
 
 // KF: the kernel width Kw when fixed at compile time (1 or 3), 0 = read at run time.
-template <int FMT, int SI, int KF, int kKS, bool GL>
+template <int FMT, int SI, int KF, int kKS, bool GL, int SC>
 __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
 {
     warm_kernel_args<WgradArgs>();
-    constexpr int kPWg = StagePixels<SI, kKS, GL>::kPW;
+    static_assert(SC == 64 || (GL && (SC == 32 || SC == 16)), "narrow slots with GL only");
+    constexpr int kPWg = stage_pixels(SI, kKS, GL, SC);
     constexpr int KWM = KF ? KF : 3;
     constexpr int HCM = (kPWg - 1) * SI + KWM;
-    constexpr int GBYTES = kPWg * kKS * 64 * kRowBytes, XBYTES = HCM * kKS * 64 * kRowBytes;
-    constexpr int ITEMS = (kPWg * 16 * kKS + HCM * 16 * kKS + kNP - 1) / kNP;
+    constexpr int C4S = SC / 4; // channel squares per pixel slot
+    constexpr int GBYTES = kPWg * kKS * SC * kRowBytes, XBYTES = HCM * kKS * SC * kRowBytes;
+    constexpr int ITEMS = (kPWg * C4S * kKS + HCM * C4S * kKS + kNP - 1) / kNP;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][GBYTES + XBYTES];
     static_assert(3 * KWM * 16 * 64 * 4 <= GBYTES + XBYTES, "small-tile sums fit one stage buffer");
 
@@ -100,12 +112,12 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
     // over every fourth pixel of a stage, and their sums meet in LDS at the end (in wave order,
     // so the result stays deterministic). Otherwise three waves would run padding only while one
     // carried the stage's every MFMA.
-    const bool small = a.Cout - co4_0 * 4 <= 32 && a.Cin - ci4_0 * 4 <= 32;
+    const bool small = SC < 64 || (a.Cout - co4_0 * 4 <= 32 && a.Cin - ci4_0 * 4 <= 32);
 
     if (wave >= 4) {
         // ================= producer =================
         const int ptid = tid - 256;
-        const int nG = kPWg * 16 * kKS, nGX = nG + HC * 16 * kKS;
+        const int nG = kPWg * C4S * kKS, nGX = nG + HC * C4S * kKS;
         constexpr int CB = (FMT == kFP4) ? 8 : 12;
         const uint32_t g_sq = (uint32_t)a.Ho * a.Wo * a.Cout4 * a.N4;
         const uint32_t x_sq = (uint32_t)a.H * a.W * a.Cin4 * a.N4;
@@ -128,15 +140,17 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
         // channels and its arrays are fixed
         static_assert(!GL || ITEMS == 1, "one staging item per producer lane");
         constexpr int SHg = kKS == 2 ? 1 : 0;
+        constexpr int SHc = SC == 64 ? 4 : SC == 32 ? 3 : 2; // log2(C4S)
         const bool gl_isG = ptid < nG;
         const int gl_i2 = gl_isG ? ptid : ptid - nG;
-        const int gl_pix = gl_i2 >> (4 + SHg), gl_c4 = (gl_i2 >> SHg) & 15, gl_nh = gl_i2 & (kKS - 1);
+        const int gl_pix = gl_i2 >> (SHc + SHg), gl_c4 = (gl_i2 >> SHg) & (C4S - 1),
+                  gl_nh = gl_i2 & (kKS - 1);
         const bool gl_inv = ptid < nGX && (gl_isG ? co4_0 + gl_c4 < a.Cout4 : ci4_0 + gl_c4 < a.Cin4);
         const int gl_lsq = (gl_pix * (gl_isG ? a.Cout4 : a.Cin4) + (gl_isG ? co4_0 : ci4_0) + gl_c4) * a.N4 +
                            4 * gl_nh;
         const uint8_t *gl_cb = gl_isG ? a.g_codes : a.x_codes;
         const uint8_t *gl_sb = gl_isG ? a.g_scales : a.x_scales;
-        const int gl_row = (gl_pix * kKS + gl_nh) * 64 + 4 * gl_c4;
+        const int gl_row = (gl_pix * kKS + gl_nh) * SC + 4 * gl_c4;
         auto load = [&](int st, RawItem<FMT>(&dst)[ITEMS]) {
             const int nc = l_nc, ob = l_ob, oh = l_oh;
             if constexpr (GL) {
@@ -270,6 +284,13 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
         for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
     const int half = lane >> 5, l32 = lane & 31;
     const int loff = lds_row_off(l32, half);
+    // LDS offset of this lane's operand row in slot P (SC rows per slot; with 16-row slots,
+    // lanes 16-31 read rows 0-15 again)
+    const int loff16 = lds_row_off(l32 & 15, half);
+    auto slot = [&](int P) {
+        if constexpr (SC == 16) return lds_row_off16(P, loff16);
+        else return lds_row_off32(P * SC, loff);
+    };
     __syncthreads();
     if (small) {
         for (int c = 0; c < nst; ++c) {
@@ -282,13 +303,13 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
                     if (px < kPWg) {
                         const f16x8_t gf = __builtin_bit_cast(
                             f16x8_t, *reinterpret_cast<const u32x4_t *>(
-                                         Gs + lds_row_off32((px * kKS + ks) * 64, loff)));
+                                         Gs + slot(px * kKS + ks)));
 #pragma unroll
                         for (int t = 0; t < KWM; ++t)
                             if (t < kw) {
                                 const f16x8_t xb = __builtin_bit_cast(
                                     f16x8_t, *reinterpret_cast<const u32x4_t *>(
-                                                 Xs + lds_row_off32(((px * SI + t) * kKS + ks) * 64, loff)));
+                                                 Xs + slot((px * SI + t) * kKS + ks)));
                                 acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gf, xb, acc[t], 0, 0, 0);
                             }
                     }
@@ -307,13 +328,15 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
         }
         __syncthreads();
         if (wave != 0) return;
-#pragma unroll
+        // one wave's sums at a time (unrolled over the waves, the compiler loaded all three
+        // sets ahead of the additions and spilled)
+#pragma unroll 1
         for (int w = 0; w < 3; ++w)
 #pragma unroll
             for (int t = 0; t < KWM; ++t)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[t][r] += red[((w * KWM + t) * 16 + r) * 64 + lane];
-    } else {
+    } else if constexpr (SC == 64) {
     for (int c = 0; c < nst; ++c) {
         const uint8_t *Gs = lds[c & 1], *Xs = lds[c & 1] + GBYTES;
 #pragma unroll
@@ -380,7 +403,7 @@ Plan plan(const ConvGeom &g)
 {
     Plan p;
     const int ks = stage_ks(g.N4);
-    const int kPWg = stage_pixels(g.sh, ks, stage_gl(g.N4, g.sh));
+    const int kPWg = stage_pixels(g.sh, ks, stage_gl(g.N4, g.sh), stage_sc(g));
     p.owb = (g.Wo + kPWg - 1) / kPWg;
     p.nch = (g.N4 + 4 * ks - 1) / (4 * ks);
     p.stages = g.Ho * p.owb * p.nch;
@@ -434,28 +457,31 @@ bool wgrad_fast_supported(const ConvGeom &g)
 
 size_t wgrad_fast_workspace_bytes(const ConvGeom &g) { return plan(g).bytes; }
 
-template <int FMT, int SI, int KS, bool GL>
+template <int FMT, int SI, int KS, bool GL, int SC>
 static void launch_wgrad_ks(const ConvGeom &g, dim3 grid, const WgradArgs &a, hipStream_t st)
 {
     if (g.Kw == 3)
-        hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 3, KS, GL>), grid, dim3(kWgradThreads), 0, st, a);
+        hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 3, KS, GL, SC>), grid, dim3(kWgradThreads), 0, st, a);
     else if (g.Kw == 1)
-        hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 1, KS, GL>), grid, dim3(kWgradThreads), 0, st, a);
-    else hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 0, KS, GL>), grid, dim3(kWgradThreads), 0, st, a);
+        hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 1, KS, GL, SC>), grid, dim3(kWgradThreads), 0, st, a);
+    else hipLaunchKernelGGL((conv_wgrad_kernel<FMT, SI, 0, KS, GL, SC>), grid, dim3(kWgradThreads), 0, st, a);
+}
+
+template <int FMT, int SI, int KS>
+static void launch_wgrad_gl(const ConvGeom &g, dim3 grid, const WgradArgs &a, hipStream_t st)
+{
+    const int sc = stage_sc(g); // below 64 with GL only
+    if (sc == 16) launch_wgrad_ks<FMT, SI, KS, true, 16>(g, grid, a, st);
+    else if (sc == 32) launch_wgrad_ks<FMT, SI, KS, true, 32>(g, grid, a, st);
+    else if (stage_gl(g.N4, SI)) launch_wgrad_ks<FMT, SI, KS, true, 64>(g, grid, a, st);
+    else launch_wgrad_ks<FMT, SI, KS, false, 64>(g, grid, a, st);
 }
 
 template <int FMT, int SI>
 static void launch_wgrad_si(const ConvGeom &g, dim3 grid, const WgradArgs &a, hipStream_t st)
 {
-    constexpr bool kGL = true;
-    const bool gl = stage_gl(g.N4, SI);
-    if (stage_ks(g.N4) == 2) {
-        if (gl) launch_wgrad_ks<FMT, SI, 2, kGL>(g, grid, a, st);
-        else launch_wgrad_ks<FMT, SI, 2, false>(g, grid, a, st);
-    } else {
-        if (gl) launch_wgrad_ks<FMT, SI, 1, kGL>(g, grid, a, st);
-        else launch_wgrad_ks<FMT, SI, 1, false>(g, grid, a, st);
-    }
+    if (stage_ks(g.N4) == 2) launch_wgrad_gl<FMT, SI, 2>(g, grid, a, st);
+    else launch_wgrad_gl<FMT, SI, 1>(g, grid, a, st);
 }
 
 template <int FMT>

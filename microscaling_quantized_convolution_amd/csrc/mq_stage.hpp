@@ -150,6 +150,14 @@ __device__ __forceinline__ int lds_row_off32(int R, int lane_off)
     return (R << 5) + (lane_off ^ (R & 96));
 }
 
+// LDS offset of row P*16 + r for operands laid out in 16-row slots (a pixel of a 16-batch halo,
+// or of a layer with at most 16 channels), from lane_off16 = lds_row_off(r, chunk), r < 16: the
+// swizzle of lds_row_off takes bits 2 and 3 of the row from r and bits 4-6 from P.
+__device__ __forceinline__ int lds_row_off16(int P, int lane_off16)
+{
+    return (P << 9) + (lane_off16 ^ (((P << 4) & 32) | (((P ^ (P >> 2)) & 1) << 6)));
+}
+
 // The hardware hands workgroups to the 8 XCDs in turn (linear id mod 8), and each XCD has an L2
 // of its own. A launch renumbers its P workgroups so that the XCD running linear id n holds a
 // contiguous range of numbers: the first P8 = P - P % 8 ids map to (n mod 8) * P8 / 8 + n / 8,
