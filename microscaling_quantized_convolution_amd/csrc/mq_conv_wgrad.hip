@@ -297,21 +297,51 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
             const uint8_t *Gs = lds[c & 1], *Xs = lds[c & 1] + GBYTES;
 #pragma unroll
             for (int ks = 0; ks < kKS; ++ks) {
+                if constexpr (SC == 16) {
+                    // Two pixels per MFMA: lanes 0-15 carry pixel 2j (operand rows and columns
+                    // 0-15), lanes 16-31 pixel 2j + 1 (rows and columns 16-31), so the two
+                    // diagonal 16x16 blocks of the product are the two pixels' terms (the others
+                    // are cross terms, never used). A pair past the stage's last pixel reads an
+                    // in-range slot with a zero G_Y operand.
+                    constexpr int NPAIR = (kPWg + 1) / 2;
+                    const int hi = l32 >> 4;
 #pragma unroll
-                for (int i = 0; i < (kPWg + 3) / 4; ++i) {
-                    const int px = wave + 4 * i;
-                    if (px < kPWg) {
-                        const f16x8_t gf = __builtin_bit_cast(
-                            f16x8_t, *reinterpret_cast<const u32x4_t *>(
-                                         Gs + slot(px * kKS + ks)));
+                    for (int i = 0; i < (NPAIR + 3) / 4; ++i) {
+                        const int j = wave + 4 * i;
+                        if (j < NPAIR) {
+                            const int pxl = 2 * j + hi;
+                            const bool real = pxl < kPWg;
+                            const int px = real ? pxl : 2 * j;
+                            u32x4_t gu = *reinterpret_cast<const u32x4_t *>(Gs + slot(px * kKS + ks));
+                            if (!real) gu = u32x4_t{0u, 0u, 0u, 0u};
+                            const f16x8_t gf = __builtin_bit_cast(f16x8_t, gu);
 #pragma unroll
-                        for (int t = 0; t < KWM; ++t)
-                            if (t < kw) {
-                                const f16x8_t xb = __builtin_bit_cast(
-                                    f16x8_t, *reinterpret_cast<const u32x4_t *>(
-                                                 Xs + slot((px * SI + t) * kKS + ks)));
-                                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gf, xb, acc[t], 0, 0, 0);
-                            }
+                            for (int t = 0; t < KWM; ++t)
+                                if (t < kw) {
+                                    const f16x8_t xb = __builtin_bit_cast(
+                                        f16x8_t, *reinterpret_cast<const u32x4_t *>(
+                                                     Xs + slot((px * SI + t) * kKS + ks)));
+                                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gf, xb, acc[t], 0, 0, 0);
+                                }
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < (kPWg + 3) / 4; ++i) {
+                        const int px = wave + 4 * i;
+                        if (px < kPWg) {
+                            const f16x8_t gf = __builtin_bit_cast(
+                                f16x8_t, *reinterpret_cast<const u32x4_t *>(
+                                             Gs + slot(px * kKS + ks)));
+#pragma unroll
+                            for (int t = 0; t < KWM; ++t)
+                                if (t < kw) {
+                                    const f16x8_t xb = __builtin_bit_cast(
+                                        f16x8_t, *reinterpret_cast<const u32x4_t *>(
+                                                     Xs + slot((px * SI + t) * kKS + ks)));
+                                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(gf, xb, acc[t], 0, 0, 0);
+                                }
+                        }
                     }
                 }
             }
@@ -336,6 +366,14 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
             for (int t = 0; t < KWM; ++t)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[t][r] += red[((w * KWM + t) * 16 + r) * 64 + lane];
+        if constexpr (SC == 16) {
+            // the second pixel's block (rows and columns 16-31: lane l32 + 16, registers 8-15)
+            // onto the first's (rows and columns 0-15, which the epilogue writes)
+#pragma unroll
+            for (int t = 0; t < KWM; ++t)
+#pragma unroll
+                for (int r = 0; r < 8; ++r) acc[t][r] += __shfl_down(acc[t][r + 8], 16);
+        }
     } else if constexpr (SC == 64) {
     for (int c = 0; c < nst; ++c) {
         const uint8_t *Gs = lds[c & 1], *Xs = lds[c & 1] + GBYTES;

@@ -278,4 +278,13 @@ def parity_layers() -> List[ConvLayer]:
                   x_dist="silu", seed=124, sr_seed=30),
         ConvLayer("p.b16.w23.fp6", N=16, Cin=36, H=13, W=23, Cout=72, Kh=3, Kw=3, stride=1,
                   pad=1, fmt=FP6, x_dist="relu", seed=125, sr_seed=31),
+        # at most 16 channels on both sides and whole 16-element batch groups: the weight
+        # gradient's 16-row slots with two pixels per MFMA, for 32-element stages at stride 1
+        # and 2 and 16-element stages at stride 2, each over several ragged pixel blocks
+        ConvLayer("p.b32.c16", N=32, Cin=12, H=19, W=71, Cout=16, Kh=3, Kw=3, stride=1, pad=1,
+                  x_dist="relu", seed=126, sr_seed=32),
+        ConvLayer("p.b48.c16.s2.fp6", N=48, Cin=8, H=17, W=91, Cout=16, Kh=3, Kw=3, stride=2,
+                  pad=1, fmt=FP6, x_dist="normal", seed=127, sr_seed=33),
+        ConvLayer("p.b16.c16.s2.fp6", N=16, Cin=16, H=21, W=101, Cout=12, Kh=3, Kw=3, stride=2,
+                  pad=1, fmt=FP6, x_dist="silu", seed=128, sr_seed=34),
     ]
