@@ -455,6 +455,12 @@ conv_spatial_kernel(SpatialArgs a)
         const int i = i0 + wr;
         const int n = NB == 32 ? nb * 32 + l32 : nb * 16 + (l32 & 15);
         const bool full_m = 4 * m4_0 + 64 <= a.M;
+        // Copies of the store loop for the scale's two forms and for whether the item's 64
+        // rows all lie inside M, chosen by wave-uniform branches: with one loop the compiler
+        // computed both scale forms for every element (double conversions and multiply, then a
+        // select) and tested every element's row, most of the epilogue's instructions.
+        auto epilogue = [&](auto fs, auto fm) {
+        constexpr bool FS = decltype(fs)::value != 0, FM = decltype(fm)::value != 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int jj = j0 + wp * PPW + (NB == 32 ? j : 2 * j + h16);
@@ -478,10 +484,10 @@ conv_spatial_kernel(SpatialArgs a)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     // stores whose eight rows all lie past M are not issued (wave-uniform)
-                    if (NB == 16 && !full_m && mrow0 + 8 * (r >> 2) >= a.M) continue;
+                    if (NB == 16 && !FM && mrow0 + 8 * (r >> 2) >= a.M) continue;
                     const int dm = 8 * (r >> 2) + (r & 3);
-                    const float v = fsafe ? acc[u][j][r] * sf : (float)((double)acc[u][j][r] * sd);
-                    const uint32_t voff = (full_m || mrow + dm < a.M) ? vbase : kBad;
+                    const float v = FS ? acc[u][j][r] * sf : (float)((double)acc[u][j][r] * sd);
+                    const uint32_t voff = (FM || mrow + dm < a.M) ? vbase : kBad;
                     // non-temporal: the output is not read again by this pass (streaming writes
                     // measured ~10% faster than cached ones for this write-bound epilogue)
                     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), out_r,
@@ -489,6 +495,10 @@ conv_spatial_kernel(SpatialArgs a)
                 }
             }
         }
+        };
+        if (fsafe && full_m) epilogue(IntC<1>{}, IntC<1>{});
+        else if (fsafe) epilogue(IntC<1>{}, IntC<0>{});
+        else epilogue(IntC<0>{}, IntC<0>{});
     }
     if (a.amax_ws) {
         // this workgroup's partial: the waves' maxima meet in LDS (the producers pass the same
