@@ -17,6 +17,8 @@
 // 32 x 32 x Kw block. The fp32 partial block goes to the workspace, and a second kernel sums the
 // splits in a fixed order (deterministic) and applies the tensor scales. A reduction that is not
 // split (one split) writes G_W itself, scaled, with no partial block and no sum.
+#include <type_traits>
+
 #include "mq_kernels.hpp"
 #include "mq_stage.hpp"
 #include "mq_wgrad_sum.hpp"
@@ -403,20 +405,27 @@ __global__ void __launch_bounds__(kWgradThreads) conv_wgrad_kernel(WgradArgs a)
 
     // ---- partial block part[split][kh*Kw + kw][co][ci], or (one split) G_W itself, scaled
     // as the split sum scales a sum of one partial: (float)(acc * (double)T_G * T_X) ----
-    float *out = a.direct ? a.gw : a.part + (int64_t)split * a.split_stride;
-    const double sc = a.direct ? (double)*a.tg * (double)*a.tx : 1.0;
+    // (a copy per form, chosen by a wave-uniform branch: with one loop the compiler computed the
+    // scaled form for every partial too)
     const int ci = ci4_0 * 4 + wc * 32 + l32;
+    auto write = [&](auto direct) {
+        constexpr bool D = decltype(direct)::value != 0;
+        float *out = D ? a.gw : a.part + (int64_t)split * a.split_stride;
+        const double sc = D ? (double)*a.tg * (double)*a.tx : 1.0;
 #pragma unroll
-    for (int t = 0; t < KWM; ++t) {
-        if (t >= kw) continue;
-        float *o = out + (int64_t)(kh * kw + t) * a.Cout * a.Cin;
+        for (int t = 0; t < KWM; ++t) {
+            if (t >= kw) continue;
+            float *o = out + (int64_t)(kh * kw + t) * a.Cout * a.Cin;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int co = co4_0 * 4 + wm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            const float v = a.direct ? (float)((double)acc[t][r] * sc) : acc[t][r];
-            if (co < a.Cout && ci < a.Cin) o[(int64_t)co * a.Cin + ci] = v;
+            for (int r = 0; r < 16; ++r) {
+                const int co = co4_0 * 4 + wm * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                const float v = D ? (float)((double)acc[t][r] * sc) : acc[t][r];
+                if (co < a.Cout && ci < a.Cin) o[(int64_t)co * a.Cin + ci] = v;
+            }
         }
-    }
+    };
+    if (a.direct) write(std::integral_constant<int, 1>{});
+    else write(std::integral_constant<int, 0>{});
 }
 
 // The split sum as a kernel of its own: blocks grid-stride over the 256-lane workgroups (a
