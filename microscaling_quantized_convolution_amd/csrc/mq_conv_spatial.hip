@@ -117,6 +117,9 @@ conv_spatial_kernel(SpatialArgs a)
     constexpr int WCOLS = (NB == 32 ? 3 : 6) * SI + KWM;
     constexpr int HPI = NB / 4; // halo items per pixel: 4 channel squares x NB / 16 batch groups
     constexpr int ABYTES = KHM * KWM * 64 * 32, BBYTES = HRM * HCM * NB * 32;
+    // producer register stages: a chunk's loads are issued RS chunk steps before its decode
+    // (three or four stages measured no faster on any layer here)
+    constexpr int RS = 2;
     // items: weight (tap, m4) in [0, nA), halo (pixel, n4) in [nA64, nA64 + nB); nA64 rounds nA
     // up to whole waves so that no wave runs both item kinds in one slot
     constexpr int ITEMS = ((KHM * KWM * 16 + 63) / 64 * 64 + HRM * HCM * HPI + NP - 1) / NP;
@@ -246,12 +249,12 @@ conv_spatial_kernel(SpatialArgs a)
                 row[q] = hp * NB + 16 * g;
             }
         }
-        // Two register stages: chunk g + 3 of the stream is loaded into the slot chunk g + 1 was
-        // just decoded from, so every load has two stage times to arrive. Loads are issued
+        // RS register stages: chunk c + RS of the stream is loaded into the slot chunk c was
+        // just decoded from, so every load has RS stage times to arrive. Loads are issued
         // without branches, the same number per stage (a chunk past the end loads nothing:
-        // mask 0), and the loop is unrolled by two so that slots are never copied: the
+        // mask 0), and the loop is unrolled by RS so that slots are never copied: the
         // compiler's wait before a decode then covers exactly that chunk's loads.
-        RawItem<FMT> raw[2][ITEMS];
+        RawItem<FMT> raw[RS][ITEMS];
         // Per slot: first square of an item's chunk 0 and its static validity, for the item
         // `p`. With one item per workgroup it is set once; in the persistent case it is
         // recomputed for every load (without a branch: a branch here makes the compiler wait for
@@ -289,7 +292,7 @@ conv_spatial_kernel(SpatialArgs a)
         // the item and chunk of the next load (loads go through the stream in order)
         int lp_nb = first.nb, lp_tj = first.tj, lp_ti = first.ti, lp_mb = first.mb;
         int lc = 0;
-        auto load = [&](int gs, RawItem<FMT>(&dst)[ITEMS]) {
+        auto plan = [&](int gs, ItemPlan(&pl)[ITEMS]) {
             const bool valid = gs < G;
             int c = gs;
             uint32_t sqb[ITEMS], vm[ITEMS];
@@ -316,9 +319,20 @@ conv_spatial_kernel(SpatialArgs a)
                 const uint32_t sq0 = sqb[q] + (uint32_t)c * sq_chunk[q];
                 const bool kin = 4 * c + kcl_of[q] < a.K4;
                 const uint32_t m = (isA && !A_KR) ? (vm[q] & kmask) : (kin ? vm[q] : 0u);
-                load_item_contig<FMT>(dst[q], isA ? w_c : in_c, isA ? w_s : in_s, sq0,
-                                      valid ? m : 0u);
+                pl[q] = plan_item<FMT>(sq0, valid ? m : 0u);
             }
+        };
+        auto issue = [&](const ItemPlan(&pl)[ITEMS], RawItem<FMT>(&dst)[ITEMS]) {
+#pragma unroll
+            for (int q = 0; q < ITEMS; ++q) {
+                const bool isA = wave_uniform((ptid + q * NP) & ~63) < nA64;
+                issue_item<FMT>(dst[q], isA ? w_c : in_c, isA ? w_s : in_s, pl[q]);
+            }
+        };
+        auto load = [&](int gs, RawItem<FMT>(&dst)[ITEMS]) {
+            ItemPlan pl[ITEMS];
+            plan(gs, pl);
+            issue(pl, dst);
         };
         auto store = [&](int buf, const RawItem<FMT>(&src)[ITEMS]) {
 #pragma unroll
@@ -335,24 +349,39 @@ conv_spatial_kernel(SpatialArgs a)
                 }
             }
         };
-        // chunk 0 alone first (issued together with chunk 1, it landed about 0.4 us later);
-        // then step g: decode chunk g + 1 from slot (g + 1) & 1 into LDS buffer (g + 1) & 1,
-        // then load chunk g + 3 into that slot
-        load(0, raw[0]);
-        store(0, raw[0]);
-        load(1, raw[1]);
-        load(2, raw[0]);
-        __syncthreads();
-        int gs = 0;
-        for (; gs + 1 < G; gs += 2) {
-            store(1, raw[1]);
-            load(gs + 3, raw[1]);
-            __syncthreads();
-            if (gs + 2 < G) store(0, raw[0]);
-            load(gs + 4, raw[0]);
-            __syncthreads();
+        // Step c = 0 .. G: decode chunk c from slot c % RS into LDS buffer c & 1 (chunk G does
+        // not exist: the last step only waits), load chunk c + RS into that slot, and meet the
+        // consumers (step 0's barrier is their first; at step c >= 1 they have just finished
+        // chunk c - 1). The steps run in whole groups of RS, ending with empty steps that the
+        // consumers match with barriers of their own after their last item. The loop then has a single
+        // way back to its head, and the prologue only loads chunks 0 .. RS - 1, so the loop head
+        // sees the same loads in flight from both sides (a step group left early made the
+        // compiler wait there for every load in flight).
+        //
+        // The loads stay in chunk order and take their offsets from a plan made before the
+        // decode: scheduling fences keep the compiler from interleaving two chunks' loads or
+        // computing offsets into registers whose loads are still in flight. Either made its wait
+        // before a decode cover the next chunk's loads too, which emptied the pipeline.
+#pragma unroll
+        for (int s = 0; s < RS; ++s) {
+            __builtin_amdgcn_sched_barrier(0);
+            load(s, raw[s]);
         }
-        if (gs < G) __syncthreads(); // last chunk: nothing left to decode
+        __builtin_amdgcn_sched_barrier(0);
+        for (int c0 = 0; c0 <= G; c0 += RS) {
+#pragma unroll
+            for (int s = 0; s < RS; ++s) {
+                const int c = c0 + s;
+                ItemPlan pl[ITEMS];
+                plan(c + RS, pl);
+                __builtin_amdgcn_sched_barrier(0);
+                if (c < G) store(c & 1, raw[s]);
+                __builtin_amdgcn_sched_barrier(0);
+                issue(pl, raw[s]);
+                __builtin_amdgcn_sched_barrier(0);
+                __syncthreads();
+            }
+        }
         if (a.amax_ws) __syncthreads(); // the consumers' output-amax reduction
         return;
     }
@@ -500,6 +529,8 @@ conv_spatial_kernel(SpatialArgs a)
         else if (fsafe) epilogue(IntC<1>{}, IntC<0>{});
         else epilogue(IntC<0>{}, IntC<0>{});
     }
+    // the producer's steps past chunk G, in whole groups of its register stages
+    for (int c = G + 1; c % RS != 0; ++c) __syncthreads();
     if (a.amax_ws) {
         // this workgroup's partial: the waves' maxima meet in LDS (the producers pass the same
         // barrier), scaled as the outputs were

@@ -102,6 +102,45 @@ __device__ __forceinline__ void load_item_contig(RawItem<FMT> &r, rsrc_t codes, 
     r.m = mask | ((sq0 & 3u) << 8);
 }
 
+// load_item_contig in two steps: the offsets and mask of an item (plan_item), then its loads
+// (issue_item). A caller that plans the next chunk's loads before decoding the current one
+// leaves the loads nothing to compute, so the compiler takes no register that a load still in
+// flight will write as a temporary for them (such a reuse made it wait for loads of later
+// chunks too).
+struct ItemPlan {
+    uint32_t coff, soff, m;
+};
+template <int FMT>
+__device__ __forceinline__ ItemPlan plan_item(uint32_t sq0, uint32_t mask)
+{
+    ItemPlan p;
+    p.coff = mask ? sq0 * (uint32_t)(RawItem<FMT>::kW * 4) : kBad;
+    p.soff = mask ? (sq0 & ~3u) : kBad;
+    p.m = mask | ((sq0 & 3u) << 8);
+    return p;
+}
+template <int FMT>
+__device__ __forceinline__ void issue_item(RawItem<FMT> &r, rsrc_t codes, rsrc_t scales,
+                                           const ItemPlan &p)
+{
+    const u32x4_t v0 = __builtin_amdgcn_raw_buffer_load_b128(codes, (int)p.coff, 0, 0);
+    const u32x4_t v1 = __builtin_amdgcn_raw_buffer_load_b128(codes, (int)(p.coff + 16u), 0, 0);
+    if constexpr (FMT == kFP4) {
+        r.w[0][0] = v0[0]; r.w[0][1] = v0[1]; r.w[1][0] = v0[2]; r.w[1][1] = v0[3];
+        r.w[2][0] = v1[0]; r.w[2][1] = v1[1]; r.w[3][0] = v1[2]; r.w[3][1] = v1[3];
+    } else {
+        const u32x4_t v2 = __builtin_amdgcn_raw_buffer_load_b128(codes, (int)(p.coff + 32u), 0, 0);
+        r.w[0][0] = v0[0]; r.w[0][1] = v0[1]; r.w[0][2] = v0[2];
+        r.w[1][0] = v0[3]; r.w[1][1] = v1[0]; r.w[1][2] = v1[1];
+        r.w[2][0] = v1[2]; r.w[2][1] = v1[3]; r.w[2][2] = v2[0];
+        r.w[3][0] = v2[1]; r.w[3][1] = v2[2]; r.w[3][2] = v2[3];
+    }
+    // (an item outside the tensor has soff = kBad; kBad + 4 is out of range too)
+    r.sc = __builtin_amdgcn_raw_buffer_load_b32(scales, (int)p.soff, 0, 0);
+    r.sh = __builtin_amdgcn_raw_buffer_load_b32(scales, (int)(p.soff + 4u), 0, 0);
+    r.m = p.m;
+}
+
 // The four squares' scales as fp16 (squares 0,1 in sc[0], 2,3 in sc[1]); a square whose bit of
 // the item mask is clear gets scale 0, so it decodes to zeros whatever codes were loaded.
 template <int FMT>
