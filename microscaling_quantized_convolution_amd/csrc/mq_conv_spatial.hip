@@ -409,6 +409,27 @@ conv_spatial_kernel(SpatialArgs a)
     // the non-negative scale is monotonic). Padded rows and batch columns hold exact zeros, so
     // only whole pixels outside the output are left out.
     uint32_t amx = 0u;
+    // Deferred output blocks (persistent launches of 64-row waves and 32-batch items): of an
+    // item with a next item, whose rows and batch block are whole, the wave's last DB 32 x 32
+    // blocks (u = MW - 1, j = 4 - DB .. 3) are scaled into an LDS area of the wave's own and
+    // written during the next item's first chunks, 16 bytes per lane, under its MFMAs, instead
+    // of in the store burst that every workgroup of the launch runs at the same moment.
+    constexpr int DB = (PERSIST && NB == 32 && MW == 2) ? 2 : 0;
+    __shared__ __attribute__((aligned(16))) float dstage[DB ? NCW : 1][DB ? DB : 1][32 * 32];
+    uint32_t dvoff[DB ? DB : 1]; // per deferred block: the byte offset of this lane's first piece
+    bool dpend = false;          // deferred blocks wait to be written (wave-uniform)
+    // a lane's 16-byte piece of a block: row drow + 8 * pass, batch columns dcol .. dcol + 3
+    const int drow = lane >> 3, dcol = 4 * (lane & 7);
+    auto flush = [&](auto bc) {
+        constexpr int B = decltype(bc)::value;
+#pragma unroll
+        for (int pass = 0; pass < 4; ++pass) {
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(
+                &dstage[wave][B][(drow + 8 * pass) * 32 + dcol]);
+            __builtin_amdgcn_raw_buffer_store_b128(v, out_r, (int)dvoff[B], pass * 8 * a.N * 4,
+                                                   kStoreNT);
+        }
+    };
     __syncthreads();
     int gc = 0; // chunk of the stream: LDS buffer gc & 1
     ItemPos cp = first;
@@ -427,6 +448,11 @@ conv_spatial_kernel(SpatialArgs a)
         auto chunks = [&](auto un) {
             constexpr int UN = decltype(un)::value;
             for (int c = 0; c < nchunk; ++c, ++gc) {
+                if constexpr (DB > 0) {
+                    // the previous item's deferred blocks, one per chunk
+                    if (dpend && c == 0) flush(IntC<0>{});
+                    if (dpend && c == 1) flush(IntC<1>{});
+                }
                 const uint8_t *As = lds[gc & 1], *Bs = lds[gc & 1] + ABYTES;
 #pragma unroll
                 for (int th = 0; th < KHM; ++th) {
@@ -475,6 +501,12 @@ conv_spatial_kernel(SpatialArgs a)
         };
         if constexpr (NB == 32) {
             chunks(IntC<MW>{}); // batch blocks of 32 compute every row block (one loop copy)
+            if constexpr (DB > 0) {
+                // deferred blocks the chunks did not take (an item of one chunk)
+                if (dpend && nchunk < 1) flush(IntC<0>{});
+                if (dpend && nchunk < 2) flush(IntC<1>{});
+                dpend = false;
+            }
         } else {
             if (rows_left > 32 * (MW - 1)) chunks(IntC<MW>{});
             else if (rows_left > 0) chunks(IntC<1>{});
@@ -484,6 +516,9 @@ conv_spatial_kernel(SpatialArgs a)
         const int i = i0 + wr;
         const int n = NB == 32 ? nb * 32 + l32 : nb * 16 + (l32 & 15);
         const bool full_m = 4 * m4_0 + 64 <= a.M;
+        // (deferred blocks: the FS/FM copy below, for whole batch blocks of 16-byte rows)
+        const bool defer = DB > 0 && k + 1 < nmine && fsafe && full_m && nb * 32 + 32 <= a.N &&
+                           (a.N & 3) == 0;
         // Copies of the store loop for the scale's two forms and for whether the item's 64
         // rows all lie inside M, chosen by wave-uniform branches: with one loop the compiler
         // computed both scale forms for every element (double conversions and multiply, then a
@@ -507,6 +542,19 @@ conv_spatial_kernel(SpatialArgs a)
             for (int u = 0; u < MW; ++u) {
                 const int mrow0 = 4 * m4_0 + 32 * (wm * MW + u); // wave-uniform
                 if (NB == 16 && mrow0 >= a.M) continue;          // a block of padding rows
+                if constexpr (DB > 0 && FS && FM) {
+                    if (u == MW - 1 && j >= 4 - DB && defer) {
+                        const int B = j - (4 - DB); // (a constant once the j loop unrolls)
+                        float *dst = dstage[wave][B];
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            dst[(4 * half + 8 * (r >> 2) + (r & 3)) * 32 + l32] = acc[u][j][r] * sf;
+                        dvoff[B] = pix_in ? ((((uint32_t)oh * a.OWf + ow) * a.M + mrow0 + drow) * a.N +
+                                             nb * 32 + dcol) * 4u
+                                          : kBad;
+                        continue;
+                    }
+                }
                 const int mrow = mrow0 + 4 * half;
                 const uint32_t vbase =
                     pix_ok ? ((((uint32_t)oh * a.OWf + ow) * a.M + mrow) * a.N + n) * 4u : kBad;
@@ -528,6 +576,7 @@ conv_spatial_kernel(SpatialArgs a)
         if (fsafe && full_m) epilogue(IntC<1>{}, IntC<1>{});
         else if (fsafe) epilogue(IntC<1>{}, IntC<0>{});
         else epilogue(IntC<0>{}, IntC<0>{});
+        if constexpr (DB > 0) dpend = defer;
     }
     // the producer's steps past chunk G, in whole groups of its register stages
     for (int c = G + 1; c % RS != 0; ++c) __syncthreads();
