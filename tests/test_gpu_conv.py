@@ -19,7 +19,7 @@ from gpu_parity import (check_layer, log, oracle_layer, run_gpu_layer, run_layer
 
 pytestmark = pytest.mark.gpu
 
-SMALL = workloads.config1() + workloads.parity_layers()
+SMALL = workloads.config1() + workloads.parity_layers() + workloads.persistent_layers()
 
 
 @pytest.mark.parametrize("layer", SMALL, ids=lambda l: l.name)

@@ -213,6 +213,21 @@ CONFIGS = {
 }
 
 
+def persistent_layers() -> List[ConvLayer]:
+    """Layers with enough 64-row, 2 x 8 pixel, 32-batch work items for the persistent forward and
+    input-gradient launches (at least 640), whose items are not all whole: a ragged last batch
+    block (36 elements) and an output row block partly past the channels (80 output channels).
+    The outputs of whole items partly leave through LDS under the next item's MFMAs; these
+    layers put whole and partial items in one launch.
+    """
+    return [
+        ConvLayer("q.b36.80x64", N=36, Cin=64, H=80, W=64, Cout=64, Kh=3, Kw=3, stride=1, pad=1,
+                  x_dist="relu", seed=131, sr_seed=35),
+        ConvLayer("q.m80.80x64", N=32, Cin=16, H=80, W=64, Cout=80, Kh=3, Kw=3, stride=1, pad=1,
+                  x_dist="normal", seed=132, sr_seed=36),
+    ]
+
+
 def parity_layers() -> List[ConvLayer]:
     """Mid-sized layers that span several kernel tiles with ragged tails everywhere.
 
