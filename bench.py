@@ -117,6 +117,9 @@ def parse(argv=None):
     ap.add_argument("--summarize-trace", metavar="TRACE_DB",
                     help="print a kernel-trace summary (per kernel and launch shape) from a "
                          "rocprofv3 --kernel-trace database")
+    ap.add_argument("--summarize-stalls", nargs=3, metavar=("DB_A", "DB_B", "DB_C"),
+                    help="print wave waiting, LDS and MFMA shares per convolution kernel from three "
+                         "rocprofv3 --pmc databases (the counter sets are in summarize_stalls)")
     ap.add_argument("--summarize-mfma", metavar="DB",
                     help="print MFMA busy and MFMA op counts per kernel from a rocprofv3 --pmc "
                          "database of SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_F16, "
@@ -248,6 +251,9 @@ def main(argv=None):
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma)
+        return
+    if args.summarize_stalls:
+        summarize_stalls(*args.summarize_stalls)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the hot path here is single-device; "
@@ -732,6 +738,58 @@ def summarize_mfma(db: str):
     for _, k, n, us, b, act, util, gf, tf in sorted(rows):
         print(f"| `{k.replace('(anonymous namespace)::', '')[:130]}` | {n} | {us:.2f} | {b:.3e} | "
               f"{act:.3e} | {util:.3f} | {gf:.3f} | {tf:.1f} | {tf / MFMA_PEAK_TFLOPS:.3f} |")
+
+
+# the three counter passes of summarize_stalls (at most 8 SQ counters and GRBM_GUI_ACTIVE each)
+STALL_COUNTERS = (
+    ["SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_LDS",
+     "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_UNALIGNED_STALL",
+     "SQ_LDS_DATA_FIFO_FULL", "GRBM_GUI_ACTIVE"],
+    ["SQ_INSTS_LDS_LOAD", "SQ_INSTS_LDS_STORE", "SQ_INSTS_LDS_LOAD_BANDWIDTH",
+     "SQ_INSTS_LDS_STORE_BANDWIDTH", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_MISC", "SQ_WAIT_ANY",
+     "SQ_LDS_ADDR_CONFLICT", "GRBM_GUI_ACTIVE"],
+    ["SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY",
+     "SQ_INST_LEVEL_LDS", "SQ_ACTIVE_INST_VMEM", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"],
+)
+
+
+def summarize_stalls(db_a: str, db_b: str, db_c: str):
+    """Per convolution kernel and grid, from three rocprofv3 --pmc runs of STALL_COUNTERS:
+    MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs' active cycles, as summarize_mfma);
+    the share of wave-cycles spent waiting on any dependency (SQ_WAIT_ANY / SQ_WAVE_CYCLES) and
+    waiting to issue an LDS instruction (SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES); LDS bank-conflict
+    cycles over LDS indexed-active cycles; and SQ_LDS_IDX_ACTIVE over 256 CUs' active cycles (the
+    LDS's busy share per CU, read as a sum over the CUs)."""
+    vals = collections_dd()
+    for db, cs in zip((db_a, db_b, db_c), STALL_COUNTERS):
+        for c, d in _pmc_per_kernel(db, cs, by_grid=True).items():
+            for k, (v, n) in d.items():
+                vals[k][c if c != "GRBM_GUI_ACTIVE" else c + db] = v
+                vals[k]["n"] = n
+    print(f"kernel_sources_sha256: {kernel_source_hash()}")
+    print()
+    print("| kernel (workgroups x lanes) | dispatches | MFMA busy | waves waiting | waiting on LDS "
+          "issue | LDS bank conflicts / LDS active | LDS active per CU |")
+    print("|---|---|---|---|---|---|---|")
+    for k in sorted(vals):
+        v = vals[k]
+        if "conv_" not in k or not v.get("SQ_WAVE_CYCLES"):
+            continue
+        act = v.get("GRBM_GUI_ACTIVE" + db_c, 0.0) / 8
+        act_a = v.get("GRBM_GUI_ACTIVE" + db_a, 0.0) / 8
+        mfma = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (act * 1024) if act else 0.0
+        wait = v.get("SQ_WAIT_ANY", 0.0) / v["SQ_WAVE_CYCLES"]
+        wlds = v.get("SQ_WAIT_INST_LDS", 0.0) / v["SQ_WAVE_CYCLES"]
+        lact = v.get("SQ_LDS_IDX_ACTIVE", 0.0)
+        bc = v.get("SQ_LDS_BANK_CONFLICT", 0.0) / lact if lact else 0.0
+        lcu = lact / (act_a * 256) if act_a else 0.0
+        print(f"| `{k.replace('(anonymous namespace)::', '')[:130]}` | {v['n']} | {mfma:.3f} | "
+              f"{wait:.3f} | {wlds:.3f} | {bc:.4f} | {lcu:.3f} |")
+
+
+def collections_dd():
+    import collections
+    return collections.defaultdict(dict)
 
 
 if __name__ == "__main__":
