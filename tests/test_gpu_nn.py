@@ -101,3 +101,40 @@ def test_resnet18_training_step_small():
     assert all(np.isfinite(losses))
     assert all(not torch.equal(b, c.weight) for b, c in zip(before, model.mq_convs))
     assert [c.step for c in model.mq_convs] == [3] * 19
+
+
+def test_each_tensor_quantized_once_per_step(monkeypatch):
+    """One training step of a layer quantizes X and W once (one batched call) and G_Y once (one
+    call), and both gradient GEMMs read those same quantized tensors: nothing is re-quantized
+    between the GEMMs that share an operand (the quantize-once premise of the method)."""
+    from microscaling_quantized_convolution_amd import nn as mqnn
+    calls = []
+
+    def wrap(name):
+        real = getattr(mqnn, name)
+
+        def rec(*args):
+            calls.append((name, args))
+            return real(*args)
+        monkeypatch.setattr(mqnn, name, rec)
+
+    for name in ("quant_job", "mq_quantize_batch", "mq_quantize_nchw", "mq_quantize_weight",
+                 "mq_conv_fwd", "mq_conv_backward", "mq_conv_wgrad", "mq_conv_dgrad"):
+        wrap(name)
+    layer = workloads.parity_layers()[0]
+    x, w, g = workloads.make_tensors(layer)
+    xt = torch.from_numpy(x).cuda().requires_grad_(True)
+    wt = torch.from_numpy(w).cuda().requires_grad_(True)
+    y = MQConv2dFunction.apply(xt, wt, layer.stride, layer.pad, layer.fmt, layer.sr_seed, None)
+    y.backward(torch.from_numpy(g).cuda())
+    torch.cuda.synchronize()
+    names = [c[0] for c in calls]
+    assert names == ["quant_job", "quant_job", "mq_quantize_batch", "mq_conv_fwd",
+                     "mq_quantize_nchw", "mq_conv_backward"]
+    assert len(calls[2][1][0]) == 2          # the batch holds the two jobs
+    qx, qw = calls[0][1][2], calls[1][1][2]  # quant_job(src, order, dst, ...): X, then W
+    _, fqx, fqw, _ = calls[3][1]             # conv_fwd(conv, qx, qw, y)
+    _, qg, _, _, _ = calls[4][1]             # quantize_nchw(gy, qg, rounding, seed, ws)
+    _, bqw, bqg, bqx, _, _, _ = calls[5][1]  # conv_backward(conv, qw, qg, qx, gw, gx, ws)
+    assert fqx is qx and fqw is qw
+    assert bqw is qw and bqx is qx and bqg is qg
