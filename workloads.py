@@ -218,13 +218,16 @@ def persistent_layers() -> List[ConvLayer]:
     input-gradient launches (at least 640), whose items are not all whole: a ragged last batch
     block (36 elements) and an output row block partly past the channels (80 output channels).
     The outputs of whole items partly leave through LDS under the next item's MFMAs; these
-    layers put whole and partial items in one launch.
+    layers put whole and partial items in one launch. The third is NVFP6, with whole items only
+    in its forward launch.
     """
     return [
         ConvLayer("q.b36.80x64", N=36, Cin=64, H=80, W=64, Cout=64, Kh=3, Kw=3, stride=1, pad=1,
                   x_dist="relu", seed=131, sr_seed=35),
         ConvLayer("q.m80.80x64", N=32, Cin=16, H=80, W=64, Cout=80, Kh=3, Kw=3, stride=1, pad=1,
                   x_dist="normal", seed=132, sr_seed=36),
+        ConvLayer("q.fp6.80x64", N=64, Cin=32, H=80, W=64, Cout=64, Kh=3, Kw=3, stride=1, pad=1,
+                  fmt=FP6, x_dist="silu", seed=133, sr_seed=37),
     ]
 
 
